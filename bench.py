@@ -1,0 +1,214 @@
+"""Throughput of the CLSA decode step on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config 3] [--gpus 1]
+
+One step = routing scores over the whole shared cache + top-k once + all L layers of sparse
+attention over the selection (clsa_step, layer-batched), on inputs already resident in HBM.
+Prints one JSON line.  ``value`` is decoded tokens/s of the whole step (B tokens per step).
+``roofline`` covers the dominant kernel (the routing-score stream over K_idx), timed live with
+HIP events on the launch stream; ``cpu_baseline`` times the fp64 oracle on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+HBM_PEAK_GBPS = 8000.0
+METRIC = "decode tokens/sec + HBM GB/s (% roofline), index+top-k+L-layer attn at 128K"
+INDEX_KERNEL_SOURCES = ["cross_layer_token_amd/csrc/k_index.hip", "cross_layer_token_amd/csrc/device_common.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_index_scores_decode_b16_n128k.json")
+
+
+def algorithmic_bytes(w) -> dict:
+    """Bytes the method must move per decode step: the K_idx scan once, each selected K and V row
+    once, the queries and outputs of every layer, and the index output."""
+    kidx = q_idx = kv = qo = idx = 0
+    row_kv = 2 * w.hkv * w.head_dim  # one token's K (or V) row, bytes
+    for n in w.seq_lens:
+        m = min(w.topk, n)
+        kidx += 2 * w.d_idx * n
+        q_idx += 2 * w.d_idx
+        kv += 2 * row_kv * m
+        idx += 4 * m
+    qo = 2 * 2 * w.batch * w.n_layers * w.hq * w.head_dim
+    return {"k_idx": kidx, "q_idx": q_idx, "kv_selected": kv, "q_and_out": qo, "indices": idx,
+            "total": kidx + q_idx + kv + qo + idx}
+
+
+def index_kernel_sha() -> str:
+    h = hashlib.sha256()
+    for p in INDEX_KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(bytes_alg_launch: float):
+    """HBM bytes per launch of the score kernel from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source; otherwise None."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha") != index_kernel_sha():
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s: float) -> dict:
+    """The fp64 oracle on host cores (one thread), over whole decode rows until the budget is used.
+    Input regeneration is excluded from the timed part; scores, top-k and attention are timed."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import clsa_oracle as O
+    cu = w.cu_seqlens
+    t_oracle = 0.0
+    rows = 0
+    wall0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        for r in range(w.n_rows):
+            n = w.row_len(r)
+            qi = w.q_idx_f64([r])[0]
+            ki = w.k_idx_f64(cu[r] + np.arange(n))
+            ql = w.q_f64([r])[0]
+            t0 = time.perf_counter()
+            sel = O.topk_select(O.index_scores(qi, ki), w.topk)
+            t1 = time.perf_counter()
+            kf, vf = w.kv_f64(cu[r] + sel)
+            t2 = time.perf_counter()
+            O.sparse_attention(ql, kf, vf)
+            t3 = time.perf_counter()
+            t_oracle += (t1 - t0) + (t3 - t2)
+            rows += 1
+            if time.perf_counter() - wall0 > budget_s:
+                break
+    return {"value": rows / t_oracle, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{rows} of {w.n_rows} decode rows of {w.name} (scores+top-k+{w.n_layers}-layer attention, "
+                      f"fp64 numpy, 1 thread; input regeneration not timed); oracle time {t_oracle:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of wall time for the oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-per-layer", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import clsa_synth as cs
+    import cross_layer_token_amd as clsa
+    from clsa_synth.device import DeviceWorkload
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    w = cs.config(args.config, args.seed)
+    if w.mode != "decode":
+        print("bench.py times the decode step; the prefill workload is covered by the tests", file=sys.stderr)
+        sys.exit(2)
+    dw = DeviceWorkload(w)
+    dims = clsa.make_dims(**dw.dims())
+    rows = clsa.make_rows(**dw.rows())
+    R, k = w.n_rows, w.topk
+    out = torch.empty((R, w.n_layers, w.hq, 128), dtype=torch.int16, device="cuda")
+    idx = torch.empty((R, k), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((R,), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def run_steps(n, schedule, ws, nws):
+        for _ in range(n):
+            clsa.step(dims, rows, dw.q_idx, dw.k_idx, dw.k_cache, dw.v_cache, dw.cu_seqlens, dw.q, out, idx, cnt, ws,
+                      nws, schedule=schedule, stream=stream)
+
+    def timed(fn, n):
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        fn(n)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return ev0.elapsed_time(ev1) / 1e3, wall
+
+    # ---- the step (layer-batched schedule) ------------------------------------------------------
+    nws = clsa.workspace_bytes(dims, rows, clsa.SCHEDULE_LAYER_BATCHED)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    run_steps(args.warmup, clsa.SCHEDULE_LAYER_BATCHED, ws, nws)
+    t_gpu, t_wall = timed(lambda n: run_steps(n, clsa.SCHEDULE_LAYER_BATCHED, ws, nws), args.steps)
+    t_step = t_wall / args.steps
+    balg = algorithmic_bytes(w)
+    hbm_gbps = balg["total"] / t_step / 1e9
+
+    # ---- the dominant kernel alone: routing scores streamed from K_idx --------------------------
+    ld = ((w.max_row_len + 63) // 64) * 64
+    scores = torch.empty((R, ld), dtype=torch.float32, device="cuda")
+
+    def run_scores(n):
+        for _ in range(n):
+            clsa.index_scores(dims, rows, dw.q_idx, dw.k_idx, dw.cu_seqlens, scores, ld, stream=stream)
+
+    run_scores(args.warmup)
+    t_idx, _ = timed(run_scores, args.steps)
+    t_idx /= args.steps
+    idx_bytes = balg["k_idx"] + balg["q_idx"] + 4 * w.total_tokens   # K_idx + q_idx read, scores written
+    achieved = idx_bytes / t_idx / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(idx_bytes),
+                "kernel": "k_index_scores_decode<128>", "bytes_per_launch": idx_bytes,
+                "us_per_launch": round(t_idx * 1e6, 2)}
+
+    # ---- dependent-layer schedule (one attention pass per layer), reported beside -----------------
+    per_layer = None
+    if not args.no_per_layer:
+        nws2 = clsa.workspace_bytes(dims, rows, clsa.SCHEDULE_PER_LAYER)
+        ws2 = torch.empty(nws2, dtype=torch.uint8, device="cuda")
+        run_steps(args.warmup, clsa.SCHEDULE_PER_LAYER, ws2, nws2)
+        t2, w2 = timed(lambda n: run_steps(n, clsa.SCHEDULE_PER_LAYER, ws2, nws2), args.steps)
+        per_layer = {"ms_per_step": round(w2 / args.steps * 1e3, 4), "tokens_per_s": round(R * args.steps / w2, 1),
+                     "hbm_gbps_alg": round(balg["total"] / (w2 / args.steps) / 1e9, 1)}
+        del ws2
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_budget)
+    line = {
+        "metric": METRIC,
+        "value": round(R * args.steps / t_wall, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_step * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "context": w.max_row_len, "d_idx": w.d_idx,
+                   "topk": w.topk, "layers": w.n_layers, "hq": w.hq, "hkv": w.hkv, "head_dim": w.head_dim,
+                   "schedule": "layer_batched", "seed": w.seed},
+        "hbm_gbps": round(hbm_gbps, 1),
+        "step_roofline_frac": round(hbm_gbps / HBM_PEAK_GBPS, 4),
+        "bytes_alg_per_step": balg["total"],
+        "gpu_event_ms_per_step": round(t_gpu / args.steps * 1e3, 4),
+        "roofline": roofline,
+        "per_layer_schedule": per_layer,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,276 @@
+// The C ABI of include/clsa.h: validate on the host, then enqueue the kernels on the stream.
+#include <cstring>
+#include <string>
+
+#include "clsa_internal.h"
+
+using namespace clsa;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+clsa_status set_error(clsa_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+// Every check writes its message into g_err; CLSA_TRY forwards it to the thread-local slot.
+#define CLSA_TRY(expr)                              \
+  do {                                              \
+    const clsa_status _s = (expr);                  \
+    if (_s != CLSA_OK) return set_error(_s, g_err); \
+  } while (0)
+
+thread_local std::string g_err;
+
+clsa_status device_status(int err, const char* what) {
+  if (err == 0) return CLSA_OK;
+  return set_error(CLSA_ERR_DEVICE, std::string(what) + ": " + device_error_string(err));
+}
+
+RowsDev rows_dev(const clsa_rows* r, const int32_t* cu) {
+  RowsDev d;
+  d.mode = r->mode;
+  d.n_rows = r->n_rows;
+  d.seq = r->seq;
+  d.pos0 = r->pos0;
+  d.max_row_len = r->max_row_len;
+  d.cu = cu;
+  return d;
+}
+
+clsa_status check_common(const clsa_dims* dims, const clsa_rows* rows) {
+  CLSA_TRY(check_dims(dims, g_err));
+  CLSA_TRY(check_rows(dims, rows, g_err));
+  return CLSA_OK;
+}
+
+clsa_status check_ld(int64_t ld, const clsa_rows* rows, const char* name) {
+  if (ld < rows->max_row_len) return set_error(CLSA_ERR_INVALID_ARGUMENT, std::string(name) + " < rows.max_row_len");
+  if (ld % 4 != 0) return set_error(CLSA_ERR_INVALID_ARGUMENT, std::string(name) + " must be a multiple of 4");
+  return CLSA_OK;
+}
+
+clsa_status check_workspace(void* ws, size_t have, size_t need) {
+  if (need == 0) return CLSA_OK;
+  if (ws == nullptr || have < need)
+    return set_error(CLSA_ERR_WORKSPACE, "workspace of " + std::to_string(have) + " bytes given, " +
+                                             std::to_string(need) + " needed");
+  if (reinterpret_cast<uintptr_t>(ws) % 256 != 0)
+    return set_error(CLSA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  return CLSA_OK;
+}
+
+clsa_status check_attn_strides(const clsa_dims* d, int lc, int64_t q_stride, int64_t o_stride) {
+  const int64_t need = (int64_t)lc * d->hq * CLSA_HEAD_DIM;
+  if (q_stride < need || o_stride < need)
+    return set_error(CLSA_ERR_INVALID_ARGUMENT, "row stride smaller than n_layers_call * hq * 128");
+  if (q_stride % 8 != 0 || o_stride % 8 != 0)
+    return set_error(CLSA_ERR_INVALID_ARGUMENT, "row strides must be multiples of 8 elements");
+  return CLSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* clsa_status_string(clsa_status s) {
+  switch (s) {
+    case CLSA_OK: return "CLSA_OK";
+    case CLSA_ERR_INVALID_ARGUMENT: return "CLSA_ERR_INVALID_ARGUMENT";
+    case CLSA_ERR_UNSUPPORTED: return "CLSA_ERR_UNSUPPORTED";
+    case CLSA_ERR_WORKSPACE: return "CLSA_ERR_WORKSPACE";
+    case CLSA_ERR_DEVICE: return "CLSA_ERR_DEVICE";
+  }
+  return "CLSA_STATUS_UNKNOWN";
+}
+
+const char* clsa_last_error_message(void) { return g_last_error.c_str(); }
+
+int32_t clsa_abi_version(void) { return CLSA_ABI_VERSION; }
+
+size_t clsa_workspace_bytes(const clsa_dims* dims, const clsa_rows* rows, int32_t schedule) {
+  if (check_common(dims, rows) != CLSA_OK) return 0;
+  if (schedule != CLSA_SCHEDULE_LAYER_BATCHED && schedule != CLSA_SCHEDULE_PER_LAYER) {
+    set_error(CLSA_ERR_INVALID_ARGUMENT, "unknown schedule");
+    return 0;
+  }
+  return workspace_bytes(dims, rows, schedule);
+}
+
+clsa_status clsa_index_scores(const clsa_dims* dims, const clsa_rows* rows, const clsa_bf16* q_idx,
+                              const clsa_bf16* k_idx, const int32_t* cu_seqlens, float* scores, int64_t ld_scores,
+                              clsa_stream stream) {
+  g_last_error.clear();
+  CLSA_TRY(check_common(dims, rows));
+  CLSA_TRY(check_ptr(q_idx, "q_idx", g_err));
+  CLSA_TRY(check_ptr(k_idx, "k_idx", g_err));
+  CLSA_TRY(check_ptr(cu_seqlens, "cu_seqlens", g_err));
+  CLSA_TRY(check_ptr(scores, "scores", g_err));
+  if (clsa_status s = check_ld(ld_scores, rows, "ld_scores"); s != CLSA_OK) return s;
+  const RowsDev rd = rows_dev(rows, cu_seqlens);
+  int e;
+  if (rows->mode == CLSA_MODE_DECODE)
+    e = launch_index_scores_decode(rd, dims->d_idx, rows->total_tokens, q_idx, k_idx, scores, ld_scores, stream);
+  else
+    e = launch_index_scores_prefill(rd, dims->d_idx, q_idx, k_idx, scores, ld_scores, stream);
+  return device_status(e, "clsa_index_scores");
+}
+
+clsa_status clsa_topk(const clsa_dims* dims, const clsa_rows* rows, const int32_t* cu_seqlens, const float* scores,
+                      int64_t ld_scores, int32_t* idx, int32_t* count, void* workspace, size_t workspace_bytes_,
+                      clsa_stream stream) {
+  g_last_error.clear();
+  CLSA_TRY(check_common(dims, rows));
+  CLSA_TRY(check_ptr(cu_seqlens, "cu_seqlens", g_err));
+  CLSA_TRY(check_ptr(scores, "scores", g_err));
+  CLSA_TRY(check_ptr(idx, "idx", g_err));
+  CLSA_TRY(check_ptr(count, "count", g_err));
+  if (clsa_status s = check_ld(ld_scores, rows, "ld_scores"); s != CLSA_OK) return s;
+  const TopkPlan plan = plan_topk(dims, rows);
+  if (clsa_status s = check_workspace(workspace, workspace_bytes_, plan.bytes); s != CLSA_OK) return s;
+  const RowsDev rd = rows_dev(rows, cu_seqlens);
+  return device_status(launch_topk(rd, dims->topk, plan, scores, ld_scores, idx, count, workspace, stream),
+                       "clsa_topk");
+}
+
+clsa_status clsa_gather_kv(const clsa_dims* dims, const clsa_rows* rows, const clsa_bf16* k_cache,
+                           const clsa_bf16* v_cache, const int32_t* cu_seqlens, const int32_t* idx,
+                           const int32_t* count, clsa_bf16* k_sel, clsa_bf16* v_sel, clsa_stream stream) {
+  g_last_error.clear();
+  CLSA_TRY(check_common(dims, rows));
+  CLSA_TRY(check_ptr(k_cache, "k_cache", g_err));
+  CLSA_TRY(check_ptr(v_cache, "v_cache", g_err));
+  CLSA_TRY(check_ptr(cu_seqlens, "cu_seqlens", g_err));
+  CLSA_TRY(check_ptr(idx, "idx", g_err));
+  CLSA_TRY(check_ptr(count, "count", g_err));
+  CLSA_TRY(check_ptr(k_sel, "k_sel", g_err));
+  CLSA_TRY(check_ptr(v_sel, "v_sel", g_err));
+  const RowsDev rd = rows_dev(rows, cu_seqlens);
+  return device_status(
+      launch_gather(rd, dims->topk, dims->hkv, k_cache, v_cache, idx, count, k_sel, v_sel, stream), "clsa_gather_kv");
+}
+
+clsa_status clsa_sparse_attn(const clsa_dims* dims, const clsa_rows* rows, const clsa_bf16* q, int64_t q_row_stride,
+                             int32_t n_layers_call, const clsa_bf16* k_sel, const clsa_bf16* v_sel,
+                             const clsa_bf16* k_cache, const clsa_bf16* v_cache, const int32_t* cu_seqlens,
+                             const int32_t* idx, const int32_t* count, clsa_bf16* out, int64_t out_row_stride,
+                             void* workspace, size_t workspace_bytes_, clsa_stream stream) {
+  g_last_error.clear();
+  CLSA_TRY(check_common(dims, rows));
+  if (n_layers_call < 1 || n_layers_call > dims->n_layers)
+    return set_error(CLSA_ERR_UNSUPPORTED, "n_layers_call must be in [1, n_layers]");
+  CLSA_TRY(check_ptr(q, "q", g_err));
+  CLSA_TRY(check_ptr(out, "out", g_err));
+  CLSA_TRY(check_ptr(count, "count", g_err));
+  CLSA_TRY(check_ptr(cu_seqlens, "cu_seqlens", g_err));
+  const bool compact = k_sel != nullptr || v_sel != nullptr;
+  if (compact) {
+    CLSA_TRY(check_ptr(k_sel, "k_sel", g_err));
+    CLSA_TRY(check_ptr(v_sel, "v_sel", g_err));
+  } else {
+    CLSA_TRY(check_ptr(k_cache, "k_cache", g_err));
+    CLSA_TRY(check_ptr(v_cache, "v_cache", g_err));
+    CLSA_TRY(check_ptr(idx, "idx", g_err));
+  }
+  if (clsa_status s = check_attn_strides(dims, n_layers_call, q_row_stride, out_row_stride); s != CLSA_OK) return s;
+  const AttnPlan plan = plan_attn(dims, rows->n_rows, n_layers_call);
+  if (clsa_status s = check_workspace(workspace, workspace_bytes_, plan.part_bytes); s != CLSA_OK) return s;
+  const RowsDev rd = rows_dev(rows, cu_seqlens);
+  return device_status(launch_attn(rd, dims->topk, dims->hq, dims->hkv, n_layers_call, softmax_scale(dims), plan, q,
+                                   q_row_stride, compact ? k_sel : nullptr, compact ? v_sel : nullptr, k_cache,
+                                   v_cache, idx, count, out, out_row_stride, workspace, stream),
+                       "clsa_sparse_attn");
+}
+
+clsa_status clsa_step(const clsa_dims* dims, const clsa_rows* rows, const clsa_step_args* a, void* workspace,
+                      size_t workspace_bytes_, clsa_stream stream) {
+  g_last_error.clear();
+  CLSA_TRY(check_common(dims, rows));
+  if (a == nullptr) return set_error(CLSA_ERR_INVALID_ARGUMENT, "args is NULL");
+  if (a->schedule != CLSA_SCHEDULE_LAYER_BATCHED && a->schedule != CLSA_SCHEDULE_PER_LAYER)
+    return set_error(CLSA_ERR_INVALID_ARGUMENT, "unknown schedule");
+  if (a->prefill_chunk_rows < 0) return set_error(CLSA_ERR_INVALID_ARGUMENT, "prefill_chunk_rows must be >= 0");
+  CLSA_TRY(check_ptr(a->q_idx, "q_idx", g_err));
+  CLSA_TRY(check_ptr(a->k_idx, "k_idx", g_err));
+  CLSA_TRY(check_ptr(a->k_cache, "k_cache", g_err));
+  CLSA_TRY(check_ptr(a->v_cache, "v_cache", g_err));
+  CLSA_TRY(check_ptr(a->cu_seqlens, "cu_seqlens", g_err));
+  CLSA_TRY(check_ptr(a->q, "q", g_err));
+  CLSA_TRY(check_ptr(a->out, "out", g_err));
+  CLSA_TRY(check_ptr(a->idx, "idx", g_err));
+  CLSA_TRY(check_ptr(a->count, "count", g_err));
+  CLSA_TRY(check_ptr_opt(a->scores, "scores", g_err));
+  CLSA_TRY(check_ptr_opt(a->k_sel, "k_sel", g_err));
+  CLSA_TRY(check_ptr_opt(a->v_sel, "v_sel", g_err));
+  if ((a->k_sel == nullptr) != (a->v_sel == nullptr))
+    return set_error(CLSA_ERR_INVALID_ARGUMENT, "k_sel and v_sel must both be given or both be NULL");
+  if (a->scores != nullptr)
+    if (clsa_status s = check_ld(a->ld_scores, rows, "ld_scores"); s != CLSA_OK) return s;
+  const bool prefill = rows->mode == CLSA_MODE_PREFILL;
+  const StepPlan sp = plan_step(dims, rows, a->schedule, a->scores != nullptr, a->k_sel != nullptr,
+                                a->prefill_chunk_rows);
+  if (clsa_status s = check_workspace(workspace, workspace_bytes_, sp.total); s != CLSA_OK) return s;
+
+  char* ws = static_cast<char*>(workspace);
+  const int L = dims->n_layers, hq = dims->hq, hkv = dims->hkv, k = dims->topk;
+  const int64_t row_elems = (int64_t)L * hq * CLSA_HEAD_DIM;
+  const float scale = softmax_scale(dims);
+  const int chunk = sp.chunk_rows;
+  for (int c0 = 0; c0 < rows->n_rows; c0 += chunk) {
+    clsa_rows cr = *rows;
+    cr.n_rows = rows->n_rows - c0 < chunk ? rows->n_rows - c0 : chunk;
+    if (prefill) {
+      cr.pos0 = rows->pos0 + c0;
+      cr.max_row_len = cr.pos0 + cr.n_rows;
+    }
+    const RowsDev rd = rows_dev(&cr, a->cu_seqlens);
+    float* scores;
+    int64_t ld;
+    if (a->scores != nullptr) {
+      scores = a->scores + (int64_t)c0 * a->ld_scores;
+      ld = a->ld_scores;
+    } else {
+      scores = reinterpret_cast<float*>(ws + sp.scores_off);
+      ld = sp.ld_scores;
+    }
+    const clsa_bf16* q_idx = a->q_idx + (int64_t)c0 * dims->d_idx;
+    int e = prefill ? launch_index_scores_prefill(rd, dims->d_idx, q_idx, a->k_idx, scores, ld, stream)
+                    : launch_index_scores_decode(rd, dims->d_idx, rows->total_tokens, q_idx, a->k_idx, scores, ld,
+                                                 stream);
+    if (e) return device_status(e, "clsa_step: index scores");
+    int32_t* idx = a->idx + (int64_t)c0 * k;
+    int32_t* count = a->count + c0;
+    const TopkPlan tp = plan_topk(dims, &cr);
+    e = launch_topk(rd, k, tp, scores, ld, idx, count, ws + sp.topk_off, stream);
+    if (e) return device_status(e, "clsa_step: top-k");
+    const clsa_bf16* q = a->q + (int64_t)c0 * row_elems;
+    clsa_bf16* out = a->out + (int64_t)c0 * row_elems;
+    if (a->schedule == CLSA_SCHEDULE_LAYER_BATCHED) {
+      const AttnPlan ap = plan_attn(dims, cr.n_rows, L);
+      e = launch_attn(rd, k, hq, hkv, L, scale, ap, q, row_elems, nullptr, nullptr, a->k_cache, a->v_cache, idx, count,
+                      out, row_elems, ws + sp.part_off, stream);
+      if (e) return device_status(e, "clsa_step: attention");
+    } else {
+      const AttnPlan ap = plan_attn(dims, cr.n_rows, 1);
+      clsa_bf16* ksel = nullptr;
+      clsa_bf16* vsel = nullptr;
+      if (!prefill) {
+        ksel = a->k_sel ? a->k_sel : reinterpret_cast<clsa_bf16*>(ws + sp.ksel_off);
+        vsel = a->v_sel ? a->v_sel : reinterpret_cast<clsa_bf16*>(ws + sp.vsel_off);
+        e = launch_gather(rd, k, hkv, a->k_cache, a->v_cache, idx, count, ksel, vsel, stream);
+        if (e) return device_status(e, "clsa_step: gather");
+      }
+      for (int l = 0; l < L; ++l) {
+        e = launch_attn(rd, k, hq, hkv, 1, scale, ap, q + (int64_t)l * hq * CLSA_HEAD_DIM, row_elems, ksel, vsel,
+                        a->k_cache, a->v_cache, idx, count, out + (int64_t)l * hq * CLSA_HEAD_DIM, row_elems,
+                        ws + sp.part_off, stream);
+        if (e) return device_status(e, "clsa_step: attention layer");
+      }
+    }
+  }
+  return CLSA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,99 @@
+// Device helpers shared by the CLSA kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "clsa_internal.h"
+
+namespace clsa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// fp32 -> bf16 round-to-nearest-even (inputs here are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16(float x) {
+  uint32_t u = __float_as_uint(x);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Order-preserving map of a score to an unsigned key: a larger score gives a larger key.
+// -0.0 is mapped like +0.0 so that the two compare equal.
+__device__ __forceinline__ uint32_t score_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ int row_seq(const RowsDev& rw, int r) { return rw.mode == CLSA_MODE_DECODE ? r : rw.seq; }
+
+// Tokens row r sees, clamped to the host bound so that no write leaves the caller's buffers.
+__device__ __forceinline__ int row_len(const RowsDev& rw, int r) {
+  if (rw.mode == CLSA_MODE_DECODE) {
+    const int n = rw.cu[r + 1] - rw.cu[r];
+    return n < 0 ? 0 : (n > rw.max_row_len ? rw.max_row_len : n);
+  }
+  return rw.pos0 + r + 1;
+}
+
+// 16-byte streaming load that is not expected to be reused (non-temporal hint).
+__device__ __forceinline__ uint4 load_stream16(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+template <typename T>
+__device__ __forceinline__ T bitcast(const uint4& v) {
+  return __builtin_bit_cast(T, v);
+}
+
+// DPP lane exchange inside rows of 16 lanes.  The pairing partner of each step has the
+// opposite bit `M` of the lane id and the same higher bits (8: rotate by 8; 4: mirror inside
+// half-rows; 2 and 1: quad permutes).
+template <int M>
+__device__ __forceinline__ float dpp_partner(float v) {
+  int x = __float_as_int(v);
+  if constexpr (M == 8) x = __builtin_amdgcn_update_dpp(0, x, 0x128, 0xF, 0xF, false);       // row_ror:8
+  else if constexpr (M == 4) x = __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false);  // row_half_mirror
+  else if constexpr (M == 2) x = __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);   // quad_perm 2,3,0,1
+  else x = __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false);                          // quad_perm 1,0,3,2
+  return __int_as_float(x);
+}
+
+// Block-wide exclusive scan of one int per thread (blockDim.x a multiple of 64, <= 1024).
+// `scratch` holds at least blockDim.x / 64 + 1 ints.  Returns the exclusive prefix and sets
+// *total.  Contains __syncthreads().
+__device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) scratch[wave] = incl;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int w = 0; w < nw; ++w) {
+      const int t = scratch[w];
+      scratch[w] = run;
+      run += t;
+    }
+    scratch[nw] = run;
+  }
+  __syncthreads();
+  const int res = scratch[wave] + incl - v;
+  *total = scratch[nw];
+  __syncthreads();
+  return res;
+}
+
+}  // namespace clsa

@@ -1,0 +1,313 @@
+// Sparse attention over the shared selection (picx.dev summary of "You Only Index Once",
+// Methodology > Architecture Overview, eq. 3: every cross-decoder layer attends to the same
+// selected rows K_{S_t}, V_{S_t} of the one shared cache), with the softmax(QK^T/sqrt(d))V of
+// the zhichai.net explainer (Background: Attention and Its Limits), and the Selector that
+// gathers those rows (same explainer, CLSA: Sharing the Index Across Layers).
+//
+// One workgroup owns (query row r, KV head g, a block of up to 64 query rows, a split of the
+// selected keys).  The query rows of a KV head are all layers x the heads of its GQA group, so
+// in the layer-batched schedule every K/V tile brought into LDS serves L * Hq / Hkv queries.
+// Per 64-key tile: S^T = K Q^T and O^T += V^T P^T on bf16 MFMA 16x16x32 with fp32 accumulate;
+// the online softmax (exp2 domain) keeps every statistic of a query in the lane that owns the
+// query's column, so rescaling needs no cross-lane traffic.  Splits are recombined by a small
+// kernel from fp32 partials (m, l, acc).
+#include "device_common.h"
+
+namespace clsa {
+
+namespace {
+
+constexpr int kAttnThreads = 256;
+constexpr int kKsStride = CLSA_HEAD_DIM + 8;  // bf16 elements per K row in LDS (16-byte pad)
+constexpr int kVtStride = kAttnTile + 4;      // bf16 elements per transposed V row in LDS
+
+struct AttnArgs {
+  RowsDev rw;
+  int k, hq, hkv, lc, group, qrows, qblocks, splits, kps;
+  float scale_log2;
+  const uint16_t* q;
+  int64_t q_stride;
+  const uint16_t* ksrc;  // compact buffer [R, hkv, k, 128] or cache [T, hkv, 128]
+  const uint16_t* vsrc;
+  const int32_t* idx;
+  const int32_t* count;
+  uint16_t* out;
+  int64_t o_stride;
+  float* part;  // [splits, R, lc, hq, kPartStride]
+};
+
+template <bool FROM_CACHE>
+__global__ __launch_bounds__(kAttnThreads) void k_sparse_attn(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t ks[kAttnTile * kKsStride];
+  __shared__ __attribute__((aligned(16))) uint16_t vt[CLSA_HEAD_DIM * kVtStride];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, grp = lane >> 4;
+  int bid = blockIdx.x;
+  const int split = bid % a.splits;
+  bid /= a.splits;
+  const int qb = bid % a.qblocks;
+  const int g = bid / a.qblocks;
+  const int r = blockIdx.y;
+  const int cnt = a.count[r];
+  const int kbeg = split * a.kps;
+  const int kend_raw = kbeg + a.kps;
+  const int kend = kend_raw < cnt ? kend_raw : cnt;
+
+  // this lane's query column: query row qr -> (layer, head) of the GQA group of KV head g
+  const int qr = qb * 64 + wave * 16 + l16;
+  const bool wave_active = qb * 64 + wave * 16 < a.qrows;
+  const bool q_valid = qr < a.qrows;
+  const int layer = q_valid ? qr / a.group : 0;
+  const int head = g * a.group + (q_valid ? qr % a.group : 0);
+  bf16x8_t qf[4];
+  {
+    const uint16_t* qp = a.q + (int64_t)r * a.q_stride + ((int64_t)layer * a.hq + head) * CLSA_HEAD_DIM;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (q_valid) v = *reinterpret_cast<const uint4*>(qp + s * 32 + grp * 8);
+      qf[s] = bitcast<bf16x8_t>(v);
+    }
+  }
+  float m_run = -INFINITY, l_run = 0.f;
+  floatx4_t acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int seq = row_seq(a.rw, r);
+  const int64_t tok_base = FROM_CACHE ? (int64_t)a.rw.cu[seq] : 0;
+  const int32_t* irow = a.idx + (int64_t)r * a.k;
+  // loader mapping: thread -> (4 consecutive keys, one 16-byte chunk of head_dim)
+  const int ld_chunk = threadIdx.x & 15;  // 8 head_dim elements
+  const int ld_key4 = threadIdx.x >> 4;   // keys 4*ld_key4 .. +3
+
+  for (int kt = kbeg; kt < kend; kt += kAttnTile) {
+    const int nvalid = kend - kt < kAttnTile ? kend - kt : kAttnTile;
+    uint4 kv[4], vv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = ld_key4 * 4 + i;
+      kv[i] = make_uint4(0u, 0u, 0u, 0u);
+      vv[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (key < nvalid) {
+        int64_t src;
+        if (FROM_CACHE)
+          src = ((tok_base + irow[kt + key]) * a.hkv + g) * CLSA_HEAD_DIM + ld_chunk * 8;
+        else
+          src = (((int64_t)r * a.hkv + g) * a.k + kt + key) * CLSA_HEAD_DIM + ld_chunk * 8;
+        kv[i] = *reinterpret_cast<const uint4*>(a.ksrc + src);
+        vv[i] = *reinterpret_cast<const uint4*>(a.vsrc + src);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<uint4*>(&ks[(ld_key4 * 4 + i) * kKsStride + ld_chunk * 8]) = kv[i];
+    // transpose 4 keys x 8 head_dim elements in registers, store 8 rows of 4 keys (8 bytes each)
+    {
+      const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vv[0]);
+      const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vv[1]);
+      const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vv[2]);
+      const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vv[3]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // element 2e (low half) and 2e+1 (high half) of each key
+        const uint32_t lo01 = (w0[e] & 0xFFFFu) | (w1[e] << 16);
+        const uint32_t lo23 = (w2[e] & 0xFFFFu) | (w3[e] << 16);
+        const uint32_t hi01 = (w0[e] >> 16) | (w1[e] & 0xFFFF0000u);
+        const uint32_t hi23 = (w2[e] >> 16) | (w3[e] & 0xFFFF0000u);
+        const int d0 = ld_chunk * 8 + 2 * e;
+        *reinterpret_cast<uint2*>(&vt[d0 * kVtStride + ld_key4 * 4]) = make_uint2(lo01, lo23);
+        *reinterpret_cast<uint2*>(&vt[(d0 + 1) * kVtStride + ld_key4 * 4]) = make_uint2(hi01, hi23);
+      }
+    }
+    __syncthreads();
+    if (wave_active) {
+      floatx4_t s[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        s[mt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const uint4 av = *reinterpret_cast<const uint4*>(&ks[(mt * 16 + l16) * kKsStride + kk * 32 + grp * 8]);
+          s[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8_t>(av), qf[kk], s[mt], 0, 0, 0);
+        }
+      }
+      // s[mt][j]: key mt*16 + grp*4 + j, query column l16
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int key = mt * 16 + grp * 4 + j;
+          const float v = key < nvalid ? s[mt][j] * a.scale_log2 : -INFINITY;
+          s[mt][j] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_run, mx);
+      const float corr = exp2f(m_run - m_new);
+      m_run = m_new;
+      float psum = 0.f;
+      uint32_t pk[4][2];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        float p[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          p[j] = exp2f(s[mt][j] - m_new);
+          psum += p[j];
+        }
+        pk[mt][0] = f32_to_bf16(p[0]) | (f32_to_bf16(p[1]) << 16);
+        pk[mt][1] = f32_to_bf16(p[2]) | (f32_to_bf16(p[3]) << 16);
+      }
+      l_run = l_run * corr + psum;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] *= corr;
+      // P^T operand of k-step kk: slots 0..3 <- keys 32kk + 4grp + j, slots 4..7 <- keys 32kk + 16 + 4grp + j
+      bf16x8_t pb[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+        pb[kk] = bitcast<bf16x8_t>(make_uint4(pk[2 * kk][0], pk[2 * kk][1], pk[2 * kk + 1][0], pk[2 * kk + 1][1]));
+#pragma unroll
+      for (int ht = 0; ht < 8; ++ht) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const uint16_t* vr = &vt[(ht * 16 + l16) * kVtStride + kk * 32 + grp * 4];
+          const uint2 v0 = *reinterpret_cast<const uint2*>(vr);
+          const uint2 v1 = *reinterpret_cast<const uint2*>(vr + 16);
+          acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8_t>(make_uint4(v0.x, v0.y, v1.x, v1.y)),
+                                                            pb[kk], acc[ht], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (!wave_active) return;
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+  if (!q_valid) return;
+  // acc[ht][j]: head_dim ht*16 + grp*4 + j of this lane's query
+  if (a.splits == 1) {
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    uint16_t* op = a.out + (int64_t)r * a.o_stride + ((int64_t)layer * a.hq + head) * CLSA_HEAD_DIM;
+#pragma unroll
+    for (int ht = 0; ht < 8; ++ht) {
+      const uint32_t lo = f32_to_bf16(acc[ht][0] * inv) | (f32_to_bf16(acc[ht][1] * inv) << 16);
+      const uint32_t hi = f32_to_bf16(acc[ht][2] * inv) | (f32_to_bf16(acc[ht][3] * inv) << 16);
+      *reinterpret_cast<uint2*>(op + ht * 16 + grp * 4) = make_uint2(lo, hi);
+    }
+  } else {
+    const int R = a.rw.n_rows;
+    float* pp = a.part + ((((int64_t)split * R + r) * a.lc + layer) * a.hq + head) * kPartStride;
+#pragma unroll
+    for (int ht = 0; ht < 8; ++ht)
+      *reinterpret_cast<float4*>(pp + ht * 16 + grp * 4) = make_float4(acc[ht][0], acc[ht][1], acc[ht][2], acc[ht][3]);
+    if (grp == 0) {
+      pp[CLSA_HEAD_DIM] = m_run;
+      pp[CLSA_HEAD_DIM + 1] = l_run;
+    }
+  }
+}
+
+// Recombine the splits of one (row, layer, head): O = sum_s e^(m_s - M) acc_s / sum_s e^(m_s - M) l_s.
+__global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ part, int splits, int R, int lc,
+                                                       int hq, uint16_t* __restrict__ out, int64_t o_stride) {
+  const int r = blockIdx.y;
+  const int lh = blockIdx.x;  // layer * hq + head
+  const int d = threadIdx.x;
+  const int64_t stride_s = (int64_t)R * lc * hq * kPartStride;
+  const float* p0 = part + ((int64_t)r * lc * hq + lh) * kPartStride;
+  float M = -INFINITY;
+  for (int s = 0; s < splits; ++s) M = fmaxf(M, p0[s * stride_s + CLSA_HEAD_DIM]);
+  float num = 0.f, den = 0.f;
+  for (int s = 0; s < splits; ++s) {
+    const float* ps = p0 + s * stride_s;
+    const float ms = ps[CLSA_HEAD_DIM];
+    if (ms == -INFINITY) continue;
+    const float w = exp2f(ms - M);
+    num += w * ps[d];
+    den += w * ps[CLSA_HEAD_DIM + 1];
+  }
+  const float o = den > 0.f ? num / den : 0.f;
+  out[(int64_t)r * o_stride + (int64_t)lh * CLSA_HEAD_DIM + d] = (uint16_t)f32_to_bf16(o);
+}
+
+// Selector: k_sel[r, g, i, :] = k_cache[cu[seq] + idx[r, i], g, :] for i < count[r], zero after.
+constexpr int kGatherTok = 16;
+__global__ __launch_bounds__(256) void k_gather_kv(RowsDev rw, int k, int hkv, const uint16_t* __restrict__ kc,
+                                                    const uint16_t* __restrict__ vc, const int32_t* __restrict__ idx,
+                                                    const int32_t* __restrict__ count, uint16_t* __restrict__ ksel,
+                                                    uint16_t* __restrict__ vsel) {
+  const int r = blockIdx.y;
+  const int cnt = count[r];
+  const int64_t base = rw.cu[row_seq(rw, r)];
+  const int per_tok = hkv * 16;  // 16-byte chunks per token
+  const int total = kGatherTok * per_tok;
+  for (int c = threadIdx.x; c < total; c += blockDim.x) {
+    const int t = c / per_tok;
+    const int rem = c - t * per_tok;
+    const int g = rem >> 4, ch = rem & 15;
+    const int i = blockIdx.x * kGatherTok + t;
+    if (i >= k) continue;
+    const int64_t dst = (((int64_t)r * hkv + g) * k + i) * CLSA_HEAD_DIM + ch * 8;
+    uint4 kv = make_uint4(0u, 0u, 0u, 0u), vv = make_uint4(0u, 0u, 0u, 0u);
+    if (i < cnt) {
+      const int64_t src = ((base + idx[(int64_t)r * k + i]) * hkv + g) * CLSA_HEAD_DIM + ch * 8;
+      kv = *reinterpret_cast<const uint4*>(kc + src);
+      vv = *reinterpret_cast<const uint4*>(vc + src);
+    }
+    *reinterpret_cast<uint4*>(ksel + dst) = kv;
+    *reinterpret_cast<uint4*>(vsel + dst) = vv;
+  }
+}
+
+}  // namespace
+
+int launch_attn(const RowsDev& rows, int k, int hq, int hkv, int n_layers_call, float scale, const AttnPlan& plan,
+                const uint16_t* q, int64_t q_stride, const uint16_t* ksel, const uint16_t* vsel, const uint16_t* kc,
+                const uint16_t* vc, const int32_t* idx, const int32_t* count, uint16_t* out, int64_t o_stride,
+                void* part, void* stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  AttnArgs a;
+  a.rw = rows;
+  a.k = k;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.lc = n_layers_call;
+  a.group = plan.group;
+  a.qrows = plan.qrows;
+  a.qblocks = plan.qblocks;
+  a.splits = plan.splits;
+  a.kps = plan.keys_per_split;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.q = q;
+  a.q_stride = q_stride;
+  const bool from_cache = ksel == nullptr;
+  a.ksrc = from_cache ? kc : ksel;
+  a.vsrc = from_cache ? vc : vsel;
+  a.idx = idx;
+  a.count = count;
+  a.out = out;
+  a.o_stride = o_stride;
+  a.part = static_cast<float*>(part);
+  const dim3 grid((unsigned)(plan.splits * plan.qblocks * hkv), (unsigned)rows.n_rows);
+  if (from_cache)
+    hipLaunchKernelGGL(k_sparse_attn<true>, grid, dim3(kAttnThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_sparse_attn<false>, grid, dim3(kAttnThreads), 0, s, a);
+  if (plan.splits > 1)
+    hipLaunchKernelGGL(k_attn_combine, dim3((unsigned)(n_layers_call * hq), (unsigned)rows.n_rows), dim3(128), 0, s,
+                       static_cast<const float*>(part), plan.splits, rows.n_rows, n_layers_call, hq, out, o_stride);
+  return (int)hipGetLastError();
+}
+
+int launch_gather(const RowsDev& rows, int k, int hkv, const uint16_t* kc, const uint16_t* vc, const int32_t* idx,
+                  const int32_t* count, uint16_t* ks, uint16_t* vs, void* stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const dim3 grid((unsigned)((k + kGatherTok - 1) / kGatherTok), (unsigned)rows.n_rows);
+  hipLaunchKernelGGL(k_gather_kv, grid, dim3(256), 0, s, rows, k, hkv, kc, vc, idx, count, ks, vs);
+  return (int)hipGetLastError();
+}
+
+}  // namespace clsa

@@ -1,0 +1,176 @@
+// Host-side validation and workspace planning of the CLSA ABI.  Pure C++: no HIP call is made
+// here, so every error path can be exercised on a machine without a GPU.
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "clsa_internal.h"
+
+namespace clsa {
+
+namespace {
+clsa_status fail(std::string& err, clsa_status s, const std::string& msg) {
+  err = msg;
+  return s;
+}
+}  // namespace
+
+clsa_status check_ptr(const void* p, const char* name, std::string& err) {
+  if (p == nullptr) return fail(err, CLSA_ERR_INVALID_ARGUMENT, std::string(name) + " is NULL");
+  if (reinterpret_cast<uintptr_t>(p) % 16 != 0)
+    return fail(err, CLSA_ERR_INVALID_ARGUMENT, std::string(name) + " is not 16-byte aligned");
+  return CLSA_OK;
+}
+
+clsa_status check_ptr_opt(const void* p, const char* name, std::string& err) {
+  if (p != nullptr && reinterpret_cast<uintptr_t>(p) % 16 != 0)
+    return fail(err, CLSA_ERR_INVALID_ARGUMENT, std::string(name) + " is not 16-byte aligned");
+  return CLSA_OK;
+}
+
+clsa_status check_dims(const clsa_dims* d, std::string& err) {
+  if (d == nullptr) return fail(err, CLSA_ERR_INVALID_ARGUMENT, "dims is NULL");
+  if (d->batch < 1) return fail(err, CLSA_ERR_INVALID_ARGUMENT, "batch must be >= 1");
+  if (d->topk < 1) return fail(err, CLSA_ERR_INVALID_ARGUMENT, "topk must be >= 1");
+  if (d->n_layers < 1) return fail(err, CLSA_ERR_INVALID_ARGUMENT, "n_layers must be >= 1");
+  if (d->hq < 1 || d->hkv < 1) return fail(err, CLSA_ERR_INVALID_ARGUMENT, "hq and hkv must be >= 1");
+  if (d->hq % d->hkv != 0) return fail(err, CLSA_ERR_INVALID_ARGUMENT, "hq must be a multiple of hkv");
+  if (d->head_dim != CLSA_HEAD_DIM) return fail(err, CLSA_ERR_UNSUPPORTED, "head_dim must be 128");
+  if (d->d_idx != 64 && d->d_idx != 128) return fail(err, CLSA_ERR_UNSUPPORTED, "d_idx must be 64 or 128");
+  if (d->topk > CLSA_MAX_TOPK) return fail(err, CLSA_ERR_UNSUPPORTED, "topk above CLSA_MAX_TOPK");
+  if (d->sm_scale != d->sm_scale) return fail(err, CLSA_ERR_INVALID_ARGUMENT, "sm_scale is NaN");
+  return CLSA_OK;
+}
+
+clsa_status check_rows(const clsa_dims* d, const clsa_rows* r, std::string& err) {
+  if (r == nullptr) return fail(err, CLSA_ERR_INVALID_ARGUMENT, "rows is NULL");
+  if (r->mode != CLSA_MODE_DECODE && r->mode != CLSA_MODE_PREFILL)
+    return fail(err, CLSA_ERR_INVALID_ARGUMENT, "rows.mode must be CLSA_MODE_DECODE or CLSA_MODE_PREFILL");
+  if (r->n_rows < 1) return fail(err, CLSA_ERR_INVALID_ARGUMENT, "rows.n_rows must be >= 1");
+  if (r->max_row_len < 1) return fail(err, CLSA_ERR_INVALID_ARGUMENT, "rows.max_row_len must be >= 1");
+  if (r->max_row_len > CLSA_MAX_ROW_LEN) return fail(err, CLSA_ERR_UNSUPPORTED, "rows.max_row_len too large");
+  if (r->total_tokens < 1) return fail(err, CLSA_ERR_INVALID_ARGUMENT, "rows.total_tokens must be >= 1");
+  if (r->mode == CLSA_MODE_DECODE) {
+    if (r->n_rows != d->batch) return fail(err, CLSA_ERR_INVALID_ARGUMENT, "decode requires n_rows == batch");
+  } else {
+    if (r->seq < 0 || r->seq >= d->batch) return fail(err, CLSA_ERR_INVALID_ARGUMENT, "rows.seq out of range");
+    if (r->pos0 < 0) return fail(err, CLSA_ERR_INVALID_ARGUMENT, "rows.pos0 must be >= 0");
+    if ((int64_t)r->pos0 + r->n_rows != (int64_t)r->max_row_len)
+      return fail(err, CLSA_ERR_INVALID_ARGUMENT, "prefill requires max_row_len == pos0 + n_rows");
+  }
+  if (r->max_row_len > r->total_tokens)
+    return fail(err, CLSA_ERR_INVALID_ARGUMENT, "rows.max_row_len exceeds total_tokens");
+  if (r->cu_seqlens_host != nullptr) {
+    const int32_t* cu = r->cu_seqlens_host;
+    if (cu[0] != 0) return fail(err, CLSA_ERR_INVALID_ARGUMENT, "cu_seqlens[0] must be 0");
+    for (int b = 0; b < d->batch; ++b) {
+      const int64_t n = (int64_t)cu[b + 1] - cu[b];
+      if (n < 0) return fail(err, CLSA_ERR_INVALID_ARGUMENT, "cu_seqlens is not non-decreasing");
+      if (r->mode == CLSA_MODE_DECODE) {
+        if (n < 1) return fail(err, CLSA_ERR_INVALID_ARGUMENT, "decode sequence of length 0");
+        if (n > r->max_row_len)
+          return fail(err, CLSA_ERR_INVALID_ARGUMENT, "a sequence is longer than rows.max_row_len");
+      }
+    }
+    if (cu[d->batch] != r->total_tokens)
+      return fail(err, CLSA_ERR_INVALID_ARGUMENT, "cu_seqlens[batch] != rows.total_tokens");
+    if (r->mode == CLSA_MODE_PREFILL && (int64_t)cu[r->seq + 1] - cu[r->seq] < (int64_t)r->pos0 + r->n_rows)
+      return fail(err, CLSA_ERR_INVALID_ARGUMENT, "prefill rows reach past the end of their sequence");
+  }
+  return CLSA_OK;
+}
+
+TopkPlan plan_topk(const clsa_dims* d, const clsa_rows* r) {
+  TopkPlan p;
+  p.multi_wg = r->max_row_len > kLdsRowCap;
+  if (!p.multi_wg) return p;
+  const size_t R = (size_t)r->n_rows;
+  size_t off = 0;
+  p.hist_off = off;
+  off = align_up(off + R * kHist1Bins * 4, 256);
+  p.state_off = off;
+  off = align_up(off + R * kTopkStateWords * 4, 256);
+  p.sure_off = off;
+  off = align_up(off + R * (size_t)d->topk * 4, 256);
+  p.cand_off = off;
+  off = align_up(off + R * (size_t)r->max_row_len * 8, 256);
+  p.bytes = off;
+  return p;
+}
+
+AttnPlan plan_attn(const clsa_dims* d, int n_rows, int n_layers_call) {
+  AttnPlan p;
+  p.group = d->hq / d->hkv;
+  p.qrows = n_layers_call * p.group;
+  p.qblocks = (p.qrows + 63) / 64;
+  const int64_t base = (int64_t)n_rows * d->hkv * p.qblocks;
+  const int tiles = (d->topk + kAttnTile - 1) / kAttnTile;
+  int splits = 1;
+  if (base < 512) splits = (int)((512 + base - 1) / base);
+  if (splits > tiles) splits = tiles;
+  if (splits < 1) splits = 1;
+  const int tiles_per_split = (tiles + splits - 1) / splits;
+  p.splits = (tiles + tiles_per_split - 1) / tiles_per_split;
+  p.keys_per_split = tiles_per_split * kAttnTile;
+  p.part_bytes = p.splits > 1
+                     ? align_up((size_t)p.splits * n_rows * n_layers_call * d->hq * kPartStride * 4, 256)
+                     : 0;
+  return p;
+}
+
+StepPlan plan_step(const clsa_dims* d, const clsa_rows* r, int schedule, bool user_scores, bool user_sel,
+                   int prefill_chunk_rows) {
+  StepPlan s;
+  const bool prefill = r->mode == CLSA_MODE_PREFILL;
+  s.chunk_rows = prefill ? (prefill_chunk_rows > 0 ? prefill_chunk_rows : kPrefillChunkRows) : r->n_rows;
+  if (s.chunk_rows > r->n_rows) s.chunk_rows = r->n_rows;
+  clsa_rows chunk = *r;
+  chunk.n_rows = s.chunk_rows;
+  if (prefill) chunk.max_row_len = r->max_row_len;  // a chunk never sees more than the last row
+  s.topk = plan_topk(d, &chunk);
+  const int lc = schedule == CLSA_SCHEDULE_PER_LAYER ? 1 : d->n_layers;
+  s.attn = plan_attn(d, s.chunk_rows, lc);
+  const int tail = r->n_rows % s.chunk_rows;
+  if (tail) {  // the last, shorter chunk may split its keys more finely
+    const AttnPlan at = plan_attn(d, tail, lc);
+    if (at.part_bytes > s.attn.part_bytes) s.attn.part_bytes = at.part_bytes;
+  }
+  s.ld_scores = (int64_t)align_up((size_t)r->max_row_len, 64);
+  size_t off = 0;
+  if (!user_scores) {
+    s.scores_off = off;
+    s.scores_bytes = align_up((size_t)s.chunk_rows * s.ld_scores * 4, 256);
+    off += s.scores_bytes;
+  }
+  s.topk_off = off;
+  off += s.topk.bytes;
+  s.part_off = off;
+  off += s.attn.part_bytes;
+  if (schedule == CLSA_SCHEDULE_PER_LAYER && !prefill && !user_sel) {
+    s.sel_bytes = align_up((size_t)r->n_rows * d->hkv * d->topk * CLSA_HEAD_DIM * 2, 256);
+    s.ksel_off = off;
+    off += s.sel_bytes;
+    s.vsel_off = off;
+    off += s.sel_bytes;
+  }
+  s.total = off;
+  return s;
+}
+
+size_t workspace_bytes(const clsa_dims* d, const clsa_rows* r, int schedule) {
+  const TopkPlan t = plan_topk(d, r);
+  const int lc = schedule == CLSA_SCHEDULE_PER_LAYER ? 1 : d->n_layers;
+  const AttnPlan a = plan_attn(d, r->n_rows, lc);
+  const StepPlan s = plan_step(d, r, schedule, false, false, 0);
+  size_t m = t.bytes;
+  if (a.part_bytes > m) m = a.part_bytes;
+  // a standalone clsa_sparse_attn call may cover any number of layers up to L
+  for (int l = 1; l <= d->n_layers; ++l) {
+    const AttnPlan al = plan_attn(d, r->n_rows, l);
+    if (al.part_bytes > m) m = al.part_bytes;
+  }
+  if (s.total > m) m = s.total;
+  return m < 256 ? 256 : m;
+}
+
+}  // namespace clsa

@@ -1,0 +1,155 @@
+"""The C-ABI library on a machine without a GPU: it loads, exports every declared entry point,
+and rejects bad arguments on the host before any launch (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from cross_layer_token_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x7F0000000000  # 256-byte aligned stand-in address; never dereferenced by these tests
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "clsa.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\*?\s+\*?(clsa_[a-z_]+)\(", text, re.M)))
+
+
+def test_header_declares_the_five_entry_points_and_helpers():
+    names = _declared_functions()
+    for f in ["clsa_index_scores", "clsa_topk", "clsa_gather_kv", "clsa_sparse_attn", "clsa_step",
+              "clsa_workspace_bytes", "clsa_status_string", "clsa_last_error_message", "clsa_abi_version"]:
+        assert f in names, f
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(B.LIB_PATH)
+    for f in _declared_functions():
+        assert hasattr(lib, f), f
+    assert set(_declared_functions()) == set(B.FUNCTIONS)
+    assert B.LIB.clsa_abi_version() == 1
+
+
+def test_synth_library_exports():
+    lib = ctypes.CDLL(os.path.join(ROOT, "clsa_synth", "libclsa_synth.so"))
+    for f in ["synth_fill_uniform_int", "synth_fill_normal", "synth_plant_needles", "synth_tensor_key"]:
+        assert hasattr(lib, f)
+
+
+def test_host_tensor_key_matches_python_generator():
+    from clsa_synth import gen
+    lib = ctypes.CDLL(os.path.join(ROOT, "clsa_synth", "libclsa_synth.so"))
+    lib.synth_tensor_key.argtypes = [ctypes.c_uint64, ctypes.c_uint32]
+    lib.synth_tensor_key.restype = ctypes.c_uint64
+    for seed, tid in [(0, 1), (3, 5), (2 ** 63 + 11, 7)]:
+        assert lib.synth_tensor_key(seed, tid) == int(gen.tensor_key(seed, tid))
+
+
+def test_status_strings():
+    assert B.status_string(0) == "CLSA_OK"
+    assert B.status_string(3) == "CLSA_ERR_WORKSPACE"
+
+
+def _dims(**kw):
+    d = dict(batch=2, d_idx=128, topk=64, n_layers=2, hq=8, hkv=2)
+    d.update(kw)
+    return B.make_dims(**d)
+
+
+def _rows(**kw):
+    r = dict(mode=B.MODE_DECODE, n_rows=2, max_row_len=1000, total_tokens=1500, cu_seqlens_host=[0, 1000, 1500])
+    r.update(kw)
+    return B.make_rows(**r)
+
+
+def _scores(dims, rows, **over):
+    args = dict(q_idx=FAKE, k_idx=FAKE, cu=FAKE, scores=FAKE, ld=1024)
+    args.update(over)
+    return B.LIB.clsa_index_scores(ctypes.byref(dims), ctypes.byref(rows), args["q_idx"], args["k_idx"], args["cu"],
+                                   args["scores"], args["ld"], None)
+
+
+@pytest.mark.parametrize("dims_kw,rows_kw,over,status,needle", [
+    (dict(head_dim=64), {}, {}, B.ERR_UNSUPPORTED, "head_dim"),
+    (dict(d_idx=96), {}, {}, B.ERR_UNSUPPORTED, "d_idx"),
+    (dict(hq=6, hkv=4), {}, {}, B.ERR_INVALID_ARGUMENT, "multiple of hkv"),
+    (dict(topk=0), {}, {}, B.ERR_INVALID_ARGUMENT, "topk"),
+    (dict(topk=70000), {}, {}, B.ERR_UNSUPPORTED, "topk"),
+    (dict(n_layers=0), {}, {}, B.ERR_INVALID_ARGUMENT, "n_layers"),
+    ({}, dict(n_rows=3), {}, B.ERR_INVALID_ARGUMENT, "n_rows == batch"),
+    ({}, dict(mode=7), {}, B.ERR_INVALID_ARGUMENT, "mode"),
+    ({}, dict(cu_seqlens_host=[0, 1200, 1500]), {}, B.ERR_INVALID_ARGUMENT, "longer than"),
+    ({}, dict(cu_seqlens_host=[0, 900, 800]), {}, B.ERR_INVALID_ARGUMENT, "non-decreasing"),
+    ({}, dict(cu_seqlens_host=[0, 500, 1400]), {}, B.ERR_INVALID_ARGUMENT, "total_tokens"),
+    ({}, dict(cu_seqlens_host=[1, 500, 1500]), {}, B.ERR_INVALID_ARGUMENT, "cu_seqlens[0]"),
+    ({}, dict(cu_seqlens_host=[0, 0, 1500]), {}, B.ERR_INVALID_ARGUMENT, "length 0"),
+    ({}, dict(max_row_len=2000), {}, B.ERR_INVALID_ARGUMENT, "exceeds total_tokens"),
+    ({}, {}, dict(q_idx=0), B.ERR_INVALID_ARGUMENT, "q_idx is NULL"),
+    ({}, {}, dict(k_idx=FAKE + 2), B.ERR_INVALID_ARGUMENT, "aligned"),
+    ({}, {}, dict(ld=512), B.ERR_INVALID_ARGUMENT, "ld_scores"),
+    ({}, dict(mode=B.MODE_PREFILL, n_rows=100, pos0=0, max_row_len=101, seq=0), {}, B.ERR_INVALID_ARGUMENT, "pos0 + n_rows"),
+    ({}, dict(mode=B.MODE_PREFILL, n_rows=100, pos0=1000, max_row_len=1100, seq=0, total_tokens=1500), {},
+     B.ERR_INVALID_ARGUMENT, "past the end"),
+    ({}, dict(mode=B.MODE_PREFILL, n_rows=10, pos0=0, max_row_len=10, seq=2), {}, B.ERR_INVALID_ARGUMENT, "seq"),
+])
+def test_index_scores_rejects(dims_kw, rows_kw, over, status, needle):
+    s = _scores(_dims(**dims_kw), _rows(**rows_kw), **over)
+    assert s == status
+    assert needle in B.last_error()
+
+
+def test_topk_rejects_small_workspace():
+    dims, rows = _dims(), _rows(max_row_len=50000, total_tokens=60000, cu_seqlens_host=[0, 50000, 60000])
+    need = B.workspace_bytes(dims, rows)
+    assert need > 2 * 50000 * 8  # candidate lists of the long-row select
+    s = B.LIB.clsa_topk(ctypes.byref(dims), ctypes.byref(rows), FAKE, FAKE, 50048, FAKE, FAKE, FAKE, 1024, None)
+    assert s == B.ERR_WORKSPACE and "needed" in B.last_error()
+    s = B.LIB.clsa_topk(ctypes.byref(dims), ctypes.byref(rows), FAKE, FAKE, 50048, FAKE, FAKE, None, need, None)
+    assert s == B.ERR_WORKSPACE
+
+
+def test_sparse_attn_rejects():
+    dims, rows = _dims(), _rows()
+    L = B.LIB
+
+    def call(lc=2, qs=2 * 8 * 128, os_=2 * 8 * 128, ksel=None, vsel=None, kc=FAKE, vc=FAKE, idx=FAKE):
+        return L.clsa_sparse_attn(ctypes.byref(dims), ctypes.byref(rows), FAKE, qs, lc, ksel, vsel, kc, vc, FAKE, idx,
+                                  FAKE, FAKE, os_, FAKE, 1 << 40, None)
+    assert call(lc=3) == B.ERR_UNSUPPORTED
+    assert call(lc=0) == B.ERR_UNSUPPORTED
+    assert call(qs=100) == B.ERR_INVALID_ARGUMENT
+    assert call(ksel=FAKE) == B.ERR_INVALID_ARGUMENT and "v_sel" in B.last_error()
+    assert call(kc=None) == B.ERR_INVALID_ARGUMENT and "k_cache" in B.last_error()
+
+
+def test_step_rejects():
+    dims, rows = _dims(), _rows()
+    ws = B.workspace_bytes(dims, rows)
+
+    def call(**kw):
+        a = dict(q_idx=FAKE, k_idx=FAKE, k_cache=FAKE, v_cache=FAKE, cu_seqlens=FAKE, q=FAKE, out=FAKE, idx=FAKE,
+                 count=FAKE, scores=None, ld_scores=0, k_sel=None, v_sel=None, schedule=0, prefill_chunk_rows=0)
+        wsz = kw.pop("ws", ws)
+        a.update(kw)
+        sa = B.StepArgs(**a)
+        return B.LIB.clsa_step(ctypes.byref(dims), ctypes.byref(rows), ctypes.byref(sa), FAKE, wsz, None)
+    assert call(schedule=5) == B.ERR_INVALID_ARGUMENT
+    assert call(out=None) == B.ERR_INVALID_ARGUMENT
+    assert call(k_sel=FAKE) == B.ERR_INVALID_ARGUMENT
+    assert call(scores=FAKE, ld_scores=10) == B.ERR_INVALID_ARGUMENT
+    assert call(ws=ws - 1) == B.ERR_WORKSPACE
+    assert call(prefill_chunk_rows=-1) == B.ERR_INVALID_ARGUMENT
+
+
+def test_workspace_sizes_cover_every_call():
+    # 128K decode: candidate lists dominate; per-layer schedule adds the two compact buffers
+    dims = B.make_dims(16, 128, 2048, 16, 32, 8)
+    rows = B.make_rows(B.MODE_DECODE, 16, 131072, 16 * 131072)
+    batched = B.workspace_bytes(dims, rows, B.SCHEDULE_LAYER_BATCHED)
+    per_layer = B.workspace_bytes(dims, rows, B.SCHEDULE_PER_LAYER)
+    assert batched >= 16 * 131072 * 8 + 16 * 131072 * 4
+    assert per_layer >= 2 * 16 * 8 * 2048 * 128 * 2 + 16 * 131072 * (8 + 4)
+    with pytest.raises(B.CLSAError):
+        B.workspace_bytes(B.make_dims(16, 128, 2048, 16, 32, 8, head_dim=64), rows)

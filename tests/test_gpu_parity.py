@@ -1,0 +1,336 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 CPU oracle, on the five workloads
+and on edge cases.  Indices and scores must match bit for bit; attention outputs within the
+tolerance in _gpu_helpers (max-abs 2e-2, mean-abs 2e-3, relative Frobenius 5e-3)."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import clsa_synth as cs
+import cross_layer_token_amd as clsa
+from _gpu_helpers import (assert_outputs_close, bf16_dev_to_f64, cu_tensor, device_workload, dims_of, rows_of,
+                          workspace)
+from clsa_synth import gen
+from oracle import clsa_oracle as O
+from oracle.workload_oracle import oracle_row
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    yield
+    torch.cuda.synchronize()
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+# ----------------------------------------------------------------------------- generator
+@pytest.mark.parametrize("cfg", [1, 3])
+def test_device_generator_matches_host(cfg):
+    w = cs.config(cfg)
+    dw = device_workload(w)
+    rng = np.random.default_rng(cfg)
+    T = w.total_tokens
+    toks = np.unique(np.concatenate([rng.integers(0, T, 300), [t for t, _ in w.needle_pairs()][:64], [0, T - 1]]))
+    assert np.array_equal(dw.k_idx[torch.from_numpy(toks).cuda()].cpu().numpy().view(np.uint16), w.k_idx_bits(toks))
+    assert np.array_equal(dw.q_idx.cpu().numpy().view(np.uint16), w.q_idx_bits(np.arange(w.n_rows)))
+    for which, t in (("k", dw.k_cache), ("v", dw.v_cache)):
+        got = t[torch.from_numpy(toks).cuda()].cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, w.kv_bits(toks, which))
+    rows = np.array([0, w.n_rows - 1])
+    assert np.array_equal(dw.q[torch.from_numpy(rows).cuda()].cpu().numpy().view(np.uint16), w.q_bits(rows))
+
+
+# ----------------------------------------------------------------------------- a1 scores
+def _decode_scores(dw):
+    w = dw.w
+    dims, rows = dims_of(dw), rows_of(dw)
+    ld = ((w.max_row_len + 63) // 64) * 64
+    scores = torch.full((w.n_rows, ld), float("nan"), dtype=torch.float32, device="cuda")
+    clsa.index_scores(dims, rows, dw.q_idx, dw.k_idx, dw.cu_seqlens, scores, ld)
+    torch.cuda.synchronize()
+    return scores
+
+
+@pytest.mark.parametrize("cfg,check_rows", [(1, None), (2, None), (3, [0, 15]), (5, [0, 1, 17, 63])])
+def test_index_scores_decode_bitwise(cfg, check_rows):
+    w = cs.config(cfg)
+    dw = device_workload(w)
+    scores = _decode_scores(dw)
+    cu = w.cu_seqlens
+    for r in (range(w.n_rows) if check_rows is None else check_rows):
+        n = w.row_len(r)
+        ref = O.index_scores(w.q_idx_f64([r])[0], w.k_idx_f64(cu[r] + np.arange(n)))
+        got = scores[r, :n].cpu().numpy().astype(np.float64)
+        assert np.array_equal(got, ref), f"cfg{cfg} row {r}: {np.sum(got != ref)} mismatches"
+    _say(f"cfg{cfg} scores bitwise OK")
+
+
+def test_index_scores_prefill_bitwise():
+    w = cs.config(4)
+    dw = device_workload(w, with_kv=False, with_q=False)
+    n = w.n_rows
+    scores = torch.full((n, n), float("nan"), dtype=torch.float32, device="cuda")
+    clsa.index_scores(dims_of(dw), rows_of(dw), dw.q_idx, dw.k_idx, dw.cu_seqlens, scores, n)
+    torch.cuda.synchronize()
+    kf = w.k_idx_f64(np.arange(n))
+    for t in [0, 1, 15, 63, 64, 1000, 2047, 2048, 4095, 6000, 8191]:
+        ref = O.index_scores(w.q_idx_f64([t])[0], kf[: t + 1])
+        got = scores[t, : t + 1].cpu().numpy().astype(np.float64)
+        assert np.array_equal(got, ref), f"row {t}"
+        if t + 1 < n:
+            assert torch.isnan(scores[t, t + 1:]).all(), "wrote above the causal diagonal"
+    # a chunk of rows starting mid-sequence
+    pos0, m = 3000, 200
+    sc2 = torch.full((m, pos0 + m), float("nan"), dtype=torch.float32, device="cuda")
+    clsa.index_scores(dims_of(dw), rows_of(dw, row0=pos0, n_rows=m), dw.q_idx[pos0:], dw.k_idx, dw.cu_seqlens, sc2,
+                      pos0 + m)
+    torch.cuda.synchronize()
+    for i in [0, 77, 199]:
+        t = pos0 + i
+        ref = O.index_scores(w.q_idx_f64([t])[0], kf[: t + 1])
+        assert np.array_equal(sc2[i, : t + 1].cpu().numpy().astype(np.float64), ref)
+
+
+# ----------------------------------------------------------------------------- a2 top-k
+def _score_rows(kind, lengths, rng):
+    out = []
+    for n in lengths:
+        if kind == "ties":
+            s = rng.integers(-3, 4, n).astype(np.float32) * 0.5
+        elif kind == "normal":
+            s = rng.standard_normal(n).astype(np.float32) * 4
+        elif kind == "equal":
+            s = np.full(n, 1.25, dtype=np.float32)
+        elif kind == "zeros":
+            s = np.where(rng.integers(0, 2, n) == 1, np.float32(0.0), np.float32(-0.0)).astype(np.float32)
+            s[rng.integers(0, n, max(1, n // 100))] = 1.0
+        else:  # quantised to 1/16 in [-8, 8], like the ragged workload
+            s = (rng.integers(-128, 129, n) / 16.0).astype(np.float32)
+        out.append(s)
+    return out
+
+
+def _run_topk_decode(rows_scores, k):
+    lengths = [len(s) for s in rows_scores]
+    B = len(lengths)
+    ld = ((max(lengths) + 63) // 64) * 64
+    host = np.full((B, ld), np.nan, dtype=np.float32)
+    for i, s in enumerate(rows_scores):
+        host[i, : len(s)] = s
+    dims = clsa.make_dims(B, 128, k, 1, 8, 2)
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    rows = clsa.make_rows(clsa.MODE_DECODE, B, max(lengths), int(cu[-1]), cu_seqlens_host=cu.tolist())
+    ws, nws = workspace(dims, rows)
+    idx = torch.full((B, k), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    clsa.topk(dims, rows, cu_tensor(lengths), torch.from_numpy(host).cuda(), ld, idx, cnt, ws, nws)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), cnt.cpu().numpy()
+
+
+SHORT_ROWS = [1, 5, 300, 2048, 4096, 12288]                       # one workgroup per row (LDS)
+LONG_ROWS = [1, 5, 300, 2048, 4096, 12288, 12289, 50000, 131072]   # histogram select over many workgroups
+
+
+@pytest.mark.parametrize("lengths", [SHORT_ROWS, LONG_ROWS], ids=["short", "long"])
+@pytest.mark.parametrize("kind", ["ties", "normal", "equal", "zeros", "q16"])
+@pytest.mark.parametrize("k", [1, 7, 256, 2048])
+def test_topk_matches_oracle_on_given_scores(kind, k, lengths):
+    rng = np.random.default_rng(zlib.crc32(f"{kind}-{k}-{len(lengths)}".encode()))
+    rs = _score_rows(kind, lengths, rng)
+    idx, cnt = _run_topk_decode(rs, k)
+    for i, s in enumerate(rs):
+        sel = O.topk_select(s.astype(np.float64), k)
+        want, m = O.pad_selection(sel, k)
+        assert cnt[i] == m, (kind, k, lengths[i])
+        assert np.array_equal(idx[i], want), f"{kind} k={k} n={lengths[i]}: {np.sum(idx[i] != want)} mismatches"
+
+
+def test_topk_prefill_rows_lds_path():
+    rng = np.random.default_rng(5)
+    n, k = 3000, 256
+    s = (rng.integers(-40, 41, (n, n)) / 8.0).astype(np.float32)
+    dims = clsa.make_dims(1, 128, k, 1, 8, 2)
+    rows = clsa.make_rows(clsa.MODE_PREFILL, n, n, n, seq=0, pos0=0, cu_seqlens_host=[0, n])
+    idx = torch.empty((n, k), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((n,), dtype=torch.int32, device="cuda")
+    ws, nws = workspace(dims, rows)
+    clsa.topk(dims, rows, cu_tensor([n]), torch.from_numpy(s).cuda(), n, idx, cnt, ws, nws)
+    torch.cuda.synchronize()
+    idx, cnt = idx.cpu().numpy(), cnt.cpu().numpy()
+    for t in list(range(0, 300)) + [1000, 2999]:
+        want, m = O.pad_selection(O.topk_select(s[t, : t + 1].astype(np.float64), k), k)
+        assert cnt[t] == m and np.array_equal(idx[t], want), t
+
+
+# ----------------------------------------------------------------------------- a3 gather, a4 attention
+def _oracle_idx(w, rows):
+    res = [oracle_row(w, r) for r in rows]
+    return res
+
+
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_gather_and_attention_on_oracle_selection(cfg):
+    w = cs.config(cfg)
+    dw = device_workload(w)
+    res = _oracle_idx(w, range(w.n_rows))
+    idx = torch.from_numpy(np.stack([r["idx"] for r in res])).cuda()
+    cnt = torch.from_numpy(np.array([r["count"] for r in res], dtype=np.int32)).cuda()
+    dims, rows = dims_of(dw), rows_of(dw)
+    R, k = w.n_rows, w.topk
+    ksel = torch.empty((R, w.hkv, k, 128), dtype=torch.int16, device="cuda")
+    vsel = torch.empty_like(ksel)
+    clsa.gather_kv(dims, rows, dw.k_cache, dw.v_cache, dw.cu_seqlens, idx, cnt, ksel, vsel)
+    torch.cuda.synchronize()
+    cu = w.cu_seqlens
+    for r in range(R):
+        m = res[r]["count"]
+        toks = cu[r] + res[r]["sel"]
+        assert np.array_equal(ksel[r, :, :m].permute(1, 0, 2).cpu().numpy().view(np.uint16), w.kv_bits(toks, "k"))
+        assert np.array_equal(vsel[r, :, :m].permute(1, 0, 2).cpu().numpy().view(np.uint16), w.kv_bits(toks, "v"))
+        assert not ksel[r, :, m:].any() and not vsel[r, :, m:].any()
+    ref = np.stack([r["out"] for r in res])
+    L, hq = w.n_layers, w.hq
+    row_el = L * hq * 128
+    ws, nws = workspace(dims, rows, clsa.SCHEDULE_PER_LAYER)
+    for src in ("compact", "cache"):
+        out = torch.zeros((R, L, hq, 128), dtype=torch.int16, device="cuda")
+        ks_, vs_ = (ksel, vsel) if src == "compact" else (None, None)
+        clsa.sparse_attn(dims, rows, dw.q, row_el, L, ks_, vs_, dw.k_cache, dw.v_cache, dw.cu_seqlens, idx, cnt, out,
+                         row_el, ws, nws)
+        torch.cuda.synchronize()
+        st = assert_outputs_close(bf16_dev_to_f64(out), ref, f"cfg{cfg} {src} all layers")
+        _say(f"cfg{cfg} attention {src} L-batched", st)
+        out.zero_()
+        for layer in range(L):   # one layer per call, strided rows
+            clsa.sparse_attn(dims, rows, dw.q[:, layer], row_el, 1, ks_, vs_, dw.k_cache, dw.v_cache, dw.cu_seqlens,
+                             idx, cnt, out[:, layer], row_el, ws, nws)
+        torch.cuda.synchronize()
+        assert_outputs_close(bf16_dev_to_f64(out), ref, f"cfg{cfg} {src} per layer")
+
+
+@pytest.mark.parametrize("counts", [[1, 2, 63, 64, 65, 100], [5, 5, 5, 5, 5, 5]])
+def test_attention_ragged_counts_and_splits(counts):
+    """Short selections (count < k), single-row selections, tiles with a ragged tail."""
+    w = cs.custom(seq_lens=(700, 300, 128, 90, 1000, 256), topk=100, n_layers=3, hq=8, hkv=2, seed=21)
+    dw = device_workload(w)
+    rng = np.random.default_rng(3)
+    k = w.topk
+    idx_h = np.full((w.batch, k), -1, dtype=np.int32)
+    sels = []
+    for b, c in enumerate(counts):
+        sel = np.sort(rng.choice(w.seq_lens[b], size=c, replace=False))
+        idx_h[b, :c] = sel
+        sels.append(sel)
+    idx = torch.from_numpy(idx_h).cuda()
+    cnt = torch.tensor(counts, dtype=torch.int32, device="cuda")
+    dims, rows = dims_of(dw), rows_of(dw)
+    L, hq = w.n_layers, w.hq
+    row_el = L * hq * 128
+    out = torch.zeros((w.batch, L, hq, 128), dtype=torch.int16, device="cuda")
+    ws, nws = workspace(dims, rows)
+    clsa.sparse_attn(dims, rows, dw.q, row_el, L, None, None, dw.k_cache, dw.v_cache, dw.cu_seqlens, idx, cnt, out,
+                     row_el, ws, nws)
+    torch.cuda.synchronize()
+    cu = w.cu_seqlens
+    dev = bf16_dev_to_f64(out)
+    for b in range(w.batch):
+        kf, vf = w.kv_f64(cu[b] + sels[b])
+        ref = O.sparse_attention(w.q_f64([b])[0], kf, vf)
+        assert_outputs_close(dev[b], ref, f"row {b} count {counts[b]}")
+        if counts[b] == 1:   # one selected row: every head returns that V row (bf16 exact)
+            for h in range(hq):
+                assert np.array_equal(dev[b, :, h], np.broadcast_to(vf[0, h // (hq // w.hkv)], (L, 128)))
+
+
+# ----------------------------------------------------------------------------- whole step
+def _run_step(dw, schedule, rows_kw=None, chunk=0, want_scores=False):
+    w = dw.w
+    dims = dims_of(dw)
+    rows = rows_of(dw, **(rows_kw or {}))
+    R = rows.n_rows
+    ws, nws = workspace(dims, rows, schedule)
+    out = torch.zeros((R, w.n_layers, w.hq, 128), dtype=torch.int16, device="cuda")
+    idx = torch.full((R, w.topk), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.full((R,), -7, dtype=torch.int32, device="cuda")
+    row0 = (rows_kw or {}).get("row0", 0)
+    clsa.step(dims, rows, dw.q_idx[row0:], dw.k_idx, dw.k_cache, dw.v_cache, dw.cu_seqlens, dw.q[row0:], out, idx, cnt,
+              ws, nws, schedule=schedule, prefill_chunk_rows=chunk)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), cnt.cpu().numpy(), out
+
+
+@pytest.mark.parametrize("cfg,check", [(1, None), (2, None), (3, [0, 7, 15]), (5, [0, 5, 31, 63])])
+@pytest.mark.parametrize("schedule", [clsa.SCHEDULE_LAYER_BATCHED, clsa.SCHEDULE_PER_LAYER])
+def test_step_decode_vs_oracle(cfg, check, schedule):
+    w = cs.config(cfg)
+    dw = device_workload(w)
+    idx, cnt, out = _run_step(dw, schedule)
+    dev = bf16_dev_to_f64(out)
+    rows = range(w.n_rows) if check is None else check
+    for r in rows:
+        res = oracle_row(w, r)
+        assert cnt[r] == res["count"]
+        assert np.array_equal(idx[r], res["idx"]), f"cfg{cfg} row {r}: {np.sum(idx[r] != res['idx'])} index mismatches"
+        assert set(w.needle_positions_of_row(r)) <= set(idx[r].tolist())
+        st = assert_outputs_close(dev[r], res["out"], f"cfg{cfg} row {r}")
+        _say(f"cfg{cfg} sched {schedule} row {r}: max {st[0]:.2e} mean {st[1]:.2e} rel {st[2]:.2e}")
+    # every row: count and structure (ascending, in range, -1 padded)
+    for r in range(w.n_rows):
+        m = min(w.topk, w.row_len(r))
+        assert cnt[r] == m
+        assert np.all(np.diff(idx[r, :m]) > 0) and idx[r, 0] >= 0 and idx[r, m - 1] < w.row_len(r)
+        assert np.all(idx[r, m:] == -1)
+
+
+@pytest.mark.parametrize("schedule", [clsa.SCHEDULE_LAYER_BATCHED, clsa.SCHEDULE_PER_LAYER])
+def test_step_prefill_vs_oracle(schedule):
+    w = cs.config(4)
+    dw = device_workload(w)
+    idx, cnt, out = _run_step(dw, schedule, chunk=1024)
+    n = w.n_rows
+    assert np.array_equal(cnt, np.minimum(np.arange(1, n + 1), w.topk))
+    dev = bf16_dev_to_f64(out)
+    for t in [0, 1, 2, 100, 1023, 1024, 2046, 2047, 2048, 4095, 5000, 8191]:
+        res = oracle_row(w, t)
+        assert np.array_equal(idx[t], res["idx"]), f"row {t}"
+        assert_outputs_close(dev[t], res["out"], f"prefill row {t}")
+    assert set(w.needle_positions_of_row(n - 1)) <= set(idx[n - 1].tolist())
+
+
+def test_step_prefill_chunking_invariance():
+    w = cs.config(4)
+    dw = device_workload(w)
+    a = _run_step(dw, clsa.SCHEDULE_LAYER_BATCHED, chunk=1024)
+    b = _run_step(dw, clsa.SCHEDULE_LAYER_BATCHED, chunk=300)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    assert torch.equal(a[2], b[2])
+    # the same rows run as a call starting mid-sequence
+    c = _run_step(dw, clsa.SCHEDULE_LAYER_BATCHED, rows_kw=dict(row0=5000, n_rows=1000), chunk=512)
+    assert np.array_equal(a[0][5000:6000], c[0]) and torch.equal(a[2][5000:6000], c[2])
+
+
+def test_step_is_deterministic():
+    w = cs.config(2)
+    dw = device_workload(w)
+    a = _run_step(dw, clsa.SCHEDULE_LAYER_BATCHED)
+    b = _run_step(dw, clsa.SCHEDULE_LAYER_BATCHED)
+    assert np.array_equal(a[0], b[0]) and torch.equal(a[2], b[2])
+
+
+def test_step_k_at_least_n_is_dense_attention():
+    w = cs.custom(seq_lens=(200, 77, 513), topk=600, n_layers=2, hq=8, hkv=2, seed=31)
+    dw = device_workload(w)
+    idx, cnt, out = _run_step(dw, clsa.SCHEDULE_LAYER_BATCHED)
+    dev = bf16_dev_to_f64(out)
+    cu = w.cu_seqlens
+    for b, n in enumerate(w.seq_lens):
+        assert cnt[b] == n and np.array_equal(idx[b, :n], np.arange(n))
+        kf, vf = w.kv_f64(cu[b] + np.arange(n))
+        assert_outputs_close(dev[b], O.sparse_attention(w.q_f64([b])[0], kf, vf), f"dense row {b}")
