@@ -59,7 +59,7 @@ def _load():
         "clsa_status_string": (c_char_p, [c_int32]),
         "clsa_last_error_message": (c_char_p, []),
         "clsa_abi_version": (c_int32, []),
-        "clsa_workspace_bytes": (c_size_t, [POINTER(Dims), POINTER(Rows), c_int32]),
+        "clsa_workspace_bytes": (c_size_t, [POINTER(Dims), POINTER(Rows), c_int32, c_int32]),
         "clsa_index_scores": (c_int32, [POINTER(Dims), POINTER(Rows), P, P, P, P, c_int64, P]),
         "clsa_topk": (c_int32, [POINTER(Dims), POINTER(Rows), P, P, c_int64, P, P, P, c_size_t, P]),
         "clsa_gather_kv": (c_int32, [POINTER(Dims), POINTER(Rows), P, P, P, P, P, P, P, P]),
@@ -120,8 +120,8 @@ def make_rows(mode, n_rows, max_row_len, total_tokens, seq=0, pos0=0, cu_seqlens
     return r
 
 
-def workspace_bytes(dims: Dims, rows: Rows, schedule: int = SCHEDULE_LAYER_BATCHED) -> int:
-    n = LIB.clsa_workspace_bytes(ctypes.byref(dims), ctypes.byref(rows), schedule)
+def workspace_bytes(dims: Dims, rows: Rows, schedule: int = SCHEDULE_LAYER_BATCHED, prefill_chunk_rows: int = 0) -> int:
+    n = LIB.clsa_workspace_bytes(ctypes.byref(dims), ctypes.byref(rows), schedule, prefill_chunk_rows)
     if n == 0:
         raise CLSAError(ERR_INVALID_ARGUMENT, last_error())
     return n

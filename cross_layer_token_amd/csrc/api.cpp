@@ -90,13 +90,18 @@ const char* clsa_last_error_message(void) { return g_last_error.c_str(); }
 
 int32_t clsa_abi_version(void) { return CLSA_ABI_VERSION; }
 
-size_t clsa_workspace_bytes(const clsa_dims* dims, const clsa_rows* rows, int32_t schedule) {
+size_t clsa_workspace_bytes(const clsa_dims* dims, const clsa_rows* rows, int32_t schedule,
+                            int32_t prefill_chunk_rows) {
   if (check_common(dims, rows) != CLSA_OK) return 0;
   if (schedule != CLSA_SCHEDULE_LAYER_BATCHED && schedule != CLSA_SCHEDULE_PER_LAYER) {
     set_error(CLSA_ERR_INVALID_ARGUMENT, "unknown schedule");
     return 0;
   }
-  return workspace_bytes(dims, rows, schedule);
+  if (prefill_chunk_rows < 0) {
+    set_error(CLSA_ERR_INVALID_ARGUMENT, "prefill_chunk_rows must be >= 0");
+    return 0;
+  }
+  return workspace_bytes(dims, rows, schedule, prefill_chunk_rows);
 }
 
 clsa_status clsa_index_scores(const clsa_dims* dims, const clsa_rows* rows, const clsa_bf16* q_idx,
@@ -112,9 +117,9 @@ clsa_status clsa_index_scores(const clsa_dims* dims, const clsa_rows* rows, cons
   const RowsDev rd = rows_dev(rows, cu_seqlens);
   int e;
   if (rows->mode == CLSA_MODE_DECODE)
-    e = launch_index_scores_decode(rd, dims->d_idx, rows->total_tokens, q_idx, k_idx, scores, ld_scores, stream);
+    e = launch_index_scores_decode(rd, dims->d_idx, q_idx, k_idx, scores, ld_scores, nullptr, nullptr, 0, stream);
   else
-    e = launch_index_scores_prefill(rd, dims->d_idx, q_idx, k_idx, scores, ld_scores, stream);
+    e = launch_index_scores_prefill(rd, dims->d_idx, q_idx, k_idx, scores, ld_scores, nullptr, 0, stream);
   return device_status(e, "clsa_index_scores");
 }
 
@@ -129,9 +134,13 @@ clsa_status clsa_topk(const clsa_dims* dims, const clsa_rows* rows, const int32_
   CLSA_TRY(check_ptr(count, "count", g_err));
   if (clsa_status s = check_ld(ld_scores, rows, "ld_scores"); s != CLSA_OK) return s;
   const TopkPlan plan = plan_topk(dims, rows);
-  if (clsa_status s = check_workspace(workspace, workspace_bytes_, plan.bytes); s != CLSA_OK) return s;
+  if (clsa_status s = check_workspace(workspace, workspace_bytes_, topk_workspace(dims, rows)); s != CLSA_OK)
+    return s;
   const RowsDev rd = rows_dev(rows, cu_seqlens);
-  return device_status(launch_topk(rd, dims->topk, plan, scores, ld_scores, idx, count, workspace, stream),
+  char* ws = static_cast<char*>(workspace);
+  uint32_t* tickets = reinterpret_cast<uint32_t*>(ws);
+  return device_status(launch_topk(rd, dims->topk, plan, scores, ld_scores, idx, count,
+                                   ws + ticket_region(plan.tickets), tickets, false, stream),
                        "clsa_topk");
 }
 
@@ -175,12 +184,14 @@ clsa_status clsa_sparse_attn(const clsa_dims* dims, const clsa_rows* rows, const
     CLSA_TRY(check_ptr(idx, "idx", g_err));
   }
   if (clsa_status s = check_attn_strides(dims, n_layers_call, q_row_stride, out_row_stride); s != CLSA_OK) return s;
-  const AttnPlan plan = plan_attn(dims, rows->n_rows, n_layers_call);
-  if (clsa_status s = check_workspace(workspace, workspace_bytes_, plan.part_bytes); s != CLSA_OK) return s;
+  const AttnPlan plan = plan_attn(dims, rows->n_rows, n_layers_call, 0);
+  if (clsa_status s = check_workspace(workspace, workspace_bytes_, attn_workspace(plan)); s != CLSA_OK) return s;
   const RowsDev rd = rows_dev(rows, cu_seqlens);
+  char* ws = static_cast<char*>(workspace);
   return device_status(launch_attn(rd, dims->topk, dims->hq, dims->hkv, n_layers_call, softmax_scale(dims), plan, q,
                                    q_row_stride, compact ? k_sel : nullptr, compact ? v_sel : nullptr, k_cache,
-                                   v_cache, idx, count, out, out_row_stride, workspace, stream),
+                                   v_cache, idx, count, out, out_row_stride, ws + ticket_region(plan.tickets),
+                                   reinterpret_cast<uint32_t*>(ws), false, stream),
                        "clsa_sparse_attn");
 }
 
@@ -218,6 +229,10 @@ clsa_status clsa_step(const clsa_dims* dims, const clsa_rows* rows, const clsa_s
   const int64_t row_elems = (int64_t)L * hq * CLSA_HEAD_DIM;
   const float scale = softmax_scale(dims);
   const int chunk = sp.chunk_rows;
+  // tickets: [top-k select, R][attention, R * hkv * qblocks]; the chunk's first kernel clears them
+  uint32_t* tickets = reinterpret_cast<uint32_t*>(ws + sp.ticket_off);
+  uint32_t* topk_tickets = tickets;
+  uint32_t* attn_tickets = tickets + sp.topk.tickets;
   for (int c0 = 0; c0 < rows->n_rows; c0 += chunk) {
     clsa_rows cr = *rows;
     cr.n_rows = rows->n_rows - c0 < chunk ? rows->n_rows - c0 : chunk;
@@ -235,25 +250,33 @@ clsa_status clsa_step(const clsa_dims* dims, const clsa_rows* rows, const clsa_s
       scores = reinterpret_cast<float*>(ws + sp.scores_off);
       ld = sp.ld_scores;
     }
+    const TopkPlan tp = plan_topk(dims, &cr);
+    char* topk_ws = ws + sp.topk_off;
     const clsa_bf16* q_idx = a->q_idx + (int64_t)c0 * dims->d_idx;
-    int e = prefill ? launch_index_scores_prefill(rd, dims->d_idx, q_idx, a->k_idx, scores, ld, stream)
-                    : launch_index_scores_decode(rd, dims->d_idx, rows->total_tokens, q_idx, a->k_idx, scores, ld,
-                                                 stream);
+    int e;
+    bool have_hist = false;
+    if (prefill) {
+      e = launch_index_scores_prefill(rd, dims->d_idx, q_idx, a->k_idx, scores, ld, tickets, sp.n_tickets, stream);
+    } else {
+      uint16_t* hpart = tp.multi_wg ? reinterpret_cast<uint16_t*>(topk_ws + tp.hpart_off) : nullptr;
+      have_hist = tp.multi_wg;
+      e = launch_index_scores_decode(rd, dims->d_idx, q_idx, a->k_idx, scores, ld, hpart, tickets, sp.n_tickets,
+                                     stream);
+    }
     if (e) return device_status(e, "clsa_step: index scores");
     int32_t* idx = a->idx + (int64_t)c0 * k;
     int32_t* count = a->count + c0;
-    const TopkPlan tp = plan_topk(dims, &cr);
-    e = launch_topk(rd, k, tp, scores, ld, idx, count, ws + sp.topk_off, stream);
+    e = launch_topk(rd, k, tp, scores, ld, idx, count, topk_ws, topk_tickets, have_hist, stream);
     if (e) return device_status(e, "clsa_step: top-k");
     const clsa_bf16* q = a->q + (int64_t)c0 * row_elems;
     clsa_bf16* out = a->out + (int64_t)c0 * row_elems;
     if (a->schedule == CLSA_SCHEDULE_LAYER_BATCHED) {
-      const AttnPlan ap = plan_attn(dims, cr.n_rows, L);
+      const AttnPlan ap = plan_attn(dims, cr.n_rows, L, rows->n_rows);
       e = launch_attn(rd, k, hq, hkv, L, scale, ap, q, row_elems, nullptr, nullptr, a->k_cache, a->v_cache, idx, count,
-                      out, row_elems, ws + sp.part_off, stream);
+                      out, row_elems, ws + sp.part_off, attn_tickets, true, stream);
       if (e) return device_status(e, "clsa_step: attention");
     } else {
-      const AttnPlan ap = plan_attn(dims, cr.n_rows, 1);
+      const AttnPlan ap = plan_attn(dims, cr.n_rows, 1, rows->n_rows);
       clsa_bf16* ksel = nullptr;
       clsa_bf16* vsel = nullptr;
       if (!prefill) {
@@ -265,7 +288,7 @@ clsa_status clsa_step(const clsa_dims* dims, const clsa_rows* rows, const clsa_s
       for (int l = 0; l < L; ++l) {
         e = launch_attn(rd, k, hq, hkv, 1, scale, ap, q + (int64_t)l * hq * CLSA_HEAD_DIM, row_elems, ksel, vsel,
                         a->k_cache, a->v_cache, idx, count, out + (int64_t)l * hq * CLSA_HEAD_DIM, row_elems,
-                        ws + sp.part_off, stream);
+                        ws + sp.part_off, attn_tickets, true, stream);
         if (e) return device_status(e, "clsa_step: attention layer");
       }
     }

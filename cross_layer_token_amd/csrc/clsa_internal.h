@@ -14,24 +14,32 @@ namespace clsa {
 // Rows no longer than this are selected by one workgroup holding the whole row in LDS;
 // longer rows use the multi-workgroup histogram select.
 constexpr int kLdsRowCap = 12288;
-// Bins of the first histogram level of the multi-workgroup select (top 12 key bits).
-constexpr int kHist1Bins = 4096;
-// Per-row state words of the multi-workgroup select.
-constexpr int kTopkStateWords = 16;
-// Scores handled by one workgroup of the multi-workgroup select passes.
-constexpr int kTopkChunk = 8192;
+// Tokens per workgroup of the decode score kernel (also the histogram partial granularity).
+constexpr int kIdxChunk = 4096;
+// First histogram level of the long-row select: the top kTopkBinBits bits of the score key.
+constexpr int kTopkBinBits = 11;
+constexpr int kTopkBins = 1 << kTopkBinBits;
+// Scores classified by one workgroup of the long-row select.
+constexpr int kSelectSpan = 16384;
 // Keys per attention tile.
 constexpr int kAttnTile = 64;
-// fp32 words per split partial record: acc[128], m, l, 2 words of padding (16-byte records).
-constexpr int kPartStride = 132;
+// fp32 words of one attention split partial per (row, KV head, query block): 4 waves x 64 lanes
+// x (32 accumulators + m + l).
+constexpr int kAttnPartFloats = 4 * 34 * 64;
 // Default rows per prefill chunk of clsa_step.
 constexpr int kPrefillChunkRows = 1024;
 
 // ---- host-side plan (pure functions, no HIP) ------------------------------------------------
 struct TopkPlan {
   bool multi_wg = false;   // long rows: histogram select over many workgroups
-  size_t hist_off = 0, state_off = 0, sure_off = 0, cand_off = 0;
+  int hist_chunks = 0;     // histogram partials per row (kIdxChunk scores each)
+  int spans = 0;           // select workgroups per row (kSelectSpan scores each)
+  size_t hpart_off = 0;    // uint16 [R, hist_chunks, kTopkBins]
+  size_t cnt_off = 0;      // uint32 [R, spans]
+  size_t slot_off = 0;     // uint2 [R, max_row_len]: per-span ordered lists (key, index)
+  size_t list_off = 0;     // uint2 [R, max_row_len]: the concatenated list of the last workgroup
   size_t bytes = 0;
+  int tickets = 0;         // uint32 words of ticket memory needed (R when multi_wg)
 };
 
 struct AttnPlan {
@@ -40,14 +48,19 @@ struct AttnPlan {
   int qblocks = 0;         // blocks of 64 query rows
   int splits = 1;          // the selected rows are split over this many workgroups
   int keys_per_split = 0;  // multiple of kAttnTile
-  size_t part_bytes = 0;   // fp32 partials (m, l, acc[128]) when splits > 1
+  size_t part_bytes = 0;   // fp32 partials [splits, R, hkv, qblocks, kAttnPartFloats] when splits > 1
+  int tickets = 0;         // uint32 words of ticket memory: one per (row, KV head, query block)
 };
 
+// Ticket words live in one region that the first kernel of a call clears; every ticket is
+// reset by the workgroup that consumes it, so later launches of the same call can reuse it.
 struct StepPlan {
   TopkPlan topk;
   AttnPlan attn;
   int chunk_rows = 0;      // prefill: rows per chunk; decode: R
   int64_t ld_scores = 0;   // workspace scores leading dimension
+  size_t ticket_off = 0;   // [topk tickets | attention tickets]
+  int n_tickets = 0;
   size_t scores_off = 0, scores_bytes = 0;
   size_t topk_off = 0;
   size_t part_off = 0;
@@ -62,12 +75,19 @@ clsa_status check_ptr(const void* p, const char* name, std::string& err);
 clsa_status check_ptr_opt(const void* p, const char* name, std::string& err);
 
 TopkPlan plan_topk(const clsa_dims* d, const clsa_rows* r);
-AttnPlan plan_attn(const clsa_dims* d, int n_rows, int n_layers_call);
+// n_rows: rows of this launch (buffer sizes); split_rows: rows that decide the split count
+// (0 = n_rows).
+AttnPlan plan_attn(const clsa_dims* d, int n_rows, int n_layers_call, int split_rows);
 StepPlan plan_step(const clsa_dims* d, const clsa_rows* r, int schedule, bool user_scores, bool user_sel,
                    int prefill_chunk_rows);
-size_t workspace_bytes(const clsa_dims* d, const clsa_rows* r, int schedule);
+size_t workspace_bytes(const clsa_dims* d, const clsa_rows* r, int schedule, int prefill_chunk_rows);
+// Standalone calls: [tickets][plan buffers].
+size_t topk_workspace(const clsa_dims* d, const clsa_rows* r);
+size_t attn_workspace(const AttnPlan& a);
+
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline size_t ticket_region(int words) { return words ? align_up((size_t)words * 4, 256) : 0; }
 inline float softmax_scale(const clsa_dims* d) {
   return d->sm_scale > 0.f ? d->sm_scale : 1.0f / 11.313708498984761f;  // 1/sqrt(128)
 }
@@ -79,18 +99,23 @@ struct RowsDev {
   const int32_t* cu;  // device cu_seqlens
 };
 
-int launch_index_scores_decode(const RowsDev& rows, int d_idx, int64_t total_tokens, const uint16_t* q_idx,
-                               const uint16_t* k_idx, float* scores, int64_t ld, void* stream);
+// `clear` (n_clear words) is zeroed by the launch before any other kernel of the call reads it.
+int launch_index_scores_decode(const RowsDev& rows, int d_idx, const uint16_t* q_idx, const uint16_t* k_idx,
+                               float* scores, int64_t ld, uint16_t* hpart, uint32_t* clear, int n_clear,
+                               void* stream);
 int launch_index_scores_prefill(const RowsDev& rows, int d_idx, const uint16_t* q_idx, const uint16_t* k_idx,
-                                float* scores, int64_t ld, void* stream);
+                                float* scores, int64_t ld, uint32_t* clear, int n_clear, void* stream);
+// have_hist: the score kernel already wrote the histogram partials and cleared the tickets.
 int launch_topk(const RowsDev& rows, int k, const TopkPlan& plan, const float* scores, int64_t ld,
-                int32_t* idx, int32_t* count, void* ws, void* stream);
+                int32_t* idx, int32_t* count, void* ws, uint32_t* tickets, bool have_hist, void* stream);
 int launch_gather(const RowsDev& rows, int k, int hkv, const uint16_t* kc, const uint16_t* vc,
                   const int32_t* idx, const int32_t* count, uint16_t* ks, uint16_t* vs, void* stream);
+// tickets_clear: the tickets are known to be zero (cleared earlier in the call).
 int launch_attn(const RowsDev& rows, int k, int hq, int hkv, int n_layers_call, float scale,
                 const AttnPlan& plan, const uint16_t* q, int64_t q_stride, const uint16_t* ksel,
                 const uint16_t* vsel, const uint16_t* kc, const uint16_t* vc, const int32_t* idx,
-                const int32_t* count, uint16_t* out, int64_t o_stride, void* part, void* stream);
+                const int32_t* count, uint16_t* out, int64_t o_stride, void* part, uint32_t* tickets,
+                bool tickets_clear, void* stream);
 const char* device_error_string(int err);
 
 }  // namespace clsa

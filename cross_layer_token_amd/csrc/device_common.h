@@ -67,6 +67,48 @@ __device__ __forceinline__ float dpp_partner(float v) {
   return __int_as_float(x);
 }
 
+// ---- handing data from one workgroup to another inside a kernel ----------------------------
+// A device-scope fence (__threadfence) writes back and invalidates the whole L2 of the XCD; done
+// by every workgroup it serialises the chip.  Instead, data that another workgroup will read is
+// stored with device-scope relaxed atomic stores (written through to the device coherence point),
+// each thread waits for its stores to complete, and the reader uses device-scope relaxed atomic
+// loads.  The one atomic ticket per workgroup then orders "all producers done" before the reads.
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_dev(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_dev(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every memory operation this wave issued has completed.
+__device__ __forceinline__ void wait_memory() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Every thread calls this after storing (with st_dev) what the last workgroup will read.  Returns
+// true in all threads of the workgroup that arrives last (of `arrivals`), which also resets the
+// ticket to zero for the next launch.  `flag` is one int of LDS.
+__device__ __forceinline__ bool arrive_last(uint32_t* ticket, uint32_t arrivals, int* flag) {
+  wait_memory();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    flag[0] = prev == arrivals - 1;
+    if (prev == arrivals - 1) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  return flag[0] != 0;
+}
+
 // Block-wide exclusive scan of one int per thread (blockDim.x a multiple of 64, <= 1024).
 // `scratch` holds at least blockDim.x / 64 + 1 ints.  Returns the exclusive prefix and sets
 // *total.  Contains __syncthreads().

@@ -9,8 +9,11 @@
 // in the layer-batched schedule every K/V tile brought into LDS serves L * Hq / Hkv queries.
 // Per 64-key tile: S^T = K Q^T and O^T += V^T P^T on bf16 MFMA 16x16x32 with fp32 accumulate;
 // the online softmax (exp2 domain) keeps every statistic of a query in the lane that owns the
-// query's column, so rescaling needs no cross-lane traffic.  Splits are recombined by a small
-// kernel from fp32 partials (m, l, acc).
+// query's column, so rescaling needs no cross-lane traffic.  The next tile's K/V rows are loaded
+// into registers while the current tile is computed.  When the keys are split over several
+// workgroups, each writes fp32 partials (m, l, acc) with device-scope stores and the last to
+// arrive (atomic ticket) recombines them, so no separate pass is launched and no workgroup
+// needs a device-wide cache flush.
 #include "device_common.h"
 
 namespace clsa {
@@ -18,6 +21,8 @@ namespace clsa {
 namespace {
 
 constexpr int kAttnThreads = 256;
+constexpr int kAttnPartWave = 34 * 64;             // floats per wave: acc 32 x 64 lanes, m, l
+constexpr int kAttnPartWG = 4 * kAttnPartWave;     // floats per workgroup partial
 constexpr int kKsStride = CLSA_HEAD_DIM + 8;  // bf16 elements per K row in LDS (16-byte pad)
 constexpr int kVtStride = kAttnTile + 4;      // bf16 elements per transposed V row in LDS
 
@@ -33,13 +38,15 @@ struct AttnArgs {
   const int32_t* count;
   uint16_t* out;
   int64_t o_stride;
-  float* part;  // [splits, R, lc, hq, kPartStride]
+  float* part;         // [splits, R, hkv, qblocks, kAttnPartWG] in the lanes' layout
+  uint32_t* tickets;   // [R, hkv, qblocks], zero on entry, reset by their last workgroup
 };
 
 template <bool FROM_CACHE>
 __global__ __launch_bounds__(kAttnThreads) void k_sparse_attn(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t ks[kAttnTile * kKsStride];
   __shared__ __attribute__((aligned(16))) uint16_t vt[CLSA_HEAD_DIM * kVtStride];
+  __shared__ int flag[1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, grp = lane >> 4;
   int bid = blockIdx.x;
@@ -81,24 +88,42 @@ __global__ __launch_bounds__(kAttnThreads) void k_sparse_attn(AttnArgs a) {
   const int ld_chunk = threadIdx.x & 15;  // 8 head_dim elements
   const int ld_key4 = threadIdx.x >> 4;   // keys 4*ld_key4 .. +3
 
-  for (int kt = kbeg; kt < kend; kt += kAttnTile) {
-    const int nvalid = kend - kt < kAttnTile ? kend - kt : kAttnTile;
-    uint4 kv[4], vv[4];
+  // token ids of this thread's 4 keys in the tile starting at kt (cache source only)
+  auto load_ids = [&](int kt, int (&ids)[4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int key = ld_key4 * 4 + i;
+      const int key = kt + ld_key4 * 4 + i;
+      ids[i] = (FROM_CACHE && key < kend) ? irow[key] : 0;
+    }
+  };
+  auto load_kv = [&](int kt, const int (&ids)[4], uint4 (&kv)[4], uint4 (&vv)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = kt + ld_key4 * 4 + i;
       kv[i] = make_uint4(0u, 0u, 0u, 0u);
       vv[i] = make_uint4(0u, 0u, 0u, 0u);
-      if (key < nvalid) {
+      if (key < kend) {
         int64_t src;
         if (FROM_CACHE)
-          src = ((tok_base + irow[kt + key]) * a.hkv + g) * CLSA_HEAD_DIM + ld_chunk * 8;
+          src = ((tok_base + ids[i]) * a.hkv + g) * CLSA_HEAD_DIM + ld_chunk * 8;
         else
-          src = (((int64_t)r * a.hkv + g) * a.k + kt + key) * CLSA_HEAD_DIM + ld_chunk * 8;
+          src = (((int64_t)r * a.hkv + g) * a.k + key) * CLSA_HEAD_DIM + ld_chunk * 8;
         kv[i] = *reinterpret_cast<const uint4*>(a.ksrc + src);
         vv[i] = *reinterpret_cast<const uint4*>(a.vsrc + src);
       }
     }
+  };
+
+  int ids_next[4];
+  uint4 kv[4], vv[4];
+  if (kbeg < kend) {
+    int ids0[4];
+    load_ids(kbeg, ids0);
+    load_kv(kbeg, ids0, kv, vv);
+    load_ids(kbeg + kAttnTile, ids_next);
+  }
+  for (int kt = kbeg; kt < kend; kt += kAttnTile) {
+    const int nvalid = kend - kt < kAttnTile ? kend - kt : kAttnTile;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       *reinterpret_cast<uint4*>(&ks[(ld_key4 * 4 + i) * kKsStride + ld_chunk * 8]) = kv[i];
@@ -121,6 +146,12 @@ __global__ __launch_bounds__(kAttnThreads) void k_sparse_attn(AttnArgs a) {
       }
     }
     __syncthreads();
+    // issue the next tile's loads now; they land while this tile is computed
+    const int nxt = kt + kAttnTile;
+    if (nxt < kend) {
+      load_kv(nxt, ids_next, kv, vv);
+      load_ids(nxt + kAttnTile, ids_next);
+    }
     if (wave_active) {
       floatx4_t s[4];
 #pragma unroll
@@ -183,54 +214,85 @@ __global__ __launch_bounds__(kAttnThreads) void k_sparse_attn(AttnArgs a) {
     }
     __syncthreads();
   }
-  if (!wave_active) return;
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
-  if (!q_valid) return;
   // acc[ht][j]: head_dim ht*16 + grp*4 + j of this lane's query
+  uint16_t* op = a.out + (int64_t)r * a.o_stride + ((int64_t)layer * a.hq + head) * CLSA_HEAD_DIM;
   if (a.splits == 1) {
+    if (!q_valid) return;
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    uint16_t* op = a.out + (int64_t)r * a.o_stride + ((int64_t)layer * a.hq + head) * CLSA_HEAD_DIM;
 #pragma unroll
     for (int ht = 0; ht < 8; ++ht) {
       const uint32_t lo = f32_to_bf16(acc[ht][0] * inv) | (f32_to_bf16(acc[ht][1] * inv) << 16);
       const uint32_t hi = f32_to_bf16(acc[ht][2] * inv) | (f32_to_bf16(acc[ht][3] * inv) << 16);
       *reinterpret_cast<uint2*>(op + ht * 16 + grp * 4) = make_uint2(lo, hi);
     }
-  } else {
-    const int R = a.rw.n_rows;
-    float* pp = a.part + ((((int64_t)split * R + r) * a.lc + layer) * a.hq + head) * kPartStride;
+    return;
+  }
+  // Split partial of this workgroup, in the lanes' own layout (each store instruction of a wave
+  // covers 256 contiguous bytes): per wave [acc: 8 ht x 4 j x 64 lanes][m: 64][l: 64].  The last
+  // split of this (row, KV head, query block) to arrive recombines them.
+  const int64_t wg_rec = (((int64_t)r * a.hkv + g) * a.qblocks + qb) * kAttnPartWG;
+  const int64_t split_stride = (int64_t)a.rw.n_rows * a.hkv * a.qblocks * kAttnPartWG;
+  float* pw = a.part + wg_rec + wave * kAttnPartWave;
+  {
+    float* pp = pw + split * split_stride;
 #pragma unroll
     for (int ht = 0; ht < 8; ++ht)
-      *reinterpret_cast<float4*>(pp + ht * 16 + grp * 4) = make_float4(acc[ht][0], acc[ht][1], acc[ht][2], acc[ht][3]);
-    if (grp == 0) {
-      pp[CLSA_HEAD_DIM] = m_run;
-      pp[CLSA_HEAD_DIM + 1] = l_run;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) st_dev(pp + (ht * 4 + j) * 64 + lane, acc[ht][j]);
+    st_dev(pp + 32 * 64 + lane, m_run);
+    st_dev(pp + 33 * 64 + lane, l_run);
+  }
+  uint32_t* ticket = a.tickets + ((int64_t)r * a.hkv + g) * a.qblocks + qb;
+  if (!arrive_last(ticket, (uint32_t)a.splits, flag)) return;
+  if (!q_valid) return;
+  // Fold the splits in split order (whichever workgroup arrives last, the arithmetic is the
+  // same, so the result is deterministic); this workgroup's own partial is still in registers.
+  float M = -INFINITY, den = 0.f;
+  float tot[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) tot[i] = 0.f;
+  for (int s2 = 0; s2 < a.splits; ++s2) {
+    float v[32], ms, ls;
+    if (s2 == split) {
+#pragma unroll
+      for (int ht = 0; ht < 8; ++ht)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[ht * 4 + j] = acc[ht][j];
+      ms = m_run;
+      ls = l_run;
+    } else {
+      const float* ps = pw + s2 * split_stride;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) v[i] = ld_dev(ps + i * 64 + lane);
+      ms = ld_dev(ps + 32 * 64 + lane);
+      ls = ld_dev(ps + 33 * 64 + lane);
     }
+    if (ms == -INFINITY) continue;
+    const float m_new = fmaxf(M, ms);
+    const float c_old = exp2f(M - m_new), c_new = exp2f(ms - m_new);
+    den = den * c_old + ls * c_new;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) tot[i] = tot[i] * c_old + v[i] * c_new;
+    M = m_new;
+  }
+#pragma unroll
+  for (int ht = 0; ht < 8; ++ht)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[ht][j] = tot[ht * 4 + j];
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+#pragma unroll
+  for (int ht = 0; ht < 8; ++ht) {
+    const uint32_t lo = f32_to_bf16(acc[ht][0] * inv) | (f32_to_bf16(acc[ht][1] * inv) << 16);
+    const uint32_t hi = f32_to_bf16(acc[ht][2] * inv) | (f32_to_bf16(acc[ht][3] * inv) << 16);
+    *reinterpret_cast<uint2*>(op + ht * 16 + grp * 4) = make_uint2(lo, hi);
   }
 }
 
-// Recombine the splits of one (row, layer, head): O = sum_s e^(m_s - M) acc_s / sum_s e^(m_s - M) l_s.
-__global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ part, int splits, int R, int lc,
-                                                       int hq, uint16_t* __restrict__ out, int64_t o_stride) {
-  const int r = blockIdx.y;
-  const int lh = blockIdx.x;  // layer * hq + head
-  const int d = threadIdx.x;
-  const int64_t stride_s = (int64_t)R * lc * hq * kPartStride;
-  const float* p0 = part + ((int64_t)r * lc * hq + lh) * kPartStride;
-  float M = -INFINITY;
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, p0[s * stride_s + CLSA_HEAD_DIM]);
-  float num = 0.f, den = 0.f;
-  for (int s = 0; s < splits; ++s) {
-    const float* ps = p0 + s * stride_s;
-    const float ms = ps[CLSA_HEAD_DIM];
-    if (ms == -INFINITY) continue;
-    const float w = exp2f(ms - M);
-    num += w * ps[d];
-    den += w * ps[CLSA_HEAD_DIM + 1];
-  }
-  const float o = den > 0.f ? num / den : 0.f;
-  out[(int64_t)r * o_stride + (int64_t)lh * CLSA_HEAD_DIM + d] = (uint16_t)f32_to_bf16(o);
+__global__ void k_clear_u32(uint32_t* __restrict__ p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
 }
 
 // Selector: k_sel[r, g, i, :] = k_cache[cu[seq] + idx[r, i], g, :] for i < count[r], zero after.
@@ -267,7 +329,7 @@ __global__ __launch_bounds__(256) void k_gather_kv(RowsDev rw, int k, int hkv, c
 int launch_attn(const RowsDev& rows, int k, int hq, int hkv, int n_layers_call, float scale, const AttnPlan& plan,
                 const uint16_t* q, int64_t q_stride, const uint16_t* ksel, const uint16_t* vsel, const uint16_t* kc,
                 const uint16_t* vc, const int32_t* idx, const int32_t* count, uint16_t* out, int64_t o_stride,
-                void* part, void* stream) {
+                void* part, uint32_t* tickets, bool tickets_clear, void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   AttnArgs a;
   a.rw = rows;
@@ -291,14 +353,14 @@ int launch_attn(const RowsDev& rows, int k, int hq, int hkv, int n_layers_call, 
   a.out = out;
   a.o_stride = o_stride;
   a.part = static_cast<float*>(part);
+  a.tickets = tickets;
+  if (plan.splits > 1 && !tickets_clear)
+    hipLaunchKernelGGL(k_clear_u32, dim3((plan.tickets + 255) / 256), dim3(256), 0, s, tickets, plan.tickets);
   const dim3 grid((unsigned)(plan.splits * plan.qblocks * hkv), (unsigned)rows.n_rows);
   if (from_cache)
     hipLaunchKernelGGL(k_sparse_attn<true>, grid, dim3(kAttnThreads), 0, s, a);
   else
     hipLaunchKernelGGL(k_sparse_attn<false>, grid, dim3(kAttnThreads), 0, s, a);
-  if (plan.splits > 1)
-    hipLaunchKernelGGL(k_attn_combine, dim3((unsigned)(n_layers_call * hq), (unsigned)rows.n_rows), dim3(128), 0, s,
-                       static_cast<const float*>(part), plan.splits, rows.n_rows, n_layers_call, hq, out, o_stride);
   return (int)hipGetLastError();
 }
 

@@ -1,12 +1,12 @@
 // Routing scores I_t[j] = q_idx,t . K_idx[j] - the first half of the routing equation on the
 // picx.dev summary of "You Only Index Once" (Methodology > Architecture Overview, eq. 2).
 //
-// Decode: a bandwidth-bound GEMV that streams every K_idx row exactly once.  Workgroups own
-// equal slices of the packed token axis (so ragged batches are balanced by tokens, not by
-// sequences); a slice that crosses a sequence boundary is processed per sequence segment.
-// Each 16-byte K_idx chunk meets the query chunk in v_dot2 (bf16 x bf16 -> fp32), and the
-// per-lane partial sums of 16 rows are reduce-scattered over the row's lanes with DPP, so that
-// every lane ends up owning one finished row score.
+// Decode: a bandwidth-bound GEMV that streams every K_idx row exactly once.  A workgroup owns
+// one chunk of one sequence.  Each 16-byte K_idx chunk meets the query chunk in v_dot2 (bf16 x
+// bf16 -> fp32), and the per-lane partial sums of 16 rows are reduce-scattered over the row's
+// lanes with DPP, so that every lane ends up owning one finished row score.  When asked, the
+// workgroup also histograms the top key bits of its scores (the first level of the top-k
+// select), which saves the select a pass over the scores.
 //
 // Prefill: the causal product Q_idx K_idx^T on the matrix cores (bf16 MFMA 16x16x32, fp32
 // accumulate), skipping tiles above the diagonal.
@@ -40,65 +40,69 @@ __device__ __forceinline__ void rs_step(float* p, int sub) {
 
 constexpr int kIdxThreads = 256;
 
+// One workgroup = one chunk of kIdxChunk tokens of one sequence.  Besides the scores it can
+// write the chunk's histogram of the top kTopkBinBits key bits (for the top-k select) and
+// clear the select's per-row tickets (consumed by later kernels on the same stream).
 template <int D>
 __global__ __launch_bounds__(kIdxThreads) void k_index_scores_decode(const uint16_t* __restrict__ q_idx,
                                                                        const uint16_t* __restrict__ k_idx,
-                                                                       const int32_t* __restrict__ cu, int batch,
-                                                                       int64_t total_tokens, int max_row_len,
-                                                                       float* __restrict__ scores, int64_t ld,
-                                                                       int chunk) {
+                                                                       const int32_t* __restrict__ cu,
+                                                                       int max_row_len, float* __restrict__ scores,
+                                                                       int64_t ld, uint16_t* __restrict__ hpart,
+                                                                       int hpart_chunks, uint32_t* __restrict__ clear,
+                                                                       int n_clear) {
   constexpr int LPR = D / 8;   // lanes per K_idx row (16 bytes each)
   constexpr int NG = 64 / LPR; // row groups per wave
   constexpr int NR = LPR;      // rows per lane per iteration: one finished row per lane
+  __shared__ uint32_t hist[kTopkBins];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lg = lane / LPR, sub = lane % LPR;
-  const int64_t t0 = (int64_t)blockIdx.x * chunk;
-  const int64_t t1 = t0 + chunk < total_tokens ? t0 + chunk : total_tokens;
-  if (t0 >= t1) return;
-  // sequence holding t0: the largest b < batch with cu[b] <= t0
-  int lo = 0, hi = batch - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if ((int64_t)cu[mid] <= t0) lo = mid; else hi = mid - 1;
+  const int b = blockIdx.y;
+  const int c = blockIdx.x;
+  if (clear != nullptr && b == 0 && c == 0)
+    for (int i = threadIdx.x; i < n_clear; i += blockDim.x) clear[i] = 0u;
+  int n = cu[b + 1] - cu[b];
+  n = n < 0 ? 0 : (n > max_row_len ? max_row_len : n);
+  const int t0 = c * kIdxChunk;
+  if (t0 >= n) return;
+  const int t1 = t0 + kIdxChunk < n ? t0 + kIdxChunk : n;
+  if (hpart != nullptr) {
+    for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) hist[i] = 0u;
+    __syncthreads();
   }
-  int b = lo;
-  int64_t t = t0;
-  while (t < t1) {
-    while (b < batch - 1 && (int64_t)cu[b + 1] <= t) ++b;
-    const int64_t seq_end = (int64_t)cu[b + 1];
-    const int64_t seg_end = seq_end < t1 ? seq_end : t1;
-    if (seg_end <= t) break;  // inconsistent cu_seqlens: nothing valid left in this slice
-    const int64_t base = cu[b];
-    const uint4 qv = *reinterpret_cast<const uint4*>(q_idx + (size_t)b * D + sub * 8);
-    float* srow = scores + (int64_t)b * ld;
-    for (int64_t it = t + wave * 64; it < seg_end; it += (kIdxThreads / 64) * 64) {
-      uint4 kv[NR];
+  const uint16_t* kbase = k_idx + (int64_t)cu[b] * D;
+  const uint4 qv = *reinterpret_cast<const uint4*>(q_idx + (size_t)b * D + sub * 8);
+  float* srow = scores + (int64_t)b * ld;
+  for (int it = t0 + wave * 64; it < t1; it += (kIdxThreads / 64) * 64) {
+    uint4 kv[NR];
 #pragma unroll
-      for (int i = 0; i < NR; ++i) {
-        const int64_t row = it + i * NG + lg;
-        kv[i] = row < seg_end ? load_stream16(k_idx + row * D + sub * 8)
-                              : make_uint4(0u, 0u, 0u, 0u);
-      }
-      float p[NR];
-#pragma unroll
-      for (int i = 0; i < NR; ++i) p[i] = dot8(kv[i], qv, 0.f);
-      if constexpr (LPR == 16) {
-        rs_step<8, 8>(p, sub);
-        rs_step<4, 4>(p, sub);
-        rs_step<2, 2>(p, sub);
-        rs_step<1, 1>(p, sub);
-      } else {
-        rs_step<4, 4>(p, sub);
-        rs_step<2, 2>(p, sub);
-        rs_step<1, 1>(p, sub);
-      }
-      const int64_t row = it + sub * NG + lg;
-      if (row < seg_end) {
-        const int64_t local = row - base;
-        if (local < max_row_len) srow[local] = p[0];
-      }
+    for (int i = 0; i < NR; ++i) {
+      const int row = it + i * NG + lg;
+      kv[i] = row < t1 ? load_stream16(kbase + (int64_t)row * D + sub * 8) : make_uint4(0u, 0u, 0u, 0u);
     }
-    t = seg_end;
+    float p[NR];
+#pragma unroll
+    for (int i = 0; i < NR; ++i) p[i] = dot8(kv[i], qv, 0.f);
+    if constexpr (LPR == 16) {
+      rs_step<8, 8>(p, sub);
+      rs_step<4, 4>(p, sub);
+      rs_step<2, 2>(p, sub);
+      rs_step<1, 1>(p, sub);
+    } else {
+      rs_step<4, 4>(p, sub);
+      rs_step<2, 2>(p, sub);
+      rs_step<1, 1>(p, sub);
+    }
+    const int row = it + sub * NG + lg;
+    if (row < t1) {
+      srow[row] = p[0];
+      if (hpart != nullptr) atomicAdd(&hist[score_key(p[0]) >> (32 - kTopkBinBits)], 1u);
+    }
+  }
+  if (hpart != nullptr) {
+    __syncthreads();
+    uint16_t* hp = hpart + ((int64_t)b * hpart_chunks + c) * kTopkBins;
+    for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) hp[i] = (uint16_t)hist[i];
   }
 }
 
@@ -109,10 +113,13 @@ template <int D>
 __global__ __launch_bounds__(256) void k_index_scores_prefill(const uint16_t* __restrict__ q_idx,
                                                                const uint16_t* __restrict__ k_idx,
                                                                const int32_t* __restrict__ cu, int seq, int pos0,
-                                                               int n_rows, float* __restrict__ scores, int64_t ld) {
+                                                               int n_rows, float* __restrict__ scores, int64_t ld,
+                                                               uint32_t* __restrict__ clear, int n_clear) {
   constexpr int KS = D / 32;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  if (clear != nullptr && blockIdx.x == 0 && blockIdx.y == 0)
+    for (int i = threadIdx.x; i < n_clear; i += blockDim.x) clear[i] = 0u;
   const int last_row = (r0 + 63 < n_rows - 1) ? r0 + 63 : n_rows - 1;
   if (c0 > pos0 + last_row) return;  // tile entirely above the causal diagonal
   const int64_t base = cu[seq];
@@ -150,31 +157,32 @@ __global__ __launch_bounds__(256) void k_index_scores_prefill(const uint16_t* __
 
 }  // namespace
 
-int launch_index_scores_decode(const RowsDev& rows, int d_idx, int64_t total_tokens, const uint16_t* q_idx,
-                               const uint16_t* k_idx, float* scores, int64_t ld, void* stream) {
-  const int chunk = 4096;
-  const int64_t nblk = (total_tokens + chunk - 1) / chunk;
+int launch_index_scores_decode(const RowsDev& rows, int d_idx, const uint16_t* q_idx, const uint16_t* k_idx,
+                               float* scores, int64_t ld, uint16_t* hpart, uint32_t* clear, int n_clear,
+                               void* stream) {
+  const int chunks = (rows.max_row_len + kIdxChunk - 1) / kIdxChunk;
+  const dim3 grid((unsigned)chunks, (unsigned)rows.n_rows);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (d_idx == 128)
-    hipLaunchKernelGGL(k_index_scores_decode<128>, dim3((unsigned)nblk), dim3(kIdxThreads), 0, s, q_idx, k_idx,
-                       rows.cu, rows.n_rows, total_tokens, rows.max_row_len, scores, ld, chunk);
+    hipLaunchKernelGGL(k_index_scores_decode<128>, grid, dim3(kIdxThreads), 0, s, q_idx, k_idx, rows.cu,
+                       rows.max_row_len, scores, ld, hpart, chunks, clear, n_clear);
   else
-    hipLaunchKernelGGL(k_index_scores_decode<64>, dim3((unsigned)nblk), dim3(kIdxThreads), 0, s, q_idx, k_idx,
-                       rows.cu, rows.n_rows, total_tokens, rows.max_row_len, scores, ld, chunk);
+    hipLaunchKernelGGL(k_index_scores_decode<64>, grid, dim3(kIdxThreads), 0, s, q_idx, k_idx, rows.cu,
+                       rows.max_row_len, scores, ld, hpart, chunks, clear, n_clear);
   return (int)hipGetLastError();
 }
 
 int launch_index_scores_prefill(const RowsDev& rows, int d_idx, const uint16_t* q_idx, const uint16_t* k_idx,
-                                float* scores, int64_t ld, void* stream) {
+                                float* scores, int64_t ld, uint32_t* clear, int n_clear, void* stream) {
   const int ncols = rows.pos0 + rows.n_rows;
   dim3 grid((ncols + 63) / 64, (rows.n_rows + 63) / 64);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (d_idx == 128)
     hipLaunchKernelGGL(k_index_scores_prefill<128>, grid, dim3(256), 0, s, q_idx, k_idx, rows.cu, rows.seq,
-                       rows.pos0, rows.n_rows, scores, ld);
+                       rows.pos0, rows.n_rows, scores, ld, clear, n_clear);
   else
     hipLaunchKernelGGL(k_index_scores_prefill<64>, grid, dim3(256), 0, s, q_idx, k_idx, rows.cu, rows.seq,
-                       rows.pos0, rows.n_rows, scores, ld);
+                       rows.pos0, rows.n_rows, scores, ld, clear, n_clear);
   return (int)hipGetLastError();
 }
 

@@ -8,11 +8,11 @@
 // decisions are integer counts, so the result is unique and independent of thread timing.
 //
 // Short rows (<= kLdsRowCap): one workgroup per row holds the row's keys in LDS.
-// Long rows: many workgroups per row.  Pass 1 builds a per-row histogram of the top 12 key
-// bits; the last workgroup of a row (atomic ticket) finds the bin holding T.  Pass 2 appends
-// the tokens above that bin ("sure") and inside it ("candidates") to per-row lists; the last
-// workgroup of the row refines T and the index cut-off among the candidates and writes the
-// ascending index list through an LDS bitmap.
+// Long rows: a first-level histogram of the top key bits comes in per-chunk partials (written
+// by the score kernel, or by k_topk_hist_partials); each select workgroup sums them, finds the
+// bin holding T, and compacts its span's scores at or above that bin in index order; the last
+// workgroup of the row (one atomic ticket per workgroup, nothing contended) finishes the
+// selection over that short list.  No workgroup ever waits for another.
 #include "device_common.h"
 
 namespace clsa {
@@ -21,7 +21,6 @@ namespace {
 
 constexpr int kRowThreads = 512;
 constexpr int kPassThreads = 256;
-constexpr int kBitmapWords = 4096;  // 2^17 tokens per bitmap segment
 
 // Find the bin d (scanning from the top bin down) whose cumulative count from the top first
 // reaches `need`; returns d and sets *above = count of bins above d.  hist has nb bins in LDS;
@@ -148,137 +147,192 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_rows_lds(RowsDev rw, const
 }
 
 // ---------------------------------------------------------------------------- long rows
-// Per-row state words (uint32): 0 done1, 1 done2, 2 nsure, 3 ncand, 4 t1, 5 above1, 6 need1
-struct LongRowsArgs {
+struct SelectArgs {
   RowsDev rw;
   const float* scores;
   int64_t ld;
   int k;
   int32_t* out;
   int32_t* count;
-  uint32_t* hist1;  // [R, kHist1Bins]
-  uint32_t* state;  // [R, kTopkStateWords]
-  int32_t* sure;    // [R, k]
-  uint2* cand;      // [R, max_row_len] (key, index)
+  uint16_t* hpart;        // [R, hist_chunks, kTopkBins] per-chunk histograms of key >> (32 - kTopkBinBits)
+  int hist_chunks;
+  uint32_t* ticket;       // [R], zero on entry
+  uint32_t* cnt;          // [R, spans]
+  int spans;
+  uint2* slot;            // [R, max_row_len]
+  uint2* list;            // [R, max_row_len]
 };
 
-__global__ void k_topk_clear(uint32_t* __restrict__ hist1, uint32_t* __restrict__ state, int n_rows) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < (int64_t)n_rows * kHist1Bins) hist1[i] = 0;
-  if (i < (int64_t)n_rows * kTopkStateWords) state[i] = 0;
+constexpr int kSelThreads = 1024;
+constexpr int kHistThreads = 256;
+
+// Histogram partials of the scores (used when no score kernel produced them); clears the tickets.
+__global__ __launch_bounds__(kHistThreads) void k_topk_hist_partials(SelectArgs a) {
+  __shared__ uint32_t hist[kTopkBins];
+  const int r = blockIdx.y, c = blockIdx.x;
+  if (r == 0 && c == 0)
+    for (int i = threadIdx.x; i < a.rw.n_rows; i += blockDim.x) a.ticket[i] = 0u;
+  const int n = row_len(a.rw, r);
+  const int t0 = c * kIdxChunk;
+  if (t0 >= n || (n <= a.k)) return;
+  const int t1 = t0 + kIdxChunk < n ? t0 + kIdxChunk : n;
+  for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) hist[i] = 0u;
+  __syncthreads();
+  const float* srow = a.scores + (int64_t)r * a.ld;
+  constexpr int PER = kIdxChunk / kHistThreads;
+  float v[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = t0 + threadIdx.x + j * kHistThreads;
+    v[j] = i < t1 ? srow[i] : 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < PER; ++j)
+    if (t0 + (int)threadIdx.x + j * kHistThreads < t1) atomicAdd(&hist[score_key(v[j]) >> (32 - kTopkBinBits)], 1u);
+  __syncthreads();
+  uint16_t* hp = a.hpart + ((int64_t)r * a.hist_chunks + c) * kTopkBins;
+  for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) hp[i] = (uint16_t)hist[i];
 }
 
-__device__ __forceinline__ bool last_block_of_row(uint32_t* ticket, int nchunks, int* flag) {
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) flag[0] = atomicAdd(ticket, 1u) == (uint32_t)(nchunks - 1);
-  __syncthreads();
-  const bool last = flag[0] != 0;
-  if (last) __threadfence();
-  return last;
-}
+// Long-row select.  Workgroup (span, row) handles scores [span * kSelectSpan, +kSelectSpan).
+//  1. Sum the row's histogram partials; find the bin t1 holding the m-th largest key.
+//  2. Append (key, index) of every score whose bin is >= t1 to the span's slot, in index order.
+//  3. The last workgroup of the row (ticket) concatenates the span lists (still in index order),
+//     refines the exact m-th largest key T over the remaining key bits, and writes the output:
+//     keys above T, then the lowest-index ties at T up to m, in list (= index) order.
+constexpr int kListLds = 5120;   // (key, index) pairs the last workgroup keeps in LDS
+constexpr int kCopyBatch = 6;    // list loads each thread keeps in flight
 
-__global__ __launch_bounds__(kPassThreads) void k_topk_hist(LongRowsArgs a) {
-  __shared__ uint32_t hist[kHist1Bins];
-  __shared__ int scan[kPassThreads / 64 + 1];
+__global__ __launch_bounds__(kSelThreads) void k_topk_select(SelectArgs a) {
+  __shared__ uint32_t hist[kTopkBins];
+  __shared__ int scan[kSelThreads / 64 + 1];
   __shared__ int res[2];
   __shared__ int flag[1];
-  const int r = blockIdx.y;
+  __shared__ int span_pre[kSelThreads + 1];
+  __shared__ uint2 list_lds[kListLds];
+  const int r = blockIdx.y, sp = blockIdx.x;
   const int n = row_len(a.rw, r);
   const int m = n < a.k ? n : a.k;
-  const int c0 = blockIdx.x * kTopkChunk;
-  if (c0 >= n) return;
-  if (m == n) {  // every visible token is selected: identity list, no histogram needed
-    const int c1 = c0 + kTopkChunk < n ? c0 + kTopkChunk : n;
-    for (int i = c0 + threadIdx.x; i < c1; i += blockDim.x) a.out[(int64_t)r * a.k + i] = i;
-    if (blockIdx.x == 0) {
-      for (int i = n + threadIdx.x; i < a.k; i += blockDim.x) a.out[(int64_t)r * a.k + i] = -1;
+  const int s0 = sp * kSelectSpan;
+  if (s0 >= n) return;
+  const int s1 = s0 + kSelectSpan < n ? s0 + kSelectSpan : n;
+  int32_t* orow = a.out + (int64_t)r * a.k;
+  if (m == n) {  // every visible token is selected
+    for (int i = s0 + threadIdx.x; i < s1; i += blockDim.x) orow[i] = i;
+    if (sp == 0) {
+      for (int i = n + threadIdx.x; i < a.k; i += blockDim.x) orow[i] = -1;
       if (threadIdx.x == 0) a.count[r] = n;
     }
     return;
   }
-  for (int i = threadIdx.x; i < kHist1Bins; i += blockDim.x) hist[i] = 0;
-  __syncthreads();
-  const float* srow = a.scores + (int64_t)r * a.ld;
-  const int c1 = c0 + kTopkChunk < n ? c0 + kTopkChunk : n;
-  for (int i = c0 + threadIdx.x; i < c1; i += blockDim.x) atomicAdd(&hist[score_key(srow[i]) >> 20], 1u);
-  __syncthreads();
-  uint32_t* g = a.hist1 + (int64_t)r * kHist1Bins;
-  for (int i = threadIdx.x; i < kHist1Bins; i += blockDim.x)
-    if (hist[i]) atomicAdd(&g[i], hist[i]);
-  const int nchunks = (n + kTopkChunk - 1) / kTopkChunk;
-  uint32_t* st = a.state + (int64_t)r * kTopkStateWords;
-  if (!last_block_of_row(&st[0], nchunks, flag)) return;
-  for (int i = threadIdx.x; i < kHist1Bins; i += blockDim.x) hist[i] = __hip_atomic_load(&g[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  find_bin_from_top(hist, kHist1Bins, m, scan, res);
-  if (threadIdx.x == 0) {
-    st[4] = (uint32_t)res[0];
-    st[5] = (uint32_t)res[1];
-    st[6] = (uint32_t)(m - res[1]);
-  }
-}
-
-__global__ __launch_bounds__(kPassThreads) void k_topk_collect(LongRowsArgs a) {
-  __shared__ uint32_t hist[2048];
-  __shared__ uint32_t bitmap[kBitmapWords];
-  __shared__ int scan[kPassThreads / 64 + 1];
-  __shared__ int res[2];
-  __shared__ int flag[1];
-  const int r = blockIdx.y;
-  const int n = row_len(a.rw, r);
-  const int m = n < a.k ? n : a.k;
-  const int c0 = blockIdx.x * kTopkChunk;
-  if (c0 >= n || m == n) return;
-  uint32_t* st = a.state + (int64_t)r * kTopkStateWords;
-  const uint32_t t1 = st[4];
-  const float* srow = a.scores + (int64_t)r * a.ld;
-  int32_t* sure = a.sure + (int64_t)r * a.k;
-  uint2* cand = a.cand + (int64_t)r * a.rw.max_row_len;
-  const int c1 = c0 + kTopkChunk < n ? c0 + kTopkChunk : n;
-  const int lane = threadIdx.x & 63;
-  for (int base = c0; base < c1; base += blockDim.x) {
-    const int i = base + threadIdx.x;
-    uint32_t key = 0, bin = 0;
-    const bool valid = i < c1;
-    if (valid) {
-      key = score_key(srow[i]);
-      bin = key >> 20;
+  // 1. row histogram from the partials (thread t owns bins 2t, 2t+1), 32 partials per round
+  {
+    const int nch = (n + kIdxChunk - 1) / kIdxChunk;
+    const uint32_t* hp = reinterpret_cast<const uint32_t*>(a.hpart + (int64_t)r * a.hist_chunks * kTopkBins);
+    uint32_t lo = 0, hi = 0;
+    for (int c = 0; c < nch; c += 32) {
+      uint32_t w[32];
+#pragma unroll
+      for (int j = 0; j < 32; ++j) w[j] = c + j < nch ? hp[(int64_t)(c + j) * (kTopkBins / 2) + threadIdx.x] : 0u;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        lo += w[j] & 0xFFFFu;
+        hi += w[j] >> 16;
+      }
     }
-    const bool is_sure = valid && bin > t1;
-    const bool is_cand = valid && bin == t1;
-    // wave-aggregated appends
-    const uint64_t ms = __ballot(is_sure);
-    const uint64_t mc = __ballot(is_cand);
-    uint32_t ps = 0, pc = 0;
-    if (lane == 0) {
-      if (ms) ps = atomicAdd(&st[2], (uint32_t)__popcll(ms));
-      if (mc) pc = atomicAdd(&st[3], (uint32_t)__popcll(mc));
-    }
-    ps = __shfl(ps, 0, 64);
-    pc = __shfl(pc, 0, 64);
-    const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
-    if (is_sure) sure[ps + __popcll(ms & below)] = i;
-    if (is_cand) cand[pc + __popcll(mc & below)] = make_uint2(key, (uint32_t)i);
+    hist[2 * threadIdx.x] = lo;
+    hist[2 * threadIdx.x + 1] = hi;
   }
-  const int nchunks = (n + kTopkChunk - 1) / kTopkChunk;
-  if (!last_block_of_row(&st[1], nchunks, flag)) return;
-
-  // ---- last workgroup of the row: refine the threshold among the candidates -------------------
-  const int nsure = (int)__hip_atomic_load(&st[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const int ncand = (int)__hip_atomic_load(&st[3], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  int need = (int)st[6];
-  uint32_t prefix = t1 << 20, pmask = 0xFFF00000u;
-  const int shifts[2] = {9, 0};
-  const int widths[2] = {11, 9};
-  int eq_count = 0;
+  __syncthreads();
+  find_bin_from_top(hist, kTopkBins, m, scan, res);
+  const uint32_t t1 = (uint32_t)res[0];
+  const int above1 = res[1];
+  // 2. ordered compaction of the span's scores with bin >= t1
+  const float* srow = a.scores + (int64_t)r * a.ld;
+  uint2* slot = a.slot + (int64_t)r * a.rw.max_row_len + s0;
+  constexpr int ROUND = kSelThreads * 4;
+  constexpr int ROUNDS = kSelectSpan / ROUND;
+  float4 v[ROUNDS];
+#pragma unroll
+  for (int q = 0; q < ROUNDS; ++q) {
+    const int i = s0 + q * ROUND + threadIdx.x * 4;
+    v[q] = i + 3 < s1 ? *reinterpret_cast<const float4*>(srow + i)
+                      : make_float4(i < s1 ? srow[i] : 0.f, i + 1 < s1 ? srow[i + 1] : 0.f,
+                                    i + 2 < s1 ? srow[i + 2] : 0.f, 0.f);
+  }
+  int written = 0;
+#pragma unroll
+  for (int q = 0; q < ROUNDS; ++q) {
+    const int i = s0 + q * ROUND + threadIdx.x * 4;
+    const float x[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+    uint32_t key[4];
+    bool f[4];
+    int c = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      key[j] = score_key(x[j]);
+      f[j] = (i + j < s1) && (key[j] >> (32 - kTopkBinBits)) >= t1;
+      c += f[j];
+    }
+    int tot;
+    int pos = written + block_exclusive_scan(c, scan, &tot);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (f[j]) st_dev(reinterpret_cast<uint64_t*>(slot + pos++), ((uint64_t)(uint32_t)(i + j) << 32) | key[j]);
+    written += tot;
+  }
+  if (threadIdx.x == 0) st_dev(&a.cnt[(int64_t)r * a.spans + sp], (uint32_t)written);
+  // 3. the last workgroup of the row finishes the selection
+  const int nsp = (n + kSelectSpan - 1) / kSelectSpan;
+  if (!arrive_last(&a.ticket[r], (uint32_t)nsp, flag)) return;
+  // concatenate the span lists (spans in order, so the list stays in index order); the list
+  // lives in LDS when it fits, else in the workspace
+  int L = 0;
+  {
+    const int mine = threadIdx.x < nsp ? (int)ld_dev(&a.cnt[(int64_t)r * a.spans + threadIdx.x]) : 0;
+    const int pre = block_exclusive_scan(mine, scan, &L);
+    if (threadIdx.x < nsp) span_pre[threadIdx.x] = pre;
+    if (threadIdx.x == 0) span_pre[nsp] = L;
+    __syncthreads();
+  }
+  uint2* list = L <= kListLds ? list_lds : a.list + (int64_t)r * a.rw.max_row_len;
+  {
+    const uint2* rslot = a.slot + (int64_t)r * a.rw.max_row_len;
+    for (int p0 = 0; p0 < L; p0 += kSelThreads * kCopyBatch) {
+      uint64_t v[kCopyBatch];
+      int at[kCopyBatch];
+#pragma unroll
+      for (int j = 0; j < kCopyBatch; ++j) {
+        const int p = p0 + j * kSelThreads + threadIdx.x;
+        at[j] = p;
+        v[j] = 0;
+        if (p < L) {
+          int lo = 0, hi = nsp - 1;  // span holding list position p
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (span_pre[mid] <= p) lo = mid; else hi = mid - 1;
+          }
+          v[j] = ld_dev(reinterpret_cast<const uint64_t*>(rslot + (int64_t)lo * kSelectSpan + (p - span_pre[lo])));
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kCopyBatch; ++j)
+        if (at[j] < L) list[at[j]] = make_uint2((uint32_t)v[j], (uint32_t)(v[j] >> 32));
+    }
+    __syncthreads();
+  }
+  // refine T below the first level: bits [20:10], then [9:0]
+  int need = m - above1;
+  uint32_t prefix = t1 << (32 - kTopkBinBits), pmask = ~0u << (32 - kTopkBinBits);
+  const int shifts[2] = {10, 0};
+  const int widths[2] = {32 - kTopkBinBits - 10, 10};
   for (int pass = 0; pass < 2; ++pass) {
     const int nb = 1 << widths[pass];
     const int sh = shifts[pass];
-    for (int i = threadIdx.x; i < nb; i += blockDim.x) hist[i] = 0;
+    for (int i = threadIdx.x; i < nb; i += blockDim.x) hist[i] = 0u;
     __syncthreads();
-    for (int i = threadIdx.x; i < ncand; i += blockDim.x) {
-      const uint32_t key = __builtin_nontemporal_load(&cand[i].x);
+    for (int i = threadIdx.x; i < L; i += blockDim.x) {
+      const uint32_t key = list[i].x;
       if ((key & pmask) == prefix) atomicAdd(&hist[(key >> sh) & (nb - 1)], 1u);
     }
     __syncthreads();
@@ -286,70 +340,33 @@ __global__ __launch_bounds__(kPassThreads) void k_topk_collect(LongRowsArgs a) {
     prefix |= (uint32_t)res[0] << sh;
     pmask |= (uint32_t)(nb - 1) << sh;
     need -= res[1];
-    if (pass == 1) eq_count = (int)hist[res[0]];
     __syncthreads();
   }
   const uint32_t T = prefix;
-  // index cut-off among the keys equal to T: the need-th smallest index
-  uint32_t jstar = 0xFFFFFFFFu;
-  if (need < eq_count) {
-    uint32_t ip = 0, im = 0;
-    int need_i = need;
-    const int ishift[3] = {20, 10, 0};
-    const int iwidth[3] = {11, 10, 10};
-    for (int pass = 0; pass < 3; ++pass) {
-      const int nb = 1 << iwidth[pass];
-      const int sh = ishift[pass];
-      for (int i = threadIdx.x; i < nb; i += blockDim.x) hist[i] = 0;
-      __syncthreads();
-      for (int i = threadIdx.x; i < ncand; i += blockDim.x) {
-        const uint2 c = cand[i];
-        if (c.x == T && (c.y & im) == ip) atomicAdd(&hist[(c.y >> sh) & (nb - 1)], 1u);
-      }
-      __syncthreads();
-      find_bin_from_bottom(hist, nb, need_i, scan, res);
-      ip |= (uint32_t)res[0] << sh;
-      im |= (uint32_t)(nb - 1) << sh;
-      need_i -= res[1];
-      __syncthreads();
+  // ordered output over contiguous per-thread ranges of the list
+  const int E = (L + blockDim.x - 1) / blockDim.x;
+  const int p0 = threadIdx.x * E;
+  int gt = 0, eq = 0;
+  for (int j = 0; j < E; ++j) {
+    const int p = p0 + j;
+    if (p < L) {
+      const uint32_t key = list[p].x;
+      gt += key > T;
+      eq += key == T;
     }
-    jstar = ip;
   }
-  // ---- ascending output through an LDS bitmap, one 2^17-token segment at a time --------------
-  int32_t* orow = a.out + (int64_t)r * a.k;
-  int written = 0;
-  const int seg_bits = kBitmapWords * 32;
-  for (int s0 = 0; s0 < n; s0 += seg_bits) {
-    for (int i = threadIdx.x; i < kBitmapWords; i += blockDim.x) bitmap[i] = 0;
-    __syncthreads();
-    for (int i = threadIdx.x; i < nsure; i += blockDim.x) {
-      const int j = sure[i] - s0;
-      if (j >= 0 && j < seg_bits) atomicOr(&bitmap[j >> 5], 1u << (j & 31));
+  int tot;
+  int gt_before = block_exclusive_scan(gt, scan, &tot);
+  int eq_before = block_exclusive_scan(eq, scan, &tot);
+  for (int j = 0; j < E; ++j) {
+    const int p = p0 + j;
+    if (p < L) {
+      const uint2 e = list[p];
+      const bool take = e.x > T || (e.x == T && eq_before < need);
+      if (take) orow[gt_before + (eq_before < need ? eq_before : need)] = (int32_t)e.y;
+      gt_before += e.x > T;
+      eq_before += e.x == T;
     }
-    for (int i = threadIdx.x; i < ncand; i += blockDim.x) {
-      const uint2 c = cand[i];
-      const bool take = c.x > T || (c.x == T && c.y <= jstar);
-      const int j = (int)c.y - s0;
-      if (take && j >= 0 && j < seg_bits) atomicOr(&bitmap[j >> 5], 1u << (j & 31));
-    }
-    __syncthreads();
-    constexpr int WPT = kBitmapWords / kPassThreads;  // words per thread
-    int local = 0;
-    for (int w = 0; w < WPT; ++w) local += __popc(bitmap[threadIdx.x * WPT + w]);
-    int tot;
-    int pos = written + block_exclusive_scan(local, scan, &tot);
-    for (int w = 0; w < WPT; ++w) {
-      uint32_t bits = bitmap[threadIdx.x * WPT + w];
-      const int tok0 = s0 + (threadIdx.x * WPT + w) * 32;
-      while (bits) {
-        const int b = __ffs(bits) - 1;
-        bits &= bits - 1;
-        if (pos < a.k) orow[pos] = tok0 + b;
-        ++pos;
-      }
-    }
-    written += tot;
-    __syncthreads();
   }
   for (int i = m + threadIdx.x; i < a.k; i += blockDim.x) orow[i] = -1;
   if (threadIdx.x == 0) a.count[r] = m;
@@ -358,30 +375,30 @@ __global__ __launch_bounds__(kPassThreads) void k_topk_collect(LongRowsArgs a) {
 }  // namespace
 
 int launch_topk(const RowsDev& rows, int k, const TopkPlan& plan, const float* scores, int64_t ld, int32_t* idx,
-                int32_t* count, void* ws, void* stream) {
+                int32_t* count, void* ws, uint32_t* tickets, bool have_hist, void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (!plan.multi_wg) {
     hipLaunchKernelGGL(k_topk_rows_lds, dim3(rows.n_rows), dim3(kRowThreads), 0, s, rows, scores, ld, k, idx, count);
     return (int)hipGetLastError();
   }
   char* w = static_cast<char*>(ws);
-  LongRowsArgs a;
+  SelectArgs a;
   a.rw = rows;
   a.scores = scores;
   a.ld = ld;
   a.k = k;
   a.out = idx;
   a.count = count;
-  a.hist1 = reinterpret_cast<uint32_t*>(w + plan.hist_off);
-  a.state = reinterpret_cast<uint32_t*>(w + plan.state_off);
-  a.sure = reinterpret_cast<int32_t*>(w + plan.sure_off);
-  a.cand = reinterpret_cast<uint2*>(w + plan.cand_off);
-  const int64_t nclear = (int64_t)rows.n_rows * kHist1Bins;
-  hipLaunchKernelGGL(k_topk_clear, dim3((unsigned)((nclear + 255) / 256)), dim3(256), 0, s, a.hist1, a.state,
-                     rows.n_rows);
-  const dim3 grid((rows.max_row_len + kTopkChunk - 1) / kTopkChunk, rows.n_rows);
-  hipLaunchKernelGGL(k_topk_hist, grid, dim3(kPassThreads), 0, s, a);
-  hipLaunchKernelGGL(k_topk_collect, grid, dim3(kPassThreads), 0, s, a);
+  a.hpart = reinterpret_cast<uint16_t*>(w + plan.hpart_off);
+  a.hist_chunks = plan.hist_chunks;
+  a.ticket = tickets;
+  a.cnt = reinterpret_cast<uint32_t*>(w + plan.cnt_off);
+  a.spans = plan.spans;
+  a.slot = reinterpret_cast<uint2*>(w + plan.slot_off);
+  a.list = reinterpret_cast<uint2*>(w + plan.list_off);
+  if (!have_hist)
+    hipLaunchKernelGGL(k_topk_hist_partials, dim3(plan.hist_chunks, rows.n_rows), dim3(kHistThreads), 0, s, a);
+  hipLaunchKernelGGL(k_topk_select, dim3(plan.spans, rows.n_rows), dim3(kSelThreads), 0, s, a);
   return (int)hipGetLastError();
 }
 

@@ -85,25 +85,30 @@ TopkPlan plan_topk(const clsa_dims* d, const clsa_rows* r) {
   p.multi_wg = r->max_row_len > kLdsRowCap;
   if (!p.multi_wg) return p;
   const size_t R = (size_t)r->n_rows;
+  p.hist_chunks = (r->max_row_len + kIdxChunk - 1) / kIdxChunk;
+  p.spans = (r->max_row_len + kSelectSpan - 1) / kSelectSpan;
+  p.tickets = r->n_rows;
   size_t off = 0;
-  p.hist_off = off;
-  off = align_up(off + R * kHist1Bins * 4, 256);
-  p.state_off = off;
-  off = align_up(off + R * kTopkStateWords * 4, 256);
-  p.sure_off = off;
-  off = align_up(off + R * (size_t)d->topk * 4, 256);
-  p.cand_off = off;
+  p.hpart_off = off;
+  off = align_up(off + R * p.hist_chunks * kTopkBins * 2, 256);
+  p.cnt_off = off;
+  off = align_up(off + R * p.spans * 4, 256);
+  p.slot_off = off;
+  off = align_up(off + R * (size_t)r->max_row_len * 8, 256);
+  p.list_off = off;
   off = align_up(off + R * (size_t)r->max_row_len * 8, 256);
   p.bytes = off;
+  (void)d;
   return p;
 }
 
-AttnPlan plan_attn(const clsa_dims* d, int n_rows, int n_layers_call) {
+AttnPlan plan_attn(const clsa_dims* d, int n_rows, int n_layers_call, int split_rows) {
   AttnPlan p;
   p.group = d->hq / d->hkv;
   p.qrows = n_layers_call * p.group;
   p.qblocks = (p.qrows + 63) / 64;
-  const int64_t base = (int64_t)n_rows * d->hkv * p.qblocks;
+  // the split count depends on split_rows only, so every chunk of a call splits alike
+  const int64_t base = (int64_t)(split_rows > 0 ? split_rows : n_rows) * d->hkv * p.qblocks;
   const int tiles = (d->topk + kAttnTile - 1) / kAttnTile;
   int splits = 1;
   if (base < 512) splits = (int)((512 + base - 1) / base);
@@ -112,9 +117,10 @@ AttnPlan plan_attn(const clsa_dims* d, int n_rows, int n_layers_call) {
   const int tiles_per_split = (tiles + splits - 1) / splits;
   p.splits = (tiles + tiles_per_split - 1) / tiles_per_split;
   p.keys_per_split = tiles_per_split * kAttnTile;
-  p.part_bytes = p.splits > 1
-                     ? align_up((size_t)p.splits * n_rows * n_layers_call * d->hq * kPartStride * 4, 256)
-                     : 0;
+  if (p.splits > 1) {
+    p.part_bytes = align_up((size_t)p.splits * n_rows * d->hkv * p.qblocks * kAttnPartFloats * 4, 256);
+    p.tickets = (int)((int64_t)n_rows * d->hkv * p.qblocks);
+  }
   return p;
 }
 
@@ -129,14 +135,14 @@ StepPlan plan_step(const clsa_dims* d, const clsa_rows* r, int schedule, bool us
   if (prefill) chunk.max_row_len = r->max_row_len;  // a chunk never sees more than the last row
   s.topk = plan_topk(d, &chunk);
   const int lc = schedule == CLSA_SCHEDULE_PER_LAYER ? 1 : d->n_layers;
-  s.attn = plan_attn(d, s.chunk_rows, lc);
-  const int tail = r->n_rows % s.chunk_rows;
-  if (tail) {  // the last, shorter chunk may split its keys more finely
-    const AttnPlan at = plan_attn(d, tail, lc);
-    if (at.part_bytes > s.attn.part_bytes) s.attn.part_bytes = at.part_bytes;
-  }
+  // every chunk (the shorter tail included) splits like the whole call, so results do not
+  // depend on the chunk size; buffers are sized for the largest chunk
+  s.attn = plan_attn(d, s.chunk_rows, lc, r->n_rows);
   s.ld_scores = (int64_t)align_up((size_t)r->max_row_len, 64);
   size_t off = 0;
+  s.ticket_off = off;
+  s.n_tickets = s.topk.tickets + s.attn.tickets;
+  off += ticket_region(s.n_tickets);
   if (!user_scores) {
     s.scores_off = off;
     s.scores_bytes = align_up((size_t)s.chunk_rows * s.ld_scores * 4, 256);
@@ -157,18 +163,21 @@ StepPlan plan_step(const clsa_dims* d, const clsa_rows* r, int schedule, bool us
   return s;
 }
 
-size_t workspace_bytes(const clsa_dims* d, const clsa_rows* r, int schedule) {
+size_t topk_workspace(const clsa_dims* d, const clsa_rows* r) {
   const TopkPlan t = plan_topk(d, r);
-  const int lc = schedule == CLSA_SCHEDULE_PER_LAYER ? 1 : d->n_layers;
-  const AttnPlan a = plan_attn(d, r->n_rows, lc);
-  const StepPlan s = plan_step(d, r, schedule, false, false, 0);
-  size_t m = t.bytes;
-  if (a.part_bytes > m) m = a.part_bytes;
+  return ticket_region(t.tickets) + t.bytes;
+}
+
+size_t attn_workspace(const AttnPlan& a) { return ticket_region(a.tickets) + a.part_bytes; }
+
+size_t workspace_bytes(const clsa_dims* d, const clsa_rows* r, int schedule, int prefill_chunk_rows) {
+  size_t m = topk_workspace(d, r);
   // a standalone clsa_sparse_attn call may cover any number of layers up to L
   for (int l = 1; l <= d->n_layers; ++l) {
-    const AttnPlan al = plan_attn(d, r->n_rows, l);
-    if (al.part_bytes > m) m = al.part_bytes;
+    const size_t a = attn_workspace(plan_attn(d, r->n_rows, l, 0));
+    if (a > m) m = a;
   }
+  const StepPlan s = plan_step(d, r, schedule, false, false, prefill_chunk_rows);
   if (s.total > m) m = s.total;
   return m < 256 ? 256 : m;
 }

@@ -62,7 +62,7 @@ enum { CLSA_SCHEDULE_LAYER_BATCHED = 0, CLSA_SCHEDULE_PER_LAYER = 1 };
 /* Limits (CLSA_ERR_UNSUPPORTED beyond them). */
 #define CLSA_HEAD_DIM 128
 #define CLSA_MAX_TOPK 65536
-#define CLSA_MAX_ROW_LEN (1 << 30)
+#define CLSA_MAX_ROW_LEN (1 << 24)
 
 typedef struct clsa_dims {
   int32_t batch;    /* B >= 1: sequences in the cache; cu_seqlens has B+1 entries          */
@@ -99,10 +99,12 @@ const char* clsa_last_error_message(void);
 int32_t clsa_abi_version(void);
 #define CLSA_ABI_VERSION 1
 
-/* Device workspace, in bytes, that clsa_topk, clsa_sparse_attn and clsa_step need for these
- * sizes (the maximum over the three; `schedule` is a CLSA_SCHEDULE_*).  Pure host function.
- * Returns 0 and sets the error message if the sizes are invalid. */
-size_t clsa_workspace_bytes(const clsa_dims* dims, const clsa_rows* rows, int32_t schedule);
+/* Device workspace, in bytes, that clsa_topk, clsa_sparse_attn (any n_layers_call) and
+ * clsa_step (with this `schedule` and `prefill_chunk_rows`, 0 = default) need for these sizes:
+ * the maximum over the three.  Pure host function.  Returns 0 and sets the error message if the
+ * arguments are invalid. */
+size_t clsa_workspace_bytes(const clsa_dims* dims, const clsa_rows* rows, int32_t schedule,
+                            int32_t prefill_chunk_rows);
 
 /*
  * Routing scores, eq. 2 first half (picx.dev summary, Architecture Overview):
@@ -126,7 +128,7 @@ clsa_status clsa_index_scores(const clsa_dims* dims, const clsa_rows* rows, cons
  *   count [R]    int32  - m
  * scores as written by clsa_index_scores (only the visible entries of each row are read;
  * -0.0 and +0.0 are equal).  The result is unique and deterministic.
- * Workspace: >= clsa_workspace_bytes(dims, rows, CLSA_SCHEDULE_LAYER_BATCHED), any content.
+ * Workspace: >= clsa_workspace_bytes(dims, rows, CLSA_SCHEDULE_LAYER_BATCHED, 0), any content.
  */
 clsa_status clsa_topk(const clsa_dims* dims, const clsa_rows* rows, const int32_t* cu_seqlens,
                       const float* scores, int64_t ld_scores, int32_t* idx, int32_t* count,
@@ -191,7 +193,8 @@ typedef struct clsa_step_args {
  * (eq. 2-3; the indexer cost is paid once rather than once per layer, picx.dev summary,
  * section Complexity Comparison).  Produces idx, count, out (and scores if requested).
  * DECODE: one launch sequence on `stream`.  PREFILL: rows processed in chunks of
- * prefill_chunk_rows.  Workspace: >= clsa_workspace_bytes(dims, rows, schedule).
+ * prefill_chunk_rows.  Workspace: >= clsa_workspace_bytes(dims, rows, schedule,
+ * prefill_chunk_rows).
  */
 clsa_status clsa_step(const clsa_dims* dims, const clsa_rows* rows, const clsa_step_args* args,
                       void* workspace, size_t workspace_bytes, clsa_stream stream);

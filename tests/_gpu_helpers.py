@@ -45,8 +45,8 @@ def bf16_dev_to_f64(t: torch.Tensor) -> np.ndarray:
     return gen.bf16_bits_to_f64(t.cpu().numpy().view(np.uint16))
 
 
-def workspace(dims, rows, schedule=clsa.SCHEDULE_LAYER_BATCHED):
-    n = clsa.workspace_bytes(dims, rows, schedule)
+def workspace(dims, rows, schedule=clsa.SCHEDULE_LAYER_BATCHED, chunk=0):
+    n = clsa.workspace_bytes(dims, rows, schedule, chunk)
     return torch.empty(n, dtype=torch.uint8, device="cuda"), n
 
 

@@ -255,7 +255,7 @@ def _run_step(dw, schedule, rows_kw=None, chunk=0, want_scores=False):
     dims = dims_of(dw)
     rows = rows_of(dw, **(rows_kw or {}))
     R = rows.n_rows
-    ws, nws = workspace(dims, rows, schedule)
+    ws, nws = workspace(dims, rows, schedule, chunk)
     out = torch.zeros((R, w.n_layers, w.hq, 128), dtype=torch.int16, device="cuda")
     idx = torch.full((R, w.topk), -7, dtype=torch.int32, device="cuda")
     cnt = torch.full((R,), -7, dtype=torch.int32, device="cuda")
