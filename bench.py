@@ -103,6 +103,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of wall time for the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-layer", action="store_true")
+    ap.add_argument("--profile-copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (a counter calibration reference)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
@@ -181,6 +183,15 @@ def main():
         per_layer = {"ms_per_step": round(w2 / args.steps * 1e3, 4), "tokens_per_s": round(R * args.steps / w2, 1),
                      "hbm_gbps_alg": round(balg["total"] / (w2 / args.steps) / 1e9, 1)}
         del ws2
+
+    if args.profile_copy_mib > 0:
+        n = args.profile_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_budget)
     line = {

@@ -16,13 +16,21 @@ namespace clsa {
 constexpr int kLdsRowCap = 12288;
 // Tokens per workgroup of the decode score kernel (also the histogram partial granularity).
 constexpr int kIdxChunk = 4096;
-// First histogram level of the long-row select: the top kTopkBinBits bits of the score key.
-constexpr int kTopkBinBits = 11;
+// First histogram level of the long-row select: the top kTopkBinBits bits of the score key
+// (sign and the high exponent bits), small enough that every select workgroup can sum a row's
+// partials cheaply.
+constexpr int kTopkBinBits = 8;
 constexpr int kTopkBins = 1 << kTopkBinBits;
 // Scores classified by one workgroup of the long-row select.
-constexpr int kSelectSpan = 16384;
+constexpr int kSelectSpan = 8192;
 // Keys per attention tile.
 constexpr int kAttnTile = 64;
+// Upper bound on the splits of the selected rows of one (row, KV head, query block).
+constexpr int kMaxAttnSplits = 16;
+// Attention workgroups the split count aims for (2 per CU on 256 CUs).
+#ifndef CLSA_ATTN_TARGET_WGS
+#define CLSA_ATTN_TARGET_WGS 512
+#endif
 // fp32 words of one attention split partial per (row, KV head, query block): 4 waves x 64 lanes
 // x (32 accumulators + m + l).
 constexpr int kAttnPartFloats = 4 * 34 * 64;

@@ -109,33 +109,86 @@ __device__ __forceinline__ bool arrive_last(uint32_t* ticket, uint32_t arrivals,
   return flag[0] != 0;
 }
 
-// Block-wide exclusive scan of one int per thread (blockDim.x a multiple of 64, <= 1024).
-// `scratch` holds at least blockDim.x / 64 + 1 ints.  Returns the exclusive prefix and sets
-// *total.  Contains __syncthreads().
+// Inclusive prefix sum over the 64 lanes of a wave with DPP: shifts by 1, 2, 4, 8 inside each row
+// of 16 lanes, then the last lane of row 0 (row_bcast15) and of rows 0-1 (row_bcast31) is added
+// to the rows above.  Lanes whose DPP source is outside the row receive 0.
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+  return x;
+}
+
+// Block-wide exclusive scan of one (or two) ints per thread (blockDim.x a multiple of 64,
+// <= 1024).  `scratch` holds at least 2 * (blockDim.x / 64) ints.  Returns the exclusive prefix and
+// sets *total.  Contains two __syncthreads(); scratch may be reused after it returns.
 __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += t;
-  }
+  const int incl = wave_inclusive_scan(v);
   if (lane == 63) scratch[wave] = incl;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int w = 0; w < nw; ++w) {
-      const int t = scratch[w];
-      scratch[w] = run;
-      run += t;
-    }
-    scratch[nw] = run;
+  int before = 0, all = 0;
+  for (int w = 0; w < nw; ++w) {
+    const int t = scratch[w];
+    before += w < wave ? t : 0;
+    all += t;
   }
   __syncthreads();
-  const int res = scratch[wave] + incl - v;
-  *total = scratch[nw];
+  *total = all;
+  return before + incl - v;
+}
+
+__device__ __forceinline__ void block_exclusive_scan2(int v0, int v1, int* scratch, int* out0, int* out1,
+                                                      int* total0, int* total1) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int i0 = wave_inclusive_scan(v0), i1 = wave_inclusive_scan(v1);
+  if (lane == 63) {
+    scratch[wave] = i0;
+    scratch[nw + wave] = i1;
+  }
   __syncthreads();
-  return res;
+  int b0 = 0, b1 = 0, a0 = 0, a1 = 0;
+  for (int w = 0; w < nw; ++w) {
+    const int t0 = scratch[w], t1 = scratch[nw + w];
+    b0 += w < wave ? t0 : 0;
+    b1 += w < wave ? t1 : 0;
+    a0 += t0;
+    a1 += t1;
+  }
+  __syncthreads();
+  *out0 = b0 + i0 - v0;
+  *out1 = b1 + i1 - v1;
+  *total0 = a0;
+  *total1 = a1;
+}
+
+// Wave 0 finds, in a 256-bin LDS histogram, the bin d (from the top bin down) whose cumulative
+// count first reaches `need`, and publishes res[0] = d, res[1] = count of the bins above d.  All
+// threads must call it; it ends with __syncthreads().
+__device__ __forceinline__ void find_bin256_from_top(const uint32_t* hist, int need, int* res) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    // lane owns bins 255 - 4 lane .. 252 - 4 lane (descending)
+    int h[4], loc = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      h[j] = (int)hist[255 - 4 * lane - j];
+      loc += h[j];
+    }
+    int run = wave_inclusive_scan(loc) - loc;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (run < need && run + h[j] >= need) {
+        res[0] = 255 - 4 * lane - j;
+        res[1] = run;
+      }
+      run += h[j];
+    }
+  }
+  __syncthreads();
 }
 
 }  // namespace clsa

@@ -23,6 +23,7 @@ namespace {
 constexpr int kAttnThreads = 256;
 constexpr int kAttnPartWave = 34 * 64;             // floats per wave: acc 32 x 64 lanes, m, l
 constexpr int kAttnPartWG = 4 * kAttnPartWave;     // floats per workgroup partial
+static_assert(kAttnPartWG == kAttnPartFloats, "partial record layout");
 constexpr int kKsStride = CLSA_HEAD_DIM + 8;  // bf16 elements per K row in LDS (16-byte pad)
 constexpr int kVtStride = kAttnTile + 4;      // bf16 elements per transposed V row in LDS
 
@@ -42,10 +43,38 @@ struct AttnArgs {
   uint32_t* tickets;   // [R, hkv, qblocks], zero on entry, reset by their last workgroup
 };
 
+// Four outputs scaled by inv, rounded to bf16 (round to nearest even) and stored as 8 bytes.
+__device__ __forceinline__ void store_out4(uint16_t* p, const floatx4_t& v, float inv) {
+  const bf16x2_t lo = {(__bf16)(v[0] * inv), (__bf16)(v[1] * inv)};
+  const bf16x2_t hi = {(__bf16)(v[2] * inv), (__bf16)(v[3] * inv)};
+  *reinterpret_cast<uint2*>(p) = make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+}
+
+// LDS tile layout: a tile holds 64 rows (keys) of 128 bf16 in row order; the 16-byte chunk c of
+// row r sits at chunk slot c ^ (r & 15).  Row stores, K fragment reads and the transposed V
+// reads then all spread over the banks without padding.
+
+typedef short shortx4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) shortx4_t lds_shortx4_t;
+
+// Transposed LDS read (ds_read_b64_tr_b16): within each group of 16 lanes, lane i reads 4
+// consecutive bf16 at its own address and receives element (i % 4) of the 4 values read by lanes
+// 4k + i / 4, k = 0..3.
+__device__ __forceinline__ uint2 lds_read_tr(const uint16_t* p) {
+  const shortx4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
+// One stage = kAttnStageTiles tiles of 64 keys in LDS (2 x 32 KB); the next stage's rows are in
+// flight into registers meanwhile (64 KB per workgroup).  Two workgroups share a CU.
+constexpr int kAttnStageTiles = 2;
+
 template <bool FROM_CACHE>
-__global__ __launch_bounds__(kAttnThreads) void k_sparse_attn(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t ks[kAttnTile * kKsStride];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[CLSA_HEAD_DIM * kVtStride];
+__global__ __launch_bounds__(kAttnThreads, 2) void k_sparse_attn(AttnArgs a) {
+  constexpr int NT = kAttnStageTiles;
+  constexpr int STAGE = NT * kAttnTile;
+  __shared__ __attribute__((aligned(16))) uint16_t ks[NT][kAttnTile * CLSA_HEAD_DIM];
+  __shared__ __attribute__((aligned(16))) uint16_t vs[NT][kAttnTile * CLSA_HEAD_DIM];
   __shared__ int flag[1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, grp = lane >> 4;
@@ -88,130 +117,164 @@ __global__ __launch_bounds__(kAttnThreads) void k_sparse_attn(AttnArgs a) {
   const int ld_chunk = threadIdx.x & 15;  // 8 head_dim elements
   const int ld_key4 = threadIdx.x >> 4;   // keys 4*ld_key4 .. +3
 
-  // token ids of this thread's 4 keys in the tile starting at kt (cache source only)
-  auto load_ids = [&](int kt, int (&ids)[4]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = kt + ld_key4 * 4 + i;
-      ids[i] = (FROM_CACHE && key < kend) ? irow[key] : 0;
-    }
+  struct Regs {
+    uint4 k[NT][4], v[NT][4];
   };
-  auto load_kv = [&](int kt, const int (&ids)[4], uint4 (&kv)[4], uint4 (&vv)[4]) {
+  // token ids of this thread's keys in the stage starting at kt (cache source only)
+  auto load_ids = [&](int kt, int (&ids)[NT][4]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = kt + ld_key4 * 4 + i;
-      kv[i] = make_uint4(0u, 0u, 0u, 0u);
-      vv[i] = make_uint4(0u, 0u, 0u, 0u);
-      if (key < kend) {
-        int64_t src;
-        if (FROM_CACHE)
-          src = ((tok_base + ids[i]) * a.hkv + g) * CLSA_HEAD_DIM + ld_chunk * 8;
-        else
-          src = (((int64_t)r * a.hkv + g) * a.k + key) * CLSA_HEAD_DIM + ld_chunk * 8;
-        kv[i] = *reinterpret_cast<const uint4*>(a.ksrc + src);
-        vv[i] = *reinterpret_cast<const uint4*>(a.vsrc + src);
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = kt + t * kAttnTile + ld_key4 * 4 + i;
+        ids[t][i] = (FROM_CACHE && key < kend) ? irow[key] : 0;
       }
-    }
   };
-
-  int ids_next[4];
-  uint4 kv[4], vv[4];
-  if (kbeg < kend) {
-    int ids0[4];
-    load_ids(kbeg, ids0);
-    load_kv(kbeg, ids0, kv, vv);
-    load_ids(kbeg + kAttnTile, ids_next);
-  }
-  for (int kt = kbeg; kt < kend; kt += kAttnTile) {
-    const int nvalid = kend - kt < kAttnTile ? kend - kt : kAttnTile;
+  // 64-bit base of this (row, KV head) once; per-row offsets then fit 32 bits
+  const int row_elems = FROM_CACHE ? a.hkv * CLSA_HEAD_DIM : CLSA_HEAD_DIM;
+  const int64_t base_off = FROM_CACHE ? (tok_base * a.hkv + g) * CLSA_HEAD_DIM
+                                      : (((int64_t)r * a.hkv + g) * a.k) * CLSA_HEAD_DIM;
+  const uint16_t* kbase = a.ksrc + base_off + ld_chunk * 8;
+  const uint16_t* vbase = a.vsrc + base_off + ld_chunk * 8;
+  auto load_stage = [&](int kt, const int (&ids)[NT][4], Regs& rg) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<uint4*>(&ks[(ld_key4 * 4 + i) * kKsStride + ld_chunk * 8]) = kv[i];
-    // transpose 4 keys x 8 head_dim elements in registers, store 8 rows of 4 keys (8 bytes each)
-    {
-      const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vv[0]);
-      const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vv[1]);
-      const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vv[2]);
-      const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vv[3]);
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // element 2e (low half) and 2e+1 (high half) of each key
-        const uint32_t lo01 = (w0[e] & 0xFFFFu) | (w1[e] << 16);
-        const uint32_t lo23 = (w2[e] & 0xFFFFu) | (w3[e] << 16);
-        const uint32_t hi01 = (w0[e] >> 16) | (w1[e] & 0xFFFF0000u);
-        const uint32_t hi23 = (w2[e] >> 16) | (w3[e] & 0xFFFF0000u);
-        const int d0 = ld_chunk * 8 + 2 * e;
-        *reinterpret_cast<uint2*>(&vt[d0 * kVtStride + ld_key4 * 4]) = make_uint2(lo01, lo23);
-        *reinterpret_cast<uint2*>(&vt[(d0 + 1) * kVtStride + ld_key4 * 4]) = make_uint2(hi01, hi23);
-      }
-    }
-    __syncthreads();
-    // issue the next tile's loads now; they land while this tile is computed
-    const int nxt = kt + kAttnTile;
-    if (nxt < kend) {
-      load_kv(nxt, ids_next, kv, vv);
-      load_ids(nxt + kAttnTile, ids_next);
-    }
-    if (wave_active) {
-      floatx4_t s[4];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        s[mt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const uint4 av = *reinterpret_cast<const uint4*>(&ks[(mt * 16 + l16) * kKsStride + kk * 32 + grp * 8]);
-          s[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8_t>(av), qf[kk], s[mt], 0, 0, 0);
+      for (int i = 0; i < 4; ++i) {
+        const int key = kt + t * kAttnTile + ld_key4 * 4 + i;
+        rg.k[t][i] = make_uint4(0u, 0u, 0u, 0u);
+        rg.v[t][i] = make_uint4(0u, 0u, 0u, 0u);
+        if (key < kend) {
+          const uint32_t off = (uint32_t)(FROM_CACHE ? ids[t][i] : key) * (uint32_t)row_elems;
+          rg.k[t][i] = *reinterpret_cast<const uint4*>(kbase + off);
+          rg.v[t][i] = *reinterpret_cast<const uint4*>(vbase + off);
         }
       }
-      // s[mt][j]: key mt*16 + grp*4 + j, query column l16
-      float mx = -INFINITY;
+  };
+  // Per-lane byte offsets into a tile (swizzled layout), fixed for the whole kernel; the parts that
+  // depend on the loop variables are compile-time immediates.
+  //   row stores: rows 4 ld_key4 + i, chunk ld_chunk
+  //   K fragment: row mt*16 + l16, chunk 4kk + grp  -> slot (grp ^ l16) ^ 4kk
+  //   V^T fragment (transposed read): row 32kk + 4grp + l16/4 (+16), head_dim 16ht + 4(l16 % 4)
+  //     -> slot (2ht + (l16/2 % 2)) ^ (4grp + l16/4) = z ^ 2ht, byte 8 (l16 % 2) inside the chunk
+  int soff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = ld_key4 * 4 + i;
+    soff[i] = row * 256 + ((ld_chunk ^ (row & 15)) << 4);
+  }
+  int koff[4];
+  const int gx = grp ^ l16;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) koff[kk] = l16 * 256 + ((gx ^ (4 * kk)) << 4);
+  int voff[8];
+  {
+    const int y = 4 * grp + (l16 >> 2);
+    const int z = ((l16 >> 1) & 1) ^ y;
+#pragma unroll
+    for (int ht = 0; ht < 8; ++ht) voff[ht] = y * 256 + ((z ^ (2 * ht)) << 4) + 8 * (l16 & 1);
+  }
+  auto store_stage = [&](const Regs& rg) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(ks[t]) + soff[i]) = rg.k[t][i];
+        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(vs[t]) + soff[i]) = rg.v[t][i];
+      }
+  };
+  const float scale = a.scale_log2;
+  // one 64-key tile: S^T = K Q^T, online softmax (exp2 domain, scaled), O^T += V^T P^T
+  auto compute_tile = [&](const uint16_t* kbuf, const uint16_t* vbuf, int nvalid) {
+    const char* kb = reinterpret_cast<const char*>(kbuf);
+    const char* vb = reinterpret_cast<const char*>(vbuf);
+    floatx4_t s[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      s[mt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const uint4 av = *reinterpret_cast<const uint4*>(kb + koff[kk] + mt * 4096);
+        s[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8_t>(av), qf[kk], s[mt], 0, 0, 0);
+      }
+    }
+    // s[mt][j]: raw q.k of key mt*16 + grp*4 + j, query column l16
+    if (nvalid < kAttnTile) {
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int key = mt * 16 + grp * 4 + j;
-          const float v = key < nvalid ? s[mt][j] * a.scale_log2 : -INFINITY;
-          s[mt][j] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx);
-      const float corr = exp2f(m_run - m_new);
-      m_run = m_new;
-      float psum = 0.f;
-      uint32_t pk[4][2];
+        for (int j = 0; j < 4; ++j)
+          if (mt * 16 + grp * 4 + j >= nvalid) s[mt][j] = -INFINITY;
+    }
+    float mx = -INFINITY;
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        float p[4];
+    for (int mt = 0; mt < 4; ++mt) mx = fmaxf(fmaxf(mx, fmaxf(s[mt][0], s[mt][1])), fmaxf(s[mt][2], s[mt][3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx * scale);
+    const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    float psum = 0.f;
+    bf16x2_t pk[4][2];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          p[j] = exp2f(s[mt][j] - m_new);
-          psum += p[j];
-        }
-        pk[mt][0] = f32_to_bf16(p[0]) | (f32_to_bf16(p[1]) << 16);
-        pk[mt][1] = f32_to_bf16(p[2]) | (f32_to_bf16(p[3]) << 16);
+    for (int mt = 0; mt < 4; ++mt) {
+      float p[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        p[j] = __builtin_amdgcn_exp2f(fmaf(s[mt][j], scale, -m_new));
+        psum += p[j];
       }
-      l_run = l_run * corr + psum;
+      pk[mt][0] = bf16x2_t{(__bf16)p[0], (__bf16)p[1]};
+      pk[mt][1] = bf16x2_t{(__bf16)p[2], (__bf16)p[3]};
+    }
+    l_run = l_run * corr + psum;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] *= corr;
-      // P^T operand of k-step kk: slots 0..3 <- keys 32kk + 4grp + j, slots 4..7 <- keys 32kk + 16 + 4grp + j
-      bf16x8_t pb[2];
+    for (int i = 0; i < 8; ++i) acc[i] *= corr;
+    // P^T operand of k-step kk: slots 0..3 <- keys 32kk + 4grp + j, slots 4..7 <- keys 32kk + 16 + 4grp + j
+    bf16x8_t pb[2];
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-        pb[kk] = bitcast<bf16x8_t>(make_uint4(pk[2 * kk][0], pk[2 * kk][1], pk[2 * kk + 1][0], pk[2 * kk + 1][1]));
+    for (int kk = 0; kk < 2; ++kk)
+      pb[kk] = __builtin_bit_cast(bf16x8_t, make_uint4(__builtin_bit_cast(uint32_t, pk[2 * kk][0]),
+                                                       __builtin_bit_cast(uint32_t, pk[2 * kk][1]),
+                                                       __builtin_bit_cast(uint32_t, pk[2 * kk + 1][0]),
+                                                       __builtin_bit_cast(uint32_t, pk[2 * kk + 1][1])));
 #pragma unroll
-      for (int ht = 0; ht < 8; ++ht) {
+    for (int ht = 0; ht < 8; ++ht) {
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const uint16_t* vr = &vt[(ht * 16 + l16) * kVtStride + kk * 32 + grp * 4];
-          const uint2 v0 = *reinterpret_cast<const uint2*>(vr);
-          const uint2 v1 = *reinterpret_cast<const uint2*>(vr + 16);
-          acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8_t>(make_uint4(v0.x, v0.y, v1.x, v1.y)),
-                                                            pb[kk], acc[ht], 0, 0, 0);
-        }
+      for (int kk = 0; kk < 2; ++kk) {
+        const uint2 v0 = lds_read_tr(reinterpret_cast<const uint16_t*>(vb + voff[ht] + kk * 8192));
+        const uint2 v1 = lds_read_tr(reinterpret_cast<const uint16_t*>(vb + voff[ht] + kk * 8192 + 4096));
+        acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8_t>(make_uint4(v0.x, v0.y, v1.x, v1.y)),
+                                                          pb[kk], acc[ht], 0, 0, 0);
       }
     }
+  };
+  auto compute_stage = [&](int kt) {
+    if (!wave_active) return;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int tk = kt + t * kAttnTile;
+      if (tk < kend) compute_tile(ks[t], vs[t], kend - tk < kAttnTile ? kend - tk : kAttnTile);
+    }
+  };
+
+  // the next stage's rows are requested before this stage is computed
+  Regs ra;
+  int ids_next[NT][4];
+  if (kbeg < kend) {
+    int ids0[NT][4];
+    load_ids(kbeg, ids0);
+    load_stage(kbeg, ids0, ra);
+    load_ids(kbeg + STAGE, ids_next);
+  }
+  for (int kt = kbeg; kt < kend; kt += STAGE) {
+    store_stage(ra);
+    __syncthreads();
+    if (kt + STAGE < kend) {
+      load_stage(kt + STAGE, ids_next, ra);
+      load_ids(kt + 2 * STAGE, ids_next);
+    }
+    compute_stage(kt);
     __syncthreads();
   }
   l_run += __shfl_xor(l_run, 16, 64);
@@ -222,11 +285,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_sparse_attn(AttnArgs a) {
     if (!q_valid) return;
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
 #pragma unroll
-    for (int ht = 0; ht < 8; ++ht) {
-      const uint32_t lo = f32_to_bf16(acc[ht][0] * inv) | (f32_to_bf16(acc[ht][1] * inv) << 16);
-      const uint32_t hi = f32_to_bf16(acc[ht][2] * inv) | (f32_to_bf16(acc[ht][3] * inv) << 16);
-      *reinterpret_cast<uint2*>(op + ht * 16 + grp * 4) = make_uint2(lo, hi);
-    }
+    for (int ht = 0; ht < 8; ++ht) store_out4(op + ht * 16 + grp * 4, acc[ht], inv);
     return;
   }
   // Split partial of this workgroup, in the lanes' own layout (each store instruction of a wave
@@ -247,35 +306,35 @@ __global__ __launch_bounds__(kAttnThreads) void k_sparse_attn(AttnArgs a) {
   uint32_t* ticket = a.tickets + ((int64_t)r * a.hkv + g) * a.qblocks + qb;
   if (!arrive_last(ticket, (uint32_t)a.splits, flag)) return;
   if (!q_valid) return;
-  // Fold the splits in split order (whichever workgroup arrives last, the arithmetic is the
-  // same, so the result is deterministic); this workgroup's own partial is still in registers.
-  float M = -INFINITY, den = 0.f;
+  // Recombine: O = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s with M = max_s m_s, summed in
+  // split order, so whichever workgroup arrives last computes exactly the same result.  This
+  // workgroup's own partial is still in registers.
+  float M = -INFINITY;
+  for (int s2 = 0; s2 < a.splits; ++s2)
+    M = fmaxf(M, s2 == split ? m_run : ld_dev(pw + s2 * split_stride + 32 * 64 + lane));
+  float den = 0.f;
   float tot[32];
 #pragma unroll
   for (int i = 0; i < 32; ++i) tot[i] = 0.f;
   for (int s2 = 0; s2 < a.splits; ++s2) {
-    float v[32], ms, ls;
+    const float m2 = s2 == split ? m_run : ld_dev(pw + s2 * split_stride + 32 * 64 + lane);
+    if (m2 == -INFINITY) continue;
+    const float w = exp2f(m2 - M);
     if (s2 == split) {
+      den += w * l_run;
 #pragma unroll
       for (int ht = 0; ht < 8; ++ht)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) v[ht * 4 + j] = acc[ht][j];
-      ms = m_run;
-      ls = l_run;
+        for (int j = 0; j < 4; ++j) tot[ht * 4 + j] += w * acc[ht][j];
     } else {
       const float* ps = pw + s2 * split_stride;
+      float v[32];
 #pragma unroll
       for (int i = 0; i < 32; ++i) v[i] = ld_dev(ps + i * 64 + lane);
-      ms = ld_dev(ps + 32 * 64 + lane);
-      ls = ld_dev(ps + 33 * 64 + lane);
-    }
-    if (ms == -INFINITY) continue;
-    const float m_new = fmaxf(M, ms);
-    const float c_old = exp2f(M - m_new), c_new = exp2f(ms - m_new);
-    den = den * c_old + ls * c_new;
+      den += w * ld_dev(ps + 33 * 64 + lane);
 #pragma unroll
-    for (int i = 0; i < 32; ++i) tot[i] = tot[i] * c_old + v[i] * c_new;
-    M = m_new;
+      for (int i = 0; i < 32; ++i) tot[i] += w * v[i];
+    }
   }
 #pragma unroll
   for (int ht = 0; ht < 8; ++ht)
@@ -283,11 +342,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_sparse_attn(AttnArgs a) {
     for (int j = 0; j < 4; ++j) acc[ht][j] = tot[ht * 4 + j];
   const float inv = den > 0.f ? 1.f / den : 0.f;
 #pragma unroll
-  for (int ht = 0; ht < 8; ++ht) {
-    const uint32_t lo = f32_to_bf16(acc[ht][0] * inv) | (f32_to_bf16(acc[ht][1] * inv) << 16);
-    const uint32_t hi = f32_to_bf16(acc[ht][2] * inv) | (f32_to_bf16(acc[ht][3] * inv) << 16);
-    *reinterpret_cast<uint2*>(op + ht * 16 + grp * 4) = make_uint2(lo, hi);
-  }
+  for (int ht = 0; ht < 8; ++ht) store_out4(op + ht * 16 + grp * 4, acc[ht], inv);
 }
 
 __global__ void k_clear_u32(uint32_t* __restrict__ p, int n) {

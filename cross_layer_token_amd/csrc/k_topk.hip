@@ -22,69 +22,36 @@ namespace {
 constexpr int kRowThreads = 512;
 constexpr int kPassThreads = 256;
 
-// Find the bin d (scanning from the top bin down) whose cumulative count from the top first
-// reaches `need`; returns d and sets *above = count of bins above d.  hist has nb bins in LDS;
-// one thread finds it and publishes via res[0..1].  Contains __syncthreads().
-__device__ void find_bin_from_top(const uint32_t* hist, int nb, int need, int* scan_scratch, int* res) {
-  const int per = (nb + blockDim.x - 1) / blockDim.x;
-  const int u0 = threadIdx.x * per;
-  int local = 0;
-  for (int j = 0; j < per; ++j) {
-    const int u = u0 + j;
-    if (u < nb) local += (int)hist[nb - 1 - u];
-  }
-  int total;
-  int run = block_exclusive_scan(local, scan_scratch, &total);
-  for (int j = 0; j < per; ++j) {
-    const int u = u0 + j;
-    if (u < nb) {
-      const int h = (int)hist[nb - 1 - u];
-      if (run < need && run + h >= need) {
-        res[0] = nb - 1 - u;
-        res[1] = run;
-      }
-      run += h;
-    }
-  }
-  __syncthreads();
-}
-
-// Find the bin d (scanning from the bottom bin up) whose cumulative count first reaches need;
-// returns via res[0] = d, res[1] = count below d.
-__device__ void find_bin_from_bottom(const uint32_t* hist, int nb, int need, int* scan_scratch, int* res) {
-  const int per = (nb + blockDim.x - 1) / blockDim.x;
-  const int u0 = threadIdx.x * per;
-  int local = 0;
-  for (int j = 0; j < per; ++j)
-    if (u0 + j < nb) local += (int)hist[u0 + j];
-  int total;
-  int run = block_exclusive_scan(local, scan_scratch, &total);
-  for (int j = 0; j < per; ++j) {
-    const int u = u0 + j;
-    if (u < nb) {
-      const int h = (int)hist[u];
-      if (run < need && run + h >= need) {
-        res[0] = u;
-        res[1] = run;
-      }
-      run += h;
-    }
-  }
-  __syncthreads();
-}
-
 __device__ void write_all(int32_t* out, int32_t* count, int r, int n, int k) {
   for (int i = threadIdx.x; i < k; i += blockDim.x) out[(int64_t)r * k + i] = i < n ? i : -1;
   if (threadIdx.x == 0) count[r] = n;
 }
 
 // ---------------------------------------------------------------------------- short rows
+// One radix pass over 8 key bits: histogram of the keys that match the prefix found so far, then
+// the bin holding the need-th largest.  Ends with __syncthreads().
+template <typename KeyAt>
+__device__ __forceinline__ void radix_pass8(uint32_t* hist, int count, KeyAt key_at, uint32_t& prefix,
+                                            uint32_t& pmask, int shift, int& need, int* res) {
+  for (int i = threadIdx.x; i < 256; i += blockDim.x) hist[i] = 0u;
+  __syncthreads();
+  for (int i = threadIdx.x; i < count; i += blockDim.x) {
+    const uint32_t key = key_at(i);
+    if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+  }
+  __syncthreads();
+  find_bin256_from_top(hist, need, res);
+  prefix |= (uint32_t)res[0] << shift;
+  pmask |= 255u << shift;
+  need -= res[1];
+}
+
 __global__ __launch_bounds__(kRowThreads) void k_topk_rows_lds(RowsDev rw, const float* __restrict__ scores,
                                                                  int64_t ld, int k, int32_t* __restrict__ out,
                                                                  int32_t* __restrict__ count) {
   __shared__ uint32_t keys[kLdsRowCap];
-  __shared__ uint32_t hist[2048];
-  __shared__ int scan[kRowThreads / 64 + 1];
+  __shared__ uint32_t hist[256];
+  __shared__ int scan[2 * kRowThreads / 64];
   __shared__ int res[2];
   const int r = blockIdx.x;
   const int n = row_len(rw, r);
@@ -97,24 +64,8 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_rows_lds(RowsDev rw, const
   for (int i = threadIdx.x; i < n; i += blockDim.x) keys[i] = score_key(srow[i]);
   uint32_t prefix = 0, pmask = 0;
   int need = m;
-  const int shifts[3] = {21, 10, 0};
-  const int widths[3] = {11, 11, 10};
-  for (int pass = 0; pass < 3; ++pass) {
-    const int nb = 1 << widths[pass];
-    const int sh = shifts[pass];
-    for (int i = threadIdx.x; i < nb; i += blockDim.x) hist[i] = 0;
-    __syncthreads();
-    for (int i = threadIdx.x; i < n; i += blockDim.x) {
-      const uint32_t key = keys[i];
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> sh) & (nb - 1)], 1u);
-    }
-    __syncthreads();
-    find_bin_from_top(hist, nb, need, scan, res);
-    prefix |= (uint32_t)res[0] << sh;
-    pmask |= (uint32_t)(nb - 1) << sh;
-    need -= res[1];
-    __syncthreads();
-  }
+  auto key_at = [&](int i) { return keys[i]; };
+  for (int shift = 24; shift >= 0; shift -= 8) radix_pass8(hist, n, key_at, prefix, pmask, shift, need, res);
   const uint32_t T = prefix;  // the m-th largest key; `need` ties at T are taken
   // ordered compaction: thread t owns the contiguous element range [t*E, t*E + E)
   const int E = (n + blockDim.x - 1) / blockDim.x;
@@ -128,9 +79,8 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_rows_lds(RowsDev rw, const
       eq += key == T;
     }
   }
-  int tot;
-  int gt_before = block_exclusive_scan(gt, scan, &tot);
-  int eq_before = block_exclusive_scan(eq, scan, &tot);
+  int gt_before, eq_before, t0, t1;
+  block_exclusive_scan2(gt, eq, scan, &gt_before, &eq_before, &t0, &t1);
   int32_t* orow = out + (int64_t)r * k;
   for (int j = 0; j < E; ++j) {
     const int i = i0 + j;
@@ -200,15 +150,17 @@ __global__ __launch_bounds__(kHistThreads) void k_topk_hist_partials(SelectArgs 
 //  3. The last workgroup of the row (ticket) concatenates the span lists (still in index order),
 //     refines the exact m-th largest key T over the remaining key bits, and writes the output:
 //     keys above T, then the lowest-index ties at T up to m, in list (= index) order.
-constexpr int kListLds = 5120;   // (key, index) pairs the last workgroup keeps in LDS
-constexpr int kCopyBatch = 6;    // list loads each thread keeps in flight
+constexpr int kListLds = 8192;   // (key, index) pairs the last workgroup keeps in LDS
+constexpr int kCopyBatch = 8;    // list loads each thread keeps in flight
+constexpr int kMaxSpans = 2 * kSelThreads;
+static_assert(kSelectSpan == kSelThreads * 8, "each select thread classifies 8 consecutive scores");
 
 __global__ __launch_bounds__(kSelThreads) void k_topk_select(SelectArgs a) {
-  __shared__ uint32_t hist[kTopkBins];
-  __shared__ int scan[kSelThreads / 64 + 1];
+  __shared__ uint32_t hist[256];
+  __shared__ int scan[2 * kSelThreads / 64];
   __shared__ int res[2];
   __shared__ int flag[1];
-  __shared__ int span_pre[kSelThreads + 1];
+  __shared__ int span_pre[kMaxSpans + 1];
   __shared__ uint2 list_lds[kListLds];
   const int r = blockIdx.y, sp = blockIdx.x;
   const int n = row_len(a.rw, r);
@@ -225,63 +177,67 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select(SelectArgs a) {
     }
     return;
   }
-  // 1. row histogram from the partials (thread t owns bins 2t, 2t+1), 32 partials per round
+  // this thread's 8 consecutive scores (loaded first; the latency overlaps the histogram)
+  const float* srow = a.scores + (int64_t)r * a.ld;
+  const int i0 = s0 + threadIdx.x * 8;
+  float x[8];
+  if (i0 + 7 < s1) {
+    const float4 v0 = *reinterpret_cast<const float4*>(srow + i0);
+    const float4 v1 = *reinterpret_cast<const float4*>(srow + i0 + 4);
+    x[0] = v0.x; x[1] = v0.y; x[2] = v0.z; x[3] = v0.w;
+    x[4] = v1.x; x[5] = v1.y; x[6] = v1.z; x[7] = v1.w;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = i0 + j < s1 ? srow[i0 + j] : 0.f;
+  }
+  // 1. row histogram from the partials: thread t sums bin pair (t % 128) over partials t / 128,
+  //    t / 128 + 8, ...; the 8 groups meet in LDS
+  static_assert(kTopkBins == 256 && kSelThreads == 1024, "histogram reduction layout");
+  if (threadIdx.x < kTopkBins) hist[threadIdx.x] = 0u;
+  __syncthreads();
   {
     const int nch = (n + kIdxChunk - 1) / kIdxChunk;
     const uint32_t* hp = reinterpret_cast<const uint32_t*>(a.hpart + (int64_t)r * a.hist_chunks * kTopkBins);
+    const int w = threadIdx.x & 127, pg = threadIdx.x >> 7;
     uint32_t lo = 0, hi = 0;
-    for (int c = 0; c < nch; c += 32) {
-      uint32_t w[32];
+    for (int c0 = 0; c0 < nch; c0 += 64) {
+      uint32_t v[8];
 #pragma unroll
-      for (int j = 0; j < 32; ++j) w[j] = c + j < nch ? hp[(int64_t)(c + j) * (kTopkBins / 2) + threadIdx.x] : 0u;
+      for (int j = 0; j < 8; ++j) {
+        const int c = c0 + pg + 8 * j;
+        v[j] = c < nch ? hp[(int64_t)c * (kTopkBins / 2) + w] : 0u;
+      }
 #pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        lo += w[j] & 0xFFFFu;
-        hi += w[j] >> 16;
+      for (int j = 0; j < 8; ++j) {
+        lo += v[j] & 0xFFFFu;
+        hi += v[j] >> 16;
       }
     }
-    hist[2 * threadIdx.x] = lo;
-    hist[2 * threadIdx.x + 1] = hi;
+    if (lo) atomicAdd(&hist[2 * w], lo);
+    if (hi) atomicAdd(&hist[2 * w + 1], hi);
   }
   __syncthreads();
-  find_bin_from_top(hist, kTopkBins, m, scan, res);
+  find_bin256_from_top(hist, m, res);
   const uint32_t t1 = (uint32_t)res[0];
   const int above1 = res[1];
-  // 2. ordered compaction of the span's scores with bin >= t1
-  const float* srow = a.scores + (int64_t)r * a.ld;
-  uint2* slot = a.slot + (int64_t)r * a.rw.max_row_len + s0;
-  constexpr int ROUND = kSelThreads * 4;
-  constexpr int ROUNDS = kSelectSpan / ROUND;
-  float4 v[ROUNDS];
-#pragma unroll
-  for (int q = 0; q < ROUNDS; ++q) {
-    const int i = s0 + q * ROUND + threadIdx.x * 4;
-    v[q] = i + 3 < s1 ? *reinterpret_cast<const float4*>(srow + i)
-                      : make_float4(i < s1 ? srow[i] : 0.f, i + 1 < s1 ? srow[i + 1] : 0.f,
-                                    i + 2 < s1 ? srow[i + 2] : 0.f, 0.f);
-  }
-  int written = 0;
-#pragma unroll
-  for (int q = 0; q < ROUNDS; ++q) {
-    const int i = s0 + q * ROUND + threadIdx.x * 4;
-    const float x[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
-    uint32_t key[4];
-    bool f[4];
+  // 2. ordered compaction of the span's scores with bin >= t1 into the span's slot
+  {
+    uint32_t key[8];
     int c = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 8; ++j) {
       key[j] = score_key(x[j]);
-      f[j] = (i + j < s1) && (key[j] >> (32 - kTopkBinBits)) >= t1;
-      c += f[j];
+      c += (i0 + j < s1) && (key[j] >> (32 - kTopkBinBits)) >= t1;
     }
     int tot;
-    int pos = written + block_exclusive_scan(c, scan, &tot);
+    int pos = block_exclusive_scan(c, scan, &tot);
+    uint2* slot = a.slot + (int64_t)r * a.rw.max_row_len + s0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (f[j]) st_dev(reinterpret_cast<uint64_t*>(slot + pos++), ((uint64_t)(uint32_t)(i + j) << 32) | key[j]);
-    written += tot;
+    for (int j = 0; j < 8; ++j)
+      if ((i0 + j < s1) && (key[j] >> (32 - kTopkBinBits)) >= t1)
+        st_dev(reinterpret_cast<uint64_t*>(slot + pos++), ((uint64_t)(uint32_t)(i0 + j) << 32) | key[j]);
+    if (threadIdx.x == 0) st_dev(&a.cnt[(int64_t)r * a.spans + sp], (uint32_t)tot);
   }
-  if (threadIdx.x == 0) st_dev(&a.cnt[(int64_t)r * a.spans + sp], (uint32_t)written);
   // 3. the last workgroup of the row finishes the selection
   const int nsp = (n + kSelectSpan - 1) / kSelectSpan;
   if (!arrive_last(&a.ticket[r], (uint32_t)nsp, flag)) return;
@@ -289,9 +245,12 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select(SelectArgs a) {
   // lives in LDS when it fits, else in the workspace
   int L = 0;
   {
-    const int mine = threadIdx.x < nsp ? (int)ld_dev(&a.cnt[(int64_t)r * a.spans + threadIdx.x]) : 0;
-    const int pre = block_exclusive_scan(mine, scan, &L);
-    if (threadIdx.x < nsp) span_pre[threadIdx.x] = pre;
+    const int s0i = 2 * threadIdx.x, s1i = s0i + 1;
+    const int c0 = s0i < nsp ? (int)ld_dev(&a.cnt[(int64_t)r * a.spans + s0i]) : 0;
+    const int c1 = s1i < nsp ? (int)ld_dev(&a.cnt[(int64_t)r * a.spans + s1i]) : 0;
+    const int pre = block_exclusive_scan(c0 + c1, scan, &L);
+    if (s0i < nsp) span_pre[s0i] = pre;
+    if (s1i < nsp) span_pre[s1i] = pre + c0;
     if (threadIdx.x == 0) span_pre[nsp] = L;
     __syncthreads();
   }
@@ -321,27 +280,12 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select(SelectArgs a) {
     }
     __syncthreads();
   }
-  // refine T below the first level: bits [20:10], then [9:0]
+  // refine T below the first level: three 8-bit passes over the remaining key bits
+  static_assert(kTopkBinBits == 8, "three refinement passes cover the remaining 24 key bits");
   int need = m - above1;
-  uint32_t prefix = t1 << (32 - kTopkBinBits), pmask = ~0u << (32 - kTopkBinBits);
-  const int shifts[2] = {10, 0};
-  const int widths[2] = {32 - kTopkBinBits - 10, 10};
-  for (int pass = 0; pass < 2; ++pass) {
-    const int nb = 1 << widths[pass];
-    const int sh = shifts[pass];
-    for (int i = threadIdx.x; i < nb; i += blockDim.x) hist[i] = 0u;
-    __syncthreads();
-    for (int i = threadIdx.x; i < L; i += blockDim.x) {
-      const uint32_t key = list[i].x;
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> sh) & (nb - 1)], 1u);
-    }
-    __syncthreads();
-    find_bin_from_top(hist, nb, need, scan, res);
-    prefix |= (uint32_t)res[0] << sh;
-    pmask |= (uint32_t)(nb - 1) << sh;
-    need -= res[1];
-    __syncthreads();
-  }
+  uint32_t prefix = t1 << 24, pmask = 0xFF000000u;
+  auto key_at = [&](int i) { return list[i].x; };
+  for (int shift = 16; shift >= 0; shift -= 8) radix_pass8(hist, L, key_at, prefix, pmask, shift, need, res);
   const uint32_t T = prefix;
   // ordered output over contiguous per-thread ranges of the list
   const int E = (L + blockDim.x - 1) / blockDim.x;
@@ -355,9 +299,8 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select(SelectArgs a) {
       eq += key == T;
     }
   }
-  int tot;
-  int gt_before = block_exclusive_scan(gt, scan, &tot);
-  int eq_before = block_exclusive_scan(eq, scan, &tot);
+  int gt_before, eq_before, tg, te;
+  block_exclusive_scan2(gt, eq, scan, &gt_before, &eq_before, &tg, &te);
   for (int j = 0; j < E; ++j) {
     const int p = p0 + j;
     if (p < L) {

@@ -111,7 +111,8 @@ AttnPlan plan_attn(const clsa_dims* d, int n_rows, int n_layers_call, int split_
   const int64_t base = (int64_t)(split_rows > 0 ? split_rows : n_rows) * d->hkv * p.qblocks;
   const int tiles = (d->topk + kAttnTile - 1) / kAttnTile;
   int splits = 1;
-  if (base < 512) splits = (int)((512 + base - 1) / base);
+  if (base < CLSA_ATTN_TARGET_WGS) splits = (int)((CLSA_ATTN_TARGET_WGS + base - 1) / base);
+  if (splits > kMaxAttnSplits) splits = kMaxAttnSplits;
   if (splits > tiles) splits = tiles;
   if (splits < 1) splits = 1;
   const int tiles_per_split = (tiles + splits - 1) / splits;
