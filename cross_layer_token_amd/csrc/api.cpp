@@ -117,7 +117,8 @@ clsa_status clsa_index_scores(const clsa_dims* dims, const clsa_rows* rows, cons
   const RowsDev rd = rows_dev(rows, cu_seqlens);
   int e;
   if (rows->mode == CLSA_MODE_DECODE)
-    e = launch_index_scores_decode(rd, dims->d_idx, q_idx, k_idx, scores, ld_scores, nullptr, nullptr, 0, stream);
+    e = launch_index_scores_decode(rd, dims->d_idx, idx_chunk_for(rows->n_rows, rows->max_row_len), q_idx, k_idx,
+                                   scores, ld_scores, nullptr, nullptr, 0, stream);
   else
     e = launch_index_scores_prefill(rd, dims->d_idx, q_idx, k_idx, scores, ld_scores, nullptr, 0, stream);
   return device_status(e, "clsa_index_scores");
@@ -260,8 +261,9 @@ clsa_status clsa_step(const clsa_dims* dims, const clsa_rows* rows, const clsa_s
     } else {
       uint16_t* hpart = tp.multi_wg ? reinterpret_cast<uint16_t*>(topk_ws + tp.hpart_off) : nullptr;
       have_hist = tp.multi_wg;
-      e = launch_index_scores_decode(rd, dims->d_idx, q_idx, a->k_idx, scores, ld, hpart, tickets, sp.n_tickets,
-                                     stream);
+      const int chunk = tp.multi_wg ? tp.hist_chunk : idx_chunk_for(cr.n_rows, cr.max_row_len);
+      e = launch_index_scores_decode(rd, dims->d_idx, chunk, q_idx, a->k_idx, scores, ld, hpart, tickets,
+                                     sp.n_tickets, stream);
     }
     if (e) return device_status(e, "clsa_step: index scores");
     int32_t* idx = a->idx + (int64_t)c0 * k;

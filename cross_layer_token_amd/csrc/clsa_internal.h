@@ -14,8 +14,12 @@ namespace clsa {
 // Rows no longer than this are selected by one workgroup holding the whole row in LDS;
 // longer rows use the multi-workgroup histogram select.
 constexpr int kLdsRowCap = 12288;
-// Tokens per workgroup of the decode score kernel (also the histogram partial granularity).
-constexpr int kIdxChunk = 4096;
+// Tokens per workgroup of the decode score kernel (also the histogram partial granularity):
+// kIdxChunkMax when that still gives kIdxMinWorkgroups workgroups, else halved down to
+// kIdxChunkMin (see idx_chunk_for).
+constexpr int kIdxChunkMax = 8192;
+constexpr int kIdxChunkMin = 1024;
+constexpr int kIdxMinWorkgroups = 256;
 // First histogram level of the long-row select: the top kTopkBinBits bits of the score key
 // (sign and the high exponent bits), small enough that every select workgroup can sum a row's
 // partials cheaply.
@@ -40,7 +44,8 @@ constexpr int kPrefillChunkRows = 1024;
 // ---- host-side plan (pure functions, no HIP) ------------------------------------------------
 struct TopkPlan {
   bool multi_wg = false;   // long rows: histogram select over many workgroups
-  int hist_chunks = 0;     // histogram partials per row (kIdxChunk scores each)
+  int hist_chunk = 0;      // scores per histogram partial (= the score kernel's chunk)
+  int hist_chunks = 0;     // histogram partials per row
   int spans = 0;           // select workgroups per row (kSelectSpan scores each)
   size_t hpart_off = 0;    // uint16 [R, hist_chunks, kTopkBins]
   size_t cnt_off = 0;      // uint32 [R, spans]
@@ -83,6 +88,8 @@ clsa_status check_ptr(const void* p, const char* name, std::string& err);
 clsa_status check_ptr_opt(const void* p, const char* name, std::string& err);
 
 TopkPlan plan_topk(const clsa_dims* d, const clsa_rows* r);
+// Tokens per workgroup of the decode score kernel for n_rows rows of at most max_row_len tokens.
+int idx_chunk_for(int n_rows, int max_row_len);
 // n_rows: rows of this launch (buffer sizes); split_rows: rows that decide the split count
 // (0 = n_rows).
 AttnPlan plan_attn(const clsa_dims* d, int n_rows, int n_layers_call, int split_rows);
@@ -108,7 +115,7 @@ struct RowsDev {
 };
 
 // `clear` (n_clear words) is zeroed by the launch before any other kernel of the call reads it.
-int launch_index_scores_decode(const RowsDev& rows, int d_idx, const uint16_t* q_idx, const uint16_t* k_idx,
+int launch_index_scores_decode(const RowsDev& rows, int d_idx, int chunk, const uint16_t* q_idx, const uint16_t* k_idx,
                                float* scores, int64_t ld, uint16_t* hpart, uint32_t* clear, int n_clear,
                                void* stream);
 int launch_index_scores_prefill(const RowsDev& rows, int d_idx, const uint16_t* q_idx, const uint16_t* k_idx,

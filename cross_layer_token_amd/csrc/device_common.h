@@ -49,6 +49,13 @@ __device__ __forceinline__ uint4 load_stream16(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Plain 16-byte load through a native vector type (a uint4 struct copy can become a memcpy into
+// private memory).
+__device__ __forceinline__ uint4 load16(const void* p) {
+  const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 template <typename T>
 __device__ __forceinline__ T bitcast(const uint4& v) {
   return __builtin_bit_cast(T, v);

@@ -68,6 +68,10 @@ __device__ __forceinline__ uint2 lds_read_tr(const uint16_t* p) {
 // One stage = kAttnStageTiles tiles of 64 keys in LDS (2 x 32 KB); the next stage's rows are in
 // flight into registers meanwhile (64 KB per workgroup).  Two workgroups share a CU.
 constexpr int kAttnStageTiles = 2;
+// log2 of the growth of the running max that is absorbed without rescaling (P <= 2^this).
+constexpr float kRescaleLog2 = 8.f;
+// Split partials fetched per round trip by the combining workgroup.
+constexpr int kCombineBatch = 4;
 
 template <bool FROM_CACHE>
 __global__ __launch_bounds__(kAttnThreads, 2) void k_sparse_attn(AttnArgs a) {
@@ -117,17 +121,21 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_sparse_attn(AttnArgs a) {
   const int ld_chunk = threadIdx.x & 15;  // 8 head_dim elements
   const int ld_key4 = threadIdx.x >> 4;   // keys 4*ld_key4 .. +3
 
-  struct Regs {
-    uint4 k[NT][4], v[NT][4];
-  };
+  // the next stage's K and V pieces of this thread, in flight while the current stage is computed
+  uint4 rk[NT][4], rv[NT][4];
   // token ids of this thread's keys in the stage starting at kt (cache source only)
+  // Keys past the end of this split are clamped to its last key: the load stays inside the
+  // selection (a finite row that is part of this attention anyway) and the key is masked out
+  // of the softmax, so no load needs a branch.
+  const int klast = kend - 1;
   auto load_ids = [&](int kt, int (&ids)[NT][4]) {
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int key = kt + t * kAttnTile + ld_key4 * 4 + i;
-        ids[t][i] = (FROM_CACHE && key < kend) ? irow[key] : 0;
+        ids[t][i] = key < klast ? key : klast;
+        if (FROM_CACHE) ids[t][i] = irow[ids[t][i]];
       }
   };
   // 64-bit base of this (row, KV head) once; per-row offsets then fit 32 bits
@@ -136,19 +144,14 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_sparse_attn(AttnArgs a) {
                                       : (((int64_t)r * a.hkv + g) * a.k) * CLSA_HEAD_DIM;
   const uint16_t* kbase = a.ksrc + base_off + ld_chunk * 8;
   const uint16_t* vbase = a.vsrc + base_off + ld_chunk * 8;
-  auto load_stage = [&](int kt, const int (&ids)[NT][4], Regs& rg) {
+  auto load_stage = [&](const int (&ids)[NT][4]) {
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int key = kt + t * kAttnTile + ld_key4 * 4 + i;
-        rg.k[t][i] = make_uint4(0u, 0u, 0u, 0u);
-        rg.v[t][i] = make_uint4(0u, 0u, 0u, 0u);
-        if (key < kend) {
-          const uint32_t off = (uint32_t)(FROM_CACHE ? ids[t][i] : key) * (uint32_t)row_elems;
-          rg.k[t][i] = *reinterpret_cast<const uint4*>(kbase + off);
-          rg.v[t][i] = *reinterpret_cast<const uint4*>(vbase + off);
-        }
+        const uint32_t off = (uint32_t)ids[t][i] * (uint32_t)row_elems;
+        rk[t][i] = load16(kbase + off);
+        rv[t][i] = load16(vbase + off);
       }
   };
   // Per-lane byte offsets into a tile (swizzled layout), fixed for the whole kernel; the parts that
@@ -174,106 +177,128 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_sparse_attn(AttnArgs a) {
 #pragma unroll
     for (int ht = 0; ht < 8; ++ht) voff[ht] = y * 256 + ((z ^ (2 * ht)) << 4) + 8 * (l16 & 1);
   }
-  auto store_stage = [&](const Regs& rg) {
+  auto store_stage = [&]() {
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(ks[t]) + soff[i]) = rg.k[t][i];
-        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(vs[t]) + soff[i]) = rg.v[t][i];
+        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(ks[t]) + soff[i]) = rk[t][i];
+        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(vs[t]) + soff[i]) = rv[t][i];
       }
   };
   const float scale = a.scale_log2;
-  // one 64-key tile: S^T = K Q^T, online softmax (exp2 domain, scaled), O^T += V^T P^T
-  auto compute_tile = [&](const uint16_t* kbuf, const uint16_t* vbuf, int nvalid) {
-    const char* kb = reinterpret_cast<const char*>(kbuf);
-    const char* vb = reinterpret_cast<const char*>(vbuf);
-    floatx4_t s[4];
+  // One stage of STAGE keys (both LDS tiles): S^T = K Q^T, online softmax in the exp2 domain,
+  // O^T += V^T P^T.  The running max m_run is only raised when some score of the wave exceeds it
+  // by more than 2^kRescaleLog2; until then P = 2^(s - m_run) <= 2^kRescaleLog2 is used as is.
+  // Numerator and denominator share the same m_run, so the result does not depend on when it is
+  // raised, and the common case needs neither a cross-lane reduction nor a rescale of acc.
+  auto compute_stage = [&](int kt) {
+    if (!wave_active) return;
+    const int nvalid = kend - kt < STAGE ? kend - kt : STAGE;
+    floatx4_t s[NT * 4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      s[mt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < NT; ++t) {
+      const char* kb = reinterpret_cast<const char*>(ks[t]);
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const uint4 av = *reinterpret_cast<const uint4*>(kb + koff[kk] + mt * 4096);
-        s[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8_t>(av), qf[kk], s[mt], 0, 0, 0);
+      for (int mt = 0; mt < 4; ++mt) {
+        floatx4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const uint4 av = *reinterpret_cast<const uint4*>(kb + koff[kk] + mt * 4096);
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8_t>(av), qf[kk], c, 0, 0, 0);
+        }
+        s[t * 4 + mt] = c;
       }
     }
-    // s[mt][j]: raw q.k of key mt*16 + grp*4 + j, query column l16
-    if (nvalid < kAttnTile) {
+    // s[u][j]: raw q.k of key 16u + 4grp + j of the stage, query column l16
+    if (nvalid < STAGE) {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int u = 0; u < NT * 4; ++u)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          if (mt * 16 + grp * 4 + j >= nvalid) s[mt][j] = -INFINITY;
+          if (u * 16 + grp * 4 + j >= nvalid) s[u][j] = -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) mx = fmaxf(fmaxf(mx, fmaxf(s[mt][0], s[mt][1])), fmaxf(s[mt][2], s[mt][3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx * scale);
-    const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    float psum = 0.f;
-    bf16x2_t pk[4][2];
+    for (int u = 0; u < NT * 4; ++u) mx = fmaxf(fmaxf(mx, fmaxf(s[u][0], s[u][1])), fmaxf(s[u][2], s[u][3]));
+    if (__any(mx * scale > m_run + kRescaleLog2)) {
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_run, mx * scale);
+      const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= corr;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      float p[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        p[j] = __builtin_amdgcn_exp2f(fmaf(s[mt][j], scale, -m_new));
-        psum += p[j];
-      }
-      pk[mt][0] = bf16x2_t{(__bf16)p[0], (__bf16)p[1]};
-      pk[mt][1] = bf16x2_t{(__bf16)p[2], (__bf16)p[3]};
+      for (int i = 0; i < 8; ++i) acc[i] *= corr;
     }
-    l_run = l_run * corr + psum;
+    // P^T operand of k-step kk (keys 32kk .. 32kk + 31): slots 0..3 <- keys 32kk + 4grp + j,
+    // slots 4..7 <- keys 32kk + 16 + 4grp + j
+    bf16x8_t pb[NT * 2];
+    float psum = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] *= corr;
-    // P^T operand of k-step kk: slots 0..3 <- keys 32kk + 4grp + j, slots 4..7 <- keys 32kk + 16 + 4grp + j
-    bf16x8_t pb[2];
+    for (int kk = 0; kk < NT * 2; ++kk) {
+      uint32_t w[4];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-      pb[kk] = __builtin_bit_cast(bf16x8_t, make_uint4(__builtin_bit_cast(uint32_t, pk[2 * kk][0]),
-                                                       __builtin_bit_cast(uint32_t, pk[2 * kk][1]),
-                                                       __builtin_bit_cast(uint32_t, pk[2 * kk + 1][0]),
-                                                       __builtin_bit_cast(uint32_t, pk[2 * kk + 1][1])));
+      for (int h = 0; h < 2; ++h) {
+        float p[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          p[j] = __builtin_amdgcn_exp2f(fmaf(s[2 * kk + h][j], scale, -m_run));
+          psum += p[j];
+        }
+        w[2 * h] = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)p[0], (__bf16)p[1]});
+        w[2 * h + 1] = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)p[2], (__bf16)p[3]});
+      }
+      pb[kk] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
+    }
+    l_run += psum;
 #pragma unroll
     for (int ht = 0; ht < 8; ++ht) {
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const uint2 v0 = lds_read_tr(reinterpret_cast<const uint16_t*>(vb + voff[ht] + kk * 8192));
-        const uint2 v1 = lds_read_tr(reinterpret_cast<const uint16_t*>(vb + voff[ht] + kk * 8192 + 4096));
+      for (int kk = 0; kk < NT * 2; ++kk) {
+        const char* vb = reinterpret_cast<const char*>(vs[kk >> 1]) + voff[ht] + (kk & 1) * 8192;
+        const uint2 v0 = lds_read_tr(reinterpret_cast<const uint16_t*>(vb));
+        const uint2 v1 = lds_read_tr(reinterpret_cast<const uint16_t*>(vb + 4096));
         acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8_t>(make_uint4(v0.x, v0.y, v1.x, v1.y)),
                                                           pb[kk], acc[ht], 0, 0, 0);
       }
     }
   };
-  auto compute_stage = [&](int kt) {
-    if (!wave_active) return;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int tk = kt + t * kAttnTile;
-      if (tk < kend) compute_tile(ks[t], vs[t], kend - tk < kAttnTile ? kend - tk : kAttnTile);
-    }
-  };
 
-  // the next stage's rows are requested before this stage is computed
-  Regs ra;
-  int ids_next[NT][4];
-  if (kbeg < kend) {
+  // Stage 0 is requested before the selection count has arrived: its keys are clamped into the
+  // index row, and padding entries (-1, past the count) are replaced by the split's first entry,
+  // which is selected whenever the split is not empty; when it is padding too (empty split,
+  // nothing is computed) token 0 of the row is read.  Only keys below the count reach the
+  // softmax, so the replaced rows never contribute.
+  {
     int ids0[NT][4];
-    load_ids(kbeg, ids0);
-    load_stage(kbeg, ids0, ra);
-    load_ids(kbeg + STAGE, ids_next);
+    const int kfirst = kbeg < a.k - 1 ? kbeg : a.k - 1;
+    const int id_first = FROM_CACHE ? irow[kfirst] : 0;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int key = kbeg + t * kAttnTile + ld_key4 * 4 + i;
+        key = key < a.k - 1 ? key : a.k - 1;
+        if (FROM_CACHE) {
+          int id = irow[key];
+          id = id >= 0 ? id : id_first;
+          key = id >= 0 ? id : 0;
+        }
+        ids0[t][i] = key;
+      }
+    load_stage(ids0);
   }
+  // the next stage's rows are requested before this stage is computed
+  int ids_next[NT][4];
+  if (kbeg < kend) load_ids(kbeg + STAGE, ids_next);
+  // inside the loop kend > kbeg, so every clamped key lies in [kbeg, kend); after the last
+  // stage the request for the "next" one re-reads the split's last row and is not used
   for (int kt = kbeg; kt < kend; kt += STAGE) {
-    store_stage(ra);
+    store_stage();
     __syncthreads();
-    if (kt + STAGE < kend) {
-      load_stage(kt + STAGE, ids_next, ra);
-      load_ids(kt + 2 * STAGE, ids_next);
-    }
+    load_stage(ids_next);
+    load_ids(kt + 2 * STAGE, ids_next);
     compute_stage(kt);
     __syncthreads();
   }
@@ -306,43 +331,54 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_sparse_attn(AttnArgs a) {
   uint32_t* ticket = a.tickets + ((int64_t)r * a.hkv + g) * a.qblocks + qb;
   if (!arrive_last(ticket, (uint32_t)a.splits, flag)) return;
   if (!q_valid) return;
-  // Recombine: O = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s with M = max_s m_s, summed in
-  // split order, so whichever workgroup arrives last computes exactly the same result.  This
-  // workgroup's own partial is still in registers.
-  float M = -INFINITY;
-  for (int s2 = 0; s2 < a.splits; ++s2)
-    M = fmaxf(M, s2 == split ? m_run : ld_dev(pw + s2 * split_stride + 32 * 64 + lane));
-  float den = 0.f;
+  // Recombine the splits in split order, so that whichever workgroup arrives last computes
+  // exactly the same result: a running (M, den, tot) absorbs split s as
+  //   M' = max(M, m_s),  tot' = 2^(M - M') tot + 2^(m_s - M') acc_s,  den' likewise with l_s.
+  // The partials of up to kCombineBatch splits are requested together (one round trip per batch).
+  float M = -INFINITY, den = 0.f;
   float tot[32];
 #pragma unroll
   for (int i = 0; i < 32; ++i) tot[i] = 0.f;
-  for (int s2 = 0; s2 < a.splits; ++s2) {
-    const float m2 = s2 == split ? m_run : ld_dev(pw + s2 * split_stride + 32 * 64 + lane);
-    if (m2 == -INFINITY) continue;
-    const float w = exp2f(m2 - M);
-    if (s2 == split) {
-      den += w * l_run;
+  for (int s0 = 0; s0 < a.splits; s0 += kCombineBatch) {
+    float mb[kCombineBatch], lb[kCombineBatch], vb[kCombineBatch][32];
 #pragma unroll
-      for (int ht = 0; ht < 8; ++ht)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) tot[ht * 4 + j] += w * acc[ht][j];
-    } else {
+    for (int b = 0; b < kCombineBatch; ++b) {
+      const int s2 = s0 + b;
+      if (s2 >= a.splits || s2 == split) continue;
       const float* ps = pw + s2 * split_stride;
-      float v[32];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) v[i] = ld_dev(ps + i * 64 + lane);
-      den += w * ld_dev(ps + 33 * 64 + lane);
+      for (int i = 0; i < 32; ++i) vb[b][i] = ld_dev(ps + i * 64 + lane);
+      mb[b] = ld_dev(ps + 32 * 64 + lane);
+      lb[b] = ld_dev(ps + 33 * 64 + lane);
+    }
 #pragma unroll
-      for (int i = 0; i < 32; ++i) tot[i] += w * v[i];
+    for (int b = 0; b < kCombineBatch; ++b) {
+      const int s2 = s0 + b;
+      if (s2 >= a.splits) break;
+      if (s2 == split) {
+        mb[b] = m_run;
+        lb[b] = l_run;
+#pragma unroll
+        for (int ht = 0; ht < 8; ++ht)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) vb[b][ht * 4 + j] = acc[ht][j];
+      }
+      if (mb[b] == -INFINITY) continue;  // a split with no keys
+      const float m_new = fmaxf(M, mb[b]);
+      const float c_old = __builtin_amdgcn_exp2f(M - m_new);
+      const float c_new = __builtin_amdgcn_exp2f(mb[b] - m_new);
+      M = m_new;
+      den = den * c_old + lb[b] * c_new;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) tot[i] = tot[i] * c_old + vb[b][i] * c_new;
     }
   }
-#pragma unroll
-  for (int ht = 0; ht < 8; ++ht)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[ht][j] = tot[ht * 4 + j];
   const float inv = den > 0.f ? 1.f / den : 0.f;
 #pragma unroll
-  for (int ht = 0; ht < 8; ++ht) store_out4(op + ht * 16 + grp * 4, acc[ht], inv);
+  for (int ht = 0; ht < 8; ++ht) {
+    const floatx4_t o = {tot[ht * 4], tot[ht * 4 + 1], tot[ht * 4 + 2], tot[ht * 4 + 3]};
+    store_out4(op + ht * 16 + grp * 4, o, inv);
+  }
 }
 
 __global__ void k_clear_u32(uint32_t* __restrict__ p, int n) {

@@ -40,20 +40,24 @@ __device__ __forceinline__ void rs_step(float* p, int sub) {
 
 constexpr int kIdxThreads = 256;
 
-// One workgroup = one chunk of kIdxChunk tokens of one sequence.  Besides the scores it can
-// write the chunk's histogram of the top kTopkBinBits key bits (for the top-k select) and
-// clear the select's per-row tickets (consumed by later kernels on the same stream).
+// One workgroup = one chunk of `chunk` tokens of one sequence.  Each wave takes 64 rows per
+// iteration (16 per lane, one 16-byte piece of each) and requests the next iteration's rows
+// before reducing the current ones, so every wave keeps a full set of loads in flight.  Besides
+// the scores it can write the chunk's histogram of the top kTopkBinBits key bits (for the top-k
+// select) and clear the select's per-row tickets (consumed by later kernels on the same stream).
 template <int D>
 __global__ __launch_bounds__(kIdxThreads) void k_index_scores_decode(const uint16_t* __restrict__ q_idx,
                                                                        const uint16_t* __restrict__ k_idx,
                                                                        const int32_t* __restrict__ cu,
-                                                                       int max_row_len, float* __restrict__ scores,
-                                                                       int64_t ld, uint16_t* __restrict__ hpart,
+                                                                       int max_row_len, int chunk,
+                                                                       float* __restrict__ scores, int64_t ld,
+                                                                       uint16_t* __restrict__ hpart,
                                                                        int hpart_chunks, uint32_t* __restrict__ clear,
                                                                        int n_clear) {
   constexpr int LPR = D / 8;   // lanes per K_idx row (16 bytes each)
   constexpr int NG = 64 / LPR; // row groups per wave
   constexpr int NR = LPR;      // rows per lane per iteration: one finished row per lane
+  constexpr int STEP = (kIdxThreads / 64) * 64;
   __shared__ uint32_t hist[kTopkBins];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lg = lane / LPR, sub = lane % LPR;
@@ -63,26 +67,31 @@ __global__ __launch_bounds__(kIdxThreads) void k_index_scores_decode(const uint1
     for (int i = threadIdx.x; i < n_clear; i += blockDim.x) clear[i] = 0u;
   int n = cu[b + 1] - cu[b];
   n = n < 0 ? 0 : (n > max_row_len ? max_row_len : n);
-  const int t0 = c * kIdxChunk;
+  const int t0 = c * chunk;
   if (t0 >= n) return;
-  const int t1 = t0 + kIdxChunk < n ? t0 + kIdxChunk : n;
+  const int t1 = t0 + chunk < n ? t0 + chunk : n;
   if (hpart != nullptr) {
     for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) hist[i] = 0u;
     __syncthreads();
   }
-  const uint16_t* kbase = k_idx + (int64_t)cu[b] * D;
+  const uint16_t* kbase = k_idx + (int64_t)cu[b] * D + sub * 8;
   const uint4 qv = *reinterpret_cast<const uint4*>(q_idx + (size_t)b * D + sub * 8);
   float* srow = scores + (int64_t)b * ld;
-  for (int it = t0 + wave * 64; it < t1; it += (kIdxThreads / 64) * 64) {
-    uint4 kv[NR];
+  uint4 kv[NR];
+  auto load = [&](int it) {
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
       const int row = it + i * NG + lg;
-      kv[i] = row < t1 ? load_stream16(kbase + (int64_t)row * D + sub * 8) : make_uint4(0u, 0u, 0u, 0u);
+      kv[i] = row < t1 ? load_stream16(kbase + (int64_t)row * D) : make_uint4(0u, 0u, 0u, 0u);
     }
+  };
+  int it = t0 + wave * 64;
+  if (it < t1) load(it);
+  for (; it < t1; it += STEP) {
     float p[NR];
 #pragma unroll
     for (int i = 0; i < NR; ++i) p[i] = dot8(kv[i], qv, 0.f);
+    if (it + STEP < t1) load(it + STEP);
     if constexpr (LPR == 16) {
       rs_step<8, 8>(p, sub);
       rs_step<4, 4>(p, sub);
@@ -157,18 +166,18 @@ __global__ __launch_bounds__(256) void k_index_scores_prefill(const uint16_t* __
 
 }  // namespace
 
-int launch_index_scores_decode(const RowsDev& rows, int d_idx, const uint16_t* q_idx, const uint16_t* k_idx,
-                               float* scores, int64_t ld, uint16_t* hpart, uint32_t* clear, int n_clear,
-                               void* stream) {
-  const int chunks = (rows.max_row_len + kIdxChunk - 1) / kIdxChunk;
+int launch_index_scores_decode(const RowsDev& rows, int d_idx, int chunk, const uint16_t* q_idx,
+                               const uint16_t* k_idx, float* scores, int64_t ld, uint16_t* hpart, uint32_t* clear,
+                               int n_clear, void* stream) {
+  const int chunks = (rows.max_row_len + chunk - 1) / chunk;
   const dim3 grid((unsigned)chunks, (unsigned)rows.n_rows);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (d_idx == 128)
     hipLaunchKernelGGL(k_index_scores_decode<128>, grid, dim3(kIdxThreads), 0, s, q_idx, k_idx, rows.cu,
-                       rows.max_row_len, scores, ld, hpart, chunks, clear, n_clear);
+                       rows.max_row_len, chunk, scores, ld, hpart, chunks, clear, n_clear);
   else
     hipLaunchKernelGGL(k_index_scores_decode<64>, grid, dim3(kIdxThreads), 0, s, q_idx, k_idx, rows.cu,
-                       rows.max_row_len, scores, ld, hpart, chunks, clear, n_clear);
+                       rows.max_row_len, chunk, scores, ld, hpart, chunks, clear, n_clear);
   return (int)hipGetLastError();
 }
 

@@ -105,6 +105,7 @@ struct SelectArgs {
   int32_t* out;
   int32_t* count;
   uint16_t* hpart;        // [R, hist_chunks, kTopkBins] per-chunk histograms of key >> (32 - kTopkBinBits)
+  int hist_chunk;         // scores per partial
   int hist_chunks;
   uint32_t* ticket;       // [R], zero on entry
   uint32_t* cnt;          // [R, spans]
@@ -123,22 +124,24 @@ __global__ __launch_bounds__(kHistThreads) void k_topk_hist_partials(SelectArgs 
   if (r == 0 && c == 0)
     for (int i = threadIdx.x; i < a.rw.n_rows; i += blockDim.x) a.ticket[i] = 0u;
   const int n = row_len(a.rw, r);
-  const int t0 = c * kIdxChunk;
+  const int t0 = c * a.hist_chunk;
   if (t0 >= n || (n <= a.k)) return;
-  const int t1 = t0 + kIdxChunk < n ? t0 + kIdxChunk : n;
+  const int t1 = t0 + a.hist_chunk < n ? t0 + a.hist_chunk : n;
   for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) hist[i] = 0u;
   __syncthreads();
   const float* srow = a.scores + (int64_t)r * a.ld;
-  constexpr int PER = kIdxChunk / kHistThreads;
-  float v[PER];
+  constexpr int PER = 8;
+  for (int i0 = t0 + threadIdx.x; i0 < t1; i0 += PER * kHistThreads) {
+    float v[PER];
 #pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int i = t0 + threadIdx.x + j * kHistThreads;
-    v[j] = i < t1 ? srow[i] : 0.f;
+    for (int j = 0; j < PER; ++j) {
+      const int i = i0 + j * kHistThreads;
+      v[j] = i < t1 ? srow[i] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+      if (i0 + j * kHistThreads < t1) atomicAdd(&hist[score_key(v[j]) >> (32 - kTopkBinBits)], 1u);
   }
-#pragma unroll
-  for (int j = 0; j < PER; ++j)
-    if (t0 + (int)threadIdx.x + j * kHistThreads < t1) atomicAdd(&hist[score_key(v[j]) >> (32 - kTopkBinBits)], 1u);
   __syncthreads();
   uint16_t* hp = a.hpart + ((int64_t)r * a.hist_chunks + c) * kTopkBins;
   for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) hp[i] = (uint16_t)hist[i];
@@ -196,7 +199,7 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select(SelectArgs a) {
   if (threadIdx.x < kTopkBins) hist[threadIdx.x] = 0u;
   __syncthreads();
   {
-    const int nch = (n + kIdxChunk - 1) / kIdxChunk;
+    const int nch = (n + a.hist_chunk - 1) / a.hist_chunk;
     const uint32_t* hp = reinterpret_cast<const uint32_t*>(a.hpart + (int64_t)r * a.hist_chunks * kTopkBins);
     const int w = threadIdx.x & 127, pg = threadIdx.x >> 7;
     uint32_t lo = 0, hi = 0;
@@ -333,6 +336,7 @@ int launch_topk(const RowsDev& rows, int k, const TopkPlan& plan, const float* s
   a.out = idx;
   a.count = count;
   a.hpart = reinterpret_cast<uint16_t*>(w + plan.hpart_off);
+  a.hist_chunk = plan.hist_chunk;
   a.hist_chunks = plan.hist_chunks;
   a.ticket = tickets;
   a.cnt = reinterpret_cast<uint32_t*>(w + plan.cnt_off);

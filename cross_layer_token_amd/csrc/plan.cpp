@@ -80,12 +80,19 @@ clsa_status check_rows(const clsa_dims* d, const clsa_rows* r, std::string& err)
   return CLSA_OK;
 }
 
+int idx_chunk_for(int n_rows, int max_row_len) {
+  int chunk = kIdxChunkMax;
+  while (chunk > kIdxChunkMin && (int64_t)n_rows * ((max_row_len + chunk - 1) / chunk) < kIdxMinWorkgroups) chunk >>= 1;
+  return chunk;
+}
+
 TopkPlan plan_topk(const clsa_dims* d, const clsa_rows* r) {
   TopkPlan p;
   p.multi_wg = r->max_row_len > kLdsRowCap;
   if (!p.multi_wg) return p;
   const size_t R = (size_t)r->n_rows;
-  p.hist_chunks = (r->max_row_len + kIdxChunk - 1) / kIdxChunk;
+  p.hist_chunk = idx_chunk_for(r->n_rows, r->max_row_len);
+  p.hist_chunks = (r->max_row_len + p.hist_chunk - 1) / p.hist_chunk;
   p.spans = (r->max_row_len + kSelectSpan - 1) / kSelectSpan;
   p.tickets = r->n_rows;
   size_t off = 0;
