@@ -61,6 +61,98 @@ def measured_traffic(bytes_alg_launch: float):
     return t.get("traffic_bytes_per_launch")
 
 
+# ---- rocprofv3 summaries (text under profiles/, made from rocprofv3's own CSV output) ----------
+WORKLOAD_TAG = "decode_b16_n128k"
+PROFILE_COMMANDS = {
+    "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_trace -o bench -- "
+             "python3 bench.py --steps 20 --warmup 3 --no-cpu-baseline",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof_fetch -o bench -- "
+             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-per-layer --profile-copy-mib 1024",
+    "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof_write -o bench -- "
+             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-per-layer --profile-copy-mib 1024",
+}
+
+
+def _csv_rows(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _short_kernel(name: str) -> str:
+    n = name.replace("(anonymous namespace)::", "").split("(")[0]
+    for pre in ("void ", "clsa::", "at::native::"):
+        n = n.replace(pre, "")
+    return n.strip()
+
+
+def summarize_trace(trace_dir: str) -> str:
+    """Markdown table of rocprofv3's kernel statistics (``*_kernel_stats.csv``)."""
+    import glob
+    path = sorted(glob.glob(os.path.join(trace_dir, "*_kernel_stats.csv")))[0]
+    lines = [f"# Kernel trace: decode step, {WORKLOAD_TAG}", "",
+             "Made by (on one MI355X):", "", f"    {PROFILE_COMMANDS['trace']}",
+             f"    python bench.py --summarize-trace {trace_dir}", "",
+             "The run holds warmup + timed steps of the layer-batched step (score kernel with histogram,",
+             "top-k select, sparse attention), the score kernel alone (the roofline line), the",
+             "per-layer schedule (gather + one attention per layer), and the synthetic-input fill.", "",
+             "| kernel | calls | avg us | min us | max us | share % |", "|---|---:|---:|---:|---:|---:|"]
+    for r in _csv_rows(path):
+        lines.append(f"| `{_short_kernel(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
+    return "\n".join(lines) + "\n"
+
+
+def summarize_counters(fetch_dir: str, write_dir: str, copy_mib: int = 1024) -> tuple:
+    """HBM bytes per launch of the score kernel from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
+    each scaled by what the same counter reads for a plain device copy of copy_mib MiB."""
+    import glob
+    def rows(d):
+        return _csv_rows(sorted(glob.glob(os.path.join(d, "*_counter_collection.csv")))[0])
+    out = {}
+    for tag, d, cname in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
+        rr = [r for r in rows(d) if r["Counter_Name"] == cname]
+        copy = max((r for r in rr if "copyBuffer" in r["Kernel_Name"]), key=lambda r: int(r["Grid_Size"]))
+        scale = (copy_mib * 1024.0) / float(copy["Counter_Value"])
+        # the scores-only launches are the ones after the last attention dispatch (bench order)
+        last_attn = max(int(r["Dispatch_Id"]) for r in rr if "k_sparse_attn" in r["Kernel_Name"])
+        idx_only = [float(r["Counter_Value"]) for r in rr
+                    if "k_index_scores_decode" in r["Kernel_Name"] and int(r["Dispatch_Id"]) > last_attn]
+        in_step = [float(r["Counter_Value"]) for r in rr
+                   if "k_index_scores_decode" in r["Kernel_Name"] and int(r["Dispatch_Id"]) < last_attn]
+        out[tag] = {"copy_kib": float(copy["Counter_Value"]), "scale": scale,
+                    "kib_per_launch": sum(idx_only) / len(idx_only), "launches": len(idx_only),
+                    "kib_per_launch_in_step": sum(in_step) / len(in_step)}
+    traffic = (out["fetch"]["kib_per_launch"] * out["fetch"]["scale"]
+               + out["write"]["kib_per_launch"] * out["write"]["scale"]) * 1024.0
+    import clsa_synth as cs
+    w = cs.config(3)
+    b = algorithmic_bytes(w)
+    alg = b["k_idx"] + b["q_idx"] + 4 * w.total_tokens
+    rec = {"kernel": "k_index_scores_decode<128>", "workload": WORKLOAD_TAG, "kernel_source_sha": index_kernel_sha(),
+           "kernel_sources": INDEX_KERNEL_SOURCES, "traffic_bytes_per_launch": round(traffic),
+           "algorithmic_bytes_per_launch": alg, "traffic_over_algorithmic": round(traffic / alg, 4),
+           "fetch": out["fetch"], "write": out["write"], "copy_mib": copy_mib,
+           "commands": [PROFILE_COMMANDS["fetch"], PROFILE_COMMANDS["write"],
+                        f"python bench.py --summarize-counters {fetch_dir} {write_dir}"]}
+    md = [f"# HBM traffic of the score kernel, {WORKLOAD_TAG}", "",
+          "Made by (on one MI355X; the counter passes run separately):", "",
+          *[f"    {c}" for c in rec["commands"]], "",
+          f"Calibration: a plain device copy of {copy_mib} MiB reads as FETCH_SIZE "
+          f"{out['fetch']['copy_kib']:.2f} KiB and WRITE_SIZE {out['write']['copy_kib']:.2f} KiB, so the factors",
+          f"are {out['fetch']['scale']:.4f} (fetch) and {out['write']['scale']:.4f} (write).", "",
+          "| | FETCH_SIZE KiB | WRITE_SIZE KiB |", "|---|---:|---:|",
+          f"| scores only (per launch, {out['fetch']['launches']} launches) | {out['fetch']['kib_per_launch']:.2f} | "
+          f"{out['write']['kib_per_launch']:.2f} |",
+          f"| in the step (with the top-k histogram) | {out['fetch']['kib_per_launch_in_step']:.2f} | "
+          f"{out['write']['kib_per_launch_in_step']:.2f} |", "",
+          f"Scaled traffic per scores-only launch: {traffic:,.0f} B; algorithmic (K_idx + q_idx read, fp32",
+          f"scores written): {alg:,} B; ratio {traffic / alg:.4f}.", "",
+          f"Kernel source hash (first 16 hex of sha256 over {', '.join(INDEX_KERNEL_SOURCES)}): "
+          f"`{rec['kernel_source_sha']}`."]
+    return rec, "\n".join(md) + "\n"
+
+
 def cpu_baseline(w, budget_s: float) -> dict:
     """The fp64 oracle on host cores (one thread), over whole decode rows until the budget is used.
     Input regeneration is excluded from the timed part; scores, top-k and attention are timed."""
@@ -105,7 +197,23 @@ def main():
     ap.add_argument("--no-per-layer", action="store_true")
     ap.add_argument("--profile-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a counter calibration reference)")
+    ap.add_argument("--summarize-trace", metavar="DIR", help="write the kernel-trace summary under profiles/ and exit")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the score kernel's HBM traffic summary under profiles/ and exit")
     args = ap.parse_args()
+    if args.summarize_trace or args.summarize_counters:
+        os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+        if args.summarize_trace:
+            p = os.path.join(ROOT, "profiles", f"kernel_trace_{WORKLOAD_TAG}.md")
+            open(p, "w").write(summarize_trace(args.summarize_trace))
+            print("wrote", p)
+        if args.summarize_counters:
+            rec, md = summarize_counters(*args.summarize_counters)
+            json.dump(rec, open(TRAFFIC_FILE, "w"), indent=1)
+            p = os.path.join(ROOT, "profiles", f"hbm_traffic_index_scores_{WORKLOAD_TAG}.md")
+            open(p, "w").write(md)
+            print("wrote", TRAFFIC_FILE, "and", p)
+        return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
         sys.exit(2)
