@@ -154,35 +154,38 @@ def summarize_counters(fetch_dir: str, write_dir: str, copy_mib: int = 1024) -> 
 
 
 def cpu_baseline(w, budget_s: float) -> dict:
-    """The fp64 oracle on host cores (one thread), over whole decode rows until the budget is used.
-    Input regeneration is excluded from the timed part; scores, top-k and attention are timed."""
+    """The fp64 oracle on one host thread, on a bounded sample of the workload: whole decode rows
+    (scores over the row's full context, top-k, all L layers of attention).  Rows are regenerated
+    once (not timed, at most budget_s / 2 of wall time); then the oracle passes over them until
+    about budget_s / 2 of oracle time has been measured."""
     from threadpoolctl import threadpool_limits
 
     from oracle import clsa_oracle as O
     cu = w.cu_seqlens
+    inputs = []
+    wall0 = time.perf_counter()
+    for r in range(w.n_rows):
+        n = w.row_len(r)
+        qi, ki = w.q_idx_f64([r])[0], w.k_idx_f64(cu[r] + np.arange(n))
+        sel = O.topk_select(O.index_scores(qi, ki), w.topk)   # only to regenerate the selected K/V rows
+        kf, vf = w.kv_f64(cu[r] + sel)
+        inputs.append((qi, ki, w.q_f64([r])[0], kf, vf))
+        if time.perf_counter() - wall0 > budget_s / 2:
+            break
     t_oracle = 0.0
     rows = 0
-    wall0 = time.perf_counter()
     with threadpool_limits(limits=1):
-        for r in range(w.n_rows):
-            n = w.row_len(r)
-            qi = w.q_idx_f64([r])[0]
-            ki = w.k_idx_f64(cu[r] + np.arange(n))
-            ql = w.q_f64([r])[0]
-            t0 = time.perf_counter()
-            sel = O.topk_select(O.index_scores(qi, ki), w.topk)
-            t1 = time.perf_counter()
-            kf, vf = w.kv_f64(cu[r] + sel)
-            t2 = time.perf_counter()
-            O.sparse_attention(ql, kf, vf)
-            t3 = time.perf_counter()
-            t_oracle += (t1 - t0) + (t3 - t2)
-            rows += 1
-            if time.perf_counter() - wall0 > budget_s:
-                break
+        while t_oracle < budget_s / 2:
+            for qi, ki, ql, kf, vf in inputs:
+                t0 = time.perf_counter()
+                O.topk_select(O.index_scores(qi, ki), w.topk)
+                O.sparse_attention(ql, kf, vf)
+                t_oracle += time.perf_counter() - t0
+                rows += 1
     return {"value": rows / t_oracle, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{rows} of {w.n_rows} decode rows of {w.name} (scores+top-k+{w.n_layers}-layer attention, "
-                      f"fp64 numpy, 1 thread; input regeneration not timed); oracle time {t_oracle:.2f} s"}
+            "sample": f"{rows} decode rows ({len(inputs)} distinct of {w.n_rows}, passed over repeatedly) of {w.name}: "
+                      f"scores over the full {w.max_row_len}-token context + top-k + {w.n_layers}-layer attention, "
+                      f"fp64 numpy on 1 thread; input regeneration not timed; oracle time {t_oracle:.2f} s"}
 
 
 def main():

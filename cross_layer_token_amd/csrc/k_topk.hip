@@ -154,7 +154,8 @@ __global__ __launch_bounds__(kHistThreads) void k_topk_hist_partials(SelectArgs 
 //     refines the exact m-th largest key T over the remaining key bits, and writes the output:
 //     keys above T, then the lowest-index ties at T up to m, in list (= index) order.
 constexpr int kListLds = 8192;   // (key, index) pairs the last workgroup keeps in LDS
-constexpr int kCopyBatch = 8;    // list loads each thread keeps in flight
+constexpr int kCopyBatch = 8;    // list loads each lane keeps in flight
+constexpr int kSpecPerLane = 4;  // span entries each lane requests before the span counts arrive
 constexpr int kMaxSpans = 2 * kSelThreads;
 static_assert(kSelectSpan == kSelThreads * 8, "each select thread classifies 8 consecutive scores");
 
@@ -244,8 +245,21 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select(SelectArgs a) {
   // 3. the last workgroup of the row finishes the selection
   const int nsp = (n + kSelectSpan - 1) / kSelectSpan;
   if (!arrive_last(&a.ticket[r], (uint32_t)nsp, flag)) return;
-  // concatenate the span lists (spans in order, so the list stays in index order); the list
-  // lives in LDS when it fits, else in the workspace
+  // Concatenate the span lists (spans in order, so the list stays in index order); the list lives
+  // in LDS when it fits, else in the workspace.  Wave w moves spans w, w + 16, ...; the first
+  // kSpecPerLane * 64 entries of its first span are requested together with the span counts, so
+  // that a typical row needs a single round trip.
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int kWaves = kSelThreads / 64;
+  const uint2* rslot = a.slot + (int64_t)r * a.rw.max_row_len;
+  uint64_t spec[kSpecPerLane];
+  if (wave < nsp) {
+#pragma unroll
+    for (int j = 0; j < kSpecPerLane; ++j) {
+      const int e = wave * kSelectSpan + j * 64 + lane;  // stays inside the row's scores
+      spec[j] = e < n ? ld_dev(reinterpret_cast<const uint64_t*>(rslot + e)) : 0;
+    }
+  }
   int L = 0;
   {
     const int s0i = 2 * threadIdx.x, s1i = s0i + 1;
@@ -258,31 +272,33 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select(SelectArgs a) {
     __syncthreads();
   }
   uint2* list = L <= kListLds ? list_lds : a.list + (int64_t)r * a.rw.max_row_len;
-  {
-    const uint2* rslot = a.slot + (int64_t)r * a.rw.max_row_len;
-    for (int p0 = 0; p0 < L; p0 += kSelThreads * kCopyBatch) {
+  for (int sp2 = wave; sp2 < nsp; sp2 += kWaves) {
+    const int base = span_pre[sp2], cnt_s = span_pre[sp2 + 1] - base;
+    const uint2* src = rslot + (int64_t)sp2 * kSelectSpan;
+    int e0 = 0;
+    if (sp2 == wave) {
+#pragma unroll
+      for (int j = 0; j < kSpecPerLane; ++j) {
+        const int e = j * 64 + lane;
+        if (e < cnt_s) list[base + e] = make_uint2((uint32_t)spec[j], (uint32_t)(spec[j] >> 32));
+      }
+      e0 = kSpecPerLane * 64;
+    }
+    for (; e0 < cnt_s; e0 += kCopyBatch * 64) {
       uint64_t v[kCopyBatch];
-      int at[kCopyBatch];
 #pragma unroll
       for (int j = 0; j < kCopyBatch; ++j) {
-        const int p = p0 + j * kSelThreads + threadIdx.x;
-        at[j] = p;
-        v[j] = 0;
-        if (p < L) {
-          int lo = 0, hi = nsp - 1;  // span holding list position p
-          while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (span_pre[mid] <= p) lo = mid; else hi = mid - 1;
-          }
-          v[j] = ld_dev(reinterpret_cast<const uint64_t*>(rslot + (int64_t)lo * kSelectSpan + (p - span_pre[lo])));
-        }
+        const int e = e0 + j * 64 + lane;
+        v[j] = e < cnt_s ? ld_dev(reinterpret_cast<const uint64_t*>(src + e)) : 0;
       }
 #pragma unroll
-      for (int j = 0; j < kCopyBatch; ++j)
-        if (at[j] < L) list[at[j]] = make_uint2((uint32_t)v[j], (uint32_t)(v[j] >> 32));
+      for (int j = 0; j < kCopyBatch; ++j) {
+        const int e = e0 + j * 64 + lane;
+        if (e < cnt_s) list[base + e] = make_uint2((uint32_t)v[j], (uint32_t)(v[j] >> 32));
+      }
     }
-    __syncthreads();
   }
+  __syncthreads();
   // refine T below the first level: three 8-bit passes over the remaining key bits
   static_assert(kTopkBinBits == 8, "three refinement passes cover the remaining 24 key bits");
   int need = m - above1;
