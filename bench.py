@@ -21,6 +21,7 @@ import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 METRIC = "decode tokens/sec + HBM GB/s (% roofline), index+top-k+L-layer attn at 128K"
 INDEX_KERNEL_SOURCES = ["cross_layer_token_amd/csrc/k_index.hip", "cross_layer_token_amd/csrc/device_common.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_index_scores_decode_b16_n128k.json")
@@ -65,11 +66,13 @@ def measured_traffic(bytes_alg_launch: float):
 WORKLOAD_TAG = "decode_b16_n128k"
 PROFILE_COMMANDS = {
     "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_trace -o bench -- "
-             "python3 bench.py --steps 20 --warmup 3 --no-cpu-baseline",
+             "python3 bench.py --steps 20 --warmup 3 --no-cpu-baseline --no-prefill",
     "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof_fetch -o bench -- "
-             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-per-layer --profile-copy-mib 1024",
+             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-per-layer --no-prefill "
+             "--profile-copy-mib 1024",
     "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof_write -o bench -- "
-             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-per-layer --profile-copy-mib 1024",
+             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-per-layer --no-prefill "
+             "--profile-copy-mib 1024",
 }
 
 
@@ -153,6 +156,64 @@ def summarize_counters(fetch_dir: str, write_dir: str, copy_mib: int = 1024) -> 
     return rec, "\n".join(md) + "\n"
 
 
+def prefill_report(steps: int = 3, chunk: int = 8192) -> dict:
+    """The causal chunked-prefill step (8192 rows, k=2048, L=8), reported beside the decode line.
+    Its attention FLOPs run against the bf16 MFMA peak. Each row gathers its own selection of K/V
+    rows (about 60 GB per step, served from the Infinity Cache and L2), so the gather rate is
+    reported too. The indexer GEMM is also timed alone."""
+    import torch
+
+    import clsa_synth as cs
+    import cross_layer_token_amd as clsa
+    from clsa_synth.device import DeviceWorkload
+
+    w = cs.config(4)
+    dw = DeviceWorkload(w)
+    dims = clsa.make_dims(**dw.dims())
+    rows = clsa.make_rows(**dw.rows())
+    R, k, L = w.n_rows, w.topk, w.n_layers
+    out = torch.empty((R, L, w.hq, 128), dtype=torch.int16, device="cuda")
+    idx = torch.empty((R, k), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((R,), dtype=torch.int32, device="cuda")
+    nws = clsa.workspace_bytes(dims, rows, clsa.SCHEDULE_LAYER_BATCHED, chunk)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def run(n):
+        for _ in range(n):
+            clsa.step(dims, rows, dw.q_idx, dw.k_idx, dw.k_cache, dw.v_cache, dw.cu_seqlens, dw.q, out, idx, cnt,
+                      ws, nws, prefill_chunk_rows=chunk, stream=stream)
+
+    run(1)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run(steps)
+    torch.cuda.synchronize()
+    t_step = (time.perf_counter() - t0) / steps
+    sel = sum(min(k, t + 1) for t in range(R))                  # selected (row, token) pairs
+    attn_flop = 4.0 * sel * L * w.hq * w.head_dim                # QK^T and PV, 2 flop per MAC
+    gather_bytes = float(sel) * w.hkv * w.head_dim * 2 * 2       # K and V rows each row reads
+    # the indexer GEMM alone: causal Q_idx K_idx^T, 2 * d_idx flop per visible (row, token)
+    ld = ((R + 63) // 64) * 64
+    scores = torch.empty((R, ld), dtype=torch.float32, device="cuda")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    clsa.index_scores(dims, rows, dw.q_idx, dw.k_idx, dw.cu_seqlens, scores, ld, stream=stream)
+    ev0.record(stream)
+    for _ in range(10):
+        clsa.index_scores(dims, rows, dw.q_idx, dw.k_idx, dw.cu_seqlens, scores, ld, stream=stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t_idx = ev0.elapsed_time(ev1) / 10 / 1e3
+    idx_flop = 2.0 * w.d_idx * (R * (R + 1) // 2)
+    return {"workload": w.name, "rows": R, "topk": k, "layers": L, "chunk_rows": chunk, "steps": steps,
+            "ms_per_step": round(t_step * 1e3, 3), "tokens_per_s": round(R / t_step, 1),
+            "attn_tflops_alg": round(attn_flop / t_step / 1e12, 1),
+            "attn_mfma_frac_of_step": round(attn_flop / t_step / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "gather_bytes": gather_bytes, "gather_tbps": round(gather_bytes / t_step / 1e12, 2),
+            "index_gemm_us": round(t_idx * 1e6, 1), "index_gemm_tflops": round(idx_flop / t_idx / 1e12, 1),
+            "index_gemm_mfma_frac": round(idx_flop / t_idx / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+
 def cpu_baseline(w, budget_s: float) -> dict:
     """The fp64 oracle on one host thread, on a bounded sample of the workload: whole decode rows
     (scores over the row's full context, top-k, all L layers of attention).  Rows are regenerated
@@ -198,6 +259,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of wall time for the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-layer", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill report")
     ap.add_argument("--profile-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a counter calibration reference)")
     ap.add_argument("--summarize-trace", metavar="DIR", help="write the kernel-trace summary under profiles/ and exit")
@@ -304,6 +366,9 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    del dw, out, idx, cnt, ws, scores
+    torch.cuda.empty_cache()
+    prefill = None if args.no_prefill else prefill_report()
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_budget)
     line = {
         "metric": METRIC,
@@ -327,6 +392,7 @@ def main():
         "gpu_event_ms_per_step": round(t_gpu / args.steps * 1e3, 4),
         "roofline": roofline,
         "per_layer_schedule": per_layer,
+        "prefill": prefill,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
