@@ -215,38 +215,30 @@ def prefill_report(steps: int = 3, chunk: int = 8192) -> dict:
 
 
 def cpu_baseline(w, budget_s: float) -> dict:
-    """The fp64 oracle on one host thread, on a bounded sample of the workload: whole decode rows
-    (scores over the row's full context, top-k, all L layers of attention).  Rows are regenerated
-    once (not timed, at most budget_s / 2 of wall time); then the oracle passes over them until
-    about budget_s / 2 of oracle time has been measured."""
-    from threadpoolctl import threadpool_limits
+    """The fp64 C++ oracle on the host, on a bounded sample of the workload: whole decode rows,
+    each evaluated from scratch (inputs regenerated from the generator definition, scores over
+    the row's full context, top-k by full sort, all L layers of attention). About budget_s / 2
+    on one core, then about budget_s / 2 with the rows spread over the host's cores (at most 16
+    threads; each row stays single-threaded)."""
+    from oracle import cpp as C
 
-    from oracle import clsa_oracle as O
-    cu = w.cu_seqlens
-    inputs = []
-    wall0 = time.perf_counter()
-    for r in range(w.n_rows):
-        n = w.row_len(r)
-        qi, ki = w.q_idx_f64([r])[0], w.k_idx_f64(cu[r] + np.arange(n))
-        sel = O.topk_select(O.index_scores(qi, ki), w.topk)   # only to regenerate the selected K/V rows
-        kf, vf = w.kv_f64(cu[r] + sel)
-        inputs.append((qi, ki, w.q_f64([r])[0], kf, vf))
-        if time.perf_counter() - wall0 > budget_s / 2:
-            break
-    t_oracle = 0.0
-    rows = 0
-    with threadpool_limits(limits=1):
-        while t_oracle < budget_s / 2:
-            for qi, ki, ql, kf, vf in inputs:
-                t0 = time.perf_counter()
-                O.topk_select(O.index_scores(qi, ki), w.topk)
-                O.sparse_attention(ql, kf, vf)
-                t_oracle += time.perf_counter() - t0
-                rows += 1
-    return {"value": rows / t_oracle, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{rows} decode rows ({len(inputs)} distinct of {w.n_rows}, passed over repeatedly) of {w.name}: "
-                      f"scores over the full {w.max_row_len}-token context + top-k + {w.n_layers}-layer attention, "
-                      f"fp64 numpy on 1 thread; input regeneration not timed; oracle time {t_oracle:.2f} s"}
+    threads = max(1, min(16, os.cpu_count() or 1))
+    one_rows, one_t = 0, 0.0
+    while one_t < budget_s / 2 and one_rows < 4 * w.n_rows:
+        _, t = C.oracle_rows_timed(w, [one_rows % w.n_rows], threads=1)
+        one_t += t
+        one_rows += 1
+    all_rows, all_t = 0, 0.0
+    while all_t < budget_s / 2:
+        _, t = C.oracle_rows_timed(w, list(range(w.n_rows)), threads=threads)
+        all_t += t
+        all_rows += w.n_rows
+    return {"value": round(all_rows / all_t, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "one_core_tokens_per_s": round(one_rows / one_t, 3),
+            "sample": f"{w.name}: {all_rows} decode rows on {threads} threads ({all_t:.1f} s) and {one_rows} rows on "
+                      f"one thread ({one_t:.1f} s); each row evaluated from scratch by the fp64 C++ oracle (inputs "
+                      f"regenerated, scores over the full {w.max_row_len}-token context, top-k by full sort, "
+                      f"{w.n_layers}-layer attention)"}
 
 
 def main():

@@ -16,14 +16,21 @@ import pytest
 import torch
 
 import clsa_synth as cs
-from oracle import clsa_oracle as O
+from oracle import clsa_oracle as numpy_oracle
+from oracle import cpp as cpp_oracle
 from oracle.workload_oracle import oracle_row
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
+@pytest.fixture(params=["numpy", "cpp"])
+def O(request):
+    """Every primitive pin runs against both oracles (numpy, and the independent C++ one)."""
+    return numpy_oracle if request.param == "numpy" else cpp_oracle
+
+
 # ----------------------------------------------------------------------------- scores (a1)
-def test_scores_one_hot_query_reads_one_key_column():
+def test_scores_one_hot_query_reads_one_key_column(O):
     rng = np.random.default_rng(0)
     k = rng.integers(-8, 9, size=(37, 16)) / 8.0
     for c in range(16):
@@ -32,13 +39,13 @@ def test_scores_one_hot_query_reads_one_key_column():
         assert np.array_equal(O.index_scores(q, k), k[:, c])
 
 
-def test_scores_hand_worked_example():
+def test_scores_hand_worked_example(O):
     g = json.load(open(os.path.join(GOLDEN, "tiny_routing.json")))
     s = O.index_scores(np.array(g["q_idx"]), np.array(g["k_idx"]))
     assert s.tolist() == g["scores"]
 
 
-def test_scores_needle_closed_form():
+def test_scores_needle_closed_form(O):
     w = cs.config(1)
     q = w.q_idx_f64([0])[0]
     needles = w.needle_positions_of_row(0)
@@ -47,7 +54,7 @@ def test_scores_needle_closed_form():
     assert np.all(s == 2.0 * float(np.dot(q, q)))   # K_idx row = 2 q  ->  score = 2 |q|^2
 
 
-def test_scores_sign_and_linearity():
+def test_scores_sign_and_linearity(O):
     rng = np.random.default_rng(1)
     k = rng.integers(-8, 9, size=(50, 8)) / 8.0
     q = rng.integers(-8, 9, size=8) / 8.0
@@ -56,7 +63,7 @@ def test_scores_sign_and_linearity():
 
 
 @pytest.mark.parametrize("cfg,rows", [(1, [0]), (2, [3]), (5, [0, 7])])
-def test_config_scores_exact_in_fp32(cfg, rows):
+def test_config_scores_exact_in_fp32(O, cfg, rows):
     """Exactness precondition of the bitwise score comparison holds on the config inputs."""
     w = cs.config(cfg)
     cu = w.cu_seqlens
@@ -79,7 +86,7 @@ def _brute_force_selection(scores, k):
     return sel
 
 
-def test_topk_equals_brute_force_on_tiny_inputs():
+def test_topk_equals_brute_force_on_tiny_inputs(O):
     rng = np.random.default_rng(2)
     for trial in range(40):
         n = int(rng.integers(1, 65))
@@ -90,24 +97,24 @@ def test_topk_equals_brute_force_on_tiny_inputs():
             assert got == _brute_force_selection(scores.tolist(), k), (trial, n, k)
 
 
-def test_topk_hand_worked_example():
+def test_topk_hand_worked_example(O):
     g = json.load(open(os.path.join(GOLDEN, "tiny_routing.json")))
     for k, want in g["selected"].items():
         assert O.topk_select(np.array(g["scores"]), int(k)).tolist() == want
 
 
-def test_topk_all_equal_takes_lowest_indices():
+def test_topk_all_equal_takes_lowest_indices(O):
     for n, k in [(10, 3), (5, 5), (4, 9)]:
         assert O.topk_select(np.zeros(n), k).tolist() == list(range(min(n, k)))
 
 
-def test_topk_negative_zero_ties_with_zero():
+def test_topk_negative_zero_ties_with_zero(O):
     s = np.array([0.0, -0.0, -0.0, 0.0, 1.0])
     assert O.topk_select(s, 3).tolist() == [0, 1, 4]
     assert O.topk_select(-s[::-1].copy(), 2).tolist() == [1, 2]   # [-1, -0, 0, 0, -0] -> first two zeros
 
 
-def test_topk_count_order_and_padding():
+def test_topk_count_order_and_padding(O):
     rng = np.random.default_rng(3)
     s = rng.standard_normal(100)
     sel = O.topk_select(s, 10)
@@ -117,7 +124,7 @@ def test_topk_count_order_and_padding():
     assert cnt == 7 and idx.tolist() == list(range(7)) + [-1, -1, -1]
 
 
-def test_topk_permutation_invariant_on_tie_free_inputs():
+def test_topk_permutation_invariant_on_tie_free_inputs(O):
     rng = np.random.default_rng(4)
     n, k = 500, 37
     s = rng.permutation(n).astype(np.float64) - 250.0     # distinct values
@@ -146,7 +153,7 @@ def _sdpa_gqa(q, k, v, scale=None):
     return o.permute(1, 0, 2).numpy()
 
 
-def test_attention_matches_library_routine():
+def test_attention_matches_library_routine(O):
     rng = np.random.default_rng(5)
     for lc, hq, hkv, m, hd in [(3, 8, 2, 40, 128), (1, 4, 4, 1, 16), (2, 6, 3, 129, 32)]:
         q = rng.standard_normal((lc, hq, hd))
@@ -155,7 +162,7 @@ def test_attention_matches_library_routine():
         np.testing.assert_allclose(O.sparse_attention(q, k, v), _sdpa_gqa(q, k, v), rtol=1e-12, atol=1e-12)
 
 
-def test_attention_zero_query_gives_mean_of_selected_values():
+def test_attention_zero_query_gives_mean_of_selected_values(O):
     rng = np.random.default_rng(6)
     k = rng.standard_normal((9, 2, 128))
     v = rng.standard_normal((9, 2, 128))
@@ -164,7 +171,7 @@ def test_attention_zero_query_gives_mean_of_selected_values():
         np.testing.assert_allclose(out[:, h, :], np.broadcast_to(v[:, h // 2, :].mean(0), (2, 128)), atol=1e-14)
 
 
-def test_attention_constant_values_and_single_row():
+def test_attention_constant_values_and_single_row(O):
     rng = np.random.default_rng(7)
     q = rng.standard_normal((2, 4, 128))
     k = rng.standard_normal((11, 1, 128))
@@ -174,7 +181,7 @@ def test_attention_constant_values_and_single_row():
     np.testing.assert_allclose(O.sparse_attention(q, k[:1], v1), np.broadcast_to(v1[0, 0], (2, 4, 128)), atol=1e-14)
 
 
-def test_attention_two_rows_closed_form_pins_scale():
+def test_attention_two_rows_closed_form_pins_scale(O):
     """Two selected rows: O = sigmoid(d) V0 + (1 - sigmoid(d)) V1 with d = (q.K0 - q.K1)/sqrt(128)."""
     rng = np.random.default_rng(8)
     q = rng.standard_normal((1, 1, 128))
@@ -185,7 +192,7 @@ def test_attention_two_rows_closed_form_pins_scale():
     np.testing.assert_allclose(O.sparse_attention(q, k, v)[0, 0], a * v[0, 0] + (1 - a) * v[1, 0], atol=1e-13)
 
 
-def test_attention_gqa_head_map_is_contiguous_groups():
+def test_attention_gqa_head_map_is_contiguous_groups(O):
     rng = np.random.default_rng(9)
     hq, hkv = 32, 8
     k = rng.standard_normal((5, hkv, 128))
@@ -197,7 +204,7 @@ def test_attention_gqa_head_map_is_contiguous_groups():
         np.testing.assert_allclose(out[:, h, :], math.floor(h * hkv / hq), atol=1e-12)
 
 
-def test_attention_dominant_logit_returns_that_row():
+def test_attention_dominant_logit_returns_that_row(O):
     rng = np.random.default_rng(10)
     k = rng.standard_normal((6, 1, 128))
     q = np.zeros((1, 1, 128))
@@ -207,7 +214,7 @@ def test_attention_dominant_logit_returns_that_row():
     np.testing.assert_allclose(O.sparse_attention(q, k, v)[0, 0], v[3, 0], atol=1e-12)
 
 
-def test_attention_is_a_function_of_the_selected_set():
+def test_attention_is_a_function_of_the_selected_set(O):
     rng = np.random.default_rng(11)
     q = rng.standard_normal((2, 4, 128))
     k = rng.standard_normal((17, 2, 128))
@@ -234,7 +241,7 @@ def test_step_every_layer_uses_the_same_selection():
         np.testing.assert_allclose(res["out"][layer], _sdpa_gqa(q[layer:layer + 1], kf, vf)[0], atol=1e-12)
 
 
-def test_prefill_row_equals_decode_of_the_truncated_sequence():
+def test_prefill_row_equals_decode_of_the_truncated_sequence(O):
     wp = cs.custom(mode="prefill", seq_lens=(64,), topk=16, n_layers=2, hq=4, hkv=1, seed=14)
     for t in [0, 5, 15, 16, 40, 63]:
         res = oracle_row(wp, t)
@@ -243,7 +250,7 @@ def test_prefill_row_equals_decode_of_the_truncated_sequence():
         assert res["sel"].tolist() == _brute_force_selection(s.tolist(), 16)
 
 
-def test_prefill_needles_against_last_row():
+def test_prefill_needles_against_last_row(O):
     w = cs.config(4)
     pos = w.needle_positions_of_row(w.n_rows - 1)
     assert len(pos) == 16
