@@ -31,9 +31,12 @@ constexpr int kSelectSpan = 8192;
 constexpr int kAttnTile = 64;
 // Upper bound on the splits of the selected rows of one (row, KV head, query block).
 constexpr int kMaxAttnSplits = 16;
-// Attention workgroups the split count aims for (2 per CU on 256 CUs).
+// Attention: (row, KV head, query block) blocks at or above this count run 4-wave workgroups,
+// two per CU, with no key split; below it, 8-wave workgroups (one per CU) and the keys are split
+// until about CLSA_ATTN_TARGET_WGS workgroups exist.
+constexpr int kAttnManyBlocks = 512;
 #ifndef CLSA_ATTN_TARGET_WGS
-#define CLSA_ATTN_TARGET_WGS 512
+#define CLSA_ATTN_TARGET_WGS 256
 #endif
 // fp32 words of one attention split partial per (row, KV head, query block): 4 waves x 64 lanes
 // x (32 accumulators + m + l).
@@ -59,6 +62,7 @@ struct AttnPlan {
   int group = 0;           // hq / hkv query heads per KV head
   int qrows = 0;           // query rows per (row, KV head) = n_layers_call * group
   int qblocks = 0;         // blocks of 64 query rows
+  int teams = 2;           // four-wave teams per workgroup (1 or 2)
   int splits = 1;          // the selected rows are split over this many workgroups
   int keys_per_split = 0;  // multiple of kAttnTile
   size_t part_bytes = 0;   // fp32 partials [splits, R, hkv, qblocks, kAttnPartFloats] when splits > 1

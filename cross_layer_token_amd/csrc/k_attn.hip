@@ -20,9 +20,9 @@ namespace clsa {
 
 namespace {
 
-constexpr int kAttnThreads = 256;
+constexpr int kAttnWaveThreads = 256;  // threads of one team (four waves)
 constexpr int kAttnPartWave = 34 * 64;             // floats per wave: acc 32 x 64 lanes, m, l
-constexpr int kAttnPartWG = 4 * kAttnPartWave;     // floats per workgroup partial
+constexpr int kAttnPartWG = 4 * kAttnPartWave;     // floats per workgroup partial (team 0's four waves)
 static_assert(kAttnPartWG == kAttnPartFloats, "partial record layout");
 constexpr int kKsStride = CLSA_HEAD_DIM + 8;  // bf16 elements per K row in LDS (16-byte pad)
 constexpr int kVtStride = kAttnTile + 4;      // bf16 elements per transposed V row in LDS
@@ -65,22 +65,34 @@ __device__ __forceinline__ uint2 lds_read_tr(const uint16_t* p) {
   return __builtin_bit_cast(uint2, v);
 }
 
-// One stage = kAttnStageTiles tiles of 64 keys in LDS (2 x 32 KB); the next stage's rows are in
-// flight into registers meanwhile (64 KB per workgroup).  Two workgroups share a CU.
-constexpr int kAttnStageTiles = 2;
+// One stage = 2 tiles of 64 keys in LDS (2 x 32 KB).  A workgroup is TEAMS teams of four waves
+// that all serve the same 64 query rows:
+//  * TEAMS = 2 (one 8-wave workgroup per CU): team t computes tile t of every stage, so each
+//    wave does one tile per stage; at the end the two teams merge their (m, l, acc) through LDS.
+//    Used when there are few (row, KV head) blocks and the keys are split across workgroups.
+//  * TEAMS = 1 (two 4-wave workgroups per CU): every wave computes both tiles.  Used when there
+//    are many blocks, so that two rows' gathers are in flight per CU.
+// The next stage's rows are in flight into registers while the current one is computed.
+constexpr int kAttnTiles = 2;
+constexpr int kAttnWavesPerTeam = 4;
 // log2 of the growth of the running max that is absorbed without rescaling (P <= 2^this).
 constexpr float kRescaleLog2 = 8.f;
 // Split partials fetched per round trip by the combining workgroup.
 constexpr int kCombineBatch = 4;
 
-template <bool FROM_CACHE>
-__global__ __launch_bounds__(kAttnThreads, 2) void k_sparse_attn(AttnArgs a) {
-  constexpr int NT = kAttnStageTiles;
-  constexpr int STAGE = NT * kAttnTile;
-  __shared__ __attribute__((aligned(16))) uint16_t ks[NT][kAttnTile * CLSA_HEAD_DIM];
-  __shared__ __attribute__((aligned(16))) uint16_t vs[NT][kAttnTile * CLSA_HEAD_DIM];
+template <bool FROM_CACHE, int TEAMS>
+__global__ __launch_bounds__(kAttnWaveThreads * TEAMS, 2 / TEAMS) void k_sparse_attn(AttnArgs a) {
+  constexpr int STAGE = kAttnTiles * kAttnTile;
+  constexpr int TILE_ELEMS = kAttnTile * CLSA_HEAD_DIM;
+  constexpr int TPT = kAttnTiles / TEAMS;          // tiles each team computes per stage
+  constexpr int LPT = 4 * TPT;                     // K (and V) pieces each thread loads per stage
+  static_assert(TEAMS == 1 || TEAMS == 2, "one or two teams");
+  // tiles: K of tile t at t * TILE_ELEMS, V of tile t at (kAttnTiles + t) * TILE_ELEMS; the same
+  // memory holds the team exchange at the end
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kAttnTiles * TILE_ELEMS];
   __shared__ int flag[1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int team = wave / kAttnWavesPerTeam, tw = wave % kAttnWavesPerTeam;
   const int l16 = lane & 15, grp = lane >> 4;
   int bid = blockIdx.x;
   const int split = bid % a.splits;
@@ -94,8 +106,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_sparse_attn(AttnArgs a) {
   const int kend = kend_raw < cnt ? kend_raw : cnt;
 
   // this lane's query column: query row qr -> (layer, head) of the GQA group of KV head g
-  const int qr = qb * 64 + wave * 16 + l16;
-  const bool wave_active = qb * 64 + wave * 16 < a.qrows;
+  const int qr = qb * 64 + tw * 16 + l16;
+  const bool wave_active = qb * 64 + tw * 16 < a.qrows;
   const bool q_valid = qr < a.qrows;
   const int layer = q_valid ? qr / a.group : 0;
   const int head = g * a.group + (q_valid ? qr % a.group : 0);
@@ -117,26 +129,26 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_sparse_attn(AttnArgs a) {
   const int seq = row_seq(a.rw, r);
   const int64_t tok_base = FROM_CACHE ? (int64_t)a.rw.cu[seq] : 0;
   const int32_t* irow = a.idx + (int64_t)r * a.k;
-  // loader mapping: thread -> (4 consecutive keys, one 16-byte chunk of head_dim)
-  const int ld_chunk = threadIdx.x & 15;  // 8 head_dim elements
-  const int ld_key4 = threadIdx.x >> 4;   // keys 4*ld_key4 .. +3
-
+  // loader mapping: thread -> one 16-byte chunk of head_dim of keys 4 (ld_key4 % 16) + i (i < 4)
+  // of the tiles ld_key4 / 16 + TEAMS * t (t < TPT)
+  const int ld_chunk = threadIdx.x & 15;
+  const int ld_key4 = threadIdx.x >> 4;  // 0 .. 16 TEAMS - 1
+  auto piece_key = [&](int p) {           // stage-relative key of load piece p (< LPT)
+    return ((ld_key4 >> 4) + TEAMS * (p >> 2)) * kAttnTile + (ld_key4 & 15) * 4 + (p & 3);
+  };
   // the next stage's K and V pieces of this thread, in flight while the current stage is computed
-  uint4 rk[NT][4], rv[NT][4];
-  // token ids of this thread's keys in the stage starting at kt (cache source only)
+  uint4 rk[LPT], rv[LPT];
   // Keys past the end of this split are clamped to its last key: the load stays inside the
   // selection (a finite row that is part of this attention anyway) and the key is masked out
   // of the softmax, so no load needs a branch.
   const int klast = kend - 1;
-  auto load_ids = [&](int kt, int (&ids)[NT][4]) {
+  auto load_ids = [&](int kt, int (&ids)[LPT]) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = kt + t * kAttnTile + ld_key4 * 4 + i;
-        ids[t][i] = key < klast ? key : klast;
-        if (FROM_CACHE) ids[t][i] = irow[ids[t][i]];
-      }
+    for (int i = 0; i < LPT; ++i) {
+      const int key = kt + piece_key(i);
+      ids[i] = key < klast ? key : klast;
+      if (FROM_CACHE) ids[i] = irow[ids[i]];
+    }
   };
   // 64-bit base of this (row, KV head) once; per-row offsets then fit 32 bits
   const int row_elems = FROM_CACHE ? a.hkv * CLSA_HEAD_DIM : CLSA_HEAD_DIM;
@@ -144,28 +156,29 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_sparse_attn(AttnArgs a) {
                                       : (((int64_t)r * a.hkv + g) * a.k) * CLSA_HEAD_DIM;
   const uint16_t* kbase = a.ksrc + base_off + ld_chunk * 8;
   const uint16_t* vbase = a.vsrc + base_off + ld_chunk * 8;
-  auto load_stage = [&](const int (&ids)[NT][4]) {
+  auto load_stage = [&](const int (&ids)[LPT]) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t off = (uint32_t)ids[t][i] * (uint32_t)row_elems;
-        rk[t][i] = load16(kbase + off);
-        rv[t][i] = load16(vbase + off);
-      }
+    for (int i = 0; i < LPT; ++i) {
+      const uint32_t off = (uint32_t)ids[i] * (uint32_t)row_elems;
+      rk[i] = load16(kbase + off);
+      rv[i] = load16(vbase + off);
+    }
   };
   // Per-lane byte offsets into a tile (swizzled layout), fixed for the whole kernel; the parts that
   // depend on the loop variables are compile-time immediates.
-  //   row stores: rows 4 ld_key4 + i, chunk ld_chunk
+  //   row stores: piece p -> its tile and row, chunk ld_chunk
   //   K fragment: row mt*16 + l16, chunk 4kk + grp  -> slot (grp ^ l16) ^ 4kk
   //   V^T fragment (transposed read): row 32kk + 4grp + l16/4 (+16), head_dim 16ht + 4(l16 % 4)
   //     -> slot (2ht + (l16/2 % 2)) ^ (4grp + l16/4) = z ^ 2ht, byte 8 (l16 % 2) inside the chunk
-  int soff[4];
+  char* const lds_bytes = reinterpret_cast<char*>(lds);
+  int soff[LPT];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = ld_key4 * 4 + i;
-    soff[i] = row * 256 + ((ld_chunk ^ (row & 15)) << 4);
+  for (int i = 0; i < LPT; ++i) {
+    const int key = piece_key(i);
+    const int row = key & (kAttnTile - 1);
+    soff[i] = (key / kAttnTile) * TILE_ELEMS * 2 + row * 256 + ((ld_chunk ^ (row & 15)) << 4);
   }
+  // fragment offsets inside tile 0; tile t adds t * TILE_ELEMS * 2 bytes
   int koff[4];
   const int gx = grp ^ l16;
 #pragma unroll
@@ -175,52 +188,45 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_sparse_attn(AttnArgs a) {
     const int y = 4 * grp + (l16 >> 2);
     const int z = ((l16 >> 1) & 1) ^ y;
 #pragma unroll
-    for (int ht = 0; ht < 8; ++ht) voff[ht] = y * 256 + ((z ^ (2 * ht)) << 4) + 8 * (l16 & 1);
+    for (int ht = 0; ht < 8; ++ht) voff[ht] = kAttnTiles * TILE_ELEMS * 2 + y * 256 + ((z ^ (2 * ht)) << 4) + 8 * (l16 & 1);
   }
   auto store_stage = [&]() {
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(ks[t]) + soff[i]) = rk[t][i];
-        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(vs[t]) + soff[i]) = rv[t][i];
-      }
+    for (int i = 0; i < LPT; ++i) {
+      *reinterpret_cast<uint4*>(lds_bytes + soff[i]) = rk[i];
+      *reinterpret_cast<uint4*>(lds_bytes + kAttnTiles * TILE_ELEMS * 2 + soff[i]) = rv[i];
+    }
   };
   const float scale = a.scale_log2;
-  // One stage of STAGE keys (both LDS tiles): S^T = K Q^T, online softmax in the exp2 domain,
-  // O^T += V^T P^T.  The running max m_run is only raised when some score of the wave exceeds it
-  // by more than 2^kRescaleLog2; until then P = 2^(s - m_run) <= 2^kRescaleLog2 is used as is.
-  // Numerator and denominator share the same m_run, so the result does not depend on when it is
-  // raised, and the common case needs neither a cross-lane reduction nor a rescale of acc.
-  auto compute_stage = [&](int kt) {
-    if (!wave_active) return;
-    const int nvalid = kend - kt < STAGE ? kend - kt : STAGE;
-    floatx4_t s[NT * 4];
+  // One tile of the stage: S^T = K Q^T, online softmax in the exp2 domain, O^T += V^T P^T.
+  // The running max m_run is only raised when some score of the wave exceeds it by more than
+  // 2^kRescaleLog2; until then P = 2^(s - m_run) <= 2^kRescaleLog2 is used as is.  Numerator and
+  // denominator share the same m_run, so the result does not depend on when it is raised, and the
+  // common case needs neither a cross-lane reduction nor a rescale of acc.
+  auto compute_tile = [&](int tile, int nvalid) {
+    const char* tb = lds_bytes + tile * TILE_ELEMS * 2;  // this tile's K; its V sits at voff + tb
+    floatx4_t s[4];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const char* kb = reinterpret_cast<const char*>(ks[t]);
+    for (int mt = 0; mt < 4; ++mt) {
+      floatx4_t c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        floatx4_t c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const uint4 av = *reinterpret_cast<const uint4*>(kb + koff[kk] + mt * 4096);
-          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8_t>(av), qf[kk], c, 0, 0, 0);
-        }
-        s[t * 4 + mt] = c;
+      for (int kk = 0; kk < 4; ++kk) {
+        const uint4 av = *reinterpret_cast<const uint4*>(tb + koff[kk] + mt * 4096);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8_t>(av), qf[kk], c, 0, 0, 0);
       }
+      s[mt] = c;
     }
-    // s[u][j]: raw q.k of key 16u + 4grp + j of the stage, query column l16
-    if (nvalid < STAGE) {
+    // s[mt][j]: raw q.k of key 16mt + 4grp + j of the tile, query column l16
+    if (nvalid < kAttnTile) {
 #pragma unroll
-      for (int u = 0; u < NT * 4; ++u)
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          if (u * 16 + grp * 4 + j >= nvalid) s[u][j] = -INFINITY;
+          if (mt * 16 + grp * 4 + j >= nvalid) s[mt][j] = -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < NT * 4; ++u) mx = fmaxf(fmaxf(mx, fmaxf(s[u][0], s[u][1])), fmaxf(s[u][2], s[u][3]));
+    for (int mt = 0; mt < 4; ++mt) mx = fmaxf(fmaxf(mx, fmaxf(s[mt][0], s[mt][1])), fmaxf(s[mt][2], s[mt][3]));
     if (__any(mx * scale > m_run + kRescaleLog2)) {
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
@@ -233,10 +239,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_sparse_attn(AttnArgs a) {
     }
     // P^T operand of k-step kk (keys 32kk .. 32kk + 31): slots 0..3 <- keys 32kk + 4grp + j,
     // slots 4..7 <- keys 32kk + 16 + 4grp + j
-    bf16x8_t pb[NT * 2];
+    bf16x8_t pb[2];
     float psum = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < NT * 2; ++kk) {
+    for (int kk = 0; kk < 2; ++kk) {
       uint32_t w[4];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -255,8 +261,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_sparse_attn(AttnArgs a) {
 #pragma unroll
     for (int ht = 0; ht < 8; ++ht) {
 #pragma unroll
-      for (int kk = 0; kk < NT * 2; ++kk) {
-        const char* vb = reinterpret_cast<const char*>(vs[kk >> 1]) + voff[ht] + (kk & 1) * 8192;
+      for (int kk = 0; kk < 2; ++kk) {
+        const char* vb = tb + voff[ht] + kk * 8192;
         const uint2 v0 = lds_read_tr(reinterpret_cast<const uint16_t*>(vb));
         const uint2 v1 = lds_read_tr(reinterpret_cast<const uint16_t*>(vb + 4096));
         acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8_t>(make_uint4(v0.x, v0.y, v1.x, v1.y)),
@@ -271,26 +277,24 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_sparse_attn(AttnArgs a) {
   // nothing is computed) token 0 of the row is read.  Only keys below the count reach the
   // softmax, so the replaced rows never contribute.
   {
-    int ids0[NT][4];
+    int ids0[LPT];
     const int kfirst = kbeg < a.k - 1 ? kbeg : a.k - 1;
     const int id_first = FROM_CACHE ? irow[kfirst] : 0;
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        int key = kbeg + t * kAttnTile + ld_key4 * 4 + i;
-        key = key < a.k - 1 ? key : a.k - 1;
-        if (FROM_CACHE) {
-          int id = irow[key];
-          id = id >= 0 ? id : id_first;
-          key = id >= 0 ? id : 0;
-        }
-        ids0[t][i] = key;
+    for (int i = 0; i < LPT; ++i) {
+      int key = kbeg + piece_key(i);
+      key = key < a.k - 1 ? key : a.k - 1;
+      if (FROM_CACHE) {
+        int id = irow[key];
+        id = id >= 0 ? id : id_first;
+        key = id >= 0 ? id : 0;
       }
+      ids0[i] = key;
+    }
     load_stage(ids0);
   }
   // the next stage's rows are requested before this stage is computed
-  int ids_next[NT][4];
+  int ids_next[LPT];
   if (kbeg < kend) load_ids(kbeg + STAGE, ids_next);
   // inside the loop kend > kbeg, so every clamped key lies in [kbeg, kend); after the last
   // stage the request for the "next" one re-reads the split's last row and is not used
@@ -299,27 +303,60 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_sparse_attn(AttnArgs a) {
     __syncthreads();
     load_stage(ids_next);
     load_ids(kt + 2 * STAGE, ids_next);
-    compute_stage(kt);
+    if (wave_active) {
+#pragma unroll
+      for (int t = 0; t < TPT; ++t) {
+        const int tile = team + TEAMS * t;
+        const int nvalid = kend - (kt + tile * kAttnTile);  // keys of this tile
+        if (nvalid > 0) compute_tile(tile, nvalid < kAttnTile ? nvalid : kAttnTile);
+      }
+    }
     __syncthreads();
   }
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
-  // acc[ht][j]: head_dim ht*16 + grp*4 + j of this lane's query
+  // Merge team 1 into team 0 through LDS (the tiles are free after the loop's last barrier):
+  // per wave [acc: 8 ht x 4 j x 64 lanes][m: 64][l: 64], fp32.
+  float* xch = reinterpret_cast<float*>(lds) + tw * kAttnPartWave;
+  static_assert(kAttnWavesPerTeam * kAttnPartWave * 4 <= (int)sizeof(lds), "team exchange fits the tiles");
+  if (TEAMS == 2 && team == 1 && wave_active) {
+#pragma unroll
+    for (int ht = 0; ht < 8; ++ht)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xch[(ht * 4 + j) * 64 + lane] = acc[ht][j];
+    xch[32 * 64 + lane] = m_run;
+    xch[33 * 64 + lane] = l_run;
+  }
+  if (TEAMS == 2) __syncthreads();
+  if (TEAMS == 2 && team == 0 && wave_active) {
+    const float m1 = xch[32 * 64 + lane], l1 = xch[33 * 64 + lane];
+    const float M = fmaxf(m_run, m1);
+    if (M != -INFINITY) {  // both -inf: no keys in this split
+      const float c0 = __builtin_amdgcn_exp2f(m_run - M), c1 = __builtin_amdgcn_exp2f(m1 - M);
+      l_run = l_run * c0 + l1 * c1;
+#pragma unroll
+      for (int ht = 0; ht < 8; ++ht)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[ht][j] = acc[ht][j] * c0 + xch[(ht * 4 + j) * 64 + lane] * c1;
+      m_run = M;
+    }
+  }
+  // acc[ht][j]: head_dim ht*16 + grp*4 + j of this lane's query (team 0 holds the workgroup's result)
   uint16_t* op = a.out + (int64_t)r * a.o_stride + ((int64_t)layer * a.hq + head) * CLSA_HEAD_DIM;
   if (a.splits == 1) {
-    if (!q_valid) return;
+    if (team != 0 || !q_valid) return;
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
 #pragma unroll
     for (int ht = 0; ht < 8; ++ht) store_out4(op + ht * 16 + grp * 4, acc[ht], inv);
     return;
   }
   // Split partial of this workgroup, in the lanes' own layout (each store instruction of a wave
-  // covers 256 contiguous bytes): per wave [acc: 8 ht x 4 j x 64 lanes][m: 64][l: 64].  The last
-  // split of this (row, KV head, query block) to arrive recombines them.
+  // covers 256 contiguous bytes).  The last split of this (row, KV head, query block) to arrive
+  // recombines them.
   const int64_t wg_rec = (((int64_t)r * a.hkv + g) * a.qblocks + qb) * kAttnPartWG;
   const int64_t split_stride = (int64_t)a.rw.n_rows * a.hkv * a.qblocks * kAttnPartWG;
-  float* pw = a.part + wg_rec + wave * kAttnPartWave;
-  {
+  float* pw = a.part + wg_rec + tw * kAttnPartWave;
+  if (team == 0) {
     float* pp = pw + split * split_stride;
 #pragma unroll
     for (int ht = 0; ht < 8; ++ht)
@@ -330,7 +367,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_sparse_attn(AttnArgs a) {
   }
   uint32_t* ticket = a.tickets + ((int64_t)r * a.hkv + g) * a.qblocks + qb;
   if (!arrive_last(ticket, (uint32_t)a.splits, flag)) return;
-  if (!q_valid) return;
+  if (team != 0 || !q_valid) return;
   // Recombine the splits in split order, so that whichever workgroup arrives last computes
   // exactly the same result: a running (M, den, tot) absorbs split s as
   //   M' = max(M, m_s),  tot' = 2^(M - M') tot + 2^(m_s - M') acc_s,  den' likewise with l_s.
@@ -448,10 +485,18 @@ int launch_attn(const RowsDev& rows, int k, int hq, int hkv, int n_layers_call, 
   if (plan.splits > 1 && !tickets_clear)
     hipLaunchKernelGGL(k_clear_u32, dim3((plan.tickets + 255) / 256), dim3(256), 0, s, tickets, plan.tickets);
   const dim3 grid((unsigned)(plan.splits * plan.qblocks * hkv), (unsigned)rows.n_rows);
-  if (from_cache)
-    hipLaunchKernelGGL(k_sparse_attn<true>, grid, dim3(kAttnThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL(k_sparse_attn<false>, grid, dim3(kAttnThreads), 0, s, a);
+  const dim3 block((unsigned)(kAttnWaveThreads * plan.teams));
+  if (plan.teams == 2) {
+    if (from_cache)
+      hipLaunchKernelGGL((k_sparse_attn<true, 2>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((k_sparse_attn<false, 2>), grid, block, 0, s, a);
+  } else {
+    if (from_cache)
+      hipLaunchKernelGGL((k_sparse_attn<true, 1>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((k_sparse_attn<false, 1>), grid, block, 0, s, a);
+  }
   return (int)hipGetLastError();
 }
 

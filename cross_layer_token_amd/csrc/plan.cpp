@@ -117,8 +117,9 @@ AttnPlan plan_attn(const clsa_dims* d, int n_rows, int n_layers_call, int split_
   // the split count depends on split_rows only, so every chunk of a call splits alike
   const int64_t base = (int64_t)(split_rows > 0 ? split_rows : n_rows) * d->hkv * p.qblocks;
   const int tiles = (d->topk + kAttnTile - 1) / kAttnTile;
+  p.teams = base >= kAttnManyBlocks ? 1 : 2;
   int splits = 1;
-  if (base < CLSA_ATTN_TARGET_WGS) splits = (int)((CLSA_ATTN_TARGET_WGS + base - 1) / base);
+  if (p.teams == 2 && base < CLSA_ATTN_TARGET_WGS) splits = (int)((CLSA_ATTN_TARGET_WGS + base - 1) / base);
   if (splits > kMaxAttnSplits) splits = kMaxAttnSplits;
   if (splits > tiles) splits = tiles;
   if (splits < 1) splits = 1;
