@@ -134,6 +134,31 @@ def test_topk_permutation_invariant_on_tie_free_inputs(O):
     assert {int(perm[j]) for j in moved} == base
 
 
+def test_topk_permutation_on_tie_heavy_workload_scores(O):
+    """Ties at the threshold are certain on the workload inputs, so lower-index-first is not
+    permutation invariant; what must hold is that the tokens strictly above the k-th score map
+    through the permutation and that the multiset of selected scores is unchanged."""
+    w = cs.config(5)
+    n = w.row_len(0)
+    s = O.index_scores(w.q_idx_f64([0])[0], w.k_idx_f64(np.arange(n)))
+    k = w.topk
+    sel = O.topk_select(s, k)
+    T = np.min(s[sel])
+    assert np.sum(s == T) > np.sum(s[sel] == T)            # the threshold value is really tied
+    perm = np.random.default_rng(6).permutation(n)          # new position i holds old token perm[i]
+    sel_p = O.topk_select(s[perm], k)
+    assert set(perm[sel_p][s[perm][sel_p] > T].tolist()) == set(sel[s[sel] > T].tolist())
+    assert np.array_equal(np.sort(s[perm][sel_p]), np.sort(s[sel]))
+
+
+def test_topk_two_level_ties(O):
+    # ties above the threshold and at it: the three 5s are all taken, then the two lowest-index 2s
+    s = np.array([2.0, 5.0, 2.0, 1.0, 5.0, 2.0, 5.0, 2.0, 0.0])
+    assert O.topk_select(s, 5).tolist() == [0, 1, 2, 4, 6]
+    assert O.topk_select(s, 3).tolist() == [1, 4, 6]
+    assert O.topk_select(s, 8).tolist() == [0, 1, 2, 3, 4, 5, 6, 7]
+
+
 def test_topk_selects_planted_needles():
     w = cs.config(1)
     res = oracle_row(w, 0)
