@@ -129,6 +129,10 @@ __global__ __launch_bounds__(kAttnWaveThreads * TEAMS, 2 / TEAMS) void k_sparse_
   const int seq = row_seq(a.rw, r);
   const int64_t tok_base = FROM_CACHE ? (int64_t)a.rw.cu[seq] : 0;
   const int32_t* irow = a.idx + (int64_t)r * a.k;
+  // token ids are clamped into the row's visible tokens, so that no index can send a load
+  // outside the cache (valid selections are unchanged by it)
+  const int tok_last = FROM_CACHE ? max(row_len(a.rw, r) - 1, 0) : 0;
+  auto tok = [&](int id) { return id < 0 ? 0 : (id > tok_last ? tok_last : id); };
   // loader mapping: thread -> one 16-byte chunk of head_dim of keys 4 (ld_key4 % 16) + i (i < 4)
   // of the tiles ld_key4 / 16 + TEAMS * t (t < TPT)
   const int ld_chunk = threadIdx.x & 15;
@@ -147,7 +151,7 @@ __global__ __launch_bounds__(kAttnWaveThreads * TEAMS, 2 / TEAMS) void k_sparse_
     for (int i = 0; i < LPT; ++i) {
       const int key = kt + piece_key(i);
       ids[i] = key < klast ? key : klast;
-      if (FROM_CACHE) ids[i] = irow[ids[i]];
+      if (FROM_CACHE) ids[i] = tok(irow[ids[i]]);
     }
   };
   // 64-bit base of this (row, KV head) once; per-row offsets then fit 32 bits
@@ -287,7 +291,7 @@ __global__ __launch_bounds__(kAttnWaveThreads * TEAMS, 2 / TEAMS) void k_sparse_
       if (FROM_CACHE) {
         int id = irow[key];
         id = id >= 0 ? id : id_first;
-        key = id >= 0 ? id : 0;
+        key = tok(id);
       }
       ids0[i] = key;
     }
@@ -432,6 +436,7 @@ __global__ __launch_bounds__(256) void k_gather_kv(RowsDev rw, int k, int hkv, c
   const int r = blockIdx.y;
   const int cnt = count[r];
   const int64_t base = rw.cu[row_seq(rw, r)];
+  const int tok_last = max(row_len(rw, r) - 1, 0);
   const int per_tok = hkv * 16;  // 16-byte chunks per token
   const int total = kGatherTok * per_tok;
   for (int c = threadIdx.x; c < total; c += blockDim.x) {
@@ -443,7 +448,9 @@ __global__ __launch_bounds__(256) void k_gather_kv(RowsDev rw, int k, int hkv, c
     const int64_t dst = (((int64_t)r * hkv + g) * k + i) * CLSA_HEAD_DIM + ch * 8;
     uint4 kv = make_uint4(0u, 0u, 0u, 0u), vv = make_uint4(0u, 0u, 0u, 0u);
     if (i < cnt) {
-      const int64_t src = ((base + idx[(int64_t)r * k + i]) * hkv + g) * CLSA_HEAD_DIM + ch * 8;
+      int id = idx[(int64_t)r * k + i];
+      id = id < 0 ? 0 : (id > tok_last ? tok_last : id);  // stays inside the row's tokens
+      const int64_t src = ((base + id) * hkv + g) * CLSA_HEAD_DIM + ch * 8;
       kv = *reinterpret_cast<const uint4*>(kc + src);
       vv = *reinterpret_cast<const uint4*>(vc + src);
     }
