@@ -151,7 +151,7 @@ __global__ __launch_bounds__(kAttnWaveThreads * TEAMS, 2 / TEAMS) void k_sparse_
     for (int i = 0; i < LPT; ++i) {
       const int key = kt + piece_key(i);
       ids[i] = key < klast ? key : klast;
-      if (FROM_CACHE) ids[i] = tok(irow[ids[i]]);
+      if (FROM_CACHE) ids[i] = irow[ids[i]];  // clamped when used, so the load is not waited for here
     }
   };
   // 64-bit base of this (row, KV head) once; per-row offsets then fit 32 bits
@@ -163,7 +163,7 @@ __global__ __launch_bounds__(kAttnWaveThreads * TEAMS, 2 / TEAMS) void k_sparse_
   auto load_stage = [&](const int (&ids)[LPT]) {
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
-      const uint32_t off = (uint32_t)ids[i] * (uint32_t)row_elems;
+      const uint32_t off = (uint32_t)(FROM_CACHE ? tok(ids[i]) : ids[i]) * (uint32_t)row_elems;
       rk[i] = load16(kbase + off);
       rv[i] = load16(vbase + off);
     }

@@ -156,7 +156,6 @@ __global__ __launch_bounds__(kHistThreads) void k_topk_hist_partials(SelectArgs 
 constexpr int kListLds = 8192;   // (key, index) pairs the last workgroup keeps in LDS
 constexpr int kCopyBatch = 8;    // list loads each lane keeps in flight
 constexpr int kSpecPerLane = 4;  // span entries each lane requests before the span counts arrive
-constexpr int kRankMax = 64;     // candidates one wave ranks directly
 constexpr int kMaxSpans = 2 * kSelThreads;
 static_assert(kSelectSpan == kSelThreads * 8, "each select thread classifies 8 consecutive scores");
 
@@ -167,8 +166,6 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select(SelectArgs a) {
   __shared__ int flag[1];
   __shared__ int span_pre[kMaxSpans + 1];
   __shared__ uint2 list_lds[kListLds];
-  __shared__ uint2 small[kRankMax];
-  __shared__ int small_n[1];
   const int r = blockIdx.y, sp = blockIdx.x;
   const int n = row_len(a.rw, r);
   const int m = n < a.k ? n : a.k;
@@ -302,52 +299,13 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select(SelectArgs a) {
     }
   }
   __syncthreads();
-  // Refine T below the first level.  One 8-bit radix pass fixes bits 16-23; the candidates that
-  // still share T's top 16 bits are then usually a few dozen, and one wave ranks them directly
-  // (a candidate is taken when fewer than `need` of them come before it in the order (key desc,
-  // index asc)).  Many ties at that prefix fall back to two more radix passes.
-  static_assert(kTopkBinBits == 8, "the refinement covers the remaining 24 key bits");
+  // refine T below the first level: three 8-bit passes over the remaining key bits
+  static_assert(kTopkBinBits == 8, "three refinement passes cover the remaining 24 key bits");
   int need = m - above1;
   uint32_t prefix = t1 << 24, pmask = 0xFF000000u;
   auto key_at = [&](int i) { return list[i].x; };
-  radix_pass8(hist, L, key_at, prefix, pmask, 16, need, res);
-  const int nb = (int)hist[(prefix >> 16) & 255u];  // candidates with T's top 16 bits (uniform)
-  __syncthreads();  // every thread has read nb before the fallback pass clears hist
-  uint32_t T;
-  if (nb <= kRankMax) {
-    if (threadIdx.x == 0) small_n[0] = 0;
-    __syncthreads();
-    for (int i = threadIdx.x; i < L; i += blockDim.x) {
-      const uint2 e = list[i];
-      if ((e.x & 0xFFFF0000u) == prefix) small[atomicAdd(&small_n[0], 1)] = e;
-    }
-    __syncthreads();
-    if (threadIdx.x < 64) {
-      const int lane = threadIdx.x;
-      const bool valid = lane < nb;
-      const uint2 me = valid ? small[lane] : make_uint2(0u, 0u);
-      int rank = 0;
-      for (int i = 0; i < nb; ++i) {
-        const uint2 o = small[i];
-        rank += (o.x > me.x) || (o.x == me.x && o.y < me.y);
-      }
-      const bool take = valid && rank < need;
-      uint32_t kmin = take ? me.x : 0xFFFFFFFFu;  // T = the smallest key taken
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off, 64));
-      const int ties = __popcll(__ballot(take && me.x == kmin));
-      if (lane == 0) {
-        res[0] = (int)kmin;
-        res[1] = ties;
-      }
-    }
-    __syncthreads();
-    T = (uint32_t)res[0];
-    need = res[1];
-  } else {
-    for (int shift = 8; shift >= 0; shift -= 8) radix_pass8(hist, L, key_at, prefix, pmask, shift, need, res);
-    T = prefix;
-  }
+  for (int shift = 16; shift >= 0; shift -= 8) radix_pass8(hist, L, key_at, prefix, pmask, shift, need, res);
+  const uint32_t T = prefix;
   // ordered output over contiguous per-thread ranges of the list
   const int E = (L + blockDim.x - 1) / blockDim.x;
   const int p0 = threadIdx.x * E;
