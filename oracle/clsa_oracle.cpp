@@ -100,8 +100,10 @@ uint16_t clsa_oracle_gen_uniform(uint64_t seed, uint64_t tid, uint64_t i, int lo
 uint16_t clsa_oracle_gen_normal(uint64_t seed, uint64_t tid, uint64_t i) {
   return normal_bits(tensor_key(seed, tid), i);
 }
-// The first `count` needle positions of row `row` in a sequence of n tokens.
-void clsa_oracle_gen_needles(uint64_t seed, int64_t row, int64_t n, int32_t count, int64_t* out) {
+// The first `count` needle positions of row `row` in a sequence of n tokens.  Returns 0, or 1 when
+// count > n (no such set of distinct positions exists).
+int clsa_oracle_gen_needles(uint64_t seed, int64_t row, int64_t n, int32_t count, int64_t* out) {
+  if (count < 0 || (int64_t)count > n) return 1;
   const uint64_t key = tensor_key(seed, kTidNeedle);
   std::vector<int64_t> got;
   for (uint64_t attempt = 0; (int32_t)got.size() < count; ++attempt) {
@@ -110,6 +112,7 @@ void clsa_oracle_gen_needles(uint64_t seed, int64_t row, int64_t n, int32_t coun
     if (std::find(got.begin(), got.end(), p) == got.end()) got.push_back(p);
   }
   std::copy(got.begin(), got.end(), out);
+  return 0;
 }
 
 // ---- eq. 2, first half: I[j] = q . K[j] over the n visible tokens ----------------------------
@@ -193,10 +196,10 @@ int clsa_oracle_row(const clsa_oracle_workload* w, int32_t row, int32_t* idx, in
   if (w->needles > 0) {
     std::vector<int64_t> pos((size_t)w->needles);
     if (decode) {
-      clsa_oracle_gen_needles(w->seed, seq, w->seq_lens[seq], w->needles, pos.data());
+      if (clsa_oracle_gen_needles(w->seed, seq, w->seq_lens[seq], w->needles, pos.data())) return 1;
       for (int64_t p : pos) needle[base + p] = seq;
     } else {
-      clsa_oracle_gen_needles(w->seed, 0, w->seq_lens[0], w->needles, pos.data());
+      if (clsa_oracle_gen_needles(w->seed, 0, w->seq_lens[0], w->needles, pos.data())) return 1;
       for (int64_t p : pos) needle[p] = w->seq_lens[0] - 1;
     }
   }

@@ -34,6 +34,7 @@ def _load():
     lib.clsa_oracle_gen_uniform.argtypes = [c_uint64, c_uint64, c_uint64, c_int, c_int, c_int]
     lib.clsa_oracle_gen_normal.restype = c_uint16
     lib.clsa_oracle_gen_normal.argtypes = [c_uint64, c_uint64, c_uint64]
+    lib.clsa_oracle_gen_needles.restype = c_int
     lib.clsa_oracle_gen_needles.argtypes = [c_uint64, c_int64, c_int64, c_int32, POINTER(c_int64)]
     lib.clsa_oracle_scores.argtypes = [dp, dp, c_int64, c_int32, dp]
     lib.clsa_oracle_topk.argtypes = [dp, c_int64, c_int32, ip, ip]
@@ -134,6 +135,9 @@ def gen_normal(seed: int, tid: int, i: int) -> int:
 
 
 def gen_needles(seed: int, row: int, n: int, count: int) -> list:
+    if count > n:
+        raise ValueError("more needles than tokens")
     out = np.empty(count, dtype=np.int64)
-    LIB.clsa_oracle_gen_needles(seed & 0xFFFFFFFFFFFFFFFF, row, n, count, out.ctypes.data_as(POINTER(c_int64)))
+    rc = LIB.clsa_oracle_gen_needles(seed & 0xFFFFFFFFFFFFFFFF, row, n, count, out.ctypes.data_as(POINTER(c_int64)))
+    assert rc == 0
     return out.tolist()

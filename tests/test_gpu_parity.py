@@ -290,6 +290,25 @@ def test_step_decode_vs_oracle(cfg, check, schedule):
 
 
 @pytest.mark.parametrize("schedule", [clsa.SCHEDULE_LAYER_BATCHED, clsa.SCHEDULE_PER_LAYER])
+def test_step_decode_mixed_lengths_vs_cpp_oracle(schedule):
+    """One batch mixing a single-token row, rows shorter than k, exactly k and k + 1 tokens, and a
+    row long enough that the select's last workgroup walks more than 16 span lists; every row
+    against the independent C++ oracle."""
+    from oracle import cpp as C
+    w = cs.custom(seq_lens=(1, 100, 2047, 2048, 2049, 12289, 200000), d_idx=128, topk=2048, n_layers=3, hq=8, hkv=2,
+                  needles=0, seed=77, name="mixed_lengths")
+    dw = device_workload(w)
+    idx, cnt, out = _run_step(dw, schedule)
+    dev = bf16_dev_to_f64(out)
+    for r in range(w.n_rows):
+        res = C.oracle_row(w, r)
+        assert cnt[r] == res["count"] == min(w.topk, w.row_len(r)), r
+        assert np.array_equal(idx[r], res["idx"]), f"row {r}: {np.sum(idx[r] != res['idx'])} index mismatches"
+        st = assert_outputs_close(dev[r], res["out"], f"mixed row {r}")
+        _say(f"mixed sched {schedule} row {r} (n={w.row_len(r)}): max {st[0]:.2e} mean {st[1]:.2e} rel {st[2]:.2e}")
+
+
+@pytest.mark.parametrize("schedule", [clsa.SCHEDULE_LAYER_BATCHED, clsa.SCHEDULE_PER_LAYER])
 def test_step_prefill_vs_oracle(schedule):
     w = cs.config(4)
     dw = device_workload(w)

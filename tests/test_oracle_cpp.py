@@ -63,3 +63,11 @@ def test_needles_selected_by_cpp_oracle():
     w = cs.config(1)
     sel = set(C.oracle_row(w, 0)["idx"].tolist())
     assert set(w.needle_positions_of_row(0)) <= sel
+
+
+def test_cpp_oracle_rejects_more_needles_than_tokens():
+    w = cs.custom(seq_lens=(1, 50), needles=4, seed=1)
+    with pytest.raises(AssertionError):
+        C.oracle_row(w, 0)
+    with pytest.raises(ValueError):
+        C.gen_needles(1, 0, 1, 4)
