@@ -21,7 +21,10 @@
  *    keeps it alive until the stream has passed the call.  The library allocates no device
  *    memory and keeps no pointer after returning.
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null stream).
- *  - Device pointers must be 16-byte aligned.  bf16 values are passed as uint16 bit patterns.
+ *  - Device pointers must be 16-byte aligned; the workspace 256-byte aligned.  bf16 values are
+ *    passed as uint16 bit patterns.
+ *  - Workspace: its content on entry does not matter (every call clears what it needs); two
+ *    calls that share one workspace must not overlap in time on the device.
  *  - Token indices are int32 and LOCAL to their sequence.
  *  - Query rows.  DECODE: row r is sequence r (n_rows == batch) and sees all N_r tokens of
  *    its sequence, N_r = cu_seqlens[r+1] - cu_seqlens[r].  PREFILL: the rows are the query
@@ -33,6 +36,8 @@
  *    shared by all layers and all query heads; the softmax scale is 1/sqrt(head_dim) unless
  *    dims.sm_scale > 0; query head h reads KV head floor(h * hkv / hq).
  *  - NaN or Inf scores are not supported (the selection is then unspecified).
+ *  - Token indices passed in idx must be tokens the row sees; out-of-range values are clamped
+ *    into the row (the output is then unspecified, but no access leaves the cache).
  *  - Device failures (a failed launch) return CLSA_ERR_DEVICE with the HIP error text.
  */
 #ifndef CLSA_H_
@@ -112,7 +117,8 @@ size_t clsa_workspace_bytes(const clsa_dims* dims, const clsa_rows* rows, int32_
  * for every token j the row sees (j < N_r in DECODE, j <= pos0 + r in PREFILL), accumulated
  * in fp32 from bf16 products.  Entries past the row's visible length are not written.
  *   q_idx      [R, d_idx] bf16         k_idx [T, d_idx] bf16 (token-major, packed by cu_seqlens)
- *   cu_seqlens [B+1] int32 (device)    scores [R, ld_scores] fp32, ld_scores >= max_row_len
+ *   cu_seqlens [B+1] int32 (device)    scores [R, ld_scores] fp32, ld_scores >= max_row_len and
+ *                                      a multiple of 4
  * DECODE streams k_idx once (bandwidth bound); PREFILL runs the causal Q_idx K_idx^T
  * product on the matrix cores.
  */
@@ -128,7 +134,7 @@ clsa_status clsa_index_scores(const clsa_dims* dims, const clsa_rows* rows, cons
  *   count [R]    int32  - m
  * scores as written by clsa_index_scores (only the visible entries of each row are read;
  * -0.0 and +0.0 are equal).  The result is unique and deterministic.
- * Workspace: >= clsa_workspace_bytes(dims, rows, CLSA_SCHEDULE_LAYER_BATCHED, 0), any content.
+ * Workspace: >= clsa_workspace_bytes(dims, rows, CLSA_SCHEDULE_LAYER_BATCHED, 0).
  */
 clsa_status clsa_topk(const clsa_dims* dims, const clsa_rows* rows, const int32_t* cu_seqlens,
                       const float* scores, int64_t ld_scores, int32_t* idx, int32_t* count,
