@@ -7,13 +7,13 @@
 // One workgroup owns (query row r, KV head g, a block of up to 64 query rows, a split of the
 // selected keys).  The query rows of a KV head are all layers x the heads of its GQA group, so
 // in the layer-batched schedule every K/V tile brought into LDS serves L * Hq / Hkv queries.
-// Per 64-key tile: S^T = K Q^T and O^T += V^T P^T on bf16 MFMA 16x16x32 with fp32 accumulate;
-// the online softmax (exp2 domain) keeps every statistic of a query in the lane that owns the
-// query's column, so rescaling needs no cross-lane traffic.  The next tile's K/V rows are loaded
-// into registers while the current tile is computed.  When the keys are split over several
-// workgroups, each writes fp32 partials (m, l, acc) with device-scope stores and the last to
-// arrive (atomic ticket) recombines them, so no separate pass is launched and no workgroup
-// needs a device-wide cache flush.
+// The selected keys stream through LDS in stages of two 64-key tiles; the next stage's K/V rows
+// are loaded into registers while the current one is computed.  Per tile: S^T = K Q^T and
+// O^T += V^T P^T on bf16 MFMA 16x16x32 with fp32 accumulate; the online softmax (exp2 domain)
+// keeps every statistic of a query in the lane that owns the query's column.  When the keys
+// are split over several workgroups, each writes fp32 partials (m, l, acc) with device-scope
+// stores and the last to arrive (atomic ticket) recombines them, so no separate pass is
+// launched and no workgroup needs a device-wide cache flush.
 #include "device_common.h"
 
 namespace clsa {
