@@ -98,7 +98,9 @@ def summarize_trace(trace_dir: str) -> str:
              f"    python bench.py --summarize-trace {trace_dir}", "",
              "The run holds warmup + timed steps of the layer-batched step (score kernel with histogram,",
              "top-k select, sparse attention), the score kernel alone (the roofline line), the",
-             "per-layer schedule (gather + one attention per layer), and the synthetic-input fill.", "",
+             "per-layer schedule (gather + one attention per layer), the per-layer routing ablation",
+             "(scores, top-k and one attention per layer), the Infinity Cache probes (torch reduce and",
+             "copy) and the synthetic-input fill.", "",
              "| kernel | calls | avg us | min us | max us | share % |", "|---|---:|---:|---:|---:|---:|"]
     for r in _csv_rows(path):
         lines.append(f"| `{_short_kernel(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
@@ -383,6 +385,28 @@ def main():
                                   "bound_ms": round(bound * 1e3, 4), "frac": round(bound / t_pl, 4)}}
         del ws2
 
+    # ---- the ablation without the shared index: route (score + top-k) once per layer ---------------
+    routing = None
+    if not args.no_per_layer:
+        lq = dw.layer_q_idx()
+        nws3 = clsa.workspace_bytes(dims, rows, clsa.SCHEDULE_PER_LAYER_ROUTING)
+        ws3 = torch.empty(nws3, dtype=torch.uint8, device="cuda")
+        idx3 = torch.empty((w.n_layers, R, k), dtype=torch.int32, device="cuda")
+        cnt3 = torch.empty((w.n_layers, R), dtype=torch.int32, device="cuda")
+
+        def run_routing(n):
+            for _ in range(n):
+                clsa.step(dims, rows, lq, dw.k_idx, dw.k_cache, dw.v_cache, dw.cu_seqlens, dw.q, out, idx3, cnt3, ws3,
+                          nws3, schedule=clsa.SCHEDULE_PER_LAYER_ROUTING, stream=stream)
+
+        n3 = max(1, args.steps // 5)
+        run_routing(max(1, args.warmup // 5))
+        _, w3 = timed(run_routing, n3)
+        t3 = w3 / n3
+        routing = {"ms_per_step": round(t3 * 1e3, 4), "tokens_per_s": round(R / t3, 1), "steps": n3,
+                   "vs_shared_routing": round(t3 / t_step, 2)}
+        del ws3, idx3, cnt3
+
     if args.profile_copy_mib > 0:
         n = args.profile_copy_mib << 20
         src = torch.ones(n, dtype=torch.uint8, device="cuda")
@@ -418,6 +442,7 @@ def main():
         "gpu_event_ms_per_step": round(t_gpu / args.steps * 1e3, 4),
         "roofline": roofline,
         "per_layer_schedule": per_layer,
+        "per_layer_routing": routing,
         "prefill": prefill,
         "cpu_baseline": cpu,
     }

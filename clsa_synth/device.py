@@ -86,6 +86,16 @@ class DeviceWorkload:
             fill_normal(self.v_cache, w.seed, gen.TID_V)
         torch.cuda.synchronize(d)
 
+    def layer_q_idx(self) -> torch.Tensor:
+        """[R, L, d_idx] per-layer indexer queries (the routing ablation), filled on first use."""
+        if getattr(self, "_layer_q_idx", None) is None:
+            w = self.w
+            t = torch.empty((w.n_rows, w.n_layers, w.d_idx), dtype=torch.int16, device=self.q_idx.device)
+            fill_uniform_int(t, w.seed, gen.TID_Q_IDX_LAYER, w.idx_lo, w.idx_hi, w.idx_den)
+            torch.cuda.synchronize(t.device)
+            self._layer_q_idx = t
+        return self._layer_q_idx
+
     # sizes of the C ABI, as plain keyword dicts
     def dims(self, sm_scale: float = 0.0) -> dict:
         w = self.w

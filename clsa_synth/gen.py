@@ -42,6 +42,7 @@ TID_K = 4
 TID_V = 5
 TID_NEEDLE = 6
 TID_LEN = 7
+TID_Q_IDX_LAYER = 8     # per-layer indexer queries of the routing ablation
 
 KIND_UNIFORM_INT = 0
 KIND_NORMAL = 1

@@ -118,6 +118,13 @@ class Workload:
                 out[hit] = gen.f32_to_bf16_bits(qv * np.float32(2.0))
         return out
 
+    def q_idx_layer_bits(self, rows, layer: int) -> np.ndarray:
+        """Layer `layer`'s own indexer query of each row (the per-layer routing ablation):
+        element (r, l, c) of a [R, L, d_idx] tensor, drawn like q_idx from its own stream."""
+        rows = np.asarray(rows, dtype=np.int64).reshape(-1)
+        flat = (rows[:, None] * self.n_layers + layer) * self.d_idx + np.arange(self.d_idx)[None, :]
+        return gen.uniform_int_bf16(self.seed, gen.TID_Q_IDX_LAYER, flat, self.idx_lo, self.idx_hi, self.idx_den)
+
     def q_bits(self, rows) -> np.ndarray:
         rows = np.asarray(rows, dtype=np.int64).reshape(-1)
         per = self.n_layers * self.hq * self.head_dim
@@ -134,6 +141,9 @@ class Workload:
     # ---- fp64 views for the oracle ---------------------------------------------------
     def q_idx_f64(self, rows) -> np.ndarray:
         return gen.bf16_bits_to_f64(self.q_idx_bits(rows))
+
+    def q_idx_layer_f64(self, rows, layer: int) -> np.ndarray:
+        return gen.bf16_bits_to_f64(self.q_idx_layer_bits(rows, layer))
 
     def k_idx_f64(self, tokens) -> np.ndarray:
         return gen.bf16_bits_to_f64(self.k_idx_bits(tokens))

@@ -4,7 +4,8 @@ The compute lives in ``libclsa.so`` (include/clsa.h); ``binding`` marshals argum
 The library is loaded on first use of an entry point (not at package import), so that
 ``python -m cross_layer_token_amd.build`` works before anything is built.
 """
-_EXPORTS = ("HEAD_DIM", "MODE_DECODE", "MODE_PREFILL", "SCHEDULE_LAYER_BATCHED", "SCHEDULE_PER_LAYER", "CLSAError",
+_EXPORTS = ("HEAD_DIM", "MODE_DECODE", "MODE_PREFILL", "SCHEDULE_LAYER_BATCHED", "SCHEDULE_PER_LAYER",
+            "SCHEDULE_PER_LAYER_ROUTING", "CLSAError",
             "gather_kv", "index_scores", "make_dims", "make_rows", "sparse_attn", "step", "topk", "workspace_bytes")
 
 __all__ = ["binding", *_EXPORTS]

@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libclsa.so")
 
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_DEVICE = 0, 1, 2, 3, 4
 MODE_DECODE, MODE_PREFILL = 0, 1
-SCHEDULE_LAYER_BATCHED, SCHEDULE_PER_LAYER = 0, 1
+SCHEDULE_LAYER_BATCHED, SCHEDULE_PER_LAYER, SCHEDULE_PER_LAYER_ROUTING = 0, 1, 2
 HEAD_DIM = 128
 
 FUNCTIONS = ["clsa_status_string", "clsa_last_error_message", "clsa_abi_version", "clsa_workspace_bytes",

@@ -93,7 +93,8 @@ int32_t clsa_abi_version(void) { return CLSA_ABI_VERSION; }
 size_t clsa_workspace_bytes(const clsa_dims* dims, const clsa_rows* rows, int32_t schedule,
                             int32_t prefill_chunk_rows) {
   if (check_common(dims, rows) != CLSA_OK) return 0;
-  if (schedule != CLSA_SCHEDULE_LAYER_BATCHED && schedule != CLSA_SCHEDULE_PER_LAYER) {
+  if (schedule != CLSA_SCHEDULE_LAYER_BATCHED && schedule != CLSA_SCHEDULE_PER_LAYER &&
+      schedule != CLSA_SCHEDULE_PER_LAYER_ROUTING) {
     set_error(CLSA_ERR_INVALID_ARGUMENT, "unknown schedule");
     return 0;
   }
@@ -117,8 +118,8 @@ clsa_status clsa_index_scores(const clsa_dims* dims, const clsa_rows* rows, cons
   const RowsDev rd = rows_dev(rows, cu_seqlens);
   int e;
   if (rows->mode == CLSA_MODE_DECODE)
-    e = launch_index_scores_decode(rd, dims->d_idx, idx_chunk_for(rows->n_rows, rows->max_row_len), q_idx, k_idx,
-                                   scores, ld_scores, nullptr, nullptr, 0, stream);
+    e = launch_index_scores_decode(rd, dims->d_idx, idx_chunk_for(rows->n_rows, rows->max_row_len), q_idx,
+                                   dims->d_idx, k_idx, scores, ld_scores, nullptr, nullptr, 0, stream);
   else
     e = launch_index_scores_prefill(rd, dims->d_idx, q_idx, k_idx, scores, ld_scores, nullptr, 0, stream);
   return device_status(e, "clsa_index_scores");
@@ -201,7 +202,8 @@ clsa_status clsa_step(const clsa_dims* dims, const clsa_rows* rows, const clsa_s
   g_last_error.clear();
   CLSA_TRY(check_common(dims, rows));
   if (a == nullptr) return set_error(CLSA_ERR_INVALID_ARGUMENT, "args is NULL");
-  if (a->schedule != CLSA_SCHEDULE_LAYER_BATCHED && a->schedule != CLSA_SCHEDULE_PER_LAYER)
+  if (a->schedule != CLSA_SCHEDULE_LAYER_BATCHED && a->schedule != CLSA_SCHEDULE_PER_LAYER &&
+      a->schedule != CLSA_SCHEDULE_PER_LAYER_ROUTING)
     return set_error(CLSA_ERR_INVALID_ARGUMENT, "unknown schedule");
   if (a->prefill_chunk_rows < 0) return set_error(CLSA_ERR_INVALID_ARGUMENT, "prefill_chunk_rows must be >= 0");
   CLSA_TRY(check_ptr(a->q_idx, "q_idx", g_err));
@@ -221,6 +223,11 @@ clsa_status clsa_step(const clsa_dims* dims, const clsa_rows* rows, const clsa_s
   if (a->scores != nullptr)
     if (clsa_status s = check_ld(a->ld_scores, rows, "ld_scores"); s != CLSA_OK) return s;
   const bool prefill = rows->mode == CLSA_MODE_PREFILL;
+  if (a->schedule == CLSA_SCHEDULE_PER_LAYER_ROUTING) {
+    if (prefill) return set_error(CLSA_ERR_UNSUPPORTED, "per-layer routing is a DECODE schedule");
+    if (a->scores != nullptr || a->k_sel != nullptr)
+      return set_error(CLSA_ERR_INVALID_ARGUMENT, "per-layer routing takes no scores, k_sel or v_sel");
+  }
   const StepPlan sp = plan_step(dims, rows, a->schedule, a->scores != nullptr, a->k_sel != nullptr,
                                 a->prefill_chunk_rows);
   if (clsa_status s = check_workspace(workspace, workspace_bytes_, sp.total); s != CLSA_OK) return s;
@@ -234,6 +241,32 @@ clsa_status clsa_step(const clsa_dims* dims, const clsa_rows* rows, const clsa_s
   uint32_t* tickets = reinterpret_cast<uint32_t*>(ws + sp.ticket_off);
   uint32_t* topk_tickets = tickets;
   uint32_t* attn_tickets = tickets + sp.topk.tickets;
+  if (a->schedule == CLSA_SCHEDULE_PER_LAYER_ROUTING) {
+    // the ablation: score, select and attend once per layer, each layer with its own query
+    const RowsDev rd = rows_dev(rows, a->cu_seqlens);
+    const TopkPlan tp = plan_topk(dims, rows);
+    char* topk_ws = ws + sp.topk_off;
+    float* scores = reinterpret_cast<float*>(ws + sp.scores_off);
+    const AttnPlan ap = plan_attn(dims, rows->n_rows, 1, rows->n_rows);
+    const int R = rows->n_rows;
+    const int ichunk = tp.multi_wg ? tp.hist_chunk : idx_chunk_for(R, rows->max_row_len);
+    for (int l = 0; l < L; ++l) {
+      uint16_t* hpart = tp.multi_wg ? reinterpret_cast<uint16_t*>(topk_ws + tp.hpart_off) : nullptr;
+      int e = launch_index_scores_decode(rd, dims->d_idx, ichunk, a->q_idx + (int64_t)l * dims->d_idx,
+                                         (int64_t)L * dims->d_idx, a->k_idx, scores, sp.ld_scores, hpart, tickets,
+                                         sp.n_tickets, stream);
+      if (e) return device_status(e, "clsa_step: index scores of a layer");
+      int32_t* idx = a->idx + (int64_t)l * R * k;
+      int32_t* count = a->count + (int64_t)l * R;
+      e = launch_topk(rd, k, tp, scores, sp.ld_scores, idx, count, topk_ws, topk_tickets, tp.multi_wg, stream);
+      if (e) return device_status(e, "clsa_step: top-k of a layer");
+      e = launch_attn(rd, k, hq, hkv, 1, scale, ap, a->q + (int64_t)l * hq * CLSA_HEAD_DIM, row_elems, nullptr,
+                      nullptr, a->k_cache, a->v_cache, idx, count, a->out + (int64_t)l * hq * CLSA_HEAD_DIM, row_elems,
+                      ws + sp.part_off, attn_tickets, true, stream);
+      if (e) return device_status(e, "clsa_step: attention of a layer");
+    }
+    return CLSA_OK;
+  }
   for (int c0 = 0; c0 < rows->n_rows; c0 += chunk) {
     clsa_rows cr = *rows;
     cr.n_rows = rows->n_rows - c0 < chunk ? rows->n_rows - c0 : chunk;
@@ -262,8 +295,8 @@ clsa_status clsa_step(const clsa_dims* dims, const clsa_rows* rows, const clsa_s
       uint16_t* hpart = tp.multi_wg ? reinterpret_cast<uint16_t*>(topk_ws + tp.hpart_off) : nullptr;
       have_hist = tp.multi_wg;
       const int chunk = tp.multi_wg ? tp.hist_chunk : idx_chunk_for(cr.n_rows, cr.max_row_len);
-      e = launch_index_scores_decode(rd, dims->d_idx, chunk, q_idx, a->k_idx, scores, ld, hpart, tickets,
-                                     sp.n_tickets, stream);
+      e = launch_index_scores_decode(rd, dims->d_idx, chunk, q_idx, dims->d_idx, a->k_idx, scores, ld, hpart,
+                                     tickets, sp.n_tickets, stream);
     }
     if (e) return device_status(e, "clsa_step: index scores");
     int32_t* idx = a->idx + (int64_t)c0 * k;

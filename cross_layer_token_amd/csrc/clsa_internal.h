@@ -119,7 +119,8 @@ struct RowsDev {
 };
 
 // `clear` (n_clear words) is zeroed by the launch before any other kernel of the call reads it.
-int launch_index_scores_decode(const RowsDev& rows, int d_idx, int chunk, const uint16_t* q_idx, const uint16_t* k_idx,
+int launch_index_scores_decode(const RowsDev& rows, int d_idx, int chunk, const uint16_t* q_idx, int64_t q_stride,
+                               const uint16_t* k_idx,
                                float* scores, int64_t ld, uint16_t* hpart, uint32_t* clear, int n_clear,
                                void* stream);
 int launch_index_scores_prefill(const RowsDev& rows, int d_idx, const uint16_t* q_idx, const uint16_t* k_idx,

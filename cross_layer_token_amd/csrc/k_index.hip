@@ -47,6 +47,7 @@ constexpr int kIdxThreads = 256;
 // select) and clear the select's per-row tickets (consumed by later kernels on the same stream).
 template <int D>
 __global__ __launch_bounds__(kIdxThreads) void k_index_scores_decode(const uint16_t* __restrict__ q_idx,
+                                                                       int64_t q_stride,
                                                                        const uint16_t* __restrict__ k_idx,
                                                                        const int32_t* __restrict__ cu,
                                                                        int max_row_len, int chunk,
@@ -75,7 +76,7 @@ __global__ __launch_bounds__(kIdxThreads) void k_index_scores_decode(const uint1
     __syncthreads();
   }
   const uint16_t* kbase = k_idx + (int64_t)cu[b] * D + sub * 8;
-  const uint4 qv = *reinterpret_cast<const uint4*>(q_idx + (size_t)b * D + sub * 8);
+  const uint4 qv = *reinterpret_cast<const uint4*>(q_idx + (int64_t)b * q_stride + sub * 8);
   float* srow = scores + (int64_t)b * ld;
   uint4 kv[NR];
   auto load = [&](int it) {
@@ -166,17 +167,17 @@ __global__ __launch_bounds__(256) void k_index_scores_prefill(const uint16_t* __
 
 }  // namespace
 
-int launch_index_scores_decode(const RowsDev& rows, int d_idx, int chunk, const uint16_t* q_idx,
+int launch_index_scores_decode(const RowsDev& rows, int d_idx, int chunk, const uint16_t* q_idx, int64_t q_stride,
                                const uint16_t* k_idx, float* scores, int64_t ld, uint16_t* hpart, uint32_t* clear,
                                int n_clear, void* stream) {
   const int chunks = (rows.max_row_len + chunk - 1) / chunk;
   const dim3 grid((unsigned)chunks, (unsigned)rows.n_rows);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (d_idx == 128)
-    hipLaunchKernelGGL(k_index_scores_decode<128>, grid, dim3(kIdxThreads), 0, s, q_idx, k_idx, rows.cu,
+    hipLaunchKernelGGL(k_index_scores_decode<128>, grid, dim3(kIdxThreads), 0, s, q_idx, q_stride, k_idx, rows.cu,
                        rows.max_row_len, chunk, scores, ld, hpart, chunks, clear, n_clear);
   else
-    hipLaunchKernelGGL(k_index_scores_decode<64>, grid, dim3(kIdxThreads), 0, s, q_idx, k_idx, rows.cu,
+    hipLaunchKernelGGL(k_index_scores_decode<64>, grid, dim3(kIdxThreads), 0, s, q_idx, q_stride, k_idx, rows.cu,
                        rows.max_row_len, chunk, scores, ld, hpart, chunks, clear, n_clear);
   return (int)hipGetLastError();
 }

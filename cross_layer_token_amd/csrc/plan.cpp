@@ -143,7 +143,9 @@ StepPlan plan_step(const clsa_dims* d, const clsa_rows* r, int schedule, bool us
   chunk.n_rows = s.chunk_rows;
   if (prefill) chunk.max_row_len = r->max_row_len;  // a chunk never sees more than the last row
   s.topk = plan_topk(d, &chunk);
-  const int lc = schedule == CLSA_SCHEDULE_PER_LAYER ? 1 : d->n_layers;
+  // one attention pass over all L layers, or one pass per layer (per-layer schedule, and the
+  // per-layer routing ablation, which also routes once per layer)
+  const int lc = schedule == CLSA_SCHEDULE_LAYER_BATCHED ? d->n_layers : 1;
   // every chunk (the shorter tail included) splits like the whole call, so results do not
   // depend on the chunk size; buffers are sized for the largest chunk
   s.attn = plan_attn(d, s.chunk_rows, lc, r->n_rows);

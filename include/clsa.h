@@ -62,7 +62,7 @@ typedef enum clsa_status {
 } clsa_status;
 
 enum { CLSA_MODE_DECODE = 0, CLSA_MODE_PREFILL = 1 };
-enum { CLSA_SCHEDULE_LAYER_BATCHED = 0, CLSA_SCHEDULE_PER_LAYER = 1 };
+enum { CLSA_SCHEDULE_LAYER_BATCHED = 0, CLSA_SCHEDULE_PER_LAYER = 1, CLSA_SCHEDULE_PER_LAYER_ROUTING = 2 };
 
 /* Limits (CLSA_ERR_UNSUPPORTED beyond them). */
 #define CLSA_HEAD_DIM 128
@@ -189,8 +189,10 @@ typedef struct clsa_step_args {
   clsa_bf16* k_sel;           /* optional compact buffers [R, hkv, k, 128] for the PER_LAYER */
   clsa_bf16* v_sel;           /*   DECODE schedule; NULL = carved from the workspace       */
   int32_t schedule;           /* CLSA_SCHEDULE_LAYER_BATCHED (all L layers in one pass over
-                                 each selected row) or CLSA_SCHEDULE_PER_LAYER (one pass per
-                                 layer, as when layer l's query waits for layer l-1)        */
+                                 each selected row), CLSA_SCHEDULE_PER_LAYER (one pass per
+                                 layer, as when layer l's query waits for layer l-1), or
+                                 CLSA_SCHEDULE_PER_LAYER_ROUTING (the ablation without the
+                                 shared index, see clsa_step)                               */
   int32_t prefill_chunk_rows; /* PREFILL: rows per chunk (0 = library default)            */
 } clsa_step_args;
 
@@ -201,6 +203,16 @@ typedef struct clsa_step_args {
  * DECODE: one launch sequence on `stream`.  PREFILL: rows processed in chunks of
  * prefill_chunk_rows.  Workspace: >= clsa_workspace_bytes(dims, rows, schedule,
  * prefill_chunk_rows).
+ */
+/*
+ * CLSA_SCHEDULE_PER_LAYER_ROUTING (DECODE only) is the ablation the method is compared with:
+ * routing is NOT shared, every layer l scores the cache with its own indexer query and selects
+ * its own set (the per-layer indexer whose cost the picx.dev summary, section Complexity
+ * Comparison, puts at eta L N instead of eta N).  The same kernels run once per layer:
+ *   q_idx [R, L, d_idx]  (layer l's indexer query of row r at q_idx + (r * L + l) * d_idx)
+ *   idx   [L, R, k], count [L, R]  (layer l's selection)
+ *   out[r, l] = attention of layer l's query over layer l's selection.
+ * scores, k_sel and v_sel must be NULL.  Workspace: clsa_workspace_bytes(..., this schedule, 0).
  */
 clsa_status clsa_step(const clsa_dims* dims, const clsa_rows* rows, const clsa_step_args* args,
                       void* workspace, size_t workspace_bytes, clsa_stream stream);

@@ -45,3 +45,24 @@ def oracle_rows(w: Workload, rows, keep_scores: bool = False) -> dict:
     if keep_scores:
         d["scores"] = scores
     return d
+
+
+def oracle_row_layer_routing(w: Workload, r: int) -> dict:
+    """fp64 oracle of query row r under per-layer routing (the ablation without the shared index):
+    layer l scores the row's visible tokens with its own indexer query, selects its own set and
+    attends with its own query.  dict(idx[L, k], count[L], out[L, Hq, hd])."""
+    from .clsa_oracle import index_scores, sparse_attention, topk_select
+    cu = w.cu_seqlens
+    base = int(cu[w.row_seq(r)])
+    tokens = base + np.arange(w.row_len(r), dtype=np.int64)
+    k_idx = w.k_idx_f64(tokens)
+    q = w.q_f64([r])[0]
+    idx, cnt, out = [], [], []
+    for l in range(w.n_layers):
+        sel = topk_select(index_scores(w.q_idx_layer_f64([r], l)[0], k_idx), w.topk)
+        kf, vf = w.kv_f64(base + sel)
+        out.append(sparse_attention(q[l:l + 1], kf, vf)[0])
+        i, c = pad_selection(sel, w.topk)
+        idx.append(i)
+        cnt.append(c)
+    return {"idx": np.stack(idx), "count": np.asarray(cnt), "out": np.stack(out)}

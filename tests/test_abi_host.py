@@ -141,6 +141,15 @@ def test_step_rejects():
     assert call(scores=FAKE, ld_scores=10) == B.ERR_INVALID_ARGUMENT
     assert call(ws=ws - 1) == B.ERR_WORKSPACE
     assert call(prefill_chunk_rows=-1) == B.ERR_INVALID_ARGUMENT
+    # the per-layer routing ablation: decode only, no caller scores or compact buffers
+    wsr = B.workspace_bytes(dims, rows, B.SCHEDULE_PER_LAYER_ROUTING)
+    assert wsr > 0
+    assert call(schedule=B.SCHEDULE_PER_LAYER_ROUTING, scores=FAKE, ld_scores=4096, ws=wsr) == B.ERR_INVALID_ARGUMENT
+    pre = B.make_rows(B.MODE_PREFILL, 100, 100, 4096, seq=0, pos0=0)
+    sa = B.StepArgs(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None, None,
+                    B.SCHEDULE_PER_LAYER_ROUTING, 0)
+    st = B.LIB.clsa_step(ctypes.byref(dims), ctypes.byref(pre), ctypes.byref(sa), FAKE, 1 << 30, None)
+    assert st == B.ERR_UNSUPPORTED and "DECODE" in B.last_error()
 
 
 def test_workspace_sizes_cover_every_call():

@@ -308,6 +308,36 @@ def test_step_decode_mixed_lengths_vs_cpp_oracle(schedule):
         _say(f"mixed sched {schedule} row {r} (n={w.row_len(r)}): max {st[0]:.2e} mean {st[1]:.2e} rel {st[2]:.2e}")
 
 
+@pytest.mark.parametrize("cfg,check", [(1, None), (2, [0, 7]), (3, [4])])
+def test_step_per_layer_routing_vs_oracle(cfg, check):
+    """The ablation without the shared index: every layer scores the cache with its own indexer
+    query, selects its own set and attends over it (same kernels, once per layer)."""
+    from oracle.workload_oracle import oracle_row_layer_routing
+    w = cs.config(cfg)
+    dw = device_workload(w)
+    lq = dw.layer_q_idx()
+    host = gen.uniform_int_bf16(w.seed, gen.TID_Q_IDX_LAYER, np.arange(lq.numel()), w.idx_lo, w.idx_hi, w.idx_den)
+    assert np.array_equal(lq.cpu().numpy().view(np.uint16).reshape(-1), host)   # device fill == host generator
+    dims, rows = dims_of(dw), rows_of(dw)
+    R, L, k = w.n_rows, w.n_layers, w.topk
+    ws, nws = workspace(dims, rows, clsa.SCHEDULE_PER_LAYER_ROUTING)
+    out = torch.zeros((R, L, w.hq, 128), dtype=torch.int16, device="cuda")
+    idx = torch.full((L, R, k), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.full((L, R), -7, dtype=torch.int32, device="cuda")
+    clsa.step(dims, rows, lq, dw.k_idx, dw.k_cache, dw.v_cache, dw.cu_seqlens, dw.q, out, idx, cnt, ws, nws,
+              schedule=clsa.SCHEDULE_PER_LAYER_ROUTING)
+    torch.cuda.synchronize()
+    idx_h, cnt_h, dev = idx.cpu().numpy(), cnt.cpu().numpy(), bf16_dev_to_f64(out)
+    for r in (range(R) if check is None else check):
+        ref = oracle_row_layer_routing(w, r)
+        for l in range(L):
+            assert cnt_h[l, r] == ref["count"][l]
+            assert np.array_equal(idx_h[l, r], ref["idx"][l]), f"cfg{cfg} row {r} layer {l}"
+        assert_outputs_close(dev[r], ref["out"], f"routing cfg{cfg} row {r}")
+    # the layers really route differently
+    assert not np.array_equal(idx_h[0, 0], idx_h[1, 0])
+
+
 @pytest.mark.parametrize("schedule", [clsa.SCHEDULE_LAYER_BATCHED, clsa.SCHEDULE_PER_LAYER])
 def test_step_prefill_vs_oracle(schedule):
     w = cs.config(4)
