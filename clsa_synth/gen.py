@@ -43,6 +43,11 @@ TID_V = 5
 TID_NEEDLE = 6
 TID_LEN = 7
 TID_Q_IDX_LAYER = 8     # per-layer indexer queries of the routing ablation
+TID_H_NEW = 9           # hidden state of each sequence's new token (indexer projection inputs)
+TID_W_Q_IDX = 10        # indexer query projection, stored [d_idx, d_model]
+TID_W_K_IDX = 11        # indexer key projection, stored [d_idx, d_model]
+TID_K_NEW = 12          # K row of each sequence's new token, appended to the cache
+TID_V_NEW = 13          # V row of each sequence's new token
 
 KIND_UNIFORM_INT = 0
 KIND_NORMAL = 1

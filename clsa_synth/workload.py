@@ -138,6 +138,40 @@ class Workload:
         tid = gen.TID_K if which == "k" else gen.TID_V
         return gen.normal_bf16(self.seed, tid, flat).reshape(len(tokens), self.hkv, self.head_dim)
 
+    # ---- the step before the routing: the new token of each decode sequence ----------
+    # Hidden state h [B, d_model] is randint[-1, 1]; the indexer projections W_q_idx, W_k_idx are
+    # stored [d_idx, d_model] (row j = the weights of indexer channel j) with entries
+    # randint[-1, 1] / 8; the new K and V rows [B, Hkv, hd] are ~N(0, 1).  With integer h and
+    # eighths in W every partial sum of a projection is a multiple of 1/8 below d_model / 8, exact
+    # in fp32 in any order, so the bf16 results are the rounding of the exact sums on any device.
+    PROJ_H = (-1, 1, 1)
+    PROJ_W = (-1, 1, 8)
+
+    def new_token(self, b: int) -> int:
+        """Cache row (global) of sequence b's new token: its last position."""
+        assert self.mode == "decode"
+        return int(self.cu_seqlens[b + 1]) - 1
+
+    def h_new_bits(self, rows, d_model: int) -> np.ndarray:
+        rows = np.asarray(rows, dtype=np.int64).reshape(-1)
+        flat = rows[:, None] * d_model + np.arange(d_model)[None, :]
+        lo, hi, den = self.PROJ_H
+        return gen.uniform_int_bf16(self.seed, gen.TID_H_NEW, flat, lo, hi, den)
+
+    def w_idx_bits(self, which: str, d_model: int) -> np.ndarray:
+        """[d_idx, d_model] weights of the indexer query ("q") or key ("k") projection."""
+        flat = np.arange(self.d_idx * d_model, dtype=np.int64).reshape(self.d_idx, d_model)
+        tid = gen.TID_W_Q_IDX if which == "q" else gen.TID_W_K_IDX
+        lo, hi, den = self.PROJ_W
+        return gen.uniform_int_bf16(self.seed, tid, flat, lo, hi, den)
+
+    def kv_new_bits(self, rows, which: str) -> np.ndarray:
+        rows = np.asarray(rows, dtype=np.int64).reshape(-1)
+        per = self.hkv * self.head_dim
+        flat = rows[:, None] * per + np.arange(per)[None, :]
+        tid = gen.TID_K_NEW if which == "k" else gen.TID_V_NEW
+        return gen.normal_bf16(self.seed, tid, flat).reshape(len(rows), self.hkv, self.head_dim)
+
     # ---- fp64 views for the oracle ---------------------------------------------------
     def q_idx_f64(self, rows) -> np.ndarray:
         return gen.bf16_bits_to_f64(self.q_idx_bits(rows))

@@ -10,7 +10,7 @@ Sources (page titles as published; sections named on the page):
 
 * [SUM] picx.dev summary of "You Only Index Once: Cross-Layer Sparse Attention
   with Shared Routing", section Methodology > Architecture Overview:
-  eq. 1 (index projections from the shared hidden states), eq. 2 (routing
+  eq. 1 (index projections from the shared hidden states, ``index_projection``), eq. 2 (routing
   scores ``I = Q_idx K_idx^T`` and ``S_t = TopK(I_t, k)``, computed once) and
   eq. 3 (every cross-decoder layer l attends with its own query ``Q_t^(l)`` to
   the selected rows ``K_{S_t}, V_{S_t}`` of the one shared cache).
@@ -35,6 +35,40 @@ tiny inputs, special cases reducing to a library attention routine).
 from __future__ import annotations
 
 import numpy as np
+
+
+# ---------------------------------------------------------------------------------------------
+# eq. 1: indexer queries and keys projected from the shared hidden states ([SUM] Architecture
+# Overview: Q_idx = H W_idx^Q, K_idx = H W_idx^K)
+# ---------------------------------------------------------------------------------------------
+def index_projection(h_rows: np.ndarray, w_rows: np.ndarray) -> np.ndarray:
+    """One projection of eq. 1 for the given hidden-state rows.
+
+    h_rows: (n, d_model) float64.  w_rows: (d_idx, d_model) float64, row j holding the weights
+    of indexer channel j (the projection matrix transposed).  Returns (n, d_idx) float64 with
+    out[t, j] = sum_c h[t, c] * w[j, c].
+    """
+    h = np.asarray(h_rows, dtype=np.float64)
+    w = np.asarray(w_rows, dtype=np.float64)
+    assert h.ndim == 2 and w.ndim == 2 and h.shape[1] == w.shape[1]
+    return h @ w.T
+
+
+def round_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest bf16 value, ties to even; uint16 bit patterns.
+
+    bf16 keeps 8 significant bits: writing x = f * 2**e with 1/2 <= |f| < 1, the result is
+    round(f * 2**8) * 2**(e - 8) with halves going to the even integer.  For finite values in
+    the normal range (the only ones the path produces)."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.zeros(x.shape, dtype=np.float64)
+    nz = x != 0
+    _, e = np.frexp(x[nz])
+    quantum = np.ldexp(1.0, e - 8)
+    out[nz] = np.round(x[nz] / quantum) * quantum   # np.round rounds halves to even
+    f32 = out.astype(np.float32)
+    assert np.all(f32.astype(np.float64) == out), "bf16 value outside the fp32 range"
+    return (f32.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
 
 
 # ---------------------------------------------------------------------------------------------

@@ -10,7 +10,9 @@ import numpy as np
 
 from clsa_synth import Workload
 
-from .clsa_oracle import assert_scores_exact, pad_selection, step_row
+from clsa_synth import gen
+
+from .clsa_oracle import assert_scores_exact, index_projection, pad_selection, round_bf16_bits, step_row
 
 
 def oracle_row(w: Workload, r: int, check_exact: bool = True) -> dict:
@@ -66,3 +68,48 @@ def oracle_row_layer_routing(w: Workload, r: int) -> dict:
         idx.append(i)
         cnt.append(c)
     return {"idx": np.stack(idx), "count": np.asarray(cnt), "out": np.stack(out)}
+
+
+# ---------------------------------------------------------------------------------------------
+# The decode step preceded by the new token's indexer projections (eq. 1) and cache append
+# ---------------------------------------------------------------------------------------------
+def oracle_projection(w: Workload, d_model: int, rows=None) -> dict:
+    """bf16 bits of the new token's indexer query and key for each sequence in `rows` (default:
+    all): q_idx [n, d_idx] = RNE(h W_idx^Q), k_idx_new [n, d_idx] = RNE(h W_idx^K)."""
+    rows = np.arange(w.batch) if rows is None else np.asarray(rows, dtype=np.int64)
+    h = gen.bf16_bits_to_f64(w.h_new_bits(rows, d_model))
+    q = index_projection(h, gen.bf16_bits_to_f64(w.w_idx_bits("q", d_model)))
+    k = index_projection(h, gen.bf16_bits_to_f64(w.w_idx_bits("k", d_model)))
+    return {"q_idx": round_bf16_bits(q), "k_idx_new": round_bf16_bits(k)}
+
+
+def oracle_row_projected(w: Workload, r: int, d_model: int) -> dict:
+    """fp64 oracle of decode row r when the step starts by appending each sequence's new token:
+    its indexer query is projected from the hidden state (eq. 1), its indexer key is projected
+    into the row's last cache position, and its K/V rows replace that position of the cache.
+    dict(scores, sel, idx[k], count, out[L, Hq, hd])."""
+    assert w.mode == "decode"
+    p = oracle_projection(w, d_model, [r])
+    base = int(w.cu_seqlens[r])
+    n = w.row_len(r)
+    tokens = base + np.arange(n, dtype=np.int64)
+    k_idx = w.k_idx_f64(tokens)
+    k_idx[n - 1] = gen.bf16_bits_to_f64(p["k_idx_new"][0])
+    k_new = gen.bf16_bits_to_f64(w.kv_new_bits([r], "k"))[0]
+    v_new = gen.bf16_bits_to_f64(w.kv_new_bits([r], "v"))[0]
+
+    def fetch(sel):
+        sel = np.asarray(sel, dtype=np.int64)
+        kf, vf = w.kv_f64(base + sel)
+        last = sel == n - 1
+        kf[last] = k_new
+        vf[last] = v_new
+        return kf, vf
+
+    res = step_row(gen.bf16_bits_to_f64(p["q_idx"][0]), k_idx, w.q_f64([r])[0], fetch, w.topk)
+    # indexer entries are multiples of 1/idx_den, projected ones multiples of 1/8
+    assert 8 % w.idx_den == 0
+    assert_scores_exact(res["scores"], 1.0 / 64.0)
+    res["idx"], res["count"] = pad_selection(res["sel"], w.topk)
+    res["q_idx"], res["k_idx_new"] = p["q_idx"][0], p["k_idx_new"][0]
+    return res
