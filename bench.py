@@ -23,6 +23,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 METRIC = "decode tokens/sec + HBM GB/s (% roofline), index+top-k+L-layer attn at 128K"
+# hidden width of the new-token indexer projections timed beside the step (the pages give none;
+# a round width of the order of the 4B-parameter models they evaluate)
+APPEND_D_MODEL = 4096
 INDEX_KERNEL_SOURCES = ["cross_layer_token_amd/csrc/k_index.hip", "cross_layer_token_amd/csrc/device_common.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_index_scores_decode_b16_n128k.json")
 
@@ -68,10 +71,10 @@ PROFILE_COMMANDS = {
     "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_trace -o bench -- "
              "python3 bench.py --steps 20 --warmup 3 --no-cpu-baseline --no-prefill",
     "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof_fetch -o bench -- "
-             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-per-layer --no-prefill "
+             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-per-layer --no-prefill --no-append "
              "--profile-copy-mib 1024",
     "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof_write -o bench -- "
-             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-per-layer --no-prefill "
+             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-per-layer --no-prefill --no-append "
              "--profile-copy-mib 1024",
 }
 
@@ -99,8 +102,9 @@ def summarize_trace(trace_dir: str) -> str:
              "The run holds warmup + timed steps of the layer-batched step (score kernel with histogram,",
              "top-k select, sparse attention), the score kernel alone (the roofline line), the",
              "per-layer schedule (gather + one attention per layer), the per-layer routing ablation",
-             "(scores, top-k and one attention per layer), the Infinity Cache probes (torch reduce and",
-             "copy) and the synthetic-input fill.", "",
+             "(scores, top-k and one attention per layer), the new-token indexer projections and cache",
+             "append ahead of the step, the Infinity Cache probes (torch reduce and copy) and the",
+             "synthetic-input fill.", "",
              "| kernel | calls | avg us | min us | max us | share % |", "|---|---:|---:|---:|---:|---:|"]
     for r in _csv_rows(path):
         lines.append(f"| `{_short_kernel(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
@@ -280,6 +284,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-layer", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill report")
+    ap.add_argument("--no-append", action="store_true", help="skip the new-token projection + append report")
     ap.add_argument("--profile-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a counter calibration reference)")
     ap.add_argument("--summarize-trace", metavar="DIR", help="write the kernel-trace summary under profiles/ and exit")
@@ -407,6 +412,32 @@ def main():
                    "vs_shared_routing": round(t3 / t_step, 2)}
         del ws3, idx3, cnt3
 
+    # ---- the step before the routing: new-token indexer projections + cache append ----------------
+    append = None
+    if not args.no_append:
+        d_model = APPEND_D_MODEL
+        pin = dw.projection_inputs(d_model)
+        q_new = torch.empty((R, w.d_idx), dtype=torch.int16, device="cuda")
+
+        def run_append_steps(n):
+            for _ in range(n):
+                clsa.index_project(dims, rows, d_model, pin["h"], pin["w_q_idx"], pin["w_k_idx"], dw.cu_seqlens,
+                                   q_new, dw.k_idx, pin["k_new"], pin["v_new"], dw.k_cache, dw.v_cache, stream=stream)
+                clsa.step(dims, rows, q_new, dw.k_idx, dw.k_cache, dw.v_cache, dw.cu_seqlens, dw.q, out, idx, cnt, ws,
+                          nws, stream=stream)
+
+        # weights (query and key projections), hidden states, q_idx and appended rows
+        p_bytes = (2 * w.d_idx * d_model + R * d_model + 2 * R * w.d_idx + 2 * R * w.hkv * w.head_dim) * 2
+        run_append_steps(args.warmup)
+        _, w4 = timed(run_append_steps, args.steps)
+        t4 = w4 / args.steps
+        # the projection's cost is what it adds to the (device-bound) step; timing the kernel alone
+        # from back-to-back host calls would measure the host's call rate instead
+        added = t4 - t_step
+        append = {"d_model": d_model, "ms_per_step": round(t4 * 1e3, 4), "tokens_per_s": round(R / t4, 1),
+                  "added_us_per_step": round(added * 1e6, 2), "project_bytes": p_bytes, "vs_step": round(t4 / t_step, 4)}
+        del pin, q_new
+
     if args.profile_copy_mib > 0:
         n = args.profile_copy_mib << 20
         src = torch.ones(n, dtype=torch.uint8, device="cuda")
@@ -443,6 +474,7 @@ def main():
         "roofline": roofline,
         "per_layer_schedule": per_layer,
         "per_layer_routing": routing,
+        "new_token_append": append,
         "prefill": prefill,
         "cpu_baseline": cpu,
     }

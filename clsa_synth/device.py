@@ -96,6 +96,24 @@ class DeviceWorkload:
             self._layer_q_idx = t
         return self._layer_q_idx
 
+    def projection_inputs(self, d_model: int) -> dict:
+        """Inputs of the new-token indexer projections and cache append (decode):
+        h [B, d_model], w_q_idx / w_k_idx [d_idx, d_model], k_new / v_new [B, Hkv, hd]."""
+        w = self.w
+        d = self.q_idx.device
+        h = torch.empty((w.batch, d_model), dtype=torch.int16, device=d)
+        wq = torch.empty((w.d_idx, d_model), dtype=torch.int16, device=d)
+        wk = torch.empty((w.d_idx, d_model), dtype=torch.int16, device=d)
+        fill_uniform_int(h, w.seed, gen.TID_H_NEW, *w.PROJ_H)
+        fill_uniform_int(wq, w.seed, gen.TID_W_Q_IDX, *w.PROJ_W)
+        fill_uniform_int(wk, w.seed, gen.TID_W_K_IDX, *w.PROJ_W)
+        k_new = torch.empty((w.batch, w.hkv, w.head_dim), dtype=torch.int16, device=d)
+        v_new = torch.empty((w.batch, w.hkv, w.head_dim), dtype=torch.int16, device=d)
+        fill_normal(k_new, w.seed, gen.TID_K_NEW)
+        fill_normal(v_new, w.seed, gen.TID_V_NEW)
+        torch.cuda.synchronize(d)
+        return {"h": h, "w_q_idx": wq, "w_k_idx": wk, "k_new": k_new, "v_new": v_new}
+
     # sizes of the C ABI, as plain keyword dicts
     def dims(self, sm_scale: float = 0.0) -> dict:
         w = self.w

@@ -20,7 +20,8 @@ SCHEDULE_LAYER_BATCHED, SCHEDULE_PER_LAYER, SCHEDULE_PER_LAYER_ROUTING = 0, 1, 2
 HEAD_DIM = 128
 
 FUNCTIONS = ["clsa_status_string", "clsa_last_error_message", "clsa_abi_version", "clsa_workspace_bytes",
-             "clsa_index_scores", "clsa_topk", "clsa_gather_kv", "clsa_sparse_attn", "clsa_step"]
+             "clsa_index_scores", "clsa_topk", "clsa_gather_kv", "clsa_sparse_attn", "clsa_step",
+             "clsa_index_project"]
 
 
 class Dims(ctypes.Structure):
@@ -66,6 +67,7 @@ def _load():
         "clsa_sparse_attn": (c_int32, [POINTER(Dims), POINTER(Rows), P, c_int64, c_int32, P, P, P, P, P, P, P, P,
                                        c_int64, P, c_size_t, P]),
         "clsa_step": (c_int32, [POINTER(Dims), POINTER(Rows), POINTER(StepArgs), P, c_size_t, P]),
+        "clsa_index_project": (c_int32, [POINTER(Dims), POINTER(Rows), c_int32, P, P, P, P, P, P, P, P, P, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -140,6 +142,13 @@ def topk(dims, rows, cu_seqlens, scores, ld_scores, idx, count, workspace, works
 def gather_kv(dims, rows, k_cache, v_cache, cu_seqlens, idx, count, k_sel, v_sel, stream=None):
     _check(LIB.clsa_gather_kv(ctypes.byref(dims), ctypes.byref(rows), _ptr(k_cache), _ptr(v_cache), _ptr(cu_seqlens),
                               _ptr(idx), _ptr(count), _ptr(k_sel), _ptr(v_sel), _stream(stream)))
+
+
+def index_project(dims, rows, d_model, h, w_q_idx, w_k_idx, cu_seqlens, q_idx, k_idx, k_new=None, v_new=None,
+                  k_cache=None, v_cache=None, stream=None):
+    _check(LIB.clsa_index_project(ctypes.byref(dims), ctypes.byref(rows), d_model, _ptr(h), _ptr(w_q_idx),
+                                  _ptr(w_k_idx), _ptr(cu_seqlens), _ptr(q_idx), _ptr(k_idx), _ptr(k_new), _ptr(v_new),
+                                  _ptr(k_cache), _ptr(v_cache), _stream(stream)))
 
 
 def sparse_attn(dims, rows, q, q_row_stride, n_layers_call, k_sel, v_sel, k_cache, v_cache, cu_seqlens, idx, count,

@@ -125,6 +125,36 @@ clsa_status clsa_index_scores(const clsa_dims* dims, const clsa_rows* rows, cons
   return device_status(e, "clsa_index_scores");
 }
 
+clsa_status clsa_index_project(const clsa_dims* dims, const clsa_rows* rows, int32_t d_model, const clsa_bf16* h,
+                               const clsa_bf16* w_q_idx, const clsa_bf16* w_k_idx, const int32_t* cu_seqlens,
+                               clsa_bf16* q_idx, clsa_bf16* k_idx, const clsa_bf16* k_new, const clsa_bf16* v_new,
+                               clsa_bf16* k_cache, clsa_bf16* v_cache, clsa_stream stream) {
+  g_last_error.clear();
+  CLSA_TRY(check_common(dims, rows));
+  if (rows->mode != CLSA_MODE_DECODE)
+    return set_error(CLSA_ERR_UNSUPPORTED, "clsa_index_project appends one new token per sequence: DECODE rows only");
+  if (d_model < 32 || d_model > CLSA_MAX_D_MODEL || d_model % 32 != 0)
+    return set_error(CLSA_ERR_UNSUPPORTED, "d_model must be a multiple of 32 in [32, CLSA_MAX_D_MODEL]");
+  CLSA_TRY(check_ptr(h, "h", g_err));
+  CLSA_TRY(check_ptr(w_q_idx, "w_q_idx", g_err));
+  CLSA_TRY(check_ptr(w_k_idx, "w_k_idx", g_err));
+  CLSA_TRY(check_ptr(cu_seqlens, "cu_seqlens", g_err));
+  CLSA_TRY(check_ptr(q_idx, "q_idx", g_err));
+  CLSA_TRY(check_ptr(k_idx, "k_idx", g_err));
+  if ((k_new == nullptr) != (v_new == nullptr))
+    return set_error(CLSA_ERR_INVALID_ARGUMENT, "k_new and v_new must be given together");
+  if (k_new != nullptr) {
+    CLSA_TRY(check_ptr(k_new, "k_new", g_err));
+    CLSA_TRY(check_ptr(v_new, "v_new", g_err));
+    CLSA_TRY(check_ptr(k_cache, "k_cache", g_err));
+    CLSA_TRY(check_ptr(v_cache, "v_cache", g_err));
+  }
+  return device_status(launch_index_project(dims->batch, dims->d_idx, d_model, dims->hkv, rows->total_tokens, h,
+                                            w_q_idx, w_k_idx, cu_seqlens, q_idx, k_idx, k_new, v_new, k_cache,
+                                            v_cache, stream),
+                       "clsa_index_project");
+}
+
 clsa_status clsa_topk(const clsa_dims* dims, const clsa_rows* rows, const int32_t* cu_seqlens, const float* scores,
                       int64_t ld_scores, int32_t* idx, int32_t* count, void* workspace, size_t workspace_bytes_,
                       clsa_stream stream) {

@@ -21,10 +21,13 @@ constexpr int kIdxChunkMax = 8192;
 constexpr int kIdxChunkMin = 1024;
 constexpr int kIdxMinWorkgroups = 256;
 // First histogram level of the long-row select: the top kTopkBinBits bits of the score key
-// (sign and the high exponent bits), small enough that every select workgroup can sum a row's
-// partials cheaply.
-constexpr int kTopkBinBits = 8;
+// (sign, exponent and the two leading mantissa bits), so a bin spans a factor of 1.25 in value
+// and the candidates at or above the bin holding the k-th score stay a few percent of the row
+// whatever the scale of the scores (one bin of sign and high exponent bits alone spans a factor
+// of 4 and can hold a fifth of the row).
+constexpr int kTopkBinBits = 11;
 constexpr int kTopkBins = 1 << kTopkBinBits;
+static_assert(kIdxChunkMax < 65536, "histogram partials hold uint16 counts");
 // Scores classified by one workgroup of the long-row select.
 constexpr int kSelectSpan = 8192;
 // Keys per attention tile.
@@ -136,6 +139,10 @@ int launch_attn(const RowsDev& rows, int k, int hq, int hkv, int n_layers_call, 
                 const uint16_t* vsel, const uint16_t* kc, const uint16_t* vc, const int32_t* idx,
                 const int32_t* count, uint16_t* out, int64_t o_stride, void* part, uint32_t* tickets,
                 bool tickets_clear, void* stream);
+int launch_index_project(int batch, int d_idx, int d_model, int hkv, int64_t total_tokens, const uint16_t* h,
+                         const uint16_t* wq, const uint16_t* wk, const int32_t* cu, uint16_t* q_idx, uint16_t* k_idx,
+                         const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_cache, uint16_t* v_cache,
+                         void* stream);
 const char* device_error_string(int err);
 
 }  // namespace clsa

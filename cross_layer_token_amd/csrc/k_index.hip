@@ -111,8 +111,9 @@ __global__ __launch_bounds__(kIdxThreads) void k_index_scores_decode(const uint1
   }
   if (hpart != nullptr) {
     __syncthreads();
-    uint16_t* hp = hpart + ((int64_t)b * hpart_chunks + c) * kTopkBins;
-    for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) hp[i] = (uint16_t)hist[i];
+    // bins 2i and 2i + 1 as the low and high halves of one word (counts <= chunk <= 65535)
+    uint32_t* hp = reinterpret_cast<uint32_t*>(hpart + ((int64_t)b * hpart_chunks + c) * kTopkBins);
+    for (int i = threadIdx.x; i < kTopkBins / 2; i += blockDim.x) hp[i] = hist[2 * i] | (hist[2 * i + 1] << 16);
   }
 }
 

@@ -159,8 +159,28 @@ constexpr int kSpecPerLane = 4;  // span entries each lane requests before the s
 constexpr int kMaxSpans = 2 * kSelThreads;
 static_assert(kSelectSpan == kSelThreads * 8, "each select thread classifies 8 consecutive scores");
 
+// Finds, in the kTopkBins-bin LDS histogram, the bin d (from the top bin down) whose cumulative
+// count first reaches `need`, and publishes res[0] = d, res[1] = count of the bins above d.
+// Thread t owns bins kTopkBins - 1 - 2t and kTopkBins - 2 - 2t; a block scan gives each thread
+// the count above its pair.  All threads must call it; it ends with __syncthreads().
+__device__ __forceinline__ void find_bin_from_top(const uint32_t* hist, int need, int* scan, int* res) {
+  static_assert(kTopkBins == 2 * kSelThreads, "one bin pair per select thread");
+  const int hi = kTopkBins - 1 - 2 * (int)threadIdx.x;
+  const int h0 = (int)hist[hi], h1 = (int)hist[hi - 1];
+  int total;
+  const int above = block_exclusive_scan(h0 + h1, scan, &total);
+  if (above < need && above + h0 >= need) {
+    res[0] = hi;
+    res[1] = above;
+  } else if (above + h0 < need && above + h0 + h1 >= need) {
+    res[0] = hi - 1;
+    res[1] = above + h0;
+  }
+  __syncthreads();
+}
+
 __global__ __launch_bounds__(kSelThreads) void k_topk_select(SelectArgs a) {
-  __shared__ uint32_t hist[256];
+  __shared__ uint32_t hist[kTopkBins];
   __shared__ int scan[2 * kSelThreads / 64];
   __shared__ int res[2];
   __shared__ int flag[1];
@@ -194,34 +214,31 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select(SelectArgs a) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) x[j] = i0 + j < s1 ? srow[i0 + j] : 0.f;
   }
-  // 1. row histogram from the partials: thread t sums bin pair (t % 128) over partials t / 128,
-  //    t / 128 + 8, ...; the 8 groups meet in LDS
-  static_assert(kTopkBins == 256 && kSelThreads == 1024, "histogram reduction layout");
-  if (threadIdx.x < kTopkBins) hist[threadIdx.x] = 0u;
-  __syncthreads();
+  // 1. row histogram from the partials: thread t sums bin pair t (one 32-bit word of each
+  //    partial) over the row's chunks and owns those two bins
   {
     const int nch = (n + a.hist_chunk - 1) / a.hist_chunk;
     const uint32_t* hp = reinterpret_cast<const uint32_t*>(a.hpart + (int64_t)r * a.hist_chunks * kTopkBins);
-    const int w = threadIdx.x & 127, pg = threadIdx.x >> 7;
+    constexpr int kBatch = 16;
     uint32_t lo = 0, hi = 0;
-    for (int c0 = 0; c0 < nch; c0 += 64) {
-      uint32_t v[8];
+    for (int c0 = 0; c0 < nch; c0 += kBatch) {
+      uint32_t v[kBatch];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int c = c0 + pg + 8 * j;
-        v[j] = c < nch ? hp[(int64_t)c * (kTopkBins / 2) + w] : 0u;
+      for (int j = 0; j < kBatch; ++j) {
+        const int c = c0 + j;
+        v[j] = c < nch ? hp[(int64_t)c * (kTopkBins / 2) + threadIdx.x] : 0u;
       }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < kBatch; ++j) {
         lo += v[j] & 0xFFFFu;
         hi += v[j] >> 16;
       }
     }
-    if (lo) atomicAdd(&hist[2 * w], lo);
-    if (hi) atomicAdd(&hist[2 * w + 1], hi);
+    hist[2 * threadIdx.x] = lo;
+    hist[2 * threadIdx.x + 1] = hi;
   }
   __syncthreads();
-  find_bin256_from_top(hist, m, res);
+  find_bin_from_top(hist, m, scan, res);
   const uint32_t t1 = (uint32_t)res[0];
   const int above1 = res[1];
   // 2. ordered compaction of the span's scores with bin >= t1 into the span's slot
@@ -299,12 +316,16 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select(SelectArgs a) {
     }
   }
   __syncthreads();
-  // refine T below the first level: three 8-bit passes over the remaining key bits
-  static_assert(kTopkBinBits == 8, "three refinement passes cover the remaining 24 key bits");
+  // refine T below the first level with 8-bit passes over the remaining key bits, the last pass
+  // aligned to bit 0 (its window overlaps bits the prefix already fixes, which then match)
   int need = m - above1;
-  uint32_t prefix = t1 << 24, pmask = 0xFF000000u;
+  uint32_t prefix = t1 << (32 - kTopkBinBits), pmask = ~0u << (32 - kTopkBinBits);
   auto key_at = [&](int i) { return list[i].x; };
-  for (int shift = 16; shift >= 0; shift -= 8) radix_pass8(hist, L, key_at, prefix, pmask, shift, need, res);
+  for (int shift = 32 - kTopkBinBits - 8;; shift -= 8) {
+    if (shift < 0) shift = 0;
+    radix_pass8(hist, L, key_at, prefix, pmask, shift, need, res);
+    if (shift == 0) break;
+  }
   const uint32_t T = prefix;
   // ordered output over contiguous per-thread ranges of the list
   const int E = (L + blockDim.x - 1) / blockDim.x;

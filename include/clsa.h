@@ -172,6 +172,33 @@ clsa_status clsa_sparse_attn(const clsa_dims* dims, const clsa_rows* rows, const
                              clsa_bf16* out, int64_t out_row_stride, void* workspace,
                              size_t workspace_bytes, clsa_stream stream);
 
+/*
+ * The step before the routing (DECODE only): the shared indexer's projections of each
+ * sequence's new token, eq. 1 of the picx.dev summary (Architecture Overview):
+ * Q_idx = H W_idx^Q, K_idx = H W_idx^K, and the append of that token to the caches.  Sequence
+ * b's new token is its LAST cache position t_b = cu_seqlens[b+1] - 1 (the caller has already
+ * counted it in cu_seqlens); a following clsa_index_scores / clsa_step sees it like any other
+ * token.
+ *   h        [B, d_model] bf16       hidden state of each sequence's new token
+ *   w_q_idx  [d_idx, d_model] bf16   row j = the weights of indexer channel j (W_idx^Q transposed)
+ *   w_k_idx  [d_idx, d_model] bf16   (W_idx^K transposed)
+ *   q_idx    [B, d_idx] bf16 (output)   q_idx[b, j] = RNE(sum_c h[b, c] * w_q_idx[j, c])
+ *   k_idx    [T, d_idx] bf16            row t_b := RNE(sum_c h[b, c] * w_k_idx[j, c]); no other
+ *                                       row is written
+ *   k_new, v_new [B, hkv, 128] bf16, optional (both or neither): copied bit for bit into row t_b
+ *            of k_cache / v_cache [T, hkv, 128] (both required when k_new is given)
+ * Products are accumulated in fp32 in an order fixed by d_model alone (not by timing); when
+ * every partial sum is exact in fp32 the result is the bf16 rounding (nearest, ties to even) of
+ * the exact sum.  d_model: a multiple of 32, at most CLSA_MAX_D_MODEL.  No workspace.  A
+ * sequence of length 0 (possible only when cu_seqlens_host is not given) gets q_idx but no
+ * append.  Returns CLSA_ERR_UNSUPPORTED for PREFILL rows or an unsupported d_model.
+ */
+#define CLSA_MAX_D_MODEL 65536
+clsa_status clsa_index_project(const clsa_dims* dims, const clsa_rows* rows, int32_t d_model, const clsa_bf16* h,
+                               const clsa_bf16* w_q_idx, const clsa_bf16* w_k_idx, const int32_t* cu_seqlens,
+                               clsa_bf16* q_idx, clsa_bf16* k_idx, const clsa_bf16* k_new, const clsa_bf16* v_new,
+                               clsa_bf16* k_cache, clsa_bf16* v_cache, clsa_stream stream);
+
 /* Everything one step reads and writes (all device pointers). */
 typedef struct clsa_step_args {
   const clsa_bf16* q_idx;     /* [R, d_idx]                                               */

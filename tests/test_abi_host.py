@@ -152,6 +152,26 @@ def test_step_rejects():
     assert st == B.ERR_UNSUPPORTED and "DECODE" in B.last_error()
 
 
+def test_index_project_rejects():
+    dims, rows = _dims(), _rows()
+
+    def call(rows_=rows, d_model=4096, h=FAKE, wq=FAKE, wk=FAKE, cu=FAKE, q_idx=FAKE, k_idx=FAKE, k_new=None,
+             v_new=None, kc=None, vc=None):
+        return B.LIB.clsa_index_project(ctypes.byref(dims), ctypes.byref(rows_), d_model, h, wq, wk, cu, q_idx,
+                                        k_idx, k_new, v_new, kc, vc, None)
+    pre = B.make_rows(B.MODE_PREFILL, 100, 100, 1500, seq=0, pos0=0)
+    assert call(rows_=pre) == B.ERR_UNSUPPORTED and "DECODE" in B.last_error()
+    assert call(d_model=48) == B.ERR_UNSUPPORTED and "d_model" in B.last_error()
+    assert call(d_model=0) == B.ERR_UNSUPPORTED
+    assert call(d_model=65536 + 32) == B.ERR_UNSUPPORTED
+    assert call(h=None) == B.ERR_INVALID_ARGUMENT and "h is NULL" in B.last_error()
+    assert call(wk=FAKE + 8) == B.ERR_INVALID_ARGUMENT and "aligned" in B.last_error()
+    assert call(k_idx=None) == B.ERR_INVALID_ARGUMENT and "k_idx" in B.last_error()
+    assert call(k_new=FAKE) == B.ERR_INVALID_ARGUMENT and "together" in B.last_error()
+    assert call(k_new=FAKE, v_new=FAKE) == B.ERR_INVALID_ARGUMENT and "k_cache" in B.last_error()
+    assert call(rows_=_rows(cu_seqlens_host=[0, 0, 1500])) == B.ERR_INVALID_ARGUMENT
+
+
 def test_workspace_sizes_cover_every_call():
     # 128K decode: candidate lists dominate; per-layer schedule adds the two compact buffers
     dims = B.make_dims(16, 128, 2048, 16, 32, 8)
