@@ -13,7 +13,8 @@ Sources (page titles as published; sections named on the page):
   eq. 1 (index projections from the shared hidden states, ``index_projection``), eq. 2 (routing
   scores ``I = Q_idx K_idx^T`` and ``S_t = TopK(I_t, k)``, computed once) and
   eq. 3 (every cross-decoder layer l attends with its own query ``Q_t^(l)`` to
-  the selected rows ``K_{S_t}, V_{S_t}`` of the one shared cache).
+  the selected rows ``K_{S_t}, V_{S_t}`` of the one shared cache); section
+  Multi-Layer Distillation, eq. 4-5 (``distill_target``, ``distill_kl``).
 * [FORUM] zhichai.net explainer "You Only Index Once ... (CLSA) Explained",
   section Background: Attention and Its Limits (softmax(Q K^T / sqrt(d_k)) V),
   and section CLSA: Sharing the Index Across Layers (the Selector gathers KV
@@ -147,6 +148,47 @@ def sparse_attention(q: np.ndarray, k_sel: np.ndarray, v_sel: np.ndarray, scale:
         p = np.exp(logits)
         out[:, h, :] = (p @ v_sel[:, g, :]) / p.sum(axis=1, keepdims=True)
     return out
+
+
+# ---------------------------------------------------------------------------------------------
+# eq. 4-5: the multi-layer distillation target and loss ([SUM] Methodology, Multi-Layer
+# Distillation): the attention distributions of every layer and head, averaged, against the
+# indexer's softmax(I_t)
+# ---------------------------------------------------------------------------------------------
+def distill_target(q: np.ndarray, k_rows: np.ndarray, scale: float | None = None) -> np.ndarray:
+    """A-bar_t of eq. 4 for one query position: the mean over every layer l and query head h of
+    the attention distribution softmax(q[l, h] . K_g^T * scale) over the position's visible keys,
+    with g = h // (Hq // Hkv) and scale 1/sqrt(head_dim) by default.
+
+    q: (L, Hq, hd) float64; k_rows: (n, Hkv, hd) float64.  Returns (n,) float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k_rows, dtype=np.float64)
+    lc, hq, hd = q.shape
+    n, hkv, hd2 = k.shape
+    assert hd2 == hd and hq % hkv == 0 and n >= 1
+    if scale is None:
+        scale = 1.0 / np.sqrt(hd)
+    group = hq // hkv
+    total = np.zeros(n, dtype=np.float64)
+    for h in range(hq):
+        logits = (q[:, h, :] @ k[:, h // group, :].T) * scale     # (L, n)
+        logits = logits - logits.max(axis=1, keepdims=True)
+        p = np.exp(logits)
+        total += (p / p.sum(axis=1, keepdims=True)).sum(axis=0)
+    return total / (lc * hq)
+
+
+def distill_kl(abar: np.ndarray, scores: np.ndarray) -> float:
+    """KL(A-bar_t || softmax(I_t)) of eq. 5 for one position, natural log:
+    sum_j A_j (log A_j - log softmax(I_t)_j), with 0 log 0 = 0.  The stop-gradient on A-bar
+    does not change the value."""
+    a = np.asarray(abar, dtype=np.float64)
+    s = np.asarray(scores, dtype=np.float64)
+    s = s - s.max()
+    log_q = s - np.log(np.exp(s).sum())
+    nz = a > 0
+    return float(np.sum(a[nz] * (np.log(a[nz]) - log_q[nz])))
 
 
 # ---------------------------------------------------------------------------------------------

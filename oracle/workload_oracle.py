@@ -12,7 +12,8 @@ from clsa_synth import Workload
 
 from clsa_synth import gen
 
-from .clsa_oracle import assert_scores_exact, index_projection, pad_selection, round_bf16_bits, step_row
+from .clsa_oracle import (assert_scores_exact, distill_kl, distill_target, index_projection, index_scores,
+                          pad_selection, round_bf16_bits, step_row)
 
 
 def oracle_row(w: Workload, r: int, check_exact: bool = True) -> dict:
@@ -113,3 +114,19 @@ def oracle_row_projected(w: Workload, r: int, d_model: int) -> dict:
     res["idx"], res["count"] = pad_selection(res["sel"], w.topk)
     res["q_idx"], res["k_idx_new"] = p["q_idx"][0], p["k_idx_new"][0]
     return res
+
+
+# ---------------------------------------------------------------------------------------------
+# The distillation target and loss of eq. 4-5 on a prefill workload
+# ---------------------------------------------------------------------------------------------
+def oracle_distill_row(w: Workload, r: int) -> dict:
+    """fp64 eq. 4-5 for query row r of a prefill workload (row r sees tokens 0..r): A-bar_r from
+    the row's per-layer queries and the shared K cache, I_r from its indexer query and K_idx, and
+    KL(A-bar_r || softmax(I_r)).  dict(abar, scores, kl)."""
+    assert w.mode == "prefill"
+    n = w.row_len(r)
+    tokens = np.arange(n, dtype=np.int64)
+    k = gen.bf16_bits_to_f64(w.kv_bits(tokens, "k"))
+    abar = distill_target(w.q_f64([r])[0], k)
+    scores = index_scores(w.q_idx_f64([r])[0], w.k_idx_f64(tokens))
+    return {"abar": abar, "scores": scores, "kl": distill_kl(abar, scores)}
