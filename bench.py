@@ -22,6 +22,8 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+# v_exp_f32 per second: 256 CUs x 4 SIMDs x 16 lanes at a quarter of the full rate, at 2.4 GHz
+EXP2_PEAK_PER_S = 256 * 4 * 16 / 4 * 2.4e9
 METRIC = "decode tokens/sec + HBM GB/s (% roofline), index+top-k+L-layer attn at 128K"
 # hidden width of the new-token indexer projections timed beside the step (the pages give none;
 # a round width of the order of the 4B-parameter models they evaluate)
@@ -71,10 +73,10 @@ PROFILE_COMMANDS = {
     "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_trace -o bench -- "
              "python3 bench.py --steps 20 --warmup 3 --no-cpu-baseline --no-prefill",
     "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof_fetch -o bench -- "
-             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-per-layer --no-prefill --no-append "
+             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-per-layer --no-prefill --no-append --no-distill "
              "--profile-copy-mib 1024",
     "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof_write -o bench -- "
-             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-per-layer --no-prefill --no-append "
+             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-per-layer --no-prefill --no-append --no-distill "
              "--profile-copy-mib 1024",
 }
 
@@ -246,6 +248,52 @@ def prefill_report(steps: int = 3, chunk: int = 8192) -> dict:
             "index_gemm_mfma_frac": round(idx_flop / t_idx / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
 
 
+def distill_report(reps: int = 3) -> dict:
+    """The multi-layer distillation target and loss (eq. 4-5) over all 8192 positions of the
+    prefill workload (L = 8, Hq = 32, Hkv = 8), from the routing scores.  Two passes over every
+    causal (position, key) pair for each of the L * Hq (layer, head) pairs: bf16 MFMA work against
+    its peak, and one exp2 per score and pass against the transcendental rate."""
+    import torch
+
+    import clsa_synth as cs
+    import cross_layer_token_amd as clsa
+    from clsa_synth.device import DeviceWorkload
+
+    w = cs.config(4)
+    dw = DeviceWorkload(w)
+    dims = clsa.make_dims(**dw.dims())
+    rows = clsa.make_rows(**dw.rows())
+    R, L, hq = w.n_rows, w.n_layers, w.hq
+    ld = ((R + 63) // 64) * 64
+    scores = torch.empty((R, ld), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    clsa.index_scores(dims, rows, dw.q_idx, dw.k_idx, dw.cu_seqlens, scores, ld, stream=stream)
+    nws = clsa.distill_workspace_bytes(dims, rows)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    kl = torch.empty(R, dtype=torch.float32, device="cuda")
+    loss = torch.empty(1, dtype=torch.float32, device="cuda")
+
+    def run(n):
+        for _ in range(n):
+            clsa.distill_kl(dims, rows, dw.q, L * hq * 128, dw.k_cache, dw.cu_seqlens, scores, ld, kl, loss, ws, nws,
+                            stream=stream)
+
+    run(1)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    run(reps)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t = ev0.elapsed_time(ev1) / reps / 1e3
+    pairs = R * (R + 1) // 2                          # causal (position, key) pairs
+    flop = 2 * pairs * L * hq * w.head_dim * 2         # two passes of q.k, 2 flop per MAC
+    exps = 2 * pairs * L * hq                          # one exp2 per score and pass
+    return {"workload": w.name, "rows": R, "layers": L, "heads": hq, "reps": reps, "ms": round(t * 1e3, 3),
+            "mfma_tflops": round(flop / t / 1e12, 1), "mfma_frac": round(flop / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "exp_per_s": float(f"{exps / t:.4g}"), "exp_frac": round(exps / t / EXP2_PEAK_PER_S, 4),
+            "loss": round(float(loss.cpu()[0]), 6)}
+
+
 def cpu_baseline(w, budget_s: float) -> dict:
     """The fp64 C++ oracle on the host, on a bounded sample of the workload: whole decode rows,
     each evaluated from scratch (inputs regenerated from the generator definition, scores over
@@ -285,6 +333,7 @@ def main():
     ap.add_argument("--no-per-layer", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill report")
     ap.add_argument("--no-append", action="store_true", help="skip the new-token projection + append report")
+    ap.add_argument("--no-distill", action="store_true", help="skip the distillation target and loss report")
     ap.add_argument("--profile-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a counter calibration reference)")
     ap.add_argument("--summarize-trace", metavar="DIR", help="write the kernel-trace summary under profiles/ and exit")
@@ -450,6 +499,7 @@ def main():
     del dw, out, idx, cnt, ws, scores
     torch.cuda.empty_cache()
     prefill = None if args.no_prefill else prefill_report()
+    distill = None if args.no_distill else distill_report()
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_budget)
     line = {
         "metric": METRIC,
@@ -476,6 +526,7 @@ def main():
         "per_layer_routing": routing,
         "new_token_append": append,
         "prefill": prefill,
+        "distill": distill,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

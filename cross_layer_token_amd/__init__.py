@@ -6,7 +6,7 @@ The library is loaded on first use of an entry point (not at package import), so
 """
 _EXPORTS = ("HEAD_DIM", "MODE_DECODE", "MODE_PREFILL", "SCHEDULE_LAYER_BATCHED", "SCHEDULE_PER_LAYER",
             "SCHEDULE_PER_LAYER_ROUTING", "CLSAError",
-            "gather_kv", "index_project", "index_scores", "make_dims", "make_rows", "sparse_attn", "step", "topk", "workspace_bytes")
+            "distill_kl", "distill_workspace_bytes", "gather_kv", "index_project", "index_scores", "make_dims", "make_rows", "sparse_attn", "step", "topk", "workspace_bytes")
 
 __all__ = ["binding", *_EXPORTS]
 

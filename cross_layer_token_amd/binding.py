@@ -21,7 +21,7 @@ HEAD_DIM = 128
 
 FUNCTIONS = ["clsa_status_string", "clsa_last_error_message", "clsa_abi_version", "clsa_workspace_bytes",
              "clsa_index_scores", "clsa_topk", "clsa_gather_kv", "clsa_sparse_attn", "clsa_step",
-             "clsa_index_project"]
+             "clsa_index_project", "clsa_distill_workspace_bytes", "clsa_distill_kl"]
 
 
 class Dims(ctypes.Structure):
@@ -68,6 +68,8 @@ def _load():
                                        c_int64, P, c_size_t, P]),
         "clsa_step": (c_int32, [POINTER(Dims), POINTER(Rows), POINTER(StepArgs), P, c_size_t, P]),
         "clsa_index_project": (c_int32, [POINTER(Dims), POINTER(Rows), c_int32, P, P, P, P, P, P, P, P, P, P, P]),
+        "clsa_distill_workspace_bytes": (c_size_t, [POINTER(Dims), POINTER(Rows)]),
+        "clsa_distill_kl": (c_int32, [POINTER(Dims), POINTER(Rows), P, c_int64, P, P, P, c_int64, P, P, P, c_size_t, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -149,6 +151,20 @@ def index_project(dims, rows, d_model, h, w_q_idx, w_k_idx, cu_seqlens, q_idx, k
     _check(LIB.clsa_index_project(ctypes.byref(dims), ctypes.byref(rows), d_model, _ptr(h), _ptr(w_q_idx),
                                   _ptr(w_k_idx), _ptr(cu_seqlens), _ptr(q_idx), _ptr(k_idx), _ptr(k_new), _ptr(v_new),
                                   _ptr(k_cache), _ptr(v_cache), _stream(stream)))
+
+
+def distill_workspace_bytes(dims: Dims, rows: Rows) -> int:
+    n = LIB.clsa_distill_workspace_bytes(ctypes.byref(dims), ctypes.byref(rows))
+    if n == 0:
+        raise CLSAError(ERR_INVALID_ARGUMENT, last_error())
+    return n
+
+
+def distill_kl(dims, rows, q, q_row_stride, k_cache, cu_seqlens, scores, ld_scores, kl, loss, workspace,
+               workspace_bytes_, stream=None):
+    _check(LIB.clsa_distill_kl(ctypes.byref(dims), ctypes.byref(rows), _ptr(q), q_row_stride, _ptr(k_cache),
+                               _ptr(cu_seqlens), _ptr(scores), ld_scores, _ptr(kl), _ptr(loss), _ptr(workspace),
+                               workspace_bytes_, _stream(stream)))
 
 
 def sparse_attn(dims, rows, q, q_row_stride, n_layers_call, k_sel, v_sel, k_cache, v_cache, cu_seqlens, idx, count,

@@ -155,6 +155,40 @@ clsa_status clsa_index_project(const clsa_dims* dims, const clsa_rows* rows, int
                        "clsa_index_project");
 }
 
+size_t clsa_distill_workspace_bytes(const clsa_dims* dims, const clsa_rows* rows) {
+  if (check_common(dims, rows) != CLSA_OK) return 0;
+  if (rows->mode != CLSA_MODE_PREFILL) {
+    set_error(CLSA_ERR_UNSUPPORTED, "the distillation loss is defined on PREFILL rows");
+    return 0;
+  }
+  return plan_distill(dims, rows).bytes;
+}
+
+clsa_status clsa_distill_kl(const clsa_dims* dims, const clsa_rows* rows, const clsa_bf16* q, int64_t q_row_stride,
+                            const clsa_bf16* k_cache, const int32_t* cu_seqlens, const float* scores,
+                            int64_t ld_scores, float* kl, float* loss, void* workspace, size_t workspace_bytes_,
+                            clsa_stream stream) {
+  g_last_error.clear();
+  CLSA_TRY(check_common(dims, rows));
+  if (rows->mode != CLSA_MODE_PREFILL)
+    return set_error(CLSA_ERR_UNSUPPORTED, "the distillation loss is defined on PREFILL rows");
+  CLSA_TRY(check_ptr(q, "q", g_err));
+  CLSA_TRY(check_ptr(k_cache, "k_cache", g_err));
+  CLSA_TRY(check_ptr(cu_seqlens, "cu_seqlens", g_err));
+  CLSA_TRY(check_ptr(scores, "scores", g_err));
+  CLSA_TRY(check_ptr(kl, "kl", g_err));
+  if (loss != nullptr && reinterpret_cast<uintptr_t>(loss) % 4 != 0)
+    return set_error(CLSA_ERR_INVALID_ARGUMENT, "loss is not 4-byte aligned");
+  if (clsa_status s = check_ld(ld_scores, rows, "ld_scores"); s != CLSA_OK) return s;
+  if (clsa_status s = check_attn_strides(dims, dims->n_layers, q_row_stride, q_row_stride); s != CLSA_OK) return s;
+  const DistillPlan plan = plan_distill(dims, rows);
+  if (clsa_status s = check_workspace(workspace, workspace_bytes_, plan.bytes); s != CLSA_OK) return s;
+  return device_status(launch_distill(rows_dev(rows, cu_seqlens), rows->total_tokens, dims->n_layers, dims->hq, dims->hkv,
+                                      softmax_scale(dims), q, q_row_stride, k_cache, scores, ld_scores, kl, loss,
+                                      workspace, plan, stream),
+                       "clsa_distill_kl");
+}
+
 clsa_status clsa_topk(const clsa_dims* dims, const clsa_rows* rows, const int32_t* cu_seqlens, const float* scores,
                       int64_t ld_scores, int32_t* idx, int32_t* count, void* workspace, size_t workspace_bytes_,
                       clsa_stream stream) {

@@ -114,6 +114,17 @@ inline float softmax_scale(const clsa_dims* d) {
   return d->sm_scale > 0.f ? d->sm_scale : 1.0f / 11.313708498984761f;  // 1/sqrt(128)
 }
 
+// Distillation target and loss (eq. 4-5): keys per KL partial, and the workspace layout.
+constexpr int kDistillKeyBlock = 512;
+struct DistillPlan {
+  int n_kb = 0;           // key blocks of kDistillKeyBlock per row
+  size_t lse2_off = 0;    // fp32 [R, L * hq]
+  size_t lse_i_off = 0;   // fp32 [R]
+  size_t part_off = 0;    // fp32 [R, n_kb]
+  size_t bytes = 0;
+};
+DistillPlan plan_distill(const clsa_dims* d, const clsa_rows* r);
+
 // ---- kernel launchers (defined in the .hip translation units) --------------------------------
 // All return hipSuccess-or-error as an int (0 = success) so this header needs no HIP include.
 struct RowsDev {
@@ -143,6 +154,9 @@ int launch_index_project(int batch, int d_idx, int d_model, int hkv, int64_t tot
                          const uint16_t* wq, const uint16_t* wk, const int32_t* cu, uint16_t* q_idx, uint16_t* k_idx,
                          const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_cache, uint16_t* v_cache,
                          void* stream);
+int launch_distill(const RowsDev& rows, int64_t total_tokens, int L, int hq, int hkv, float scale, const uint16_t* q,
+                   int64_t q_stride, const uint16_t* k, const float* scores, int64_t ld, float* kl, float* loss,
+                   void* ws, const DistillPlan& plan, void* stream);
 const char* device_error_string(int err);
 
 }  // namespace clsa

@@ -1,0 +1,427 @@
+// The multi-layer distillation target and loss (picx.dev summary of "You Only Index Once",
+// Methodology, Multi-Layer Distillation, eq. 4-5): for every prefill position t,
+//   A_t = 1/(L Hq) sum over layers l and query heads h of softmax_j(q_t^(l,h) . k_j^(g(h)) * scale)
+//   KL_t = KL(A_t || softmax_j(I_t)) = sum_j A_tj (ln A_tj - ln softmax(I_t)_j),   j = 0..t,
+// and the loss, the mean of KL_t over the positions.  The attention scale is the layers' own
+// 1/sqrt(head_dim) and KV head g(h) = floor(h Hkv / Hq), as in the attention of the step.
+//
+// A_t needs every (layer, head) distribution normalised before they are summed, so there are
+// two passes over the keys, both on bf16 MFMA (16x16x32, fp32 accumulate) with the exp2-domain
+// softmax of the attention kernel:
+//  1. k_distill_stats: the log2 normaliser of each (position, layer, head).  Workgroup = 16
+//     positions x up to 32 (layer, head) pairs of one KV head; each wave keeps 4 pairs x 16
+//     positions of queries in registers, the KV head's keys stream through LDS in 64-key tiles,
+//     S^T = K Q^T, and the running max and sum stay in the lane that owns the query column
+//     (the max is raised lazily, only past a growth of 2^8).
+//  2. k_distill_kl: A over a tile of 64 positions x 512 keys.  Each wave keeps its 64 keys of
+//     the current KV head in registers; the (layer, head) pairs' query blocks stream through LDS
+//     (double-buffered), and exp2(s * c - lse2) is added into lane-local accumulators, so the
+//     sum over the L * Hq pairs needs no exchange.  The tile's KL terms are then summed in a
+//     fixed order into one partial per (position, 512-key block).
+// k_row_lse gives the log-sum-exp of each row of I, and k_distill_reduce sums the partials of
+// every position in key order and the loss in position order, so the results do not depend on
+// timing.  The exp2 of every score in both passes, not the matrix cores, bounds the time: a
+// wave issues one v_exp_f32 per score, against 1/16 of a 16x16x32 MFMA.
+#include "device_common.h"
+
+namespace clsa {
+
+namespace {
+
+constexpr int kDstWaves = 8;
+constexpr int kDstThreads = 64 * kDstWaves;
+constexpr int kStatRows = 16;                          // positions per stats workgroup
+constexpr int kStatPairsPerWave = 4;
+constexpr int kStatPairs = kDstWaves * kStatPairsPerWave;
+constexpr int kKlRows = 64;                             // positions per KL workgroup
+constexpr int kKlKeysPerWave = 64;
+constexpr int kKlKeys = kDstWaves * kKlKeysPerWave;     // keys per KL workgroup
+static_assert(kKlKeys == kDistillKeyBlock, "key block of the KL partials");
+constexpr int kTileKeys = 64;
+constexpr int kTileBytes = kTileKeys * CLSA_HEAD_DIM * 2;  // 16 KB: 64 rows of 256 bytes
+constexpr float kLn2 = 0.69314718055994531f;
+constexpr float kRescaleLog2 = 8.f;
+
+struct DistillArgs {
+  int pos0, n_rows, seq;  // rows: positions pos0 .. pos0 + n_rows - 1 of sequence seq
+  const int32_t* cu;
+  int64_t total_tokens;   // rows of the cache; no key read goes past it
+  int L, hq, hkv, group, pairs_per_g, n_kb;
+  float c;                // softmax scale * log2(e)
+  const uint16_t* q;      // row i at q + i * q_stride: [L, hq, 128]
+  int64_t q_stride;
+  const uint16_t* k;      // [T, hkv, 128]
+  const float* scores;    // [n_rows, ld]
+  int64_t ld;
+  float* lse2;            // [n_rows, L * hq]: log2 of each (row, layer, head) softmax normaliser
+  float* lse_i;           // [n_rows]: natural log-sum-exp of the row's scores
+  float* part;            // [n_rows, n_kb]
+  float* kl;              // [n_rows]
+  float* loss;            // [1] or null
+};
+
+// Byte offset, in a tile of 64 rows x 128 bf16, of the 16-byte chunk `chunk` of row `row`: chunk
+// slot chunk ^ (row & 15), so that row stores and 16-lane fragment reads spread over the banks.
+__device__ __forceinline__ int tile_off(int row, int chunk) { return row * 256 + ((chunk ^ (row & 15)) << 4); }
+
+// ---------------------------------------------------------------------------------------------
+// log-sum-exp of each row of the scores (natural log), over the row's visible tokens
+__global__ __launch_bounds__(256) void k_row_lse(DistillArgs a) {
+  __shared__ float red[4];
+  const int i = blockIdx.x;
+  const int n = a.pos0 + i + 1;
+  const float* s = a.scores + (int64_t)i * a.ld;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float mx = -INFINITY;
+  for (int j = threadIdx.x; j < n; j += 256) mx = fmaxf(mx, s[j]);
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  float sum = 0.f;
+  for (int j = threadIdx.x; j < n; j += 256) sum += __builtin_amdgcn_exp2f((s[j] - mx) * 1.4426950408889634f);
+  for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
+  if (lane == 0) red[wave] = sum;
+  __syncthreads();
+  if (threadIdx.x == 0) a.lse_i[i] = mx + __builtin_amdgcn_logf((red[0] + red[1]) + (red[2] + red[3])) * kLn2;
+}
+
+// ---------------------------------------------------------------------------------------------
+// pass 1: log2 normaliser of every (position, layer, head)
+__global__ __launch_bounds__(kDstThreads) void k_distill_stats(DistillArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kTileKeys * CLSA_HEAD_DIM];
+  char* const lds_bytes = reinterpret_cast<char*>(lds);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, grp = lane >> 4;
+  const int r0 = blockIdx.x * kStatRows;
+  const int g = blockIdx.y % a.hkv, chunk = blockIdx.y / a.hkv;
+  const int last_row = (r0 + kStatRows < a.n_rows ? r0 + kStatRows : a.n_rows) - 1;
+  const int t_lo = a.pos0 + r0, t_hi = a.pos0 + last_row;  // keys 0 .. t_hi are read
+  const int64_t seq_base = a.cu[a.seq];
+  const int key_cap = (int)min((int64_t)t_hi, a.total_tokens - 1 - seq_base);  // loads stay in the cache
+  // this lane's query column: position t of row r0 + l16 (rows past the block repeat the last)
+  const int row = r0 + l16 <= last_row ? r0 + l16 : last_row;
+  const int t = a.pos0 + row;
+  const int p0 = chunk * kStatPairs + wave * kStatPairsPerWave;
+  const bool wave_active = p0 < a.pairs_per_g;
+  bf16x8_t qf[kStatPairsPerWave][4];
+  int qh[kStatPairsPerWave];  // layer * hq + head of each query block, -1 when past the pairs
+#pragma unroll
+  for (int qb = 0; qb < kStatPairsPerWave; ++qb) {
+    const int p = p0 + qb;
+    qh[qb] = p < a.pairs_per_g ? (p / a.group) * a.hq + g * a.group + p % a.group : -1;
+    const uint16_t* qp = a.q + (int64_t)row * a.q_stride + (int64_t)(qh[qb] < 0 ? 0 : qh[qb]) * CLSA_HEAD_DIM;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (qh[qb] >= 0) v = load16(qp + kk * 32 + grp * 8);
+      qf[qb][kk] = bitcast<bf16x8_t>(v);
+    }
+  }
+  // loader: 64 keys x 16 chunks per tile, two pieces per thread; keys past t_hi re-read t_hi
+  const int64_t kbase = (seq_base * a.hkv + g) * CLSA_HEAD_DIM;
+  int lkey[2], lchunk[2], soff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int piece = threadIdx.x + i * kDstThreads;
+    lkey[i] = piece >> 4;
+    lchunk[i] = piece & 15;
+    soff[i] = tile_off(lkey[i], lchunk[i]);
+  }
+  uint4 rk[2];
+  auto load_tile = [&](int tile) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      int key = tile * kTileKeys + lkey[i];
+      key = key < key_cap ? key : key_cap;
+      rk[i] = load16(a.k + kbase + (int64_t)key * a.hkv * CLSA_HEAD_DIM + lchunk[i] * 8);
+    }
+  };
+  int koff[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) koff[kk] = tile_off(l16, 4 * kk + grp);
+  float m_run[kStatPairsPerWave], l_run[kStatPairsPerWave];
+#pragma unroll
+  for (int qb = 0; qb < kStatPairsPerWave; ++qb) {
+    m_run[qb] = -INFINITY;
+    l_run[qb] = 0.f;
+  }
+  const float c = a.c;
+  const int ntiles = t_hi / kTileKeys + 1;
+  load_tile(0);
+  for (int tile = 0; tile < ntiles; ++tile) {
+    char* tb = lds_bytes + (tile & 1) * kTileBytes;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(tb + soff[i]) = rk[i];
+    __syncthreads();  // one barrier per tile: buffer tile & 1 was last read two tiles ago
+    if (tile + 1 < ntiles) load_tile(tile + 1);
+    if (!wave_active) continue;
+    floatx4_t s[kStatPairsPerWave][4];
+#pragma unroll
+    for (int qb = 0; qb < kStatPairsPerWave; ++qb)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) s[qb][mt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const uint4 av = *reinterpret_cast<const uint4*>(tb + koff[kk] + mt * 4096);
+#pragma unroll
+        for (int qb = 0; qb < kStatPairsPerWave; ++qb)
+          s[qb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8_t>(av), qf[qb][kk], s[qb][mt], 0, 0, 0);
+      }
+    // s[qb][mt][j]: q . k of key tile * 64 + 16 mt + 4 grp + j, query column l16; keys past the
+    // column's position are masked (only tiles reaching past the block's first position have any)
+    if (tile * kTileKeys + kTileKeys - 1 > t_lo) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (tile * kTileKeys + mt * 16 + grp * 4 + j > t)
+#pragma unroll
+            for (int qb = 0; qb < kStatPairsPerWave; ++qb) s[qb][mt][j] = -INFINITY;
+    }
+#pragma unroll
+    for (int qb = 0; qb < kStatPairsPerWave; ++qb) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) mx = fmaxf(fmaxf(mx, fmaxf(s[qb][mt][0], s[qb][mt][1])), fmaxf(s[qb][mt][2], s[qb][mt][3]));
+      if (__any(mx * c > m_run[qb] + kRescaleLog2)) {
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float m_new = fmaxf(m_run[qb], mx * c);
+        l_run[qb] *= __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+        m_run[qb] = m_new;
+      }
+      float sum = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sum += __builtin_amdgcn_exp2f(fmaf(s[qb][mt][j], c, -m_run[qb]));
+      l_run[qb] += sum;
+    }
+  }
+  if (!wave_active) return;
+#pragma unroll
+  for (int qb = 0; qb < kStatPairsPerWave; ++qb) {
+    float l = l_run[qb] + __shfl_xor(l_run[qb], 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    if (grp == 0 && r0 + l16 <= last_row && qh[qb] >= 0)
+      a.lse2[(int64_t)(r0 + l16) * a.L * a.hq + qh[qb]] = m_run[qb] + __builtin_amdgcn_logf(l);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// pass 2: A over 64 positions x 512 keys, then the tile's KL terms per position
+__global__ __launch_bounds__(kDstThreads, 1) void k_distill_kl(DistillArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t qlds[2 * kKlRows * CLSA_HEAD_DIM];
+  __shared__ float llds[2][kKlRows];
+  __shared__ float red[kDstWaves][kKlRows];
+  char* const q_bytes = reinterpret_cast<char*>(qlds);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, grp = lane >> 4;
+  const int kb = blockIdx.x, r0 = blockIdx.y * kKlRows;
+  const int last_row = (r0 + kKlRows < a.n_rows ? r0 + kKlRows : a.n_rows) - 1;
+  const int t_lo = a.pos0 + r0, t_hi = a.pos0 + last_row;
+  const int k0 = kb * kKlKeys;
+  if (k0 > t_hi) return;  // the whole key block lies past every position of the tile
+  const int wk0 = k0 + wave * kKlKeysPerWave;
+  const bool wave_active = wk0 <= t_hi;
+  const int P = a.L * a.hq;
+  // query-block loader: 64 rows x 16 chunks, two pieces per thread
+  int lrow[2], lchunk[2], soff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int piece = threadIdx.x + i * kDstThreads;
+    lrow[i] = piece >> 4;
+    lchunk[i] = piece & 15;
+    soff[i] = tile_off(lrow[i], lchunk[i]);
+    if (r0 + lrow[i] > last_row) lrow[i] = last_row - r0;
+  }
+  uint4 rq[2];
+  float rl = 0.f;
+  // pair index pi = g * pairs_per_g + p  ->  (layer p / group, head g * group + p % group)
+  auto pair_qh = [&](int pi) {
+    const int g = pi / a.pairs_per_g, p = pi % a.pairs_per_g;
+    return (p / a.group) * a.hq + g * a.group + p % a.group;
+  };
+  auto load_pair = [&](int pi) {
+    const int qh = pair_qh(pi);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      rq[i] = load16(a.q + (int64_t)(r0 + lrow[i]) * a.q_stride + (int64_t)qh * CLSA_HEAD_DIM + lchunk[i] * 8);
+    if (threadIdx.x < kKlRows) {
+      const int rr = r0 + threadIdx.x <= last_row ? r0 + threadIdx.x : last_row;
+      rl = a.lse2[(int64_t)rr * P + qh];
+    }
+  };
+  int qoff[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) qoff[kk] = tile_off(l16, 4 * kk + grp);
+  // this wave's keys: rows wk0 + 16 mt + l16 of the A operand (clamped to t_hi for the loads)
+  const int64_t seq_base = a.cu[a.seq];
+  const int key_cap = (int)min((int64_t)t_hi, a.total_tokens - 1 - seq_base);  // loads stay in the cache
+  const int64_t kbase = seq_base * a.hkv * CLSA_HEAD_DIM;
+  int64_t krow[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    int key = wk0 + mt * 16 + l16;
+    key = key < key_cap ? key : key_cap;
+    krow[mt] = kbase + (int64_t)key * a.hkv * CLSA_HEAD_DIM + grp * 8;
+  }
+  bf16x8_t kf[4][4];
+  floatx4_t abar[4][4];  // [mt][tq]: key wk0 + 16 mt + 4 grp + j, row r0 + 16 tq + l16
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int tq = 0; tq < 4; ++tq) abar[mt][tq] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  const float c = a.c;
+  load_pair(0);
+  for (int pi = 0; pi < P; ++pi) {
+    const int buf = pi & 1;
+    char* qb = q_bytes + buf * kTileBytes;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(qb + soff[i]) = rq[i];
+    if (threadIdx.x < kKlRows) llds[buf][threadIdx.x] = rl;
+    if (wave_active && pi % a.pairs_per_g == 0) {  // a new KV head: this wave's 64 keys of it
+      const int g = pi / a.pairs_per_g;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) kf[mt][kk] = bitcast<bf16x8_t>(load16(a.k + krow[mt] + g * CLSA_HEAD_DIM + kk * 32));
+    }
+    __syncthreads();  // one barrier per pair: buffer buf was last read two pairs ago
+    if (pi + 1 < P) load_pair(pi + 1);
+    if (!wave_active) continue;
+    floatx4_t s[4][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int tq = 0; tq < 4; ++tq) s[mt][tq] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int tq = 0; tq < 4; ++tq)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const bf16x8_t qv = bitcast<bf16x8_t>(*reinterpret_cast<const uint4*>(qb + qoff[kk] + tq * 4096));
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) s[mt][tq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[mt][kk], qv, s[mt][tq], 0, 0, 0);
+      }
+    // keys past a position get meaningless values here; they are never read back
+#pragma unroll
+    for (int tq = 0; tq < 4; ++tq) {
+      const float lse = llds[buf][tq * 16 + l16];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) abar[mt][tq][j] += __builtin_amdgcn_exp2f(fmaf(s[mt][tq][j], c, -lse));
+    }
+  }
+  // KL terms of the tile: sum over the visible keys j of A (ln A - (I_j - lse_I))
+  const float inv = 1.f / (float)P;
+  float klp[4];
+#pragma unroll
+  for (int tq = 0; tq < 4; ++tq) {
+    klp[tq] = 0.f;
+    const int row = r0 + tq * 16 + l16;
+    if (!wave_active || row > last_row) continue;
+    const int t = a.pos0 + row;
+    const float lse_i = a.lse_i[row];
+    const float* srow = a.scores + (int64_t)row * a.ld;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const int key0 = wk0 + mt * 16 + grp * 4;
+      if (key0 > t) continue;
+      const float4 iv = *reinterpret_cast<const float4*>(srow + key0);
+      const float ivs[4] = {iv.x, iv.y, iv.z, iv.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float av = abar[mt][tq][j] * inv;
+        // weights below the smallest normal float add less than 1e-36 and are skipped, so the
+        // logarithm never meets a flushed denormal
+        if (key0 + j <= t && av >= 1.17549435e-38f)
+          klp[tq] += av * (__builtin_amdgcn_logf(av) * kLn2 - (ivs[j] - lse_i));
+      }
+    }
+  }
+#pragma unroll
+  for (int tq = 0; tq < 4; ++tq) {
+    float v = klp[tq] + __shfl_xor(klp[tq], 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    if (grp == 0) red[wave][tq * 16 + l16] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x < kKlRows && r0 + (int)threadIdx.x <= last_row) {
+    float v = red[0][threadIdx.x];
+#pragma unroll
+    for (int w = 1; w < kDstWaves; ++w) v += red[w][threadIdx.x];
+    a.part[(int64_t)(r0 + threadIdx.x) * a.n_kb + kb] = v;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// KL of every row (its partials in key order) and the loss (the rows in order)
+constexpr int kReduceThreads = 1024;
+__global__ __launch_bounds__(kReduceThreads) void k_distill_reduce(DistillArgs a) {
+  __shared__ float red[kReduceThreads / 64];
+  float mine = 0.f;
+  for (int i = threadIdx.x; i < a.n_rows; i += kReduceThreads) {
+    const int nkb = (a.pos0 + i) / kKlKeys + 1;
+    float v = 0.f;
+    for (int b = 0; b < nkb; ++b) v += a.part[(int64_t)i * a.n_kb + b];
+    a.kl[i] = v;
+    mine += v;
+  }
+  if (a.loss == nullptr) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int o = 32; o > 0; o >>= 1) mine += __shfl_xor(mine, o, 64);
+  if (lane == 0) red[wave] = mine;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float s = 0.f;
+    for (int w = 0; w < kReduceThreads / 64; ++w) s += red[w];
+    a.loss[0] = s / (float)a.n_rows;
+  }
+}
+
+}  // namespace
+
+int launch_distill(const RowsDev& rows, int64_t total_tokens, int L, int hq, int hkv, float scale, const uint16_t* q,
+                   int64_t q_stride, const uint16_t* k, const float* scores, int64_t ld, float* kl, float* loss,
+                   void* ws, const DistillPlan& plan, void* stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  DistillArgs a;
+  a.pos0 = rows.pos0;
+  a.n_rows = rows.n_rows;
+  a.seq = rows.seq;
+  a.cu = rows.cu;
+  a.total_tokens = total_tokens;
+  a.L = L;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.group = hq / hkv;
+  a.pairs_per_g = L * a.group;
+  a.n_kb = plan.n_kb;
+  a.c = scale * 1.4426950408889634f;
+  a.q = q;
+  a.q_stride = q_stride;
+  a.k = k;
+  a.scores = scores;
+  a.ld = ld;
+  a.lse2 = reinterpret_cast<float*>(w + plan.lse2_off);
+  a.lse_i = reinterpret_cast<float*>(w + plan.lse_i_off);
+  a.part = reinterpret_cast<float*>(w + plan.part_off);
+  a.kl = kl;
+  a.loss = loss;
+  const int chunks = (a.pairs_per_g + kStatPairs - 1) / kStatPairs;
+  hipLaunchKernelGGL(k_row_lse, dim3((unsigned)rows.n_rows), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_distill_stats, dim3((unsigned)((rows.n_rows + kStatRows - 1) / kStatRows), (unsigned)(hkv * chunks)),
+                     dim3(kDstThreads), 0, s, a);
+  hipLaunchKernelGGL(k_distill_kl, dim3((unsigned)plan.n_kb, (unsigned)((rows.n_rows + kKlRows - 1) / kKlRows)),
+                     dim3(kDstThreads), 0, s, a);
+  hipLaunchKernelGGL(k_distill_reduce, dim3(1), dim3(kReduceThreads), 0, s, a);
+  return (int)hipGetLastError();
+}
+
+}  // namespace clsa

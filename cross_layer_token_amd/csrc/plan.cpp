@@ -181,6 +181,21 @@ size_t topk_workspace(const clsa_dims* d, const clsa_rows* r) {
 
 size_t attn_workspace(const AttnPlan& a) { return ticket_region(a.tickets) + a.part_bytes; }
 
+DistillPlan plan_distill(const clsa_dims* d, const clsa_rows* r) {
+  DistillPlan p;
+  const size_t R = (size_t)r->n_rows;
+  p.n_kb = (r->max_row_len + kDistillKeyBlock - 1) / kDistillKeyBlock;
+  size_t off = 0;
+  p.lse2_off = off;
+  off = align_up(off + R * d->n_layers * d->hq * 4, 256);
+  p.lse_i_off = off;
+  off = align_up(off + R * 4, 256);
+  p.part_off = off;
+  off = align_up(off + R * p.n_kb * 4, 256);
+  p.bytes = off;
+  return p;
+}
+
 size_t workspace_bytes(const clsa_dims* d, const clsa_rows* r, int schedule, int prefill_chunk_rows) {
   size_t m = topk_workspace(d, r);
   // a standalone clsa_sparse_attn call may cover any number of layers up to L

@@ -199,6 +199,32 @@ clsa_status clsa_index_project(const clsa_dims* dims, const clsa_rows* rows, int
                                clsa_bf16* q_idx, clsa_bf16* k_idx, const clsa_bf16* k_new, const clsa_bf16* v_new,
                                clsa_bf16* k_cache, clsa_bf16* v_cache, clsa_stream stream);
 
+/*
+ * The multi-layer distillation target and loss of the shared index (picx.dev summary,
+ * Methodology, Multi-Layer Distillation, eq. 4-5), PREFILL rows only.  Row i is position
+ * t = pos0 + i of sequence `seq` and sees tokens j = 0..t:
+ *   A_t[j] = 1/(L hq) sum_{l < L, h < hq} softmax_j(q[i, l, h, :] . k_cache[cu[seq] + j, g(h), :] * scale)
+ *   kl[i]  = KL(A_t || softmax_j(scores[i, j])) = sum_j A_t[j] (ln A_t[j] - ln softmax(scores[i])_j)
+ *   *loss  = (1 / n_rows) sum_i kl[i]                                   (when loss != NULL)
+ * with scale and g(h) = floor(h * hkv / hq) as in clsa_sparse_attn (the layers' own attention
+ * distributions).  L = dims.n_layers.
+ *   q       row i at q + i * q_row_stride, laid out [L, hq, 128] bf16 (q_row_stride >= L hq 128,
+ *           a multiple of 8)
+ *   k_cache [T, hkv, 128] bf16 (only K is read)
+ *   scores  [n_rows, ld_scores] fp32: the routing scores I of the same rows, as clsa_index_scores
+ *           writes them (ld_scores >= max_row_len, a multiple of 4)
+ *   kl      [n_rows] fp32 (output), loss: one fp32 (output, optional)
+ * fp32 softmax statistics and sums on bf16 products; every sum runs in an order fixed by the
+ * sizes, so the results do not depend on timing.  The stop-gradient of eq. 5 does not change
+ * these values.  Workspace: >= clsa_distill_workspace_bytes(dims, rows); its content on entry
+ * does not matter.  Returns CLSA_ERR_UNSUPPORTED for DECODE rows.
+ */
+size_t clsa_distill_workspace_bytes(const clsa_dims* dims, const clsa_rows* rows);
+clsa_status clsa_distill_kl(const clsa_dims* dims, const clsa_rows* rows, const clsa_bf16* q, int64_t q_row_stride,
+                            const clsa_bf16* k_cache, const int32_t* cu_seqlens, const float* scores,
+                            int64_t ld_scores, float* kl, float* loss, void* workspace, size_t workspace_bytes,
+                            clsa_stream stream);
+
 /* Everything one step reads and writes (all device pointers). */
 typedef struct clsa_step_args {
   const clsa_bf16* q_idx;     /* [R, d_idx]                                               */

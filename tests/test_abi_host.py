@@ -172,6 +172,26 @@ def test_index_project_rejects():
     assert call(rows_=_rows(cu_seqlens_host=[0, 0, 1500])) == B.ERR_INVALID_ARGUMENT
 
 
+def test_distill_rejects():
+    dims = _dims()
+    pre = B.make_rows(B.MODE_PREFILL, 100, 100, 1500, seq=0, pos0=0, cu_seqlens_host=[0, 1000, 1500])
+    nws = B.distill_workspace_bytes(dims, pre)
+    assert nws >= 100 * (2 * 8 + 1 + 1) * 4
+
+    def call(rows_=pre, q=FAKE, qs=2 * 8 * 128, kc=FAKE, sc=FAKE, ld=128, kl=FAKE, loss=None, ws=FAKE, wsz=nws):
+        return B.LIB.clsa_distill_kl(ctypes.byref(dims), ctypes.byref(rows_), q, qs, kc, FAKE, sc, ld, kl, loss, ws,
+                                     wsz, None)
+    assert call(rows_=_rows()) == B.ERR_UNSUPPORTED and "PREFILL" in B.last_error()
+    assert B.LIB.clsa_distill_workspace_bytes(ctypes.byref(dims), ctypes.byref(_rows())) == 0
+    assert call(q=None) == B.ERR_INVALID_ARGUMENT and "q is NULL" in B.last_error()
+    assert call(kc=FAKE + 4) == B.ERR_INVALID_ARGUMENT and "aligned" in B.last_error()
+    assert call(qs=100) == B.ERR_INVALID_ARGUMENT
+    assert call(ld=64) == B.ERR_INVALID_ARGUMENT and "ld_scores" in B.last_error()
+    assert call(loss=FAKE + 2) == B.ERR_INVALID_ARGUMENT and "loss" in B.last_error()
+    assert call(wsz=nws - 1) == B.ERR_WORKSPACE
+    assert call(ws=None) == B.ERR_WORKSPACE
+
+
 def test_workspace_sizes_cover_every_call():
     # 128K decode: candidate lists dominate; per-layer schedule adds the two compact buffers
     dims = B.make_dims(16, 128, 2048, 16, 32, 8)
