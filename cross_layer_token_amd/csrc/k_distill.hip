@@ -33,9 +33,11 @@ constexpr int kDstThreads = 64 * kDstWaves;
 constexpr int kStatRows = 16;                          // positions per stats workgroup
 constexpr int kStatPairsPerWave = 4;
 constexpr int kStatPairs = kDstWaves * kStatPairsPerWave;
+constexpr int kStatTilesPerStep = 2;                    // 64-key tiles per LDS step
 constexpr int kKlRows = 64;                             // positions per KL workgroup
 constexpr int kKlKeysPerWave = 64;
 constexpr int kKlKeys = kDstWaves * kKlKeysPerWave;     // keys per KL workgroup
+constexpr int kKlPairsPerStep = 2;                       // (layer, head) query blocks per LDS step
 static_assert(kKlKeys == kDistillKeyBlock, "key block of the KL partials");
 constexpr int kTileKeys = 64;
 constexpr int kTileBytes = kTileKeys * CLSA_HEAD_DIM * 2;  // 16 KB: 64 rows of 256 bytes
@@ -90,7 +92,7 @@ __global__ __launch_bounds__(256) void k_row_lse(DistillArgs a) {
 // ---------------------------------------------------------------------------------------------
 // pass 1: log2 normaliser of every (position, layer, head)
 __global__ __launch_bounds__(kDstThreads) void k_distill_stats(DistillArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kTileKeys * CLSA_HEAD_DIM];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kStatTilesPerStep * kTileKeys * CLSA_HEAD_DIM];
   char* const lds_bytes = reinterpret_cast<char*>(lds);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, grp = lane >> 4;
@@ -129,14 +131,16 @@ __global__ __launch_bounds__(kDstThreads) void k_distill_stats(DistillArgs a) {
     lchunk[i] = piece & 15;
     soff[i] = tile_off(lkey[i], lchunk[i]);
   }
-  uint4 rk[2];
-  auto load_tile = [&](int tile) {
+  uint4 rk[kStatTilesPerStep][2];
+  auto load_step = [&](int st) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      int key = tile * kTileKeys + lkey[i];
-      key = key < key_cap ? key : key_cap;
-      rk[i] = load16(a.k + kbase + (int64_t)key * a.hkv * CLSA_HEAD_DIM + lchunk[i] * 8);
-    }
+    for (int u = 0; u < kStatTilesPerStep; ++u)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        int key = (st * kStatTilesPerStep + u) * kTileKeys + lkey[i];
+        key = key < key_cap ? key : key_cap;
+        rk[u][i] = load16(a.k + kbase + (int64_t)key * a.hkv * CLSA_HEAD_DIM + lchunk[i] * 8);
+      }
   };
   int koff[4];
 #pragma unroll
@@ -148,29 +152,30 @@ __global__ __launch_bounds__(kDstThreads) void k_distill_stats(DistillArgs a) {
     l_run[qb] = 0.f;
   }
   const float c = a.c;
-  const int ntiles = t_hi / kTileKeys + 1;
-  load_tile(0);
-  for (int tile = 0; tile < ntiles; ++tile) {
-    char* tb = lds_bytes + (tile & 1) * kTileBytes;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(tb + soff[i]) = rk[i];
-    __syncthreads();  // one barrier per tile: buffer tile & 1 was last read two tiles ago
-    if (tile + 1 < ntiles) load_tile(tile + 1);
-    if (!wave_active) continue;
+  // One 64-key tile: S^T = K Q^T for the wave's 4 pairs x 16 positions, then the online max and
+  // sum of each query column.
+  auto compute_tile = [&](const char* tb, int tile) {
     floatx4_t s[kStatPairsPerWave][4];
 #pragma unroll
     for (int qb = 0; qb < kStatPairsPerWave; ++qb)
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) s[qb][mt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    // one block of 16 keys at a time, the next block's K fragments read from LDS meanwhile
+    uint4 av[2][4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int kk = 0; kk < 4; ++kk) av[0][kk] = *reinterpret_cast<const uint4*>(tb + koff[kk]);
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const uint4 av = *reinterpret_cast<const uint4*>(tb + koff[kk] + mt * 4096);
+    for (int mt = 0; mt < 4; ++mt) {
+      if (mt + 1 < 4) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) av[(mt + 1) & 1][kk] = *reinterpret_cast<const uint4*>(tb + koff[kk] + (mt + 1) * 4096);
+      }
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
         for (int qb = 0; qb < kStatPairsPerWave; ++qb)
-          s[qb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8_t>(av), qf[qb][kk], s[qb][mt], 0, 0, 0);
-      }
+          s[qb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8_t>(av[mt & 1][kk]), qf[qb][kk], s[qb][mt], 0, 0, 0);
+    }
     // s[qb][mt][j]: q . k of key tile * 64 + 16 mt + 4 grp + j, query column l16; keys past the
     // column's position are masked (only tiles reaching past the block's first position have any)
     if (tile * kTileKeys + kTileKeys - 1 > t_lo) {
@@ -201,6 +206,26 @@ __global__ __launch_bounds__(kDstThreads) void k_distill_stats(DistillArgs a) {
         for (int j = 0; j < 4; ++j) sum += __builtin_amdgcn_exp2f(fmaf(s[qb][mt][j], c, -m_run[qb]));
       l_run[qb] += sum;
     }
+  };
+  // steps of kStatTilesPerStep tiles: the next step is loaded while this one is computed, and the
+  // workgroup meets at one barrier per step
+  const int ntiles = t_hi / kTileKeys + 1;
+  const int steps = (ntiles + kStatTilesPerStep - 1) / kStatTilesPerStep;
+  load_step(0);
+  for (int st = 0; st < steps; ++st) {
+    char* sb = lds_bytes + (st & 1) * kStatTilesPerStep * kTileBytes;
+#pragma unroll
+    for (int u = 0; u < kStatTilesPerStep; ++u)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(sb + u * kTileBytes + soff[i]) = rk[u][i];
+    __syncthreads();  // one barrier per step: buffer st & 1 was last read two steps ago
+    if (st + 1 < steps) load_step(st + 1);
+    if (!wave_active) continue;
+#pragma unroll
+    for (int u = 0; u < kStatTilesPerStep; ++u) {
+      const int tile = st * kStatTilesPerStep + u;
+      if (tile < ntiles) compute_tile(sb + u * kTileBytes, tile);
+    }
   }
   if (!wave_active) return;
 #pragma unroll
@@ -215,15 +240,17 @@ __global__ __launch_bounds__(kDstThreads) void k_distill_stats(DistillArgs a) {
 // ---------------------------------------------------------------------------------------------
 // pass 2: A over 64 positions x 512 keys, then the tile's KL terms per position
 __global__ __launch_bounds__(kDstThreads, 1) void k_distill_kl(DistillArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t qlds[2 * kKlRows * CLSA_HEAD_DIM];
-  __shared__ float llds[2][kKlRows];
+  // two steps of kKlPairsPerStep (layer, head) query blocks: the next step is loaded while this
+  // one is computed, and the workgroup meets at one barrier per step
+  __shared__ __attribute__((aligned(16))) uint16_t qlds[2 * kKlPairsPerStep * kKlRows * CLSA_HEAD_DIM];
+  __shared__ float llds[2][kKlPairsPerStep][kKlRows];
   __shared__ float red[kDstWaves][kKlRows];
   char* const q_bytes = reinterpret_cast<char*>(qlds);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, grp = lane >> 4;
   const int kb = blockIdx.x, r0 = blockIdx.y * kKlRows;
   const int last_row = (r0 + kKlRows < a.n_rows ? r0 + kKlRows : a.n_rows) - 1;
-  const int t_lo = a.pos0 + r0, t_hi = a.pos0 + last_row;
+  const int t_hi = a.pos0 + last_row;
   const int k0 = kb * kKlKeys;
   if (k0 > t_hi) return;  // the whole key block lies past every position of the tile
   const int wk0 = k0 + wave * kKlKeysPerWave;
@@ -239,27 +266,31 @@ __global__ __launch_bounds__(kDstThreads, 1) void k_distill_kl(DistillArgs a) {
     soff[i] = tile_off(lrow[i], lchunk[i]);
     if (r0 + lrow[i] > last_row) lrow[i] = last_row - r0;
   }
-  uint4 rq[2];
-  float rl = 0.f;
+  uint4 rq[kKlPairsPerStep][2];
+  float rl[kKlPairsPerStep];
   // pair index pi = g * pairs_per_g + p  ->  (layer p / group, head g * group + p % group)
   auto pair_qh = [&](int pi) {
     const int g = pi / a.pairs_per_g, p = pi % a.pairs_per_g;
     return (p / a.group) * a.hq + g * a.group + p % a.group;
   };
-  auto load_pair = [&](int pi) {
-    const int qh = pair_qh(pi);
+  auto load_step = [&](int st) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      rq[i] = load16(a.q + (int64_t)(r0 + lrow[i]) * a.q_stride + (int64_t)qh * CLSA_HEAD_DIM + lchunk[i] * 8);
-    if (threadIdx.x < kKlRows) {
-      const int rr = r0 + threadIdx.x <= last_row ? r0 + threadIdx.x : last_row;
-      rl = a.lse2[(int64_t)rr * P + qh];
+    for (int u = 0; u < kKlPairsPerStep; ++u) {
+      const int pi = st * kKlPairsPerStep + u;
+      const int qh = pair_qh(pi < P ? pi : P - 1);  // past the last pair: re-read it, unused
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        rq[u][i] = load16(a.q + (int64_t)(r0 + lrow[i]) * a.q_stride + (int64_t)qh * CLSA_HEAD_DIM + lchunk[i] * 8);
+      if (threadIdx.x < kKlRows) {
+        const int rr = r0 + threadIdx.x <= last_row ? r0 + threadIdx.x : last_row;
+        rl[u] = a.lse2[(int64_t)rr * P + qh];
+      }
     }
   };
   int qoff[4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) qoff[kk] = tile_off(l16, 4 * kk + grp);
-  // this wave's keys: rows wk0 + 16 mt + l16 of the A operand (clamped to t_hi for the loads)
+  // this wave's keys: rows wk0 + 16 mt + l16 of the A operand (clamped for the loads)
   const int64_t seq_base = a.cu[a.seq];
   const int key_cap = (int)min((int64_t)t_hi, a.total_tokens - 1 - seq_base);  // loads stay in the cache
   const int64_t kbase = seq_base * a.hkv * CLSA_HEAD_DIM;
@@ -277,44 +308,62 @@ __global__ __launch_bounds__(kDstThreads, 1) void k_distill_kl(DistillArgs a) {
 #pragma unroll
     for (int tq = 0; tq < 4; ++tq) abar[mt][tq] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   const float c = a.c;
-  load_pair(0);
-  for (int pi = 0; pi < P; ++pi) {
-    const int buf = pi & 1;
-    char* qb = q_bytes + buf * kTileBytes;
+  // One (layer, head) pair: S^T = K Q^T for the wave's 64 keys x 64 positions, and
+  // exp2(s c - lse2) into the accumulators.  Keys past a position get meaningless values here;
+  // they are never read back.
+  auto compute_pair = [&](const char* qb, const float* lse_row) {
+    // one block of 16 positions at a time, the next block's Q fragments read from LDS meanwhile
+    bf16x8_t qv[2][4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(qb + soff[i]) = rq[i];
-    if (threadIdx.x < kKlRows) llds[buf][threadIdx.x] = rl;
-    if (wave_active && pi % a.pairs_per_g == 0) {  // a new KV head: this wave's 64 keys of it
-      const int g = pi / a.pairs_per_g;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) kf[mt][kk] = bitcast<bf16x8_t>(load16(a.k + krow[mt] + g * CLSA_HEAD_DIM + kk * 32));
-    }
-    __syncthreads();  // one barrier per pair: buffer buf was last read two pairs ago
-    if (pi + 1 < P) load_pair(pi + 1);
-    if (!wave_active) continue;
-    floatx4_t s[4][4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int tq = 0; tq < 4; ++tq) s[mt][tq] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int tq = 0; tq < 4; ++tq)
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8_t qv = bitcast<bf16x8_t>(*reinterpret_cast<const uint4*>(qb + qoff[kk] + tq * 4096));
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) s[mt][tq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[mt][kk], qv, s[mt][tq], 0, 0, 0);
-      }
-    // keys past a position get meaningless values here; they are never read back
+    for (int kk = 0; kk < 4; ++kk) qv[0][kk] = bitcast<bf16x8_t>(*reinterpret_cast<const uint4*>(qb + qoff[kk]));
 #pragma unroll
     for (int tq = 0; tq < 4; ++tq) {
-      const float lse = llds[buf][tq * 16 + l16];
+      if (tq + 1 < 4) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          qv[(tq + 1) & 1][kk] = bitcast<bf16x8_t>(*reinterpret_cast<const uint4*>(qb + qoff[kk] + (tq + 1) * 4096));
+      }
+      floatx4_t s[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) s[mt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) s[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[mt][kk], qv[tq & 1][kk], s[mt], 0, 0, 0);
+      const float lse = lse_row[tq * 16 + l16];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) abar[mt][tq][j] += __builtin_amdgcn_exp2f(fmaf(s[mt][tq][j], c, -lse));
+        for (int j = 0; j < 4; ++j) abar[mt][tq][j] += __builtin_amdgcn_exp2f(fmaf(s[mt][j], c, -lse));
+    }
+  };
+  const int steps = (P + kKlPairsPerStep - 1) / kKlPairsPerStep;
+  load_step(0);
+  for (int st = 0; st < steps; ++st) {
+    const int buf = st & 1;
+#pragma unroll
+    for (int u = 0; u < kKlPairsPerStep; ++u) {
+      char* qb = q_bytes + (buf * kKlPairsPerStep + u) * kTileBytes;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(qb + soff[i]) = rq[u][i];
+      if (threadIdx.x < kKlRows) llds[buf][u][threadIdx.x] = rl[u];
+    }
+    __syncthreads();  // one barrier per step: buffer buf was last read two steps ago
+    if (st + 1 < steps) load_step(st + 1);
+    if (!wave_active) continue;
+#pragma unroll
+    for (int u = 0; u < kKlPairsPerStep; ++u) {
+      const int pi = st * kKlPairsPerStep + u;
+      if (pi >= P) break;
+      if (pi % a.pairs_per_g == 0) {  // a new KV head: this wave's 64 keys of it
+        const int g = pi / a.pairs_per_g;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk)
+            kf[mt][kk] = bitcast<bf16x8_t>(load16(a.k + krow[mt] + g * CLSA_HEAD_DIM + kk * 32));
+      }
+      compute_pair(q_bytes + (buf * kKlPairsPerStep + u) * kTileBytes, llds[buf][u]);
     }
   }
   // KL terms of the tile: sum over the visible keys j of A (ln A - (I_j - lse_I))
