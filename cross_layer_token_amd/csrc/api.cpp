@@ -365,14 +365,23 @@ clsa_status clsa_step(const clsa_dims* dims, const clsa_rows* rows, const clsa_s
     if (e) return device_status(e, "clsa_step: index scores");
     int32_t* idx = a->idx + (int64_t)c0 * k;
     int32_t* count = a->count + c0;
-    e = launch_topk(rd, k, tp, scores, ld, idx, count, topk_ws, topk_tickets, have_hist, stream);
+    // the layer-batched decode step lets the attention workgroups finish the long-row selection
+    e = launch_topk(rd, k, tp, scores, ld, idx, count, topk_ws, topk_tickets, have_hist, stream, !sp.fused_select);
     if (e) return device_status(e, "clsa_step: top-k");
     const clsa_bf16* q = a->q + (int64_t)c0 * row_elems;
     clsa_bf16* out = a->out + (int64_t)c0 * row_elems;
     if (a->schedule == CLSA_SCHEDULE_LAYER_BATCHED) {
       const AttnPlan ap = plan_attn(dims, cr.n_rows, L, rows->n_rows);
+      SelectIn sel;
+      if (sp.fused_select) {
+        sel.slot = topk_ws + tp.slot_off;
+        sel.cnt = reinterpret_cast<const uint32_t*>(topk_ws + tp.cnt_off);
+        sel.rowinfo = reinterpret_cast<const uint32_t*>(topk_ws + tp.rowinfo_off);
+        sel.spans = tp.spans;
+      }
       e = launch_attn(rd, k, hq, hkv, L, scale, ap, q, row_elems, nullptr, nullptr, a->k_cache, a->v_cache, idx, count,
-                      out, row_elems, ws + sp.part_off, attn_tickets, true, stream);
+                      out, row_elems, ws + sp.part_off, attn_tickets, true, stream, sp.fused_select ? &sel : nullptr,
+                      idx, count);
       if (e) return device_status(e, "clsa_step: attention");
     } else {
       const AttnPlan ap = plan_attn(dims, cr.n_rows, 1, rows->n_rows);

@@ -28,8 +28,13 @@ constexpr int kIdxMinWorkgroups = 256;
 constexpr int kTopkBinBits = 11;
 constexpr int kTopkBins = 1 << kTopkBinBits;
 static_assert(kIdxChunkMax < 65536, "histogram partials hold uint16 counts");
-// Scores classified by one workgroup of the long-row select.
+// Scores classified by one workgroup of the long-row select, and the most spans of a row.
 constexpr int kSelectSpan = 8192;
+constexpr int kMaxSelectSpans = 2048;
+static_assert((int64_t)kSelectSpan * kMaxSelectSpans >= CLSA_MAX_ROW_LEN, "spans cover the longest row");
+// The layer-batched decode step may finish the long-row selection inside the attention
+// workgroups (each keeps its split's token ids in LDS) when a split holds at most this many keys.
+constexpr int kFusedMaxIds = 2048;
 // Keys per attention tile.
 constexpr int kAttnTile = 64;
 // Upper bound on the splits of the selected rows of one (row, KV head, query block).
@@ -57,6 +62,7 @@ struct TopkPlan {
   size_t cnt_off = 0;      // uint32 [R, spans]
   size_t slot_off = 0;     // uint2 [R, max_row_len]: per-span ordered lists (key, index)
   size_t list_off = 0;     // uint2 [R, max_row_len]: the concatenated list of the last workgroup
+  size_t rowinfo_off = 0;  // uint32 [R, 2]: first-level bin t1 and the count above it
   size_t bytes = 0;
   int tickets = 0;         // uint32 words of ticket memory needed (R when multi_wg)
 };
@@ -85,6 +91,7 @@ struct StepPlan {
   size_t topk_off = 0;
   size_t part_off = 0;
   size_t ksel_off = 0, vsel_off = 0, sel_bytes = 0;
+  bool fused_select = false;  // the attention workgroups finish the long-row selection
   size_t total = 0;
 };
 
@@ -140,8 +147,18 @@ int launch_index_scores_decode(const RowsDev& rows, int d_idx, int chunk, const 
 int launch_index_scores_prefill(const RowsDev& rows, int d_idx, const uint16_t* q_idx, const uint16_t* k_idx,
                                 float* scores, int64_t ld, uint32_t* clear, int n_clear, void* stream);
 // have_hist: the score kernel already wrote the histogram partials and cleared the tickets.
+// finish = false (long rows only): the select stops after writing the span lists and each row's
+// first-level bin; the attention launched with SelectIn finishes the selection.
 int launch_topk(const RowsDev& rows, int k, const TopkPlan& plan, const float* scores, int64_t ld,
-                int32_t* idx, int32_t* count, void* ws, uint32_t* tickets, bool have_hist, void* stream);
+                int32_t* idx, int32_t* count, void* ws, uint32_t* tickets, bool have_hist, void* stream,
+                bool finish = true);
+// Where the attention finds a row's unfinished selection (see launch_topk with finish = false).
+struct SelectIn {
+  const void* slot = nullptr;        // uint2 [R, max_row_len] span lists
+  const uint32_t* cnt = nullptr;     // [R, spans]
+  const uint32_t* rowinfo = nullptr; // [R, 2]
+  int spans = 0;
+};
 int launch_gather(const RowsDev& rows, int k, int hkv, const uint16_t* kc, const uint16_t* vc,
                   const int32_t* idx, const int32_t* count, uint16_t* ks, uint16_t* vs, void* stream);
 // tickets_clear: the tickets are known to be zero (cleared earlier in the call).
@@ -149,7 +166,8 @@ int launch_attn(const RowsDev& rows, int k, int hq, int hkv, int n_layers_call, 
                 const AttnPlan& plan, const uint16_t* q, int64_t q_stride, const uint16_t* ksel,
                 const uint16_t* vsel, const uint16_t* kc, const uint16_t* vc, const int32_t* idx,
                 const int32_t* count, uint16_t* out, int64_t o_stride, void* part, uint32_t* tickets,
-                bool tickets_clear, void* stream);
+                bool tickets_clear, void* stream, const SelectIn* sel = nullptr, int32_t* idx_out = nullptr,
+                int32_t* count_out = nullptr);
 int launch_index_project(int batch, int d_idx, int d_model, int hkv, int64_t total_tokens, const uint16_t* h,
                          const uint16_t* wq, const uint16_t* wk, const int32_t* cu, uint16_t* q_idx, uint16_t* k_idx,
                          const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_cache, uint16_t* v_cache,

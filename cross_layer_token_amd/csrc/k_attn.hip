@@ -14,7 +14,7 @@
 // are split over several workgroups, each writes fp32 partials (m, l, acc) with device-scope
 // stores and the last to arrive (atomic ticket) recombines them, so no separate pass is
 // launched and no workgroup needs a device-wide cache flush.
-#include "device_common.h"
+#include "select_common.h"
 
 namespace clsa {
 
@@ -41,6 +41,26 @@ struct AttnArgs {
   int64_t o_stride;
   float* part;         // [splits, R, hkv, qblocks, kAttnPartWG] in the lanes' layout
   uint32_t* tickets;   // [R, hkv, qblocks], zero on entry, reset by their last workgroup
+  // the row's unfinished selection (SELECT = true): span lists, their counts, t1 and the count
+  // above it; one workgroup of each row writes the finished selection to idx_out / count_out
+  const uint2* sel_slot;
+  const uint32_t* sel_cnt;
+  const uint32_t* sel_rowinfo;
+  int sel_spans;
+  int32_t* idx_out;
+  int32_t* count_out;
+};
+
+// LDS of the selection finished inside the workgroup (nothing when SELECT = false).
+template <bool SELECT>
+struct SelectLds {};
+template <>
+struct SelectLds<true> {
+  uint32_t hist[256];
+  int scan[2 * 2 * kAttnWaveThreads / 64];
+  int res[2];
+  int span_pre[kMaxSelectSpans + 1];
+  int32_t ids[kFusedMaxIds];  // this split's token ids, in selection order
 };
 
 // Four outputs scaled by inv, rounded to bf16 (round to nearest even) and stored as 8 bytes.
@@ -80,7 +100,10 @@ constexpr float kRescaleLog2 = 8.f;
 // Split partials fetched per round trip by the combining workgroup.
 constexpr int kCombineBatch = 4;
 
-template <bool FROM_CACHE, int TEAMS>
+// SELECT (with FROM_CACHE and TEAMS = 2): the workgroup first finishes the row's long-row
+// selection itself from the span lists of the select (see k_topk_select<false>) and keeps its
+// split's token ids in LDS, instead of reading them from idx.
+template <bool FROM_CACHE, int TEAMS, bool SELECT = false>
 __global__ __launch_bounds__(kAttnWaveThreads * TEAMS, 2 / TEAMS) void k_sparse_attn(AttnArgs a) {
   constexpr int STAGE = kAttnTiles * kAttnTile;
   constexpr int TILE_ELEMS = kAttnTile * CLSA_HEAD_DIM;
@@ -91,6 +114,9 @@ __global__ __launch_bounds__(kAttnWaveThreads * TEAMS, 2 / TEAMS) void k_sparse_
   // memory holds the team exchange at the end
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kAttnTiles * TILE_ELEMS];
   __shared__ int flag[1];
+  __shared__ SelectLds<SELECT> sl;
+  static_assert(!SELECT || (FROM_CACHE && TEAMS == 2), "the fused selection reads the cache with two teams");
+  static_assert(kListLds * sizeof(uint2) <= sizeof(lds), "the candidate list fits the tile buffers");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int team = wave / kAttnWavesPerTeam, tw = wave % kAttnWavesPerTeam;
   const int l16 = lane & 15, grp = lane >> 4;
@@ -100,7 +126,7 @@ __global__ __launch_bounds__(kAttnWaveThreads * TEAMS, 2 / TEAMS) void k_sparse_
   const int qb = bid % a.qblocks;
   const int g = bid / a.qblocks;
   const int r = blockIdx.y;
-  const int cnt = a.count[r];
+  const int cnt = SELECT ? min(a.k, row_len(a.rw, r)) : a.count[r];
   const int kbeg = split * a.kps;
   const int kend_raw = kbeg + a.kps;
   const int kend = kend_raw < cnt ? kend_raw : cnt;
@@ -133,6 +159,56 @@ __global__ __launch_bounds__(kAttnWaveThreads * TEAMS, 2 / TEAMS) void k_sparse_
   // outside the cache (valid selections are unchanged by it)
   const int tok_last = FROM_CACHE ? max(row_len(a.rw, r) - 1, 0) : 0;
   auto tok = [&](int id) { return id < 0 ? 0 : (id > tok_last ? tok_last : id); };
+  // The fused selection: this split's token ids (selection positions kbeg .. kend - 1) into LDS.
+  const int nk = kend > kbeg ? kend - kbeg : 0;
+  if constexpr (SELECT) {
+    const int n = row_len(a.rw, r);
+    if (n <= a.k) {  // every visible token is selected (the select wrote idx and count already)
+      for (int i = threadIdx.x; i < nk; i += blockDim.x) sl.ids[i] = kbeg + i;
+    } else {
+      const uint32_t t1 = a.sel_rowinfo[2 * r];
+      const int above1 = (int)a.sel_rowinfo[2 * r + 1];
+      const int nsp = (n + kSelectSpan - 1) / kSelectSpan;
+      const uint2* rslot = a.sel_slot + (int64_t)r * a.rw.max_row_len;
+      uint2* list_lds = reinterpret_cast<uint2*>(lds);  // the tiles are not in use yet
+      const int L = collect_candidates<kAttnWaveThreads * TEAMS, 2, kMaxSelectSpans>(
+          rslot, a.sel_cnt + (int64_t)r * a.sel_spans, nsp, n, sl.span_pre, sl.scan, list_lds, nullptr);
+      const bool writer = split == 0 && qb == 0 && g == 0;
+      int32_t* orow = a.idx_out + (int64_t)r * a.k;
+      auto emit = [&](int pos, int32_t t) {
+        if (pos >= kbeg && pos < kend) sl.ids[pos - kbeg] = t;
+        if (writer) orow[pos] = t;
+      };
+      if (L <= kListLds) {
+        refine_and_emit([&](int i) { return list_lds[i]; }, L, cnt, t1, above1, sl.hist, sl.scan, sl.res, emit);
+      } else {
+        // too many candidates for LDS: read them in place, span found by binary search
+        auto at = [&](int i) {
+          int lo = 0, hi = nsp - 1;
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (sl.span_pre[mid] <= i) lo = mid;
+            else hi = mid - 1;
+          }
+          return rslot[(int64_t)lo * kSelectSpan + (i - sl.span_pre[lo])];
+        };
+        refine_and_emit(at, L, cnt, t1, above1, sl.hist, sl.scan, sl.res, emit);
+      }
+      if (writer) {
+        for (int i = cnt + threadIdx.x; i < a.k; i += blockDim.x) orow[i] = -1;
+        if (threadIdx.x == 0) a.count_out[r] = cnt;
+      }
+    }
+    __syncthreads();  // the ids are complete, and the list in the tile buffers is read no more
+  }
+  auto sel_id = [&](int key) {  // token id at selection position key of this split (SELECT)
+    if constexpr (SELECT) {
+      const int p = key - kbeg;
+      return (p >= 0 && p < nk) ? sl.ids[p] : 0;
+    } else {
+      return key;
+    }
+  };
   // loader mapping: thread -> one 16-byte chunk of head_dim of keys 4 (ld_key4 % 16) + i (i < 4)
   // of the tiles ld_key4 / 16 + TEAMS * t (t < TPT)
   const int ld_chunk = threadIdx.x & 15;
@@ -151,7 +227,8 @@ __global__ __launch_bounds__(kAttnWaveThreads * TEAMS, 2 / TEAMS) void k_sparse_
     for (int i = 0; i < LPT; ++i) {
       const int key = kt + piece_key(i);
       ids[i] = key < klast ? key : klast;
-      if (FROM_CACHE) ids[i] = irow[ids[i]];  // clamped when used, so the load is not waited for here
+      if (SELECT) ids[i] = sel_id(ids[i]);
+      else if (FROM_CACHE) ids[i] = irow[ids[i]];  // clamped when used, so the load is not waited for here
     }
   };
   // 64-bit base of this (row, KV head) once; per-row offsets then fit 32 bits
@@ -280,7 +357,15 @@ __global__ __launch_bounds__(kAttnWaveThreads * TEAMS, 2 / TEAMS) void k_sparse_
   // which is selected whenever the split is not empty; when it is padding too (empty split,
   // nothing is computed) token 0 of the row is read.  Only keys below the count reach the
   // softmax, so the replaced rows never contribute.
-  {
+  if constexpr (SELECT) {
+    int ids0[LPT];
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int key = kbeg + piece_key(i);
+      ids0[i] = tok(sel_id(key < klast ? key : klast));
+    }
+    load_stage(ids0);
+  } else {
     int ids0[LPT];
     const int kfirst = kbeg < a.k - 1 ? kbeg : a.k - 1;
     const int id_first = FROM_CACHE ? irow[kfirst] : 0;
@@ -464,7 +549,8 @@ __global__ __launch_bounds__(256) void k_gather_kv(RowsDev rw, int k, int hkv, c
 int launch_attn(const RowsDev& rows, int k, int hq, int hkv, int n_layers_call, float scale, const AttnPlan& plan,
                 const uint16_t* q, int64_t q_stride, const uint16_t* ksel, const uint16_t* vsel, const uint16_t* kc,
                 const uint16_t* vc, const int32_t* idx, const int32_t* count, uint16_t* out, int64_t o_stride,
-                void* part, uint32_t* tickets, bool tickets_clear, void* stream) {
+                void* part, uint32_t* tickets, bool tickets_clear, void* stream, const SelectIn* sel,
+                int32_t* idx_out, int32_t* count_out) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   AttnArgs a;
   a.rw = rows;
@@ -489,12 +575,24 @@ int launch_attn(const RowsDev& rows, int k, int hq, int hkv, int n_layers_call, 
   a.o_stride = o_stride;
   a.part = static_cast<float*>(part);
   a.tickets = tickets;
+  a.sel_slot = sel ? static_cast<const uint2*>(sel->slot) : nullptr;
+  a.sel_cnt = sel ? sel->cnt : nullptr;
+  a.sel_rowinfo = sel ? sel->rowinfo : nullptr;
+  a.sel_spans = sel ? sel->spans : 0;
+  a.idx_out = idx_out;
+  a.count_out = count_out;
+  const bool fused = sel != nullptr;
+  if (fused && (plan.teams != 2 || ksel != nullptr || plan.keys_per_split > kFusedMaxIds || idx_out == nullptr ||
+                count_out == nullptr))
+    return (int)hipErrorInvalidValue;
   if (plan.splits > 1 && !tickets_clear)
     hipLaunchKernelGGL(k_clear_u32, dim3((plan.tickets + 255) / 256), dim3(256), 0, s, tickets, plan.tickets);
   const dim3 grid((unsigned)(plan.splits * plan.qblocks * hkv), (unsigned)rows.n_rows);
   const dim3 block((unsigned)(kAttnWaveThreads * plan.teams));
   if (plan.teams == 2) {
-    if (from_cache)
+    if (fused)
+      hipLaunchKernelGGL((k_sparse_attn<true, 2, true>), grid, block, 0, s, a);
+    else if (from_cache)
       hipLaunchKernelGGL((k_sparse_attn<true, 2>), grid, block, 0, s, a);
     else
       hipLaunchKernelGGL((k_sparse_attn<false, 2>), grid, block, 0, s, a);

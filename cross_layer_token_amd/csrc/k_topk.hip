@@ -13,7 +13,7 @@
 // bin holding T, and compacts its span's scores at or above that bin in index order; the last
 // workgroup of the row (one atomic ticket per workgroup, nothing contended) finishes the
 // selection over that short list.  No workgroup ever waits for another.
-#include "device_common.h"
+#include "select_common.h"
 
 namespace clsa {
 
@@ -28,24 +28,6 @@ __device__ void write_all(int32_t* out, int32_t* count, int r, int n, int k) {
 }
 
 // ---------------------------------------------------------------------------- short rows
-// One radix pass over 8 key bits: histogram of the keys that match the prefix found so far, then
-// the bin holding the need-th largest.  Ends with __syncthreads().
-template <typename KeyAt>
-__device__ __forceinline__ void radix_pass8(uint32_t* hist, int count, KeyAt key_at, uint32_t& prefix,
-                                            uint32_t& pmask, int shift, int& need, int* res) {
-  for (int i = threadIdx.x; i < 256; i += blockDim.x) hist[i] = 0u;
-  __syncthreads();
-  for (int i = threadIdx.x; i < count; i += blockDim.x) {
-    const uint32_t key = key_at(i);
-    if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-  }
-  __syncthreads();
-  find_bin256_from_top(hist, need, res);
-  prefix |= (uint32_t)res[0] << shift;
-  pmask |= 255u << shift;
-  need -= res[1];
-}
-
 __global__ __launch_bounds__(kRowThreads) void k_topk_rows_lds(RowsDev rw, const float* __restrict__ scores,
                                                                  int64_t ld, int k, int32_t* __restrict__ out,
                                                                  int32_t* __restrict__ count) {
@@ -112,6 +94,7 @@ struct SelectArgs {
   int spans;
   uint2* slot;            // [R, max_row_len]
   uint2* list;            // [R, max_row_len]
+  uint32_t* rowinfo;      // [R, 2]: t1 and the count above it, for a selection finished elsewhere
 };
 
 constexpr int kSelThreads = 1024;
@@ -153,10 +136,8 @@ __global__ __launch_bounds__(kHistThreads) void k_topk_hist_partials(SelectArgs 
 //  3. The last workgroup of the row (ticket) concatenates the span lists (still in index order),
 //     refines the exact m-th largest key T over the remaining key bits, and writes the output:
 //     keys above T, then the lowest-index ties at T up to m, in list (= index) order.
-constexpr int kListLds = 8192;   // (key, index) pairs the last workgroup keeps in LDS
-constexpr int kCopyBatch = 8;    // list loads each lane keeps in flight
-constexpr int kSpecPerLane = 4;  // span entries each lane requests before the span counts arrive
-constexpr int kMaxSpans = 2 * kSelThreads;
+constexpr int kMaxSpans = kMaxSelectSpans;
+static_assert(kMaxSpans % kSelThreads == 0, "whole spans per select thread");
 static_assert(kSelectSpan == kSelThreads * 8, "each select thread classifies 8 consecutive scores");
 
 // Finds, in the kTopkBins-bin LDS histogram, the bin d (from the top bin down) whose cumulative
@@ -179,6 +160,9 @@ __device__ __forceinline__ void find_bin_from_top(const uint32_t* hist, int need
   __syncthreads();
 }
 
+// FINISH = false: stop after step 2, with the row's t1 and the count above it published for
+// the attention workgroups that finish the selection themselves.
+template <bool FINISH>
 __global__ __launch_bounds__(kSelThreads) void k_topk_select(SelectArgs a) {
   __shared__ uint32_t hist[kTopkBins];
   __shared__ int scan[2 * kSelThreads / 64];
@@ -259,99 +243,25 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select(SelectArgs a) {
         st_dev(reinterpret_cast<uint64_t*>(slot + pos++), ((uint64_t)(uint32_t)(i0 + j) << 32) | key[j]);
     if (threadIdx.x == 0) st_dev(&a.cnt[(int64_t)r * a.spans + sp], (uint32_t)tot);
   }
-  // 3. the last workgroup of the row finishes the selection
+  if (!FINISH) {
+    if (sp == 0 && threadIdx.x == 0) {
+      a.rowinfo[2 * r] = t1;
+      a.rowinfo[2 * r + 1] = (uint32_t)above1;
+    }
+    return;
+  }
+  // 3. the last workgroup of the row finishes the selection: the span lists concatenated in span
+  //    order (so in token order; in LDS when they fit, else in the workspace), T refined, and the
+  //    selection written in token order
   const int nsp = (n + kSelectSpan - 1) / kSelectSpan;
   if (!arrive_last(&a.ticket[r], (uint32_t)nsp, flag)) return;
-  // Concatenate the span lists (spans in order, so the list stays in index order); the list lives
-  // in LDS when it fits, else in the workspace.  Wave w moves spans w, w + 16, ...; the first
-  // kSpecPerLane * 64 entries of its first span are requested together with the span counts, so
-  // that a typical row needs a single round trip.
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  constexpr int kWaves = kSelThreads / 64;
   const uint2* rslot = a.slot + (int64_t)r * a.rw.max_row_len;
-  uint64_t spec[kSpecPerLane];
-  if (wave < nsp) {
-#pragma unroll
-    for (int j = 0; j < kSpecPerLane; ++j) {
-      const int e = wave * kSelectSpan + j * 64 + lane;  // stays inside the row's scores
-      spec[j] = e < n ? ld_dev(reinterpret_cast<const uint64_t*>(rslot + e)) : 0;
-    }
-  }
-  int L = 0;
-  {
-    const int s0i = 2 * threadIdx.x, s1i = s0i + 1;
-    const int c0 = s0i < nsp ? (int)ld_dev(&a.cnt[(int64_t)r * a.spans + s0i]) : 0;
-    const int c1 = s1i < nsp ? (int)ld_dev(&a.cnt[(int64_t)r * a.spans + s1i]) : 0;
-    const int pre = block_exclusive_scan(c0 + c1, scan, &L);
-    if (s0i < nsp) span_pre[s0i] = pre;
-    if (s1i < nsp) span_pre[s1i] = pre + c0;
-    if (threadIdx.x == 0) span_pre[nsp] = L;
-    __syncthreads();
-  }
-  uint2* list = L <= kListLds ? list_lds : a.list + (int64_t)r * a.rw.max_row_len;
-  for (int sp2 = wave; sp2 < nsp; sp2 += kWaves) {
-    const int base = span_pre[sp2], cnt_s = span_pre[sp2 + 1] - base;
-    const uint2* src = rslot + (int64_t)sp2 * kSelectSpan;
-    int e0 = 0;
-    if (sp2 == wave) {
-#pragma unroll
-      for (int j = 0; j < kSpecPerLane; ++j) {
-        const int e = j * 64 + lane;
-        if (e < cnt_s) list[base + e] = make_uint2((uint32_t)spec[j], (uint32_t)(spec[j] >> 32));
-      }
-      e0 = kSpecPerLane * 64;
-    }
-    for (; e0 < cnt_s; e0 += kCopyBatch * 64) {
-      uint64_t v[kCopyBatch];
-#pragma unroll
-      for (int j = 0; j < kCopyBatch; ++j) {
-        const int e = e0 + j * 64 + lane;
-        v[j] = e < cnt_s ? ld_dev(reinterpret_cast<const uint64_t*>(src + e)) : 0;
-      }
-#pragma unroll
-      for (int j = 0; j < kCopyBatch; ++j) {
-        const int e = e0 + j * 64 + lane;
-        if (e < cnt_s) list[base + e] = make_uint2((uint32_t)v[j], (uint32_t)(v[j] >> 32));
-      }
-    }
-  }
-  __syncthreads();
-  // refine T below the first level with 8-bit passes over the remaining key bits, the last pass
-  // aligned to bit 0 (its window overlaps bits the prefix already fixes, which then match)
-  int need = m - above1;
-  uint32_t prefix = t1 << (32 - kTopkBinBits), pmask = ~0u << (32 - kTopkBinBits);
-  auto key_at = [&](int i) { return list[i].x; };
-  for (int shift = 32 - kTopkBinBits - 8;; shift -= 8) {
-    if (shift < 0) shift = 0;
-    radix_pass8(hist, L, key_at, prefix, pmask, shift, need, res);
-    if (shift == 0) break;
-  }
-  const uint32_t T = prefix;
-  // ordered output over contiguous per-thread ranges of the list
-  const int E = (L + blockDim.x - 1) / blockDim.x;
-  const int p0 = threadIdx.x * E;
-  int gt = 0, eq = 0;
-  for (int j = 0; j < E; ++j) {
-    const int p = p0 + j;
-    if (p < L) {
-      const uint32_t key = list[p].x;
-      gt += key > T;
-      eq += key == T;
-    }
-  }
-  int gt_before, eq_before, tg, te;
-  block_exclusive_scan2(gt, eq, scan, &gt_before, &eq_before, &tg, &te);
-  for (int j = 0; j < E; ++j) {
-    const int p = p0 + j;
-    if (p < L) {
-      const uint2 e = list[p];
-      const bool take = e.x > T || (e.x == T && eq_before < need);
-      const int pos = gt_before + (eq_before < need ? eq_before : need);
-      if (take && pos < m) orow[pos] = (int32_t)e.y;
-      gt_before += e.x > T;
-      eq_before += e.x == T;
-    }
-  }
+  uint2* glist = a.list + (int64_t)r * a.rw.max_row_len;
+  const int L = collect_candidates<kSelThreads, 1, kMaxSpans>(rslot, a.cnt + (int64_t)r * a.spans, nsp, n, span_pre,
+                                                               scan, list_lds, glist);
+  const uint2* list = L <= kListLds ? list_lds : glist;
+  refine_and_emit([&](int i) { return list[i]; }, L, m, t1, above1, hist, scan, res,
+                  [&](int pos, int32_t tok) { orow[pos] = tok; });
   for (int i = m + threadIdx.x; i < a.k; i += blockDim.x) orow[i] = -1;
   if (threadIdx.x == 0) a.count[r] = m;
 }
@@ -359,7 +269,7 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select(SelectArgs a) {
 }  // namespace
 
 int launch_topk(const RowsDev& rows, int k, const TopkPlan& plan, const float* scores, int64_t ld, int32_t* idx,
-                int32_t* count, void* ws, uint32_t* tickets, bool have_hist, void* stream) {
+                int32_t* count, void* ws, uint32_t* tickets, bool have_hist, void* stream, bool finish) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (!plan.multi_wg) {
     hipLaunchKernelGGL(k_topk_rows_lds, dim3(rows.n_rows), dim3(kRowThreads), 0, s, rows, scores, ld, k, idx, count);
@@ -381,9 +291,13 @@ int launch_topk(const RowsDev& rows, int k, const TopkPlan& plan, const float* s
   a.spans = plan.spans;
   a.slot = reinterpret_cast<uint2*>(w + plan.slot_off);
   a.list = reinterpret_cast<uint2*>(w + plan.list_off);
+  a.rowinfo = reinterpret_cast<uint32_t*>(w + plan.rowinfo_off);
   if (!have_hist)
     hipLaunchKernelGGL(k_topk_hist_partials, dim3(plan.hist_chunks, rows.n_rows), dim3(kHistThreads), 0, s, a);
-  hipLaunchKernelGGL(k_topk_select, dim3(plan.spans, rows.n_rows), dim3(kSelThreads), 0, s, a);
+  if (finish)
+    hipLaunchKernelGGL(k_topk_select<true>, dim3(plan.spans, rows.n_rows), dim3(kSelThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_topk_select<false>, dim3(plan.spans, rows.n_rows), dim3(kSelThreads), 0, s, a);
   return (int)hipGetLastError();
 }
 

@@ -104,6 +104,8 @@ TopkPlan plan_topk(const clsa_dims* d, const clsa_rows* r) {
   off = align_up(off + R * (size_t)r->max_row_len * 8, 256);
   p.list_off = off;
   off = align_up(off + R * (size_t)r->max_row_len * 8, 256);
+  p.rowinfo_off = off;
+  off = align_up(off + R * 8, 256);
   p.bytes = off;
   (void)d;
   return p;
@@ -150,6 +152,8 @@ StepPlan plan_step(const clsa_dims* d, const clsa_rows* r, int schedule, bool us
   // depend on the chunk size; buffers are sized for the largest chunk
   s.attn = plan_attn(d, s.chunk_rows, lc, r->n_rows);
   s.ld_scores = (int64_t)align_up((size_t)r->max_row_len, 64);
+  s.fused_select = !prefill && schedule == CLSA_SCHEDULE_LAYER_BATCHED && s.topk.multi_wg && s.attn.teams == 2 &&
+                   s.attn.keys_per_split <= kFusedMaxIds;
   size_t off = 0;
   s.ticket_off = off;
   s.n_tickets = s.topk.tickets + s.attn.tickets;

@@ -1,0 +1,162 @@
+// The last steps of the long-row top-k select (TopK(I_t, k) of eq. 2 in the picx.dev summary of
+// "You Only Index Once", Methodology > Architecture Overview), shared by the select's last
+// workgroup of a row and by the attention workgroups that finish the selection themselves.
+//
+// The candidates of a row are the (key, token) pairs whose first-level bin is at or above the bin
+// t1 holding the m-th largest key.  Span s of the row (kSelectSpan scores) holds cnt[s] of them
+// at slot + s * kSelectSpan, in token order, so the spans concatenated in order are in token
+// order too.  The m-th largest key T is refined with 8-bit radix passes over the candidates;
+// then every key above T is taken, and the lowest-token ties at T until m are taken.
+#pragma once
+
+#include "device_common.h"
+
+namespace clsa {
+
+constexpr int kListLds = 8192;   // (key, token) pairs a finishing workgroup keeps in LDS
+constexpr int kCopyBatch = 8;    // list loads each lane keeps in flight
+constexpr int kSpecPerLane = 4;  // span entries each lane requests before the span counts arrive
+
+// One radix pass over 8 key bits: histogram of the keys that match the prefix found so far, then
+// the bin holding the need-th largest.  Ends with __syncthreads().
+template <typename KeyAt>
+__device__ __forceinline__ void radix_pass8(uint32_t* hist, int count, KeyAt key_at, uint32_t& prefix,
+                                            uint32_t& pmask, int shift, int& need, int* res) {
+  for (int i = threadIdx.x; i < 256; i += blockDim.x) hist[i] = 0u;
+  __syncthreads();
+  for (int i = threadIdx.x; i < count; i += blockDim.x) {
+    const uint32_t key = key_at(i);
+    if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+  }
+  __syncthreads();
+  find_bin256_from_top(hist, need, res);
+  prefix |= (uint32_t)res[0] << shift;
+  pmask |= 255u << shift;
+  need -= res[1];
+}
+
+// Gathers the row's span counts into span_pre[0..nsp] (prefix counts, span_pre[nsp] = L) and
+// returns L.  NT threads, kMaxSpansSel >= nsp spans; the first kSpecPerLane * 64 entries of the
+// first NSPEC spans of every wave are requested together with the counts, so a typical row needs
+// one round trip.  When L <= kListLds the span lists are concatenated into list_lds, otherwise
+// into list_global when it is given; with neither the lists stay in the spans.  Reads use
+// device-scope loads, so the spans may come from other workgroups of the same kernel.  Ends with
+// __syncthreads().
+template <int NT, int NSPEC, int kMaxSpansSel>
+__device__ int collect_candidates(const uint2* slot, const uint32_t* cnt, int nsp, int n, int* span_pre, int* scan,
+                                  uint2* list_lds, uint2* list_global) {
+  static_assert(kMaxSpansSel % NT == 0, "whole spans per thread");
+  constexpr int SPT = kMaxSpansSel / NT;  // span counts per thread
+  constexpr int kWaves = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint64_t spec[NSPEC][kSpecPerLane];
+#pragma unroll
+  for (int u = 0; u < NSPEC; ++u) {
+    const int sp = wave + u * kWaves;
+#pragma unroll
+    for (int j = 0; j < kSpecPerLane; ++j) {
+      const int e = sp * kSelectSpan + j * 64 + lane;  // stays inside the row's scores
+      spec[u][j] = (sp < nsp && e < n) ? ld_dev(reinterpret_cast<const uint64_t*>(slot + e)) : 0;
+    }
+  }
+  int L = 0;
+  {
+    int c[SPT], mine = 0;
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+      const int sp = threadIdx.x * SPT + i;
+      c[i] = sp < nsp ? (int)ld_dev(&cnt[sp]) : 0;
+      mine += c[i];
+    }
+    int pre = block_exclusive_scan(mine, scan, &L);
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+      const int sp = threadIdx.x * SPT + i;
+      if (sp < nsp) span_pre[sp] = pre;
+      pre += c[i];
+    }
+    if (threadIdx.x == 0) span_pre[nsp] = L;
+    __syncthreads();
+  }
+  uint2* list = L <= kListLds ? list_lds : list_global;
+  if (list == nullptr) return L;
+  for (int sp2 = wave, u = 0; sp2 < nsp; sp2 += kWaves, ++u) {
+    const int base = span_pre[sp2], cnt_s = span_pre[sp2 + 1] - base;
+    const uint2* src = slot + (int64_t)sp2 * kSelectSpan;
+    int e0 = 0;
+    if (u < NSPEC) {
+#pragma unroll
+      for (int uu = 0; uu < NSPEC; ++uu) {
+        if (uu != u) continue;
+#pragma unroll
+        for (int j = 0; j < kSpecPerLane; ++j) {
+          const int e = j * 64 + lane;
+          if (e < cnt_s) list[base + e] = make_uint2((uint32_t)spec[uu][j], (uint32_t)(spec[uu][j] >> 32));
+        }
+      }
+      e0 = kSpecPerLane * 64;
+    }
+    for (; e0 < cnt_s; e0 += kCopyBatch * 64) {
+      uint64_t v[kCopyBatch];
+#pragma unroll
+      for (int j = 0; j < kCopyBatch; ++j) {
+        const int e = e0 + j * 64 + lane;
+        v[j] = e < cnt_s ? ld_dev(reinterpret_cast<const uint64_t*>(src + e)) : 0;
+      }
+#pragma unroll
+      for (int j = 0; j < kCopyBatch; ++j) {
+        const int e = e0 + j * 64 + lane;
+        if (e < cnt_s) list[base + e] = make_uint2((uint32_t)v[j], (uint32_t)(v[j] >> 32));
+      }
+    }
+  }
+  __syncthreads();
+  return L;
+}
+
+// Refines the m-th largest key T below the first level (bin t1, `above1` keys in higher bins)
+// with 8-bit passes over the L candidates entry_at(0..L-1) (in token order), the last pass
+// aligned to bit 0 (its window overlaps bits the prefix already fixes, which then match), and
+// calls emit(position, token) for every selected candidate, position = its rank in token order
+// among the selected (0 .. m-1).  Every thread calls this; it ends without a barrier after the
+// emits.
+template <typename EntryAt, typename Emit>
+__device__ void refine_and_emit(EntryAt entry_at, int L, int m, uint32_t t1, int above1, uint32_t* hist, int* scan,
+                                int* res, Emit emit) {
+  int need = m - above1;
+  uint32_t prefix = t1 << (32 - kTopkBinBits), pmask = ~0u << (32 - kTopkBinBits);
+  auto key_at = [&](int i) { return entry_at(i).x; };
+  for (int shift = 32 - kTopkBinBits - 8;; shift -= 8) {
+    if (shift < 0) shift = 0;
+    radix_pass8(hist, L, key_at, prefix, pmask, shift, need, res);
+    if (shift == 0) break;
+  }
+  const uint32_t T = prefix;
+  // ordered output over contiguous per-thread ranges of the candidates
+  const int E = (L + (int)blockDim.x - 1) / (int)blockDim.x;
+  const int p0 = threadIdx.x * E;
+  int gt = 0, eq = 0;
+  for (int j = 0; j < E; ++j) {
+    const int p = p0 + j;
+    if (p < L) {
+      const uint32_t key = key_at(p);
+      gt += key > T;
+      eq += key == T;
+    }
+  }
+  int gt_before, eq_before, tg, te;
+  block_exclusive_scan2(gt, eq, scan, &gt_before, &eq_before, &tg, &te);
+  for (int j = 0; j < E; ++j) {
+    const int p = p0 + j;
+    if (p < L) {
+      const uint2 e = entry_at(p);
+      const bool take = e.x > T || (e.x == T && eq_before < need);
+      const int pos = gt_before + (eq_before < need ? eq_before : need);
+      if (take && pos < m) emit(pos, (int32_t)e.y);
+      gt_before += e.x > T;
+      eq_before += e.x == T;
+    }
+  }
+}
+
+}  // namespace clsa

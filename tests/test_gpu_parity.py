@@ -308,6 +308,26 @@ def test_step_decode_mixed_lengths_vs_cpp_oracle(schedule):
         _say(f"mixed sched {schedule} row {r} (n={w.row_len(r)}): max {st[0]:.2e} mean {st[1]:.2e} rel {st[2]:.2e}")
 
 
+@pytest.mark.parametrize("lo,hi,den", [(-1, 1, 4), (0, 0, 1)], ids=["ties", "all_equal"])
+def test_step_decode_heavy_ties_long_rows(lo, hi, den):
+    """Long rows with tie-heavy scores.  Indexer entries {-1, 0, 1} / 4: a few thousand candidates
+    around the k-th score, many of them tied.  All entries 0: every score ties, every token is a
+    candidate - more than a workgroup keeps in LDS - and the selection (the lowest k tokens) is
+    finished from the span lists in place.  Every row against the oracle."""
+    w = cs.custom(seq_lens=(60000, 45000, 70001, 52000), d_idx=128, topk=2048, n_layers=4, hq=16, hkv=4, idx_lo=lo,
+                  idx_hi=hi, idx_den=den, needles=0, seed=41, name=f"ties_long_{lo}_{hi}")
+    dw = device_workload(w)
+    for schedule in (clsa.SCHEDULE_LAYER_BATCHED, clsa.SCHEDULE_PER_LAYER):
+        idx, cnt, out = _run_step(dw, schedule)
+        dev = bf16_dev_to_f64(out)
+        for r in range(w.n_rows):
+            res = oracle_row(w, r)
+            assert cnt[r] == res["count"]
+            assert np.array_equal(idx[r], res["idx"]), f"row {r}: {np.sum(idx[r] != res['idx'])} index mismatches"
+            assert_outputs_close(dev[r], res["out"], f"heavy ties row {r}")
+        _say(f"heavy ties, schedule {schedule}: {w.n_rows} rows match")
+
+
 @pytest.mark.parametrize("cfg,check", [(1, None), (2, [0, 7]), (3, [4])])
 def test_step_per_layer_routing_vs_oracle(cfg, check):
     """The ablation without the shared index: every layer scores the cache with its own indexer
