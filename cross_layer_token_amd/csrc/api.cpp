@@ -314,6 +314,15 @@ clsa_status clsa_step(const clsa_dims* dims, const clsa_rows* rows, const clsa_s
     const AttnPlan ap = plan_attn(dims, rows->n_rows, 1, rows->n_rows);
     const int R = rows->n_rows;
     const int ichunk = tp.multi_wg ? tp.hist_chunk : idx_chunk_for(R, rows->max_row_len);
+    // as in the layer-batched step, the attention workgroups finish each layer's long-row selection
+    const bool fused = tp.multi_wg && ap.teams == 2 && ap.keys_per_split <= kFusedMaxIds;
+    SelectIn sel;
+    if (fused) {
+      sel.slot = topk_ws + tp.slot_off;
+      sel.cnt = reinterpret_cast<const uint32_t*>(topk_ws + tp.cnt_off);
+      sel.rowinfo = reinterpret_cast<const uint32_t*>(topk_ws + tp.rowinfo_off);
+      sel.spans = tp.spans;
+    }
     for (int l = 0; l < L; ++l) {
       uint16_t* hpart = tp.multi_wg ? reinterpret_cast<uint16_t*>(topk_ws + tp.hpart_off) : nullptr;
       int e = launch_index_scores_decode(rd, dims->d_idx, ichunk, a->q_idx + (int64_t)l * dims->d_idx,
@@ -322,11 +331,12 @@ clsa_status clsa_step(const clsa_dims* dims, const clsa_rows* rows, const clsa_s
       if (e) return device_status(e, "clsa_step: index scores of a layer");
       int32_t* idx = a->idx + (int64_t)l * R * k;
       int32_t* count = a->count + (int64_t)l * R;
-      e = launch_topk(rd, k, tp, scores, sp.ld_scores, idx, count, topk_ws, topk_tickets, tp.multi_wg, stream);
+      e = launch_topk(rd, k, tp, scores, sp.ld_scores, idx, count, topk_ws, topk_tickets, tp.multi_wg, stream,
+                      !fused);
       if (e) return device_status(e, "clsa_step: top-k of a layer");
       e = launch_attn(rd, k, hq, hkv, 1, scale, ap, a->q + (int64_t)l * hq * CLSA_HEAD_DIM, row_elems, nullptr,
                       nullptr, a->k_cache, a->v_cache, idx, count, a->out + (int64_t)l * hq * CLSA_HEAD_DIM, row_elems,
-                      ws + sp.part_off, attn_tickets, true, stream);
+                      ws + sp.part_off, attn_tickets, true, stream, fused ? &sel : nullptr, idx, count);
       if (e) return device_status(e, "clsa_step: attention of a layer");
     }
     return CLSA_OK;
