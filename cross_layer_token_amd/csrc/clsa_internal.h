@@ -122,7 +122,7 @@ inline float softmax_scale(const clsa_dims* d) {
 }
 
 // Distillation target and loss (eq. 4-5): keys per KL partial, and the workspace layout.
-constexpr int kDistillKeyBlock = 512;
+constexpr int kDistillKeyBlock = 256;
 struct DistillPlan {
   int n_kb = 0;           // key blocks of kDistillKeyBlock per row
   size_t lse2_off = 0;    // fp32 [R, L * hq]

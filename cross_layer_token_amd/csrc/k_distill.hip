@@ -13,13 +13,13 @@
 //     positions of queries in registers, the KV head's keys stream through LDS in 64-key tiles,
 //     S^T = K Q^T, and the running max and sum stay in the lane that owns the query column
 //     (the max is raised lazily, only past a growth of 2^8).
-//  2. k_distill_kl: A over a tile of 64 positions x 512 keys.  Each wave keeps its 64 keys of
+//  2. k_distill_kl: A over a tile of 32 positions x 256 keys.  Each wave keeps its 64 keys of
 //     the current KV head in registers; the (layer, head) pairs' query blocks stream through LDS
 //     (double-buffered), and exp2(s * c - lse2) is added into lane-local accumulators, so the
 //     sum over the L * Hq pairs needs no exchange.  The tile's KL terms are then summed in a
-//     fixed order into one partial per (position, 512-key block).
-// k_row_lse gives the log-sum-exp of each row of I, and k_distill_reduce sums the partials of
-// every position in key order and the loss in position order, so the results do not depend on
+//     fixed order into one partial per (position, 256-key block).
+// k_row_lse gives the log-sum-exp of each row of I, k_distill_rowsum sums the partials of every
+// position and k_distill_loss the rows, each in a fixed order, so the results do not depend on
 // timing.  The exp2 of every score in both passes, not the matrix cores, bounds the time: a
 // wave issues one v_exp_f32 per score, against 1/16 of a 16x16x32 MFMA.
 #include "device_common.h"
@@ -34,10 +34,19 @@ constexpr int kStatRows = 16;                          // positions per stats wo
 constexpr int kStatPairsPerWave = 4;
 constexpr int kStatPairs = kDstWaves * kStatPairsPerWave;
 constexpr int kStatTilesPerStep = 2;                    // 64-key tiles per LDS step
-constexpr int kKlRows = 64;                             // positions per KL workgroup
+// KL pass: four-wave workgroups of 32 positions x 256 keys, three per CU (each wave keeps its 64
+// keys of the current KV head in registers and accumulates 64 keys x 32 positions of A)
+constexpr int kKlWaves = 4;
+constexpr int kKlThreads = 64 * kKlWaves;
+constexpr int kKlBlocksPerCU = 3;
+constexpr int kKlRows = 32;                              // positions per KL workgroup
+constexpr int kKlTq = kKlRows / 16;                      // 16-position MFMA blocks
 constexpr int kKlKeysPerWave = 64;
-constexpr int kKlKeys = kDstWaves * kKlKeysPerWave;     // keys per KL workgroup
+constexpr int kKlKeys = kKlWaves * kKlKeysPerWave;       // keys per KL workgroup
+constexpr int kKlPieces = kKlRows * 16 / kKlThreads;     // 16-byte query pieces per thread per pair
+constexpr int kKlQBytes = kKlRows * CLSA_HEAD_DIM * 2;   // one (layer, head) query block in LDS
 constexpr int kKlPairsPerStep = 2;                       // (layer, head) query blocks per LDS step
+static_assert(kKlPieces * kKlThreads == kKlRows * 16, "whole query pieces per thread");
 static_assert(kKlKeys == kDistillKeyBlock, "key block of the KL partials");
 constexpr int kTileKeys = 64;
 constexpr int kTileBytes = kTileKeys * CLSA_HEAD_DIM * 2;  // 16 KB: 64 rows of 256 bytes
@@ -238,13 +247,13 @@ __global__ __launch_bounds__(kDstThreads) void k_distill_stats(DistillArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// pass 2: A over 64 positions x 512 keys, then the tile's KL terms per position
-__global__ __launch_bounds__(kDstThreads, 1) void k_distill_kl(DistillArgs a) {
+// pass 2: A over 32 positions x 256 keys, then the tile's KL terms per position
+__global__ __launch_bounds__(kKlThreads, kKlBlocksPerCU) void k_distill_kl(DistillArgs a) {
   // two steps of kKlPairsPerStep (layer, head) query blocks: the next step is loaded while this
   // one is computed, and the workgroup meets at one barrier per step
   __shared__ __attribute__((aligned(16))) uint16_t qlds[2 * kKlPairsPerStep * kKlRows * CLSA_HEAD_DIM];
   __shared__ float llds[2][kKlPairsPerStep][kKlRows];
-  __shared__ float red[kDstWaves][kKlRows];
+  __shared__ float red[kKlWaves][kKlRows];
   char* const q_bytes = reinterpret_cast<char*>(qlds);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, grp = lane >> 4;
@@ -256,17 +265,17 @@ __global__ __launch_bounds__(kDstThreads, 1) void k_distill_kl(DistillArgs a) {
   const int wk0 = k0 + wave * kKlKeysPerWave;
   const bool wave_active = wk0 <= t_hi;
   const int P = a.L * a.hq;
-  // query-block loader: 64 rows x 16 chunks, two pieces per thread
-  int lrow[2], lchunk[2], soff[2];
+  // query-block loader: kKlRows rows x 16 chunks, kKlPieces pieces per thread
+  int lrow[kKlPieces], lchunk[kKlPieces], soff[kKlPieces];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int piece = threadIdx.x + i * kDstThreads;
+  for (int i = 0; i < kKlPieces; ++i) {
+    const int piece = threadIdx.x + i * kKlThreads;
     lrow[i] = piece >> 4;
     lchunk[i] = piece & 15;
     soff[i] = tile_off(lrow[i], lchunk[i]);
     if (r0 + lrow[i] > last_row) lrow[i] = last_row - r0;
   }
-  uint4 rq[kKlPairsPerStep][2];
+  uint4 rq[kKlPairsPerStep][kKlPieces];
   float rl[kKlPairsPerStep];
   // pair index pi = g * pairs_per_g + p  ->  (layer p / group, head g * group + p % group)
   auto pair_qh = [&](int pi) {
@@ -279,7 +288,7 @@ __global__ __launch_bounds__(kDstThreads, 1) void k_distill_kl(DistillArgs a) {
       const int pi = st * kKlPairsPerStep + u;
       const int qh = pair_qh(pi < P ? pi : P - 1);  // past the last pair: re-read it, unused
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < kKlPieces; ++i)
         rq[u][i] = load16(a.q + (int64_t)(r0 + lrow[i]) * a.q_stride + (int64_t)qh * CLSA_HEAD_DIM + lchunk[i] * 8);
       if (threadIdx.x < kKlRows) {
         const int rr = r0 + threadIdx.x <= last_row ? r0 + threadIdx.x : last_row;
@@ -302,34 +311,29 @@ __global__ __launch_bounds__(kDstThreads, 1) void k_distill_kl(DistillArgs a) {
     krow[mt] = kbase + (int64_t)key * a.hkv * CLSA_HEAD_DIM + grp * 8;
   }
   bf16x8_t kf[4][4];
-  floatx4_t abar[4][4];  // [mt][tq]: key wk0 + 16 mt + 4 grp + j, row r0 + 16 tq + l16
+  floatx4_t abar[4][kKlTq];  // [mt][tq]: key wk0 + 16 mt + 4 grp + j, row r0 + 16 tq + l16
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int tq = 0; tq < 4; ++tq) abar[mt][tq] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    for (int tq = 0; tq < kKlTq; ++tq) abar[mt][tq] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   const float c = a.c;
-  // One (layer, head) pair: S^T = K Q^T for the wave's 64 keys x 64 positions, and
-  // exp2(s c - lse2) into the accumulators.  Keys past a position get meaningless values here;
-  // they are never read back.
+  // One (layer, head) pair: S^T = K Q^T for the wave's 64 keys x kKlRows positions, and
+  // exp2(s c - lse2) into the accumulators, one block of 16 positions at a time.  Keys past a
+  // position get meaningless values here; they are never read back.
   auto compute_pair = [&](const char* qb, const float* lse_row) {
-    // one block of 16 positions at a time, the next block's Q fragments read from LDS meanwhile
-    bf16x8_t qv[2][4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) qv[0][kk] = bitcast<bf16x8_t>(*reinterpret_cast<const uint4*>(qb + qoff[kk]));
+    for (int tq = 0; tq < kKlTq; ++tq) {
+      bf16x8_t qv[4];
 #pragma unroll
-    for (int tq = 0; tq < 4; ++tq) {
-      if (tq + 1 < 4) {
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          qv[(tq + 1) & 1][kk] = bitcast<bf16x8_t>(*reinterpret_cast<const uint4*>(qb + qoff[kk] + (tq + 1) * 4096));
-      }
+      for (int kk = 0; kk < 4; ++kk)
+        qv[kk] = bitcast<bf16x8_t>(*reinterpret_cast<const uint4*>(qb + qoff[kk] + tq * 4096));
       floatx4_t s[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) s[mt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) s[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[mt][kk], qv[tq & 1][kk], s[mt], 0, 0, 0);
+        for (int mt = 0; mt < 4; ++mt) s[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[mt][kk], qv[kk], s[mt], 0, 0, 0);
       const float lse = lse_row[tq * 16 + l16];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
@@ -343,9 +347,9 @@ __global__ __launch_bounds__(kDstThreads, 1) void k_distill_kl(DistillArgs a) {
     const int buf = st & 1;
 #pragma unroll
     for (int u = 0; u < kKlPairsPerStep; ++u) {
-      char* qb = q_bytes + (buf * kKlPairsPerStep + u) * kTileBytes;
+      char* qb = q_bytes + (buf * kKlPairsPerStep + u) * kKlQBytes;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(qb + soff[i]) = rq[u][i];
+      for (int i = 0; i < kKlPieces; ++i) *reinterpret_cast<uint4*>(qb + soff[i]) = rq[u][i];
       if (threadIdx.x < kKlRows) llds[buf][u][threadIdx.x] = rl[u];
     }
     __syncthreads();  // one barrier per step: buffer buf was last read two steps ago
@@ -363,14 +367,14 @@ __global__ __launch_bounds__(kDstThreads, 1) void k_distill_kl(DistillArgs a) {
           for (int kk = 0; kk < 4; ++kk)
             kf[mt][kk] = bitcast<bf16x8_t>(load16(a.k + krow[mt] + g * CLSA_HEAD_DIM + kk * 32));
       }
-      compute_pair(q_bytes + (buf * kKlPairsPerStep + u) * kTileBytes, llds[buf][u]);
+      compute_pair(q_bytes + (buf * kKlPairsPerStep + u) * kKlQBytes, llds[buf][u]);
     }
   }
   // KL terms of the tile: sum over the visible keys j of A (ln A - (I_j - lse_I))
   const float inv = 1.f / (float)P;
-  float klp[4];
+  float klp[kKlTq];
 #pragma unroll
-  for (int tq = 0; tq < 4; ++tq) {
+  for (int tq = 0; tq < kKlTq; ++tq) {
     klp[tq] = 0.f;
     const int row = r0 + tq * 16 + l16;
     if (!wave_active || row > last_row) continue;
@@ -394,7 +398,7 @@ __global__ __launch_bounds__(kDstThreads, 1) void k_distill_kl(DistillArgs a) {
     }
   }
 #pragma unroll
-  for (int tq = 0; tq < 4; ++tq) {
+  for (int tq = 0; tq < kKlTq; ++tq) {
     float v = klp[tq] + __shfl_xor(klp[tq], 16, 64);
     v += __shfl_xor(v, 32, 64);
     if (grp == 0) red[wave][tq * 16 + l16] = v;
@@ -403,32 +407,40 @@ __global__ __launch_bounds__(kDstThreads, 1) void k_distill_kl(DistillArgs a) {
   if (threadIdx.x < kKlRows && r0 + (int)threadIdx.x <= last_row) {
     float v = red[0][threadIdx.x];
 #pragma unroll
-    for (int w = 1; w < kDstWaves; ++w) v += red[w][threadIdx.x];
+    for (int w = 1; w < kKlWaves; ++w) v += red[w][threadIdx.x];
     a.part[(int64_t)(r0 + threadIdx.x) * a.n_kb + kb] = v;
   }
 }
 
 // ---------------------------------------------------------------------------------------------
-// KL of every row (its partials in key order) and the loss (the rows in order)
-constexpr int kReduceThreads = 1024;
-__global__ __launch_bounds__(kReduceThreads) void k_distill_reduce(DistillArgs a) {
-  __shared__ float red[kReduceThreads / 64];
+// KL of every row: one wave per row, lane b holding the partials of key blocks b, b + 64, ...
+// summed by a fixed butterfly
+constexpr int kRowSumThreads = 256;
+__global__ __launch_bounds__(kRowSumThreads) void k_distill_rowsum(DistillArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int i = (int)blockIdx.x * (kRowSumThreads / 64) + (int)(threadIdx.x >> 6);
+  if (i >= a.n_rows) return;
+  const int nkb = (a.pos0 + i) / kKlKeys + 1;
+  const float* p = a.part + (int64_t)i * a.n_kb;
+  float v = 0.f;
+  for (int b = lane; b < nkb; b += 64) v += p[b];
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  if (lane == 0) a.kl[i] = v;
+}
+
+// the loss: mean of the rows' KL, thread t summing rows t, t + 1024, ... then a fixed tree
+constexpr int kLossThreads = 1024;
+__global__ __launch_bounds__(kLossThreads) void k_distill_loss(DistillArgs a) {
+  __shared__ float red[kLossThreads / 64];
   float mine = 0.f;
-  for (int i = threadIdx.x; i < a.n_rows; i += kReduceThreads) {
-    const int nkb = (a.pos0 + i) / kKlKeys + 1;
-    float v = 0.f;
-    for (int b = 0; b < nkb; ++b) v += a.part[(int64_t)i * a.n_kb + b];
-    a.kl[i] = v;
-    mine += v;
-  }
-  if (a.loss == nullptr) return;
+  for (int i = threadIdx.x; i < a.n_rows; i += kLossThreads) mine += a.kl[i];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int o = 32; o > 0; o >>= 1) mine += __shfl_xor(mine, o, 64);
   if (lane == 0) red[wave] = mine;
   __syncthreads();
   if (threadIdx.x == 0) {
     float s = 0.f;
-    for (int w = 0; w < kReduceThreads / 64; ++w) s += red[w];
+    for (int w = 0; w < kLossThreads / 64; ++w) s += red[w];
     a.loss[0] = s / (float)a.n_rows;
   }
 }
@@ -468,8 +480,10 @@ int launch_distill(const RowsDev& rows, int64_t total_tokens, int L, int hq, int
   hipLaunchKernelGGL(k_distill_stats, dim3((unsigned)((rows.n_rows + kStatRows - 1) / kStatRows), (unsigned)(hkv * chunks)),
                      dim3(kDstThreads), 0, s, a);
   hipLaunchKernelGGL(k_distill_kl, dim3((unsigned)plan.n_kb, (unsigned)((rows.n_rows + kKlRows - 1) / kKlRows)),
-                     dim3(kDstThreads), 0, s, a);
-  hipLaunchKernelGGL(k_distill_reduce, dim3(1), dim3(kReduceThreads), 0, s, a);
+                     dim3(kKlThreads), 0, s, a);
+  hipLaunchKernelGGL(k_distill_rowsum, dim3((unsigned)((rows.n_rows + kRowSumThreads / 64 - 1) / (kRowSumThreads / 64))),
+                     dim3(kRowSumThreads), 0, s, a);
+  if (loss != nullptr) hipLaunchKernelGGL(k_distill_loss, dim3(1), dim3(kLossThreads), 0, s, a);
   return (int)hipGetLastError();
 }
 
