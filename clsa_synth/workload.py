@@ -41,6 +41,9 @@ class Workload:
     needles: int              # decode: per sequence; prefill: planted against the last row
     seed: int
     description: str = ""
+    # decode only: extra needles at chosen places, (sequence, first local position, count) each;
+    # they pack a sequence's largest scores into a chosen stretch of tokens
+    planted: tuple = ()
     _cache: dict = field(default_factory=dict, compare=False, repr=False)
 
     # ---- shapes -------------------------------------------------------------------
@@ -89,6 +92,14 @@ class Workload:
                 n = self.seq_lens[0]
                 for p in gen.needle_positions(self.seed, 0, n, self.needles):
                     pairs.append((p, n - 1))
+        if self.planted:
+            assert self.mode == "decode", "planted needles are for decode workloads"
+            have = {t for t, _ in pairs}
+            for b, start, count in self.planted:
+                assert 0 <= start and start + count <= self.seq_lens[b]
+                for p in range(start, start + count):
+                    if int(cu[b]) + p not in have:
+                        pairs.append((int(cu[b]) + p, b))
         self._cache["needles"] = pairs
         return pairs
 
@@ -221,8 +232,8 @@ def config(i: int, seed: int | None = None) -> Workload:
 
 
 def custom(mode="decode", seq_lens=(300,), d_idx=64, topk=32, n_layers=2, hq=8, hkv=2, idx_lo=-8, idx_hi=8,
-           idx_den=8, needles=0, seed=0, name="custom") -> Workload:
+           idx_den=8, needles=0, seed=0, name="custom", planted=()) -> Workload:
     """A small workload of the same value distributions, for tests."""
     return Workload(name=name, mode=mode, seq_lens=tuple(int(x) for x in seq_lens), d_idx=d_idx, topk=topk,
                     n_layers=n_layers, hq=hq, hkv=hkv, head_dim=128, idx_lo=idx_lo, idx_hi=idx_hi,
-                    idx_den=idx_den, needles=needles, seed=seed)
+                    idx_den=idx_den, needles=needles, seed=seed, planted=tuple(planted))

@@ -119,7 +119,7 @@ clsa_status clsa_index_scores(const clsa_dims* dims, const clsa_rows* rows, cons
   int e;
   if (rows->mode == CLSA_MODE_DECODE)
     e = launch_index_scores_decode(rd, dims->d_idx, idx_chunk_for(rows->n_rows, rows->max_row_len), q_idx,
-                                   dims->d_idx, k_idx, scores, ld_scores, nullptr, nullptr, 0, stream);
+                                   dims->d_idx, k_idx, scores, ld_scores, nullptr, nullptr, 0, nullptr, 0, stream);
   else
     e = launch_index_scores_prefill(rd, dims->d_idx, q_idx, k_idx, scores, ld_scores, nullptr, 0, stream);
   return device_status(e, "clsa_index_scores");
@@ -325,9 +325,10 @@ clsa_status clsa_step(const clsa_dims* dims, const clsa_rows* rows, const clsa_s
     }
     for (int l = 0; l < L; ++l) {
       uint16_t* hpart = tp.multi_wg ? reinterpret_cast<uint16_t*>(topk_ws + tp.hpart_off) : nullptr;
+      uint32_t* hinfo = tp.multi_wg ? reinterpret_cast<uint32_t*>(topk_ws + tp.hinfo_off) : nullptr;
       int e = launch_index_scores_decode(rd, dims->d_idx, ichunk, a->q_idx + (int64_t)l * dims->d_idx,
-                                         (int64_t)L * dims->d_idx, a->k_idx, scores, sp.ld_scores, hpart, tickets,
-                                         sp.n_tickets, stream);
+                                         (int64_t)L * dims->d_idx, a->k_idx, scores, sp.ld_scores, hpart, hinfo, k,
+                                         tickets, sp.n_tickets, stream);
       if (e) return device_status(e, "clsa_step: index scores of a layer");
       int32_t* idx = a->idx + (int64_t)l * R * k;
       int32_t* count = a->count + (int64_t)l * R;
@@ -367,10 +368,11 @@ clsa_status clsa_step(const clsa_dims* dims, const clsa_rows* rows, const clsa_s
       e = launch_index_scores_prefill(rd, dims->d_idx, q_idx, a->k_idx, scores, ld, tickets, sp.n_tickets, stream);
     } else {
       uint16_t* hpart = tp.multi_wg ? reinterpret_cast<uint16_t*>(topk_ws + tp.hpart_off) : nullptr;
+      uint32_t* hinfo = tp.multi_wg ? reinterpret_cast<uint32_t*>(topk_ws + tp.hinfo_off) : nullptr;
       have_hist = tp.multi_wg;
       const int chunk = tp.multi_wg ? tp.hist_chunk : idx_chunk_for(cr.n_rows, cr.max_row_len);
-      e = launch_index_scores_decode(rd, dims->d_idx, chunk, q_idx, dims->d_idx, a->k_idx, scores, ld, hpart,
-                                     tickets, sp.n_tickets, stream);
+      e = launch_index_scores_decode(rd, dims->d_idx, chunk, q_idx, dims->d_idx, a->k_idx, scores, ld, hpart, hinfo,
+                                     k, tickets, sp.n_tickets, stream);
     }
     if (e) return device_status(e, "clsa_step: index scores");
     int32_t* idx = a->idx + (int64_t)c0 * k;

@@ -58,7 +58,8 @@ struct TopkPlan {
   int hist_chunk = 0;      // scores per histogram partial (= the score kernel's chunk)
   int hist_chunks = 0;     // histogram partials per row
   int spans = 0;           // select workgroups per row (kSelectSpan scores each)
-  size_t hpart_off = 0;    // uint16 [R, hist_chunks, kTopkBins]
+  size_t hpart_off = 0;    // uint16 [R, hist_chunks, kTopkBins]: per-chunk partials (full or windowed)
+  size_t hinfo_off = 0;    // uint32 [R, hist_chunks]: window start | full flag of each partial
   size_t cnt_off = 0;      // uint32 [R, spans]
   size_t slot_off = 0;     // uint2 [R, max_row_len]: per-span ordered lists (key, index)
   size_t list_off = 0;     // uint2 [R, max_row_len]: the concatenated list of the last workgroup
@@ -140,10 +141,11 @@ struct RowsDev {
 };
 
 // `clear` (n_clear words) is zeroed by the launch before any other kernel of the call reads it.
+// hpart / hinfo (with topk): also write each chunk's top-k histogram partial.
 int launch_index_scores_decode(const RowsDev& rows, int d_idx, int chunk, const uint16_t* q_idx, int64_t q_stride,
                                const uint16_t* k_idx,
-                               float* scores, int64_t ld, uint16_t* hpart, uint32_t* clear, int n_clear,
-                               void* stream);
+                               float* scores, int64_t ld, uint16_t* hpart, uint32_t* hinfo, int topk, uint32_t* clear,
+                               int n_clear, void* stream);
 int launch_index_scores_prefill(const RowsDev& rows, int d_idx, const uint16_t* q_idx, const uint16_t* k_idx,
                                 float* scores, int64_t ld, uint32_t* clear, int n_clear, void* stream);
 // have_hist: the score kernel already wrote the histogram partials and cleared the tickets.

@@ -6,11 +6,12 @@
 // bf16 -> fp32), and the per-lane partial sums of 16 rows are reduce-scattered over the row's
 // lanes with DPP, so that every lane ends up owning one finished row score.  When asked, the
 // workgroup also histograms the top key bits of its scores (the first level of the top-k
-// select), which saves the select a pass over the scores.
+// select) and publishes the part of the histogram the select needs (write_hist_partial), which
+// saves the select a pass over the scores.
 //
 // Prefill: the causal product Q_idx K_idx^T on the matrix cores (bf16 MFMA 16x16x32, fp32
 // accumulate), skipping tiles above the diagonal.
-#include "device_common.h"
+#include "select_common.h"
 
 namespace clsa {
 
@@ -53,6 +54,7 @@ __global__ __launch_bounds__(kIdxThreads) void k_index_scores_decode(const uint1
                                                                        int max_row_len, int chunk,
                                                                        float* __restrict__ scores, int64_t ld,
                                                                        uint16_t* __restrict__ hpart,
+                                                                       uint32_t* __restrict__ hinfo, int topk,
                                                                        int hpart_chunks, uint32_t* __restrict__ clear,
                                                                        int n_clear) {
   constexpr int LPR = D / 8;   // lanes per K_idx row (16 bytes each)
@@ -60,6 +62,8 @@ __global__ __launch_bounds__(kIdxThreads) void k_index_scores_decode(const uint1
   constexpr int NR = LPR;      // rows per lane per iteration: one finished row per lane
   constexpr int STEP = (kIdxThreads / 64) * 64;
   __shared__ uint32_t hist[kTopkBins];
+  __shared__ int scan[2 * kIdxThreads / 64];
+  __shared__ int res[4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lg = lane / LPR, sub = lane % LPR;
   const int b = blockIdx.y;
@@ -113,7 +117,7 @@ __global__ __launch_bounds__(kIdxThreads) void k_index_scores_decode(const uint1
     __syncthreads();
     // bins 2i and 2i + 1 as the low and high halves of one word (counts <= chunk <= 65535)
     uint32_t* hp = reinterpret_cast<uint32_t*>(hpart + ((int64_t)b * hpart_chunks + c) * kTopkBins);
-    for (int i = threadIdx.x; i < kTopkBins / 2; i += blockDim.x) hp[i] = hist[2 * i] | (hist[2 * i + 1] << 16);
+    write_hist_partial<kIdxThreads>(hist, t1 - t0, topk, hp, hinfo + (int64_t)b * hpart_chunks + c, scan, res);
   }
 }
 
@@ -169,17 +173,17 @@ __global__ __launch_bounds__(256) void k_index_scores_prefill(const uint16_t* __
 }  // namespace
 
 int launch_index_scores_decode(const RowsDev& rows, int d_idx, int chunk, const uint16_t* q_idx, int64_t q_stride,
-                               const uint16_t* k_idx, float* scores, int64_t ld, uint16_t* hpart, uint32_t* clear,
-                               int n_clear, void* stream) {
+                               const uint16_t* k_idx, float* scores, int64_t ld, uint16_t* hpart, uint32_t* hinfo,
+                               int topk, uint32_t* clear, int n_clear, void* stream) {
   const int chunks = (rows.max_row_len + chunk - 1) / chunk;
   const dim3 grid((unsigned)chunks, (unsigned)rows.n_rows);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (d_idx == 128)
     hipLaunchKernelGGL(k_index_scores_decode<128>, grid, dim3(kIdxThreads), 0, s, q_idx, q_stride, k_idx, rows.cu,
-                       rows.max_row_len, chunk, scores, ld, hpart, chunks, clear, n_clear);
+                       rows.max_row_len, chunk, scores, ld, hpart, hinfo, topk, chunks, clear, n_clear);
   else
     hipLaunchKernelGGL(k_index_scores_decode<64>, grid, dim3(kIdxThreads), 0, s, q_idx, q_stride, k_idx, rows.cu,
-                       rows.max_row_len, chunk, scores, ld, hpart, chunks, clear, n_clear);
+                       rows.max_row_len, chunk, scores, ld, hpart, hinfo, topk, chunks, clear, n_clear);
   return (int)hipGetLastError();
 }
 

@@ -87,6 +87,7 @@ struct SelectArgs {
   int32_t* out;
   int32_t* count;
   uint16_t* hpart;        // [R, hist_chunks, kTopkBins] per-chunk histograms of key >> (32 - kTopkBinBits)
+  uint32_t* hinfo;        // [R, hist_chunks] window start | full flag of each partial (write_hist_partial)
   int hist_chunk;         // scores per partial
   int hist_chunks;
   uint32_t* ticket;       // [R], zero on entry
@@ -103,6 +104,8 @@ constexpr int kHistThreads = 256;
 // Histogram partials of the scores (used when no score kernel produced them); clears the tickets.
 __global__ __launch_bounds__(kHistThreads) void k_topk_hist_partials(SelectArgs a) {
   __shared__ uint32_t hist[kTopkBins];
+  __shared__ int scan[2 * kHistThreads / 64];
+  __shared__ int res[4];
   const int r = blockIdx.y, c = blockIdx.x;
   if (r == 0 && c == 0)
     for (int i = threadIdx.x; i < a.rw.n_rows; i += blockDim.x) a.ticket[i] = 0u;
@@ -126,12 +129,13 @@ __global__ __launch_bounds__(kHistThreads) void k_topk_hist_partials(SelectArgs 
       if (i0 + j * kHistThreads < t1) atomicAdd(&hist[score_key(v[j]) >> (32 - kTopkBinBits)], 1u);
   }
   __syncthreads();
-  uint16_t* hp = a.hpart + ((int64_t)r * a.hist_chunks + c) * kTopkBins;
-  for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) hp[i] = (uint16_t)hist[i];
+  uint32_t* hp = reinterpret_cast<uint32_t*>(a.hpart + ((int64_t)r * a.hist_chunks + c) * kTopkBins);
+  write_hist_partial<kHistThreads>(hist, t1 - t0, a.k, hp, a.hinfo + (int64_t)r * a.hist_chunks + c, scan, res);
 }
 
 // Long-row select.  Workgroup (span, row) handles scores [span * kSelectSpan, +kSelectSpan).
-//  1. Sum the row's histogram partials; find the bin t1 holding the m-th largest key.
+//  1. Sum the row's histogram partials (exact from the largest window start up, see
+//     write_hist_partial); find the bin t1 holding the m-th largest key.
 //  2. Append (key, index) of every score whose bin is >= t1 to the span's slot, in index order.
 //  3. The last workgroup of the row (ticket) concatenates the span lists (still in index order),
 //     refines the exact m-th largest key T over the remaining key bits, and writes the output:
@@ -198,30 +202,9 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select(SelectArgs a) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) x[j] = i0 + j < s1 ? srow[i0 + j] : 0.f;
   }
-  // 1. row histogram from the partials: thread t sums bin pair t (one 32-bit word of each
-  //    partial) over the row's chunks and owns those two bins
-  {
-    const int nch = (n + a.hist_chunk - 1) / a.hist_chunk;
-    const uint32_t* hp = reinterpret_cast<const uint32_t*>(a.hpart + (int64_t)r * a.hist_chunks * kTopkBins);
-    constexpr int kBatch = 16;
-    uint32_t lo = 0, hi = 0;
-    for (int c0 = 0; c0 < nch; c0 += kBatch) {
-      uint32_t v[kBatch];
-#pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        const int c = c0 + j;
-        v[j] = c < nch ? hp[(int64_t)c * (kTopkBins / 2) + threadIdx.x] : 0u;
-      }
-#pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        lo += v[j] & 0xFFFFu;
-        hi += v[j] >> 16;
-      }
-    }
-    hist[2 * threadIdx.x] = lo;
-    hist[2 * threadIdx.x + 1] = hi;
-  }
-  __syncthreads();
+  // 1. the row's histogram from the chunk partials (exact from the largest window start up)
+  sum_hist_partials<kSelThreads>(reinterpret_cast<const uint32_t*>(a.hpart + (int64_t)r * a.hist_chunks * kTopkBins),
+                                 a.hinfo + (int64_t)r * a.hist_chunks, (n + a.hist_chunk - 1) / a.hist_chunk, hist);
   find_bin_from_top(hist, m, scan, res);
   const uint32_t t1 = (uint32_t)res[0];
   const int above1 = res[1];
@@ -284,6 +267,7 @@ int launch_topk(const RowsDev& rows, int k, const TopkPlan& plan, const float* s
   a.out = idx;
   a.count = count;
   a.hpart = reinterpret_cast<uint16_t*>(w + plan.hpart_off);
+  a.hinfo = reinterpret_cast<uint32_t*>(w + plan.hinfo_off);
   a.hist_chunk = plan.hist_chunk;
   a.hist_chunks = plan.hist_chunks;
   a.ticket = tickets;

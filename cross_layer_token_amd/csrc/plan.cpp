@@ -98,6 +98,8 @@ TopkPlan plan_topk(const clsa_dims* d, const clsa_rows* r) {
   size_t off = 0;
   p.hpart_off = off;
   off = align_up(off + R * p.hist_chunks * kTopkBins * 2, 256);
+  p.hinfo_off = off;
+  off = align_up(off + R * p.hist_chunks * 4, 256);
   p.cnt_off = off;
   off = align_up(off + R * p.spans * 4, 256);
   p.slot_off = off;

@@ -35,6 +35,117 @@ __device__ __forceinline__ void radix_pass8(uint32_t* hist, int count, KeyAt key
   need -= res[1];
 }
 
+// ---- windowed histogram partials ------------------------------------------------------------
+// A chunk of at least m keys can bound the row's first-level bin t1 (the bin of the row's m-th
+// largest key) from below by the bin lo of its own m-th largest key, since the row's m-th largest
+// is at least the chunk's.  So the chunk publishes its histogram only from lo up, kHistWin bins,
+// when its top bin lies inside that window; otherwise (or with fewer than m keys) it publishes
+// all kTopkBins bins.  Summing every chunk's partial as it stands gives exact counts for every bin
+// at or above the largest lo, t1 among them, which is all the top-down search for t1 reads.
+// Layout per chunk: kTopkBins / 2 words (bins 2i and 2i + 1 in the halves of word i; a window
+// uses the first kHistWin / 2 words, bins lo + 2i and lo + 2i + 1), and one info word lo | full.
+constexpr int kHistWin = 128;
+constexpr uint32_t kHistFull = 1u << 31;
+
+// Two searches of find_bin_from_top_block in one scan: res[0], res[1] for need0 and res[2],
+// res[3] for need1 (1 <= need <= the histogram's total).  Ends with __syncthreads().
+template <int NT>
+__device__ void find_two_bins_from_top_block(const uint32_t* hist, int need0, int need1, int* scan, int* res) {
+  static_assert(kTopkBins % NT == 0, "whole bins per thread");
+  constexpr int B = kTopkBins / NT;
+  const int hi = kTopkBins - 1 - B * (int)threadIdx.x;
+  int h[B], loc = 0;
+#pragma unroll
+  for (int j = 0; j < B; ++j) {
+    h[j] = (int)hist[hi - j];
+    loc += h[j];
+  }
+  int total;
+  int run = block_exclusive_scan(loc, scan, &total);
+#pragma unroll
+  for (int j = 0; j < B; ++j) {
+    if (run < need0 && run + h[j] >= need0) {
+      res[0] = hi - j;
+      res[1] = run;
+    }
+    if (run < need1 && run + h[j] >= need1) {
+      res[2] = hi - j;
+      res[3] = run;
+    }
+    run += h[j];
+  }
+  __syncthreads();
+}
+
+// Writes a chunk's partial from its complete LDS histogram of len keys (NT threads, all calling).
+template <int NT>
+__device__ void write_hist_partial(const uint32_t* hist, int len, int m, uint32_t* hp, uint32_t* info, int* scan,
+                                   int* res) {
+  int lo = 0;
+  bool full = true;
+  if (m >= 1 && len >= m) {
+    find_two_bins_from_top_block<NT>(hist, 1, m, scan, res);
+    lo = res[2];
+    full = res[0] - lo >= kHistWin;
+  }
+  if (full) {
+    for (int i = threadIdx.x; i < kTopkBins / 2; i += NT) hp[i] = hist[2 * i] | (hist[2 * i + 1] << 16);
+  } else {
+    for (int i = threadIdx.x; i < kHistWin / 2; i += NT) {
+      const int b = lo + 2 * i;
+      const uint32_t h0 = b < kTopkBins ? hist[b] : 0u, h1 = b + 1 < kTopkBins ? hist[b + 1] : 0u;
+      hp[i] = h0 | (h1 << 16);
+    }
+  }
+  if (threadIdx.x == 0) *info = (uint32_t)lo | (full ? kHistFull : 0u);
+}
+
+// Sums the row's chunk partials into the LDS histogram hist (NT threads; nch chunks, the partial
+// of chunk c at hp + c * kTopkBins / 2).  Window words and info words are requested kSumBatch
+// chunk groups at a time; hist is cleared while the first batch is in flight.  Ends with
+// __syncthreads().
+template <int NT>
+__device__ void sum_hist_partials(const uint32_t* hp, const uint32_t* info, int nch, uint32_t* hist) {
+  constexpr int kWords = kHistWin / 2;
+  constexpr int kGroup = NT / kWords;  // chunks per pass
+  constexpr int kSumBatch = 8;
+  const int w = threadIdx.x % kWords, cg = threadIdx.x / kWords;
+  bool cleared = false;
+  for (int cb = 0; cb < nch; cb += kGroup * kSumBatch) {
+    uint32_t iv[kSumBatch], wv[kSumBatch];
+#pragma unroll
+    for (int p = 0; p < kSumBatch; ++p) {
+      const int c = cb + p * kGroup + cg;
+      iv[p] = c < nch ? info[c] : 0u;
+      wv[p] = c < nch ? hp[(int64_t)c * (kTopkBins / 2) + w] : 0u;
+    }
+    if (!cleared) {
+      for (int i = threadIdx.x; i < kTopkBins; i += NT) hist[i] = 0u;
+      __syncthreads();
+      cleared = true;
+    }
+#pragma unroll
+    for (int p = 0; p < kSumBatch; ++p) {
+      const int c = cb + p * kGroup + cg;
+      if (c >= nch) continue;
+      if (iv[p] & kHistFull) {
+        for (int i = w; i < kTopkBins / 2; i += kWords) {
+          const uint32_t v = i == w ? wv[p] : hp[(int64_t)c * (kTopkBins / 2) + i];
+          if (v & 0xFFFFu) atomicAdd(&hist[2 * i], v & 0xFFFFu);
+          if (v >> 16) atomicAdd(&hist[2 * i + 1], v >> 16);
+        }
+      } else {
+        const int b = (int)(iv[p] & (kTopkBins - 1)) + 2 * w;
+        if ((wv[p] & 0xFFFFu) && b < kTopkBins) atomicAdd(&hist[b], wv[p] & 0xFFFFu);
+        if ((wv[p] >> 16) && b + 1 < kTopkBins) atomicAdd(&hist[b + 1], wv[p] >> 16);
+      }
+    }
+  }
+  if (!cleared)
+    for (int i = threadIdx.x; i < kTopkBins; i += NT) hist[i] = 0u;
+  __syncthreads();
+}
+
 // Gathers the row's span counts into span_pre[0..nsp] (prefix counts, span_pre[nsp] = L) and
 // returns L.  NT threads, kMaxSpansSel >= nsp spans; the first kSpecPerLane * 64 entries of the
 // first NSPEC spans of every wave are requested together with the counts, so a typical row needs

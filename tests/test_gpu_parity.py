@@ -328,6 +328,49 @@ def test_step_decode_heavy_ties_long_rows(lo, hi, den):
         _say(f"heavy ties, schedule {schedule}: {w.n_rows} rows match")
 
 
+def test_step_decode_k_near_the_median_of_a_chunk():
+    """k = 490 against 1024-token chunks of tie-heavy scores ({-1, 0, 1} / 4 indexer entries, about
+    485 positive scores per chunk): a chunk's 490th largest score is a small positive value or zero
+    or below, so some chunks publish a window of their histogram and the others (the m-th largest
+    far below their top bin) the whole histogram.  Every row against the oracle, both schedules."""
+    w = cs.custom(seq_lens=(40000, 30000), d_idx=128, topk=490, n_layers=2, hq=8, hkv=2, idx_lo=-1, idx_hi=1,
+                  idx_den=4, needles=3, seed=47, name="k_near_median")
+    dw = device_workload(w)
+    for schedule in (clsa.SCHEDULE_LAYER_BATCHED, clsa.SCHEDULE_PER_LAYER):
+        idx, cnt, out = _run_step(dw, schedule)
+        dev = bf16_dev_to_f64(out)
+        for r in range(w.n_rows):
+            res = oracle_row(w, r)
+            assert cnt[r] == res["count"]
+            assert np.array_equal(idx[r], res["idx"]), f"row {r}: {np.sum(idx[r] != res['idx'])} index mismatches"
+            assert_outputs_close(dev[r], res["out"], f"k near median row {r}")
+        _say(f"k near the chunk median, schedule {schedule}: {w.n_rows} rows match")
+
+
+@pytest.mark.parametrize("lens,planted", [
+    ((16000, 20000), ((0, 2048, 1024),)),
+    ((200000, 150000), tuple((0, c * 1024, 100) for c in range(20)) + tuple((1, c * 1024 + 500, 100) for c in range(20))),
+], ids=["one_chunk_lds", "twenty_chunks_in_place"])
+def test_step_decode_chunk_holding_the_largest_keys(lens, planted):
+    """The row's largest keys packed into a few stretches of tokens instead of spread over the
+    row: needles fill one 1024-token stretch (the candidate lists of the spans are then very
+    uneven), or twenty stretches of 100 tokens at 1024-token spacing in each of two long rows.
+    Every row against the oracle, both schedules."""
+    w = cs.custom(seq_lens=lens, d_idx=128, topk=2048, n_layers=2, hq=8, hkv=2, needles=0, seed=43,
+                  name="packed_needles", planted=planted)
+    dw = device_workload(w)
+    for schedule in (clsa.SCHEDULE_LAYER_BATCHED, clsa.SCHEDULE_PER_LAYER):
+        idx, cnt, out = _run_step(dw, schedule)
+        dev = bf16_dev_to_f64(out)
+        for r in range(w.n_rows):
+            res = oracle_row(w, r)
+            assert cnt[r] == res["count"]
+            assert np.array_equal(idx[r], res["idx"]), f"row {r}: {np.sum(idx[r] != res['idx'])} index mismatches"
+            assert set(w.needle_positions_of_row(r)) <= set(idx[r].tolist())
+            assert_outputs_close(dev[r], res["out"], f"packed needles row {r}")
+        _say(f"packed needles {lens}, schedule {schedule}: {w.n_rows} rows match")
+
+
 @pytest.mark.parametrize("cfg,check", [(1, None), (2, [0, 7]), (3, [4])])
 def test_step_per_layer_routing_vs_oracle(cfg, check):
     """The ablation without the shared index: every layer scores the cache with its own indexer

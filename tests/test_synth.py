@@ -67,6 +67,19 @@ def test_needle_rows_are_twice_the_query():
         assert np.array_equal(k, np.broadcast_to(2.0 * w.q_idx_f64([r])[0], k.shape))
 
 
+def test_planted_needles_fill_their_range_and_join_the_drawn_ones():
+    w = cs.custom(seq_lens=(3000, 2000), d_idx=64, topk=32, needles=4, seed=7, planted=((1, 100, 50),))
+    pos1 = w.needle_positions_of_row(1)
+    assert set(range(100, 150)) <= set(pos1) and len(pos1) == len(set(pos1)) >= 50
+    assert len(w.needle_positions_of_row(0)) == 4
+    k = w.k_idx_f64(w.cu_seqlens[1] + np.arange(100, 150))
+    assert np.array_equal(k, np.broadcast_to(2.0 * w.q_idx_f64([1])[0], k.shape))
+    # a token next to the range keeps its drawn values
+    plain = cs.custom(seq_lens=(3000, 2000), d_idx=64, topk=32, needles=4, seed=7)
+    t = [w.cu_seqlens[1] + 150, w.cu_seqlens[1] + 99]
+    assert np.array_equal(w.k_idx_bits(t), plain.k_idx_bits(t))
+
+
 def test_ragged_lengths_log_uniform():
     w = cs.config(5)
     lens = np.array(w.seq_lens)
