@@ -315,7 +315,7 @@ clsa_status clsa_step(const clsa_dims* dims, const clsa_rows* rows, const clsa_s
     const int R = rows->n_rows;
     const int ichunk = tp.multi_wg ? tp.hist_chunk : idx_chunk_for(R, rows->max_row_len);
     // as in the layer-batched step, the attention workgroups finish each layer's long-row selection
-    const bool fused = tp.multi_wg && ap.teams == 2 && ap.keys_per_split <= kFusedMaxIds;
+    const bool fused = tp.multi_wg && ap.teams == 2 && ap.wpt == 4 && ap.keys_per_split <= kFusedMaxIds;
     SelectIn sel;
     if (fused) {
       sel.slot = topk_ws + tp.slot_off;

@@ -71,8 +71,9 @@ struct TopkPlan {
 struct AttnPlan {
   int group = 0;           // hq / hkv query heads per KV head
   int qrows = 0;           // query rows per (row, KV head) = n_layers_call * group
-  int qblocks = 0;         // blocks of 64 query rows
-  int teams = 2;           // four-wave teams per workgroup (1 or 2)
+  int qblocks = 0;         // blocks of 16 wpt query rows
+  int teams = 2;           // teams per workgroup (1 or 2)
+  int wpt = 4;             // waves per team (4, or 2 for rows of at most 32 query rows with many blocks)
   int splits = 1;          // the selected rows are split over this many workgroups
   int keys_per_split = 0;  // multiple of kAttnTile
   size_t part_bytes = 0;   // fp32 partials [splits, R, hkv, qblocks, kAttnPartFloats] when splits > 1

@@ -85,30 +85,38 @@ __device__ __forceinline__ uint2 lds_read_tr(const uint16_t* p) {
   return __builtin_bit_cast(uint2, v);
 }
 
-// One stage = 2 tiles of 64 keys in LDS (2 x 32 KB).  A workgroup is TEAMS teams of four waves
-// that all serve the same 64 query rows:
-//  * TEAMS = 2 (one 8-wave workgroup per CU): team t computes tile t of every stage, so each
-//    wave does one tile per stage; at the end the two teams merge their (m, l, acc) through LDS.
-//    Used when there are few (row, KV head) blocks and the keys are split across workgroups.
-//  * TEAMS = 1 (two 4-wave workgroups per CU): every wave computes both tiles.  Used when there
-//    are many blocks, so that two rows' gathers are in flight per CU.
+// One stage = 2 tiles of 64 keys in LDS (2 x 32 KB).  A workgroup is TEAMS teams of WPT waves
+// that all serve the same 16 WPT query rows (one 16-column MFMA block per wave):
+//  * TEAMS = 2, WPT = 4 (one 8-wave workgroup per CU): team t computes tile t of every stage, so
+//    each wave does one tile per stage; at the end the two teams merge their (m, l, acc) through
+//    LDS.  Used when there are few (row, KV head) blocks and the keys are split across
+//    workgroups.
+//  * TEAMS = 1, WPT = 4 (two 4-wave workgroups per CU): every wave computes both tiles.  Used
+//    when there are many blocks, so that two rows' gathers are in flight per CU.
+//  * TEAMS = 2, WPT = 2 (two 4-wave workgroups per CU): as TEAMS = 1 for rows of at most 32
+//    query rows (prefill: L x Hq / Hkv = 32), where one team of four waves would leave two of
+//    them, and so two of the CU's four SIMDs, without MFMA work.
 // The next stage's rows are in flight into registers while the current one is computed.
 constexpr int kAttnTiles = 2;
-constexpr int kAttnWavesPerTeam = 4;
 // log2 of the growth of the running max that is absorbed without rescaling (P <= 2^this).
 constexpr float kRescaleLog2 = 8.f;
 // Split partials fetched per round trip by the combining workgroup.
 constexpr int kCombineBatch = 4;
 
-// SELECT (with FROM_CACHE and TEAMS = 2): the workgroup first finishes the row's long-row
-// selection itself from the span lists of the select (see k_topk_select<false>) and keeps its
-// split's token ids in LDS, instead of reading them from idx.
-template <bool FROM_CACHE, int TEAMS, bool SELECT = false>
-__global__ __launch_bounds__(kAttnWaveThreads * TEAMS, 2 / TEAMS) void k_sparse_attn(AttnArgs a) {
+// SELECT (with FROM_CACHE, TEAMS = 2 and WPT = 4): the workgroup first finishes the row's
+// long-row selection itself from the span lists of the select (see k_topk_select<false>) and
+// keeps its split's token ids in LDS, instead of reading them from idx.
+template <bool FROM_CACHE, int TEAMS, bool SELECT = false, int WPT = 4>
+__global__ __launch_bounds__(64 * WPT * TEAMS, 64 * WPT * TEAMS == 512 ? 1 : 2) void k_sparse_attn(AttnArgs a) {
+  constexpr int NTH = 64 * WPT * TEAMS;            // threads
+  constexpr int QB = 16 * WPT;                     // query rows per block
   constexpr int STAGE = kAttnTiles * kAttnTile;
   constexpr int TILE_ELEMS = kAttnTile * CLSA_HEAD_DIM;
   constexpr int TPT = kAttnTiles / TEAMS;          // tiles each team computes per stage
-  constexpr int LPT = 4 * TPT;                     // K (and V) pieces each thread loads per stage
+  constexpr int TPP = NTH / 256;                   // tiles the loader covers per group of 4 pieces
+  constexpr int LPT = 4 * (kAttnTiles / TPP);      // K (and V) pieces each thread loads per stage
+  static_assert(NTH == 256 || NTH == 512, "four or eight waves");
+  static_assert(!SELECT || WPT == 4, "the fused selection runs on eight-wave workgroups");
   static_assert(TEAMS == 1 || TEAMS == 2, "one or two teams");
   // tiles: K of tile t at t * TILE_ELEMS, V of tile t at (kAttnTiles + t) * TILE_ELEMS; the same
   // memory holds the team exchange at the end
@@ -118,7 +126,7 @@ __global__ __launch_bounds__(kAttnWaveThreads * TEAMS, 2 / TEAMS) void k_sparse_
   static_assert(!SELECT || (FROM_CACHE && TEAMS == 2), "the fused selection reads the cache with two teams");
   static_assert(kListLds * sizeof(uint2) <= sizeof(lds), "the candidate list fits the tile buffers");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int team = wave / kAttnWavesPerTeam, tw = wave % kAttnWavesPerTeam;
+  const int team = wave / WPT, tw = wave % WPT;
   const int l16 = lane & 15, grp = lane >> 4;
   int bid = blockIdx.x;
   const int split = bid % a.splits;
@@ -132,8 +140,8 @@ __global__ __launch_bounds__(kAttnWaveThreads * TEAMS, 2 / TEAMS) void k_sparse_
   const int kend = kend_raw < cnt ? kend_raw : cnt;
 
   // this lane's query column: query row qr -> (layer, head) of the GQA group of KV head g
-  const int qr = qb * 64 + tw * 16 + l16;
-  const bool wave_active = qb * 64 + tw * 16 < a.qrows;
+  const int qr = qb * QB + tw * 16 + l16;
+  const bool wave_active = qb * QB + tw * 16 < a.qrows;
   const bool q_valid = qr < a.qrows;
   const int layer = q_valid ? qr / a.group : 0;
   const int head = g * a.group + (q_valid ? qr % a.group : 0);
@@ -171,7 +179,7 @@ __global__ __launch_bounds__(kAttnWaveThreads * TEAMS, 2 / TEAMS) void k_sparse_
       const int nsp = (n + kSelectSpan - 1) / kSelectSpan;
       const uint2* rslot = a.sel_slot + (int64_t)r * a.rw.max_row_len;
       uint2* list_lds = reinterpret_cast<uint2*>(lds);  // the tiles are not in use yet
-      const int L = collect_candidates<kAttnWaveThreads * TEAMS, 2, kMaxSelectSpans>(
+      const int L = collect_candidates<NTH, 2, kMaxSelectSpans>(
           rslot, a.sel_cnt + (int64_t)r * a.sel_spans, nsp, n, sl.span_pre, sl.scan, list_lds, nullptr);
       const bool writer = split == 0 && qb == 0 && g == 0;
       int32_t* orow = a.idx_out + (int64_t)r * a.k;
@@ -210,11 +218,11 @@ __global__ __launch_bounds__(kAttnWaveThreads * TEAMS, 2 / TEAMS) void k_sparse_
     }
   };
   // loader mapping: thread -> one 16-byte chunk of head_dim of keys 4 (ld_key4 % 16) + i (i < 4)
-  // of the tiles ld_key4 / 16 + TEAMS * t (t < TPT)
+  // of the tiles ld_key4 / 16 + TPP * t (t < kAttnTiles / TPP)
   const int ld_chunk = threadIdx.x & 15;
-  const int ld_key4 = threadIdx.x >> 4;  // 0 .. 16 TEAMS - 1
+  const int ld_key4 = threadIdx.x >> 4;  // 0 .. 16 TPP - 1
   auto piece_key = [&](int p) {           // stage-relative key of load piece p (< LPT)
-    return ((ld_key4 >> 4) + TEAMS * (p >> 2)) * kAttnTile + (ld_key4 & 15) * 4 + (p & 3);
+    return ((ld_key4 >> 4) + TPP * (p >> 2)) * kAttnTile + (ld_key4 & 15) * 4 + (p & 3);
   };
   // the next stage's K and V pieces of this thread, in flight while the current stage is computed
   uint4 rk[LPT], rv[LPT];
@@ -407,7 +415,7 @@ __global__ __launch_bounds__(kAttnWaveThreads * TEAMS, 2 / TEAMS) void k_sparse_
   // Merge team 1 into team 0 through LDS (the tiles are free after the loop's last barrier):
   // per wave [acc: 8 ht x 4 j x 64 lanes][m: 64][l: 64], fp32.
   float* xch = reinterpret_cast<float*>(lds) + tw * kAttnPartWave;
-  static_assert(kAttnWavesPerTeam * kAttnPartWave * 4 <= (int)sizeof(lds), "team exchange fits the tiles");
+  static_assert(WPT * kAttnPartWave * 4 <= (int)sizeof(lds), "team exchange fits the tiles");
   if (TEAMS == 2 && team == 1 && wave_active) {
 #pragma unroll
     for (int ht = 0; ht < 8; ++ht)
@@ -582,14 +590,20 @@ int launch_attn(const RowsDev& rows, int k, int hq, int hkv, int n_layers_call, 
   a.idx_out = idx_out;
   a.count_out = count_out;
   const bool fused = sel != nullptr;
-  if (fused && (plan.teams != 2 || ksel != nullptr || plan.keys_per_split > kFusedMaxIds || idx_out == nullptr ||
+  if (fused && (plan.teams != 2 || plan.wpt != 4 || ksel != nullptr || plan.keys_per_split > kFusedMaxIds || idx_out == nullptr ||
                 count_out == nullptr))
     return (int)hipErrorInvalidValue;
   if (plan.splits > 1 && !tickets_clear)
     hipLaunchKernelGGL(k_clear_u32, dim3((plan.tickets + 255) / 256), dim3(256), 0, s, tickets, plan.tickets);
   const dim3 grid((unsigned)(plan.splits * plan.qblocks * hkv), (unsigned)rows.n_rows);
-  const dim3 block((unsigned)(kAttnWaveThreads * plan.teams));
-  if (plan.teams == 2) {
+  const dim3 block((unsigned)(64 * plan.wpt * plan.teams));
+  if (plan.teams == 2 && plan.wpt == 2) {
+    if (fused) return (int)hipErrorInvalidValue;
+    if (from_cache)
+      hipLaunchKernelGGL((k_sparse_attn<true, 2, false, 2>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((k_sparse_attn<false, 2, false, 2>), grid, block, 0, s, a);
+  } else if (plan.teams == 2) {
     if (fused)
       hipLaunchKernelGGL((k_sparse_attn<true, 2, true>), grid, block, 0, s, a);
     else if (from_cache)

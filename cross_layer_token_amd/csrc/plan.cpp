@@ -122,6 +122,13 @@ AttnPlan plan_attn(const clsa_dims* d, int n_rows, int n_layers_call, int split_
   const int64_t base = (int64_t)(split_rows > 0 ? split_rows : n_rows) * d->hkv * p.qblocks;
   const int tiles = (d->topk + kAttnTile - 1) / kAttnTile;
   p.teams = base >= kAttnManyBlocks ? 1 : 2;
+  if (p.teams == 1 && p.qrows <= 32) {
+    // one team of four waves would leave half of them (two SIMDs of the CU) without MFMA work:
+    // two teams of two waves split each stage's tiles instead
+    p.teams = 2;
+    p.wpt = 2;
+    p.qblocks = (p.qrows + 31) / 32;
+  }
   int splits = 1;
   if (p.teams == 2 && base < CLSA_ATTN_TARGET_WGS) splits = (int)((CLSA_ATTN_TARGET_WGS + base - 1) / base);
   if (splits > kMaxAttnSplits) splits = kMaxAttnSplits;
@@ -154,7 +161,7 @@ StepPlan plan_step(const clsa_dims* d, const clsa_rows* r, int schedule, bool us
   // depend on the chunk size; buffers are sized for the largest chunk
   s.attn = plan_attn(d, s.chunk_rows, lc, r->n_rows);
   s.ld_scores = (int64_t)align_up((size_t)r->max_row_len, 64);
-  s.fused_select = !prefill && schedule == CLSA_SCHEDULE_LAYER_BATCHED && s.topk.multi_wg && s.attn.teams == 2 &&
+  s.fused_select = !prefill && schedule == CLSA_SCHEDULE_LAYER_BATCHED && s.topk.multi_wg && s.attn.teams == 2 && s.attn.wpt == 4 &&
                    s.attn.keys_per_split <= kFusedMaxIds;
   size_t off = 0;
   s.ticket_off = off;
