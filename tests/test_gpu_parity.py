@@ -416,6 +416,23 @@ def test_step_prefill_vs_oracle(schedule):
     assert set(w.needle_positions_of_row(n - 1)) <= set(idx[n - 1].tolist())
 
 
+@pytest.mark.parametrize("n_layers,hq,hkv", [(2, 8, 2), (12, 16, 4)], ids=["8_query_rows", "48_query_rows"])
+def test_step_prefill_query_rows_per_kv_head(n_layers, hq, hkv):
+    """Prefill rows with 8 query rows per KV head (two teams of two waves, one of them with no
+    query columns) and with 48 (one team of four waves, 64-row blocks): every 25th row and the
+    k-boundary rows against the oracle, layer-batched."""
+    w = cs.custom(mode="prefill", seq_lens=(1500,), d_idx=64, topk=256, n_layers=n_layers, hq=hq, hkv=hkv, seed=53,
+                  name=f"prefill_q{n_layers * hq // hkv}")
+    dw = device_workload(w)
+    idx, cnt, out = _run_step(dw, clsa.SCHEDULE_LAYER_BATCHED, chunk=700)
+    assert np.array_equal(cnt, np.minimum(np.arange(1, w.n_rows + 1), w.topk))
+    dev = bf16_dev_to_f64(out)
+    for t in sorted(set(range(0, w.n_rows, 25)) | {254, 255, 256, 257, w.n_rows - 1}):
+        res = oracle_row(w, t)
+        assert np.array_equal(idx[t], res["idx"]), f"row {t}"
+        assert_outputs_close(dev[t], res["out"], f"prefill row {t}")
+
+
 def test_step_prefill_chunking_invariance():
     w = cs.config(4)
     dw = device_workload(w)
