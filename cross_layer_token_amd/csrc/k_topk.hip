@@ -220,11 +220,21 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select(SelectArgs a) {
     int tot;
     int pos = block_exclusive_scan(c, scan, &tot);
     uint2* slot = a.slot + (int64_t)r * a.rw.max_row_len + s0;
+    // the row's last workgroup of this kernel reads the lists (device scope); without FINISH only
+    // a later kernel does, and plain stores suffice
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if ((i0 + j < s1) && (key[j] >> (32 - kTopkBinBits)) >= t1)
-        st_dev(reinterpret_cast<uint64_t*>(slot + pos++), ((uint64_t)(uint32_t)(i0 + j) << 32) | key[j]);
-    if (threadIdx.x == 0) st_dev(&a.cnt[(int64_t)r * a.spans + sp], (uint32_t)tot);
+    for (int j = 0; j < 8; ++j) {
+      if ((i0 + j < s1) && (key[j] >> (32 - kTopkBinBits)) >= t1) {
+        const uint64_t e = ((uint64_t)(uint32_t)(i0 + j) << 32) | key[j];
+        if (FINISH) st_dev(reinterpret_cast<uint64_t*>(slot + pos), e);
+        else *reinterpret_cast<uint64_t*>(slot + pos) = e;
+        ++pos;
+      }
+    }
+    if (threadIdx.x == 0) {
+      if (FINISH) st_dev(&a.cnt[(int64_t)r * a.spans + sp], (uint32_t)tot);
+      else a.cnt[(int64_t)r * a.spans + sp] = (uint32_t)tot;
+    }
   }
   if (!FINISH) {
     if (sp == 0 && threadIdx.x == 0) {
