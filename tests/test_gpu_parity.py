@@ -152,6 +152,19 @@ def test_topk_matches_oracle_on_given_scores(kind, k, lengths):
         assert np.array_equal(idx[i], want), f"{kind} k={k} n={lengths[i]}: {np.sum(idx[i] != want)} mismatches"
 
 
+@pytest.mark.parametrize("kind,k", [("ties", 65536), ("normal", 2048)])
+def test_topk_at_the_maximum_row_length(kind, k):
+    """One row of CLSA_MAX_ROW_LEN = 2^24 scores (2048 select spans, the most a row has), at the
+    largest k (65536: the candidate list far exceeds LDS and is refined in the workspace) and at
+    the 128K workload's k."""
+    n = 1 << 24
+    rng = np.random.default_rng(61 if kind == "ties" else 62)
+    s = _score_rows(kind, [n], rng)[0]
+    idx, cnt = _run_topk_decode([s], k)
+    want, m = O.pad_selection(O.topk_select(s.astype(np.float64), k), k)
+    assert cnt[0] == m and np.array_equal(idx[0], want), f"{np.sum(idx[0] != want)} mismatches"
+
+
 def test_topk_prefill_rows_lds_path():
     rng = np.random.default_rng(5)
     n, k = 3000, 256
@@ -369,6 +382,20 @@ def test_step_decode_chunk_holding_the_largest_keys(lens, planted):
             assert set(w.needle_positions_of_row(r)) <= set(idx[r].tolist())
             assert_outputs_close(dev[r], res["out"], f"packed needles row {r}")
         _say(f"packed needles {lens}, schedule {schedule}: {w.n_rows} rows match")
+
+
+def test_step_decode_at_the_largest_k():
+    """k = CLSA_MAX_TOPK = 65536 of a 100000-token row (one KV head, so one attention block split
+    16 ways over 4096 keys each): selection and attention against the oracle, both schedules."""
+    w = cs.custom(seq_lens=(100000,), d_idx=64, topk=65536, n_layers=2, hq=4, hkv=1, needles=4, seed=67,
+                  name="largest_k")
+    dw = device_workload(w)
+    res = oracle_row(w, 0)
+    for schedule in (clsa.SCHEDULE_LAYER_BATCHED, clsa.SCHEDULE_PER_LAYER):
+        idx, cnt, out = _run_step(dw, schedule)
+        assert cnt[0] == res["count"] == 65536
+        assert np.array_equal(idx[0], res["idx"]), f"{np.sum(idx[0] != res['idx'])} index mismatches"
+        assert_outputs_close(bf16_dev_to_f64(out)[0], res["out"], f"largest k, schedule {schedule}")
 
 
 @pytest.mark.parametrize("cfg,check", [(1, None), (2, [0, 7]), (3, [4])])
