@@ -70,12 +70,12 @@ def measured_traffic(bytes_alg_launch: float):
 # ---- rocprofv3 summaries (text under profiles/, made from rocprofv3's own CSV output) ----------
 WORKLOAD_TAG = "decode_b16_n128k"
 PROFILE_COMMANDS = {
-    "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_trace -o bench -- "
+    "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d rocprof_out/trace -o bench -- "
              "python3 bench.py --steps 20 --warmup 3 --no-cpu-baseline --no-prefill",
-    "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof_fetch -o bench -- "
+    "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d rocprof_out/fetch -o bench -- "
              "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-per-layer --no-prefill --no-append --no-distill "
              "--profile-copy-mib 1024",
-    "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof_write -o bench -- "
+    "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d rocprof_out/write -o bench -- "
              "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-per-layer --no-prefill --no-append --no-distill "
              "--profile-copy-mib 1024",
 }

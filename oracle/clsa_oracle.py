@@ -20,7 +20,7 @@ Sources (page titles as published; sections named on the page):
   and section CLSA: Sharing the Index Across Layers (the Selector gathers KV
   rows by the shared index).
 
-Readings taken where the pages leave a step open (each is listed in the design doc):
+Readings taken where the pages leave a step open:
 
 * scores: plain dot product, no scale, no activation, single head;
 * decode row b sees all N_b cached tokens; prefill row t sees tokens 0..t;
