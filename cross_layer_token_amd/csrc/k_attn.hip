@@ -239,7 +239,8 @@ __global__ __launch_bounds__(64 * WPT * TEAMS, 64 * WPT * TEAMS == 512 ? 1 : 2) 
       else if (FROM_CACHE) ids[i] = irow[ids[i]];  // clamped when used, so the load is not waited for here
     }
   };
-  // 64-bit base of this (row, KV head) once; per-row offsets then fit 32 bits
+  // 64-bit base of this (row, KV head) once, and 64-bit row offsets: a row may see 2^24 tokens of
+  // hkv * 128 elements
   const int row_elems = FROM_CACHE ? a.hkv * CLSA_HEAD_DIM : CLSA_HEAD_DIM;
   const int64_t base_off = FROM_CACHE ? (tok_base * a.hkv + g) * CLSA_HEAD_DIM
                                       : (((int64_t)r * a.hkv + g) * a.k) * CLSA_HEAD_DIM;
@@ -248,7 +249,7 @@ __global__ __launch_bounds__(64 * WPT * TEAMS, 64 * WPT * TEAMS == 512 ? 1 : 2) 
   auto load_stage = [&](const int (&ids)[LPT]) {
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
-      const uint32_t off = (uint32_t)(FROM_CACHE ? tok(ids[i]) : ids[i]) * (uint32_t)row_elems;
+      const int64_t off = (int64_t)(FROM_CACHE ? tok(ids[i]) : ids[i]) * row_elems;
       rk[i] = load16(kbase + off);
       rv[i] = load16(vbase + off);
     }

@@ -165,6 +165,36 @@ def test_topk_at_the_maximum_row_length(kind, k):
     assert cnt[0] == m and np.array_equal(idx[0], want), f"{np.sum(idx[0] != want)} mismatches"
 
 
+def test_sparse_attn_reads_cache_rows_past_2_to_the_32_elements():
+    """A 5M-token sequence with 8 KV heads: a cache row is hkv * 128 = 1024 elements, so every
+    token from 2^22 on lies more than 2^32 elements into the cache.  Attention over 1024 selected
+    tokens spread over the whole sequence (about a sixth of them past 2^22), read from the cache
+    and from the gathered compact buffer, against the oracle."""
+    n, k = 5_000_000, 1024
+    w = cs.custom(seq_lens=(n,), d_idx=64, topk=k, n_layers=2, hq=16, hkv=8, seed=71, name="long_cache")
+    dw = device_workload(w)
+    sel = np.sort(np.random.default_rng(71).choice(n, k, replace=False))
+    assert (sel >= (1 << 22)).sum() > 100
+    idx = torch.from_numpy(sel.astype(np.int32)[None, :]).cuda()
+    cnt = torch.tensor([k], dtype=torch.int32, device="cuda")
+    kf, vf = w.kv_f64(sel)                       # sequence 0 starts at cache row 0
+    ref = O.sparse_attention(w.q_f64([0])[0], kf, vf)
+    dims, rows = dims_of(dw), rows_of(dw)
+    L, hq = w.n_layers, w.hq
+    row_el = L * hq * 128
+    ws, nws = workspace(dims, rows, clsa.SCHEDULE_PER_LAYER)
+    ksel = torch.empty((1, w.hkv, k, 128), dtype=torch.int16, device="cuda")
+    vsel = torch.empty_like(ksel)
+    clsa.gather_kv(dims, rows, dw.k_cache, dw.v_cache, dw.cu_seqlens, idx, cnt, ksel, vsel)
+    for src in ("cache", "compact"):
+        out = torch.zeros((1, L, hq, 128), dtype=torch.int16, device="cuda")
+        ks_, vs_ = (ksel, vsel) if src == "compact" else (None, None)
+        clsa.sparse_attn(dims, rows, dw.q, row_el, L, ks_, vs_, dw.k_cache, dw.v_cache, dw.cu_seqlens, idx, cnt, out,
+                         row_el, ws, nws)
+        torch.cuda.synchronize()
+        assert_outputs_close(bf16_dev_to_f64(out)[0], ref, f"5M-token cache, {src}")
+
+
 def test_topk_prefill_rows_lds_path():
     rng = np.random.default_rng(5)
     n, k = 3000, 256
