@@ -15,8 +15,6 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
-__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
-
 // fp32 -> bf16 round-to-nearest-even (inputs here are finite).
 __device__ __forceinline__ uint32_t f32_to_bf16(float x) {
   uint32_t u = __float_as_uint(x);

@@ -24,8 +24,6 @@ constexpr int kAttnWaveThreads = 256;  // threads of one team (four waves)
 constexpr int kAttnPartWave = 34 * 64;             // floats per wave: acc 32 x 64 lanes, m, l
 constexpr int kAttnPartWG = 4 * kAttnPartWave;     // floats per workgroup partial (team 0's four waves)
 static_assert(kAttnPartWG == kAttnPartFloats, "partial record layout");
-constexpr int kKsStride = CLSA_HEAD_DIM + 8;  // bf16 elements per K row in LDS (16-byte pad)
-constexpr int kVtStride = kAttnTile + 4;      // bf16 elements per transposed V row in LDS
 
 struct AttnArgs {
   RowsDev rw;
