@@ -54,7 +54,7 @@ template <bool SELECT>
 struct SelectLds {};
 template <>
 struct SelectLds<true> {
-  uint32_t hist[256];
+  uint32_t hist[512];
   int scan[2 * 2 * kAttnWaveThreads / 64];
   int res[2];
   int span_pre[kMaxSelectSpans + 1];
@@ -132,6 +132,17 @@ __global__ __launch_bounds__(64 * WPT * TEAMS, 64 * WPT * TEAMS == 512 ? 1 : 2) 
   const int qb = bid % a.qblocks;
   const int g = bid / a.qblocks;
   const int r = blockIdx.y;
+  // The fused selection's loads (span counts, the first entries of the span lists, t1 and the count
+  // above it) are requested first, bounded by the buffers' extents rather than by the row length,
+  // whose own load would otherwise have to complete before them.
+  CandidateLoads<NTH, 2, kMaxSelectSpans> cq;
+  uint32_t sel_t1 = 0u, sel_above1 = 0u;
+  if constexpr (SELECT) {
+    request_candidates<false>(cq, a.sel_slot + (int64_t)r * a.rw.max_row_len, a.sel_cnt + (int64_t)r * a.sel_spans,
+                              a.sel_spans, a.rw.max_row_len);
+    sel_t1 = a.sel_rowinfo[2 * r];
+    sel_above1 = a.sel_rowinfo[2 * r + 1];
+  }
   const int cnt = SELECT ? min(a.k, row_len(a.rw, r)) : a.count[r];
   const int kbeg = split * a.kps;
   const int kend_raw = kbeg + a.kps;
@@ -172,13 +183,12 @@ __global__ __launch_bounds__(64 * WPT * TEAMS, 64 * WPT * TEAMS == 512 ? 1 : 2) 
     if (n <= a.k) {  // every visible token is selected (the select wrote idx and count already)
       for (int i = threadIdx.x; i < nk; i += blockDim.x) sl.ids[i] = kbeg + i;
     } else {
-      const uint32_t t1 = a.sel_rowinfo[2 * r];
-      const int above1 = (int)a.sel_rowinfo[2 * r + 1];
+      const uint32_t t1 = sel_t1;
+      const int above1 = (int)sel_above1;
       const int nsp = (n + kSelectSpan - 1) / kSelectSpan;
       const uint2* rslot = a.sel_slot + (int64_t)r * a.rw.max_row_len;
       uint2* list_lds = reinterpret_cast<uint2*>(lds);  // the tiles are not in use yet
-      const int L = collect_candidates<NTH, 2, kMaxSelectSpans>(
-          rslot, a.sel_cnt + (int64_t)r * a.sel_spans, nsp, n, sl.span_pre, sl.scan, list_lds, nullptr);
+      const int L = complete_candidates<false>(cq, rslot, nsp, sl.span_pre, sl.scan, list_lds, nullptr);
       const bool writer = split == 0 && qb == 0 && g == 0;
       int32_t* orow = a.idx_out + (int64_t)r * a.k;
       auto emit = [&](int pos, int32_t t) {
@@ -186,7 +196,8 @@ __global__ __launch_bounds__(64 * WPT * TEAMS, 64 * WPT * TEAMS == 512 ? 1 : 2) 
         if (writer) orow[pos] = t;
       };
       if (L <= kListLds) {
-        refine_and_emit([&](int i) { return list_lds[i]; }, L, cnt, t1, above1, sl.hist, sl.scan, sl.res, emit);
+        static_assert(kListLds % NTH == 0, "the LDS list fits the threads' registers");
+        refine_and_emit_regs<kListLds / NTH>(list_lds, L, cnt, t1, above1, sl.hist, sl.scan, sl.res, emit);
       } else {
         // too many candidates for LDS: read them in place, span found by binary search
         auto at = [&](int i) {

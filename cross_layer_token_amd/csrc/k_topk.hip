@@ -20,7 +20,6 @@ namespace clsa {
 namespace {
 
 constexpr int kRowThreads = 512;
-constexpr int kPassThreads = 256;
 
 __device__ void write_all(int32_t* out, int32_t* count, int r, int n, int k) {
   for (int i = threadIdx.x; i < k; i += blockDim.x) out[(int64_t)r * k + i] = i < n ? i : -1;

@@ -146,37 +146,63 @@ __device__ void sum_hist_partials(const uint32_t* hp, const uint32_t* info, int 
   __syncthreads();
 }
 
-// Gathers the row's span counts into span_pre[0..nsp] (prefix counts, span_pre[nsp] = L) and
-// returns L.  NT threads, kMaxSpansSel >= nsp spans; the first kSpecPerLane * 64 entries of the
-// first NSPEC spans of every wave are requested together with the counts, so a typical row needs
-// one round trip.  When L <= kListLds the span lists are concatenated into list_lds, otherwise
-// into list_global when it is given; with neither the lists stay in the spans.  Reads use
-// device-scope loads, so the spans may come from other workgroups of the same kernel.  Ends with
-// __syncthreads().
+// Candidate collection, in two halves so that its loads can be issued before the row length is
+// known.  request_candidates loads the span counts of this thread (spans tid * SPT .. + SPT - 1)
+// and the first kSpecPerLane * 64 entries of the first NSPEC spans of every wave, bounded by
+// span_bound spans and len_bound entries (the buffers' extents, or the row's own).
+// complete_candidates then gathers the counts of the row's nsp spans into span_pre[0..nsp]
+// (prefix counts, span_pre[nsp] = L) and returns L.  When L <= kListLds the span lists are
+// concatenated into list_lds, otherwise into list_global when it is given; with neither the lists
+// stay in the spans.  DEV selects device-scope loads, for spans written by other workgroups of the
+// same kernel.  complete_candidates ends with __syncthreads().
 template <int NT, int NSPEC, int kMaxSpansSel>
-__device__ int collect_candidates(const uint2* slot, const uint32_t* cnt, int nsp, int n, int* span_pre, int* scan,
-                                  uint2* list_lds, uint2* list_global) {
+struct CandidateLoads {
   static_assert(kMaxSpansSel % NT == 0, "whole spans per thread");
-  constexpr int SPT = kMaxSpansSel / NT;  // span counts per thread
+  static constexpr int SPT = kMaxSpansSel / NT;  // span counts per thread
+  uint64_t spec[NSPEC][kSpecPerLane];
+  uint32_t c[SPT];
+};
+
+template <bool DEV>
+__device__ __forceinline__ uint64_t load_entry(const uint2* p) {
+  if constexpr (DEV) return ld_dev(reinterpret_cast<const uint64_t*>(p));
+  else return *reinterpret_cast<const uint64_t*>(p);
+}
+
+template <bool DEV, int NT, int NSPEC, int kMaxSpansSel>
+__device__ __forceinline__ void request_candidates(CandidateLoads<NT, NSPEC, kMaxSpansSel>& q, const uint2* slot,
+                                                   const uint32_t* cnt, int span_bound, int len_bound) {
   constexpr int kWaves = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint64_t spec[NSPEC][kSpecPerLane];
 #pragma unroll
   for (int u = 0; u < NSPEC; ++u) {
     const int sp = wave + u * kWaves;
 #pragma unroll
     for (int j = 0; j < kSpecPerLane; ++j) {
-      const int e = sp * kSelectSpan + j * 64 + lane;  // stays inside the row's scores
-      spec[u][j] = (sp < nsp && e < n) ? ld_dev(reinterpret_cast<const uint64_t*>(slot + e)) : 0;
+      const int e = sp * kSelectSpan + j * 64 + lane;
+      q.spec[u][j] = (sp < span_bound && e < len_bound) ? load_entry<DEV>(slot + e) : 0;
     }
   }
+#pragma unroll
+  for (int i = 0; i < q.SPT; ++i) {
+    const int sp = threadIdx.x * q.SPT + i;
+    q.c[i] = sp < span_bound ? (DEV ? ld_dev(&cnt[sp]) : cnt[sp]) : 0u;
+  }
+}
+
+template <bool DEV, int NT, int NSPEC, int kMaxSpansSel>
+__device__ int complete_candidates(const CandidateLoads<NT, NSPEC, kMaxSpansSel>& q, const uint2* slot, int nsp,
+                                   int* span_pre, int* scan, uint2* list_lds, uint2* list_global) {
+  constexpr int kWaves = NT / 64;
+  constexpr int SPT = kMaxSpansSel / NT;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int L = 0;
   {
     int c[SPT], mine = 0;
 #pragma unroll
     for (int i = 0; i < SPT; ++i) {
       const int sp = threadIdx.x * SPT + i;
-      c[i] = sp < nsp ? (int)ld_dev(&cnt[sp]) : 0;
+      c[i] = sp < nsp ? (int)q.c[i] : 0;  // counts past the row's spans are not the row's
       mine += c[i];
     }
     int pre = block_exclusive_scan(mine, scan, &L);
@@ -202,7 +228,7 @@ __device__ int collect_candidates(const uint2* slot, const uint32_t* cnt, int ns
 #pragma unroll
         for (int j = 0; j < kSpecPerLane; ++j) {
           const int e = j * 64 + lane;
-          if (e < cnt_s) list[base + e] = make_uint2((uint32_t)spec[uu][j], (uint32_t)(spec[uu][j] >> 32));
+          if (e < cnt_s) list[base + e] = make_uint2((uint32_t)q.spec[uu][j], (uint32_t)(q.spec[uu][j] >> 32));
         }
       }
       e0 = kSpecPerLane * 64;
@@ -212,7 +238,7 @@ __device__ int collect_candidates(const uint2* slot, const uint32_t* cnt, int ns
 #pragma unroll
       for (int j = 0; j < kCopyBatch; ++j) {
         const int e = e0 + j * 64 + lane;
-        v[j] = e < cnt_s ? ld_dev(reinterpret_cast<const uint64_t*>(src + e)) : 0;
+        v[j] = e < cnt_s ? load_entry<DEV>(src + e) : 0;
       }
 #pragma unroll
       for (int j = 0; j < kCopyBatch; ++j) {
@@ -223,6 +249,15 @@ __device__ int collect_candidates(const uint2* slot, const uint32_t* cnt, int ns
   }
   __syncthreads();
   return L;
+}
+
+// Both halves at once, bounded by the row (spans written by other workgroups of this kernel).
+template <int NT, int NSPEC, int kMaxSpansSel>
+__device__ int collect_candidates(const uint2* slot, const uint32_t* cnt, int nsp, int n, int* span_pre, int* scan,
+                                  uint2* list_lds, uint2* list_global) {
+  CandidateLoads<NT, NSPEC, kMaxSpansSel> q;
+  request_candidates<true>(q, slot, cnt, nsp, n);
+  return complete_candidates<true>(q, slot, nsp, span_pre, scan, list_lds, list_global);
 }
 
 // Refines the m-th largest key T below the first level (bin t1, `above1` keys in higher bins)
@@ -266,6 +301,70 @@ __device__ void refine_and_emit(EntryAt entry_at, int L, int m, uint32_t t1, int
       if (take && pos < m) emit(pos, (int32_t)e.y);
       gt_before += e.x > T;
       eq_before += e.x == T;
+    }
+  }
+}
+
+// refine_and_emit for a candidate list in LDS of at most blockDim.x * EMAX entries: each thread
+// keeps its contiguous range of E = ceil(L / blockDim.x) entries in registers for all passes, and
+// the 8-bit passes alternate between the two 256-bin halves of hist2 (one half is cleared while
+// the other is searched), so a pass costs two barriers and no list reads.  Same selection, same
+// positions.  Every thread calls this; it ends without a barrier after the emits.
+template <int EMAX, typename Emit>
+__device__ void refine_and_emit_regs(const uint2* list, int L, int m, uint32_t t1, int above1, uint32_t* hist2,
+                                     int* scan, int* res, Emit emit) {
+  const int E = (L + (int)blockDim.x - 1) / (int)blockDim.x;  // <= EMAX, checked by the caller
+  const int p0 = threadIdx.x * E;
+  uint32_t key[EMAX];
+  int32_t tok[EMAX];
+  bool ok[EMAX];
+#pragma unroll
+  for (int j = 0; j < EMAX; ++j) {
+    ok[j] = j < E && p0 + j < L;
+    const uint2 e = ok[j] ? list[p0 + j] : make_uint2(0u, 0u);
+    key[j] = e.x;
+    tok[j] = (int32_t)e.y;
+  }
+  for (int i = threadIdx.x; i < 512; i += blockDim.x) hist2[i] = 0u;
+  __syncthreads();
+  int need = m - above1;
+  uint32_t prefix = t1 << (32 - kTopkBinBits), pmask = ~0u << (32 - kTopkBinBits);
+  int half = 0;
+  for (int shift = 32 - kTopkBinBits - 8;; shift -= 8) {
+    if (shift < 0) shift = 0;
+    uint32_t* h = hist2 + 256 * half;
+#pragma unroll
+    for (int j = 0; j < EMAX; ++j)
+      if (ok[j] && (key[j] & pmask) == prefix) atomicAdd(&h[(key[j] >> shift) & 255u], 1u);
+    __syncthreads();
+    // the other half was last searched in the previous pass (finished by its barrier) and is next
+    // counted into after this pass's barrier
+    uint32_t* o = hist2 + 256 * (half ^ 1);
+    for (int i = threadIdx.x; i < 256; i += blockDim.x) o[i] = 0u;
+    find_bin256_from_top(h, need, res);
+    prefix |= (uint32_t)res[0] << shift;
+    pmask |= 255u << shift;
+    need -= res[1];
+    if (shift == 0) break;
+    half ^= 1;
+  }
+  const uint32_t T = prefix;
+  int gt = 0, eq = 0;
+#pragma unroll
+  for (int j = 0; j < EMAX; ++j) {
+    gt += ok[j] && key[j] > T;
+    eq += ok[j] && key[j] == T;
+  }
+  int gt_before, eq_before, tg, te;
+  block_exclusive_scan2(gt, eq, scan, &gt_before, &eq_before, &tg, &te);
+#pragma unroll
+  for (int j = 0; j < EMAX; ++j) {
+    if (ok[j]) {
+      const bool take = key[j] > T || (key[j] == T && eq_before < need);
+      const int pos = gt_before + (eq_before < need ? eq_before : need);
+      if (take && pos < m) emit(pos, tok[j]);
+      gt_before += key[j] > T;
+      eq_before += key[j] == T;
     }
   }
 }
