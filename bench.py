@@ -28,7 +28,8 @@ METRIC = "decode tokens/sec + HBM GB/s (% roofline), index+top-k+L-layer attn at
 # hidden width of the new-token indexer projections timed beside the step (the pages give none;
 # a round width of the order of the 4B-parameter models they evaluate)
 APPEND_D_MODEL = 4096
-INDEX_KERNEL_SOURCES = ["cross_layer_token_amd/csrc/k_index.hip", "cross_layer_token_amd/csrc/device_common.h"]
+INDEX_KERNEL_SOURCES = ["cross_layer_token_amd/csrc/k_index.hip", "cross_layer_token_amd/csrc/select_common.h",
+                        "cross_layer_token_amd/csrc/device_common.h", "cross_layer_token_amd/csrc/clsa_internal.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_index_scores_decode_b16_n128k.json")
 
 
