@@ -36,6 +36,7 @@ RowsDev rows_dev(const clsa_rows* r, const int32_t* cu) {
   d.seq = r->seq;
   d.pos0 = r->pos0;
   d.max_row_len = r->max_row_len;
+  d.total_tokens = r->total_tokens;
   d.cu = cu;
   return d;
 }
@@ -118,8 +119,8 @@ clsa_status clsa_index_scores(const clsa_dims* dims, const clsa_rows* rows, cons
   const RowsDev rd = rows_dev(rows, cu_seqlens);
   int e;
   if (rows->mode == CLSA_MODE_DECODE)
-    e = launch_index_scores_decode(rd, dims->d_idx, idx_chunk_for(rows->n_rows, rows->max_row_len), q_idx,
-                                   dims->d_idx, k_idx, scores, ld_scores, nullptr, nullptr, 0, nullptr, 0, stream);
+    e = launch_index_scores_decode(rd, dims->d_idx, idx_seg_for(rows->total_tokens), q_idx, dims->d_idx, k_idx,
+                                   scores, ld_scores, nullptr, nullptr, 0, 0, nullptr, 0, stream);
   else
     e = launch_index_scores_prefill(rd, dims->d_idx, q_idx, k_idx, scores, ld_scores, nullptr, 0, stream);
   return device_status(e, "clsa_index_scores");
@@ -313,7 +314,7 @@ clsa_status clsa_step(const clsa_dims* dims, const clsa_rows* rows, const clsa_s
     float* scores = reinterpret_cast<float*>(ws + sp.scores_off);
     const AttnPlan ap = plan_attn(dims, rows->n_rows, 1, rows->n_rows);
     const int R = rows->n_rows;
-    const int ichunk = tp.multi_wg ? tp.hist_chunk : idx_chunk_for(R, rows->max_row_len);
+    const int iseg = tp.multi_wg ? tp.hist_chunk : idx_seg_for(rows->total_tokens);
     // as in the layer-batched step, the attention workgroups finish each layer's long-row selection
     const bool fused = tp.multi_wg && ap.teams == 2 && ap.wpt == 4 && ap.keys_per_split <= kFusedMaxIds;
     SelectIn sel;
@@ -326,9 +327,9 @@ clsa_status clsa_step(const clsa_dims* dims, const clsa_rows* rows, const clsa_s
     for (int l = 0; l < L; ++l) {
       uint16_t* hpart = tp.multi_wg ? reinterpret_cast<uint16_t*>(topk_ws + tp.hpart_off) : nullptr;
       uint32_t* hinfo = tp.multi_wg ? reinterpret_cast<uint32_t*>(topk_ws + tp.hinfo_off) : nullptr;
-      int e = launch_index_scores_decode(rd, dims->d_idx, ichunk, a->q_idx + (int64_t)l * dims->d_idx,
+      int e = launch_index_scores_decode(rd, dims->d_idx, iseg, a->q_idx + (int64_t)l * dims->d_idx,
                                          (int64_t)L * dims->d_idx, a->k_idx, scores, sp.ld_scores, hpart, hinfo, k,
-                                         tickets, sp.n_tickets, stream);
+                                         tp.hist_chunks, tickets, sp.n_tickets, stream);
       if (e) return device_status(e, "clsa_step: index scores of a layer");
       int32_t* idx = a->idx + (int64_t)l * R * k;
       int32_t* count = a->count + (int64_t)l * R;
@@ -370,9 +371,9 @@ clsa_status clsa_step(const clsa_dims* dims, const clsa_rows* rows, const clsa_s
       uint16_t* hpart = tp.multi_wg ? reinterpret_cast<uint16_t*>(topk_ws + tp.hpart_off) : nullptr;
       uint32_t* hinfo = tp.multi_wg ? reinterpret_cast<uint32_t*>(topk_ws + tp.hinfo_off) : nullptr;
       have_hist = tp.multi_wg;
-      const int chunk = tp.multi_wg ? tp.hist_chunk : idx_chunk_for(cr.n_rows, cr.max_row_len);
-      e = launch_index_scores_decode(rd, dims->d_idx, chunk, q_idx, dims->d_idx, a->k_idx, scores, ld, hpart, hinfo,
-                                     k, tickets, sp.n_tickets, stream);
+      const int seg = tp.multi_wg ? tp.hist_chunk : idx_seg_for(cr.total_tokens);
+      e = launch_index_scores_decode(rd, dims->d_idx, seg, q_idx, dims->d_idx, a->k_idx, scores, ld, hpart, hinfo,
+                                     k, tp.hist_chunks, tickets, sp.n_tickets, stream);
     }
     if (e) return device_status(e, "clsa_step: index scores");
     int32_t* idx = a->idx + (int64_t)c0 * k;

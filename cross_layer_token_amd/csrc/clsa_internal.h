@@ -14,9 +14,13 @@ namespace clsa {
 // Rows no longer than this are selected by one workgroup holding the whole row in LDS;
 // longer rows use the multi-workgroup histogram select.
 constexpr int kLdsRowCap = 12288;
-// Tokens per workgroup of the decode score kernel (also the histogram partial granularity):
+// Tokens per workgroup of the decode score kernel (also the histogram partial granularity).
+// Decode: the sequences' tokens, concatenated as they lie in the cache, are cut into segments of
+// about total / kIdxMinWorkgroups tokens (idx_seg_for), so that every workgroup streams the same
+// share of K_idx whatever the mix of sequence lengths; a segment may hold the end of one sequence
+// and the start of the next.  Prefill rows and scores from the caller: per-row chunks of
 // kIdxChunkMax when that still gives kIdxMinWorkgroups workgroups, else halved down to
-// kIdxChunkMin (see idx_chunk_for).
+// kIdxChunkMin (idx_chunk_for).
 constexpr int kIdxChunkMax = 8192;
 constexpr int kIdxChunkMin = 1024;
 constexpr int kIdxMinWorkgroups = 256;
@@ -55,8 +59,8 @@ constexpr int kPrefillChunkRows = 1024;
 // ---- host-side plan (pure functions, no HIP) ------------------------------------------------
 struct TopkPlan {
   bool multi_wg = false;   // long rows: histogram select over many workgroups
-  int hist_chunk = 0;      // scores per histogram partial (= the score kernel's chunk)
-  int hist_chunks = 0;     // histogram partials per row
+  int hist_chunk = 0;      // tokens per histogram partial (the score kernel's segment or chunk)
+  int hist_chunks = 0;     // histogram partials per row (a decode row may straddle one more segment)
   int spans = 0;           // select workgroups per row (kSelectSpan scores each)
   size_t hpart_off = 0;    // uint16 [R, hist_chunks, kTopkBins]: per-chunk partials (full or windowed)
   size_t hinfo_off = 0;    // uint32 [R, hist_chunks]: window start | full flag of each partial
@@ -106,6 +110,7 @@ clsa_status check_ptr_opt(const void* p, const char* name, std::string& err);
 TopkPlan plan_topk(const clsa_dims* d, const clsa_rows* r);
 // Tokens per workgroup of the decode score kernel for n_rows rows of at most max_row_len tokens.
 int idx_chunk_for(int n_rows, int max_row_len);
+int idx_seg_for(int64_t total_tokens);
 // n_rows: rows of this launch (buffer sizes); split_rows: rows that decide the split count
 // (0 = n_rows).
 AttnPlan plan_attn(const clsa_dims* d, int n_rows, int n_layers_call, int split_rows);
@@ -138,15 +143,17 @@ DistillPlan plan_distill(const clsa_dims* d, const clsa_rows* r);
 // All return hipSuccess-or-error as an int (0 = success) so this header needs no HIP include.
 struct RowsDev {
   int mode, n_rows, seq, pos0, max_row_len;
+  int64_t total_tokens;
   const int32_t* cu;  // device cu_seqlens
 };
 
 // `clear` (n_clear words) is zeroed by the launch before any other kernel of the call reads it.
-// hpart / hinfo (with topk): also write each chunk's top-k histogram partial.
-int launch_index_scores_decode(const RowsDev& rows, int d_idx, int chunk, const uint16_t* q_idx, int64_t q_stride,
-                               const uint16_t* k_idx,
-                               float* scores, int64_t ld, uint16_t* hpart, uint32_t* hinfo, int topk, uint32_t* clear,
-                               int n_clear, void* stream);
+// seg: tokens per workgroup over the concatenated sequences (idx_seg_for).  hpart / hinfo (with
+// topk): also write, for every (row, segment) piece, the top-k histogram partial at slot
+// segment - floor(cu[row] / seg) of the row's hpart_chunks.
+int launch_index_scores_decode(const RowsDev& rows, int d_idx, int seg, const uint16_t* q_idx, int64_t q_stride,
+                               const uint16_t* k_idx, float* scores, int64_t ld, uint16_t* hpart, uint32_t* hinfo,
+                               int topk, int hpart_chunks, uint32_t* clear, int n_clear, void* stream);
 int launch_index_scores_prefill(const RowsDev& rows, int d_idx, const uint16_t* q_idx, const uint16_t* k_idx,
                                 float* scores, int64_t ld, uint32_t* clear, int n_clear, void* stream);
 // have_hist: the score kernel already wrote the histogram partials and cleared the tickets.

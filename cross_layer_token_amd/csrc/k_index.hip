@@ -2,9 +2,10 @@
 // picx.dev summary of "You Only Index Once" (Methodology > Architecture Overview, eq. 2).
 //
 // Decode: a bandwidth-bound GEMV that streams every K_idx row exactly once.  A workgroup owns
-// one chunk of one sequence.  Each 16-byte K_idx chunk meets the query chunk in v_dot2 (bf16 x
-// bf16 -> fp32), and the per-lane partial sums of 16 rows are reduce-scattered over the row's
-// lanes with DPP, so that every lane ends up owning one finished row score.  When asked, the
+// one equal segment of all the sequences' tokens.  Each 16-byte K_idx chunk meets the query
+// chunk in v_dot2 (bf16 x bf16 -> fp32), and the per-lane partial sums of 16 rows are
+// reduce-scattered over the row's lanes with DPP, so that every lane ends up owning one finished
+// row score.  When asked, the
 // workgroup also histograms the top key bits of its scores (the first level of the top-k
 // select) and publishes the part of the histogram the select needs (write_hist_partial), which
 // saves the select a pass over the scores.
@@ -41,17 +42,23 @@ __device__ __forceinline__ void rs_step(float* p, int sub) {
 
 constexpr int kIdxThreads = 256;
 
-// One workgroup = one chunk of `chunk` tokens of one sequence.  Each wave takes 64 rows per
-// iteration (16 per lane, one 16-byte piece of each) and requests the next iteration's rows
-// before reducing the current ones, so every wave keeps a full set of loads in flight.  Besides
-// the scores it can write the chunk's histogram of the top kTopkBinBits key bits (for the top-k
-// select) and clear the select's per-row tickets (consumed by later kernels on the same stream).
+// One workgroup = one segment of `seg` tokens of the sequences concatenated as they lie in the
+// cache (K_idx rows cu[b] .. cu[b + 1] - 1 belong to sequence b), so every workgroup streams the
+// same share of K_idx whatever the mix of sequence lengths.  It walks the pieces of the sequences
+// its segment overlaps, in order; each piece is scored with its sequence's query.  Each wave takes
+// 64 rows per iteration (16 per lane, one 16-byte piece of each) and requests the next
+// iteration's rows before reducing the current ones, so every wave keeps a full set of loads in
+// flight.  Besides the scores it can write, for every piece of a sequence longer than topk, the
+// histogram of the top kTopkBinBits key bits (for the top-k select), at slot
+// segment - floor(cu[b] / seg) of the sequence's partials, and clear the select's per-row tickets
+// (consumed by later kernels on the same stream).  Every K_idx row read lies inside the segment,
+// so the reads stay inside [0, total) whatever cu holds.
 template <int D>
 __global__ __launch_bounds__(kIdxThreads) void k_index_scores_decode(const uint16_t* __restrict__ q_idx,
                                                                        int64_t q_stride,
                                                                        const uint16_t* __restrict__ k_idx,
-                                                                       const int32_t* __restrict__ cu,
-                                                                       int max_row_len, int chunk,
+                                                                       const int32_t* __restrict__ cu, int n_rows,
+                                                                       int max_row_len, int seg, int64_t total,
                                                                        float* __restrict__ scores, int64_t ld,
                                                                        uint16_t* __restrict__ hpart,
                                                                        uint32_t* __restrict__ hinfo, int topk,
@@ -64,60 +71,104 @@ __global__ __launch_bounds__(kIdxThreads) void k_index_scores_decode(const uint1
   __shared__ uint32_t hist[kTopkBins];
   __shared__ int scan[2 * kIdxThreads / 64];
   __shared__ int res[4];
+  __shared__ int first_row, first_lo, first_hi;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lg = lane / LPR, sub = lane % LPR;
-  const int b = blockIdx.y;
-  const int c = blockIdx.x;
-  if (clear != nullptr && b == 0 && c == 0)
+  const int w = blockIdx.x;
+  if (clear != nullptr && w == 0)
     for (int i = threadIdx.x; i < n_clear; i += blockDim.x) clear[i] = 0u;
-  int n = cu[b + 1] - cu[b];
-  n = n < 0 ? 0 : (n > max_row_len ? max_row_len : n);
-  const int t0 = c * chunk;
-  if (t0 >= n) return;
-  const int t1 = t0 + chunk < n ? t0 + chunk : n;
-  if (hpart != nullptr) {
-    for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) hist[i] = 0u;
-    __syncthreads();
-  }
-  const uint16_t* kbase = k_idx + (int64_t)cu[b] * D + sub * 8;
-  const uint4 qv = *reinterpret_cast<const uint4*>(q_idx + (int64_t)b * q_stride + sub * 8);
-  float* srow = scores + (int64_t)b * ld;
+  // token offsets fit in 32 bits (cu_seqlens is int32): g0 = w * seg <= total - 1
+  const int g0 = w * seg;
+  const int g1 = (int)(total - g0 < seg ? total : g0 + seg);
+  // The first piece starts at g0, and K_idx rows are addressed by token alone: that piece's first
+  // iteration is requested before the search below (rows past the piece but inside the segment
+  // are read and not stored).
   uint4 kv[NR];
-  auto load = [&](int it) {
+  {
+    const uint16_t* kseg = k_idx + sub * 8;
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
-      const int row = it + i * NG + lg;
-      kv[i] = row < t1 ? load_stream16(kbase + (int64_t)row * D) : make_uint4(0u, 0u, 0u, 0u);
-    }
-  };
-  int it = t0 + wave * 64;
-  if (it < t1) load(it);
-  for (; it < t1; it += STEP) {
-    float p[NR];
-#pragma unroll
-    for (int i = 0; i < NR; ++i) p[i] = dot8(kv[i], qv, 0.f);
-    if (it + STEP < t1) load(it + STEP);
-    if constexpr (LPR == 16) {
-      rs_step<8, 8>(p, sub);
-      rs_step<4, 4>(p, sub);
-      rs_step<2, 2>(p, sub);
-      rs_step<1, 1>(p, sub);
-    } else {
-      rs_step<4, 4>(p, sub);
-      rs_step<2, 2>(p, sub);
-      rs_step<1, 1>(p, sub);
-    }
-    const int row = it + sub * NG + lg;
-    if (row < t1) {
-      srow[row] = p[0];
-      if (hpart != nullptr) atomicAdd(&hist[score_key(p[0]) >> (32 - kTopkBinBits)], 1u);
+      const int row = g0 + wave * 64 + i * NG + lg;
+      kv[i] = row < g1 ? load_stream16(kseg + (int64_t)row * D) : make_uint4(0u, 0u, 0u, 0u);
     }
   }
-  if (hpart != nullptr) {
-    __syncthreads();
-    // bins 2i and 2i + 1 as the low and high halves of one word (counts <= chunk <= 65535)
-    uint32_t* hp = reinterpret_cast<uint32_t*>(hpart + ((int64_t)b * hpart_chunks + c) * kTopkBins);
-    write_hist_partial<kIdxThreads>(hist, t1 - t0, topk, hp, hinfo + (int64_t)b * hpart_chunks + c, scan, res);
+  bool prefetched = true;
+  // the sequence holding token g0 (cu[b] <= g0 < cu[b + 1]); none found: nothing to do
+  if (threadIdx.x == 0) first_row = n_rows;
+  __syncthreads();
+  for (int j = threadIdx.x; j < n_rows; j += blockDim.x) {
+    const int c0 = cu[j], c1 = cu[j + 1];
+    if (c0 <= g0 && g0 < c1) {
+      first_row = j;
+      first_lo = c0;
+      first_hi = c1;
+    }
+  }
+  __syncthreads();
+  // the first sequence's bounds come from the search; each later one starts where the previous
+  // one ends, so only its end is loaded
+  int c0 = first_lo, c1 = first_hi;
+  for (int b = first_row; b < n_rows; ++b) {
+    if (b != first_row) {
+      c0 = c1;
+      c1 = cu[b + 1];
+    }
+    if (c0 >= g1) break;
+    int n = c1 - c0;
+    n = n < 0 ? 0 : (n > max_row_len ? max_row_len : n);
+    const int lo = g0 > c0 ? g0 : c0;
+    const int64_t e = (int64_t)c0 + n;
+    const int hi = (int)(e < g1 ? e : g1);
+    if (lo >= hi) continue;
+    const int t0 = lo - c0, t1 = hi - c0;  // the piece, in the sequence's own positions
+    const int slot = w - c0 / seg;
+    const int64_t rs = c0;
+    const bool do_hist = hpart != nullptr && n > topk && slot >= 0 && slot < hpart_chunks;
+    if (do_hist) {
+      for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) hist[i] = 0u;
+      __syncthreads();
+    }
+    const uint16_t* kbase = k_idx + rs * D + sub * 8;
+    const uint4 qv = *reinterpret_cast<const uint4*>(q_idx + (int64_t)b * q_stride + sub * 8);
+    float* srow = scores + (int64_t)b * ld;
+    auto load = [&](int it) {
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        const int row = it + i * NG + lg;
+        kv[i] = row < t1 ? load_stream16(kbase + (int64_t)row * D) : make_uint4(0u, 0u, 0u, 0u);
+      }
+    };
+    int it = t0 + wave * 64;
+    if (!(prefetched && lo == g0) && it < t1) load(it);  // else kv holds this iteration's rows already
+    prefetched = false;
+    for (; it < t1; it += STEP) {
+      float p[NR];
+#pragma unroll
+      for (int i = 0; i < NR; ++i) p[i] = dot8(kv[i], qv, 0.f);
+      if (it + STEP < t1) load(it + STEP);
+      if constexpr (LPR == 16) {
+        rs_step<8, 8>(p, sub);
+        rs_step<4, 4>(p, sub);
+        rs_step<2, 2>(p, sub);
+        rs_step<1, 1>(p, sub);
+      } else {
+        rs_step<4, 4>(p, sub);
+        rs_step<2, 2>(p, sub);
+        rs_step<1, 1>(p, sub);
+      }
+      const int row = it + sub * NG + lg;
+      if (row < t1) {
+        srow[row] = p[0];
+        if (do_hist) atomicAdd(&hist[score_key(p[0]) >> (32 - kTopkBinBits)], 1u);
+      }
+    }
+    if (do_hist) {
+      __syncthreads();
+      // bins 2i and 2i + 1 as the low and high halves of one word (counts <= seg <= 65535)
+      uint32_t* hp = reinterpret_cast<uint32_t*>(hpart + ((int64_t)b * hpart_chunks + slot) * kTopkBins);
+      write_hist_partial<kIdxThreads>(hist, t1 - t0, topk, hp, hinfo + (int64_t)b * hpart_chunks + slot, scan, res);
+      __syncthreads();  // hist is read by the partial's write before the next piece clears it
+    }
   }
 }
 
@@ -172,18 +223,20 @@ __global__ __launch_bounds__(256) void k_index_scores_prefill(const uint16_t* __
 
 }  // namespace
 
-int launch_index_scores_decode(const RowsDev& rows, int d_idx, int chunk, const uint16_t* q_idx, int64_t q_stride,
+int launch_index_scores_decode(const RowsDev& rows, int d_idx, int seg, const uint16_t* q_idx, int64_t q_stride,
                                const uint16_t* k_idx, float* scores, int64_t ld, uint16_t* hpart, uint32_t* hinfo,
-                               int topk, uint32_t* clear, int n_clear, void* stream) {
-  const int chunks = (rows.max_row_len + chunk - 1) / chunk;
-  const dim3 grid((unsigned)chunks, (unsigned)rows.n_rows);
+                               int topk, int hpart_chunks, uint32_t* clear, int n_clear, void* stream) {
+  const int64_t segs = (rows.total_tokens + seg - 1) / seg;
+  const dim3 grid((unsigned)(segs > 0 ? segs : 1));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (d_idx == 128)
     hipLaunchKernelGGL(k_index_scores_decode<128>, grid, dim3(kIdxThreads), 0, s, q_idx, q_stride, k_idx, rows.cu,
-                       rows.max_row_len, chunk, scores, ld, hpart, hinfo, topk, chunks, clear, n_clear);
+                       rows.n_rows, rows.max_row_len, seg, rows.total_tokens, scores, ld, hpart, hinfo, topk,
+                       hpart_chunks, clear, n_clear);
   else
     hipLaunchKernelGGL(k_index_scores_decode<64>, grid, dim3(kIdxThreads), 0, s, q_idx, q_stride, k_idx, rows.cu,
-                       rows.max_row_len, chunk, scores, ld, hpart, hinfo, topk, chunks, clear, n_clear);
+                       rows.n_rows, rows.max_row_len, seg, rows.total_tokens, scores, ld, hpart, hinfo, topk,
+                       hpart_chunks, clear, n_clear);
   return (int)hipGetLastError();
 }
 

@@ -87,8 +87,10 @@ struct SelectArgs {
   int32_t* count;
   uint16_t* hpart;        // [R, hist_chunks, kTopkBins] per-chunk histograms of key >> (32 - kTopkBinBits)
   uint32_t* hinfo;        // [R, hist_chunks] window start | full flag of each partial (write_hist_partial)
-  int hist_chunk;         // scores per partial
+  int hist_chunk;         // tokens per partial
   int hist_chunks;
+  int hist_flat;          // 1: the decode score kernel's partials, one per (row, segment of the
+                          // concatenated sequences); 0: per-row chunks from k_topk_hist_partials
   uint32_t* ticket;       // [R], zero on entry
   uint32_t* cnt;          // [R, spans]
   int spans;
@@ -201,9 +203,13 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select(SelectArgs a) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) x[j] = i0 + j < s1 ? srow[i0 + j] : 0.f;
   }
-  // 1. the row's histogram from the chunk partials (exact from the largest window start up)
+  // 1. the row's histogram from the chunk partials (exact from the largest window start up); a
+  //    decode row's partials are those of the segments its tokens cu[r] .. cu[r] + n - 1 fall in
+  const int hoff = a.hist_flat ? a.rw.cu[r] : 0;  // token offsets fit in 32 bits
+  const int nch_row = (hoff + n - 1) / a.hist_chunk - hoff / a.hist_chunk + 1;
+  const int nch = nch_row < a.hist_chunks ? nch_row : a.hist_chunks;
   sum_hist_partials<kSelThreads>(reinterpret_cast<const uint32_t*>(a.hpart + (int64_t)r * a.hist_chunks * kTopkBins),
-                                 a.hinfo + (int64_t)r * a.hist_chunks, (n + a.hist_chunk - 1) / a.hist_chunk, hist);
+                                 a.hinfo + (int64_t)r * a.hist_chunks, nch, hist);
   find_bin_from_top(hist, m, scan, res);
   const uint32_t t1 = (uint32_t)res[0];
   const int above1 = res[1];
@@ -279,6 +285,7 @@ int launch_topk(const RowsDev& rows, int k, const TopkPlan& plan, const float* s
   a.hinfo = reinterpret_cast<uint32_t*>(w + plan.hinfo_off);
   a.hist_chunk = plan.hist_chunk;
   a.hist_chunks = plan.hist_chunks;
+  a.hist_flat = have_hist ? 1 : 0;
   a.ticket = tickets;
   a.cnt = reinterpret_cast<uint32_t*>(w + plan.cnt_off);
   a.spans = plan.spans;

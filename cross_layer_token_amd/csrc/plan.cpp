@@ -86,13 +86,22 @@ int idx_chunk_for(int n_rows, int max_row_len) {
   return chunk;
 }
 
+int idx_seg_for(int64_t total_tokens) {
+  int64_t seg = (total_tokens + kIdxMinWorkgroups - 1) / kIdxMinWorkgroups;
+  seg = (seg + 63) / 64 * 64;
+  return (int)(seg < kIdxChunkMin ? kIdxChunkMin : (seg > kIdxChunkMax ? kIdxChunkMax : seg));
+}
+
 TopkPlan plan_topk(const clsa_dims* d, const clsa_rows* r) {
   TopkPlan p;
   p.multi_wg = r->max_row_len > kLdsRowCap;
   if (!p.multi_wg) return p;
   const size_t R = (size_t)r->n_rows;
-  p.hist_chunk = idx_chunk_for(r->n_rows, r->max_row_len);
-  p.hist_chunks = (r->max_row_len + p.hist_chunk - 1) / p.hist_chunk;
+  // decode partials come per (row, segment of the concatenated sequences), so a row may straddle
+  // one segment more than its length needs
+  const bool decode = r->mode == CLSA_MODE_DECODE;
+  p.hist_chunk = decode ? idx_seg_for(r->total_tokens) : idx_chunk_for(r->n_rows, r->max_row_len);
+  p.hist_chunks = (r->max_row_len + p.hist_chunk - 1) / p.hist_chunk + (decode ? 1 : 0);
   p.spans = (r->max_row_len + kSelectSpan - 1) / kSelectSpan;
   p.tickets = r->n_rows;
   size_t off = 0;

@@ -371,6 +371,26 @@ def test_step_decode_heavy_ties_long_rows(lo, hi, den):
         _say(f"heavy ties, schedule {schedule}: {w.n_rows} rows match")
 
 
+def test_step_decode_segments_spanning_several_sequences():
+    """The decode score kernel cuts the sequences' concatenated tokens into equal segments (1024
+    tokens here), so a segment can hold the end of one sequence, whole short sequences and the
+    start of the next.  Sequences at or below k (all taken), just above k (a partial in each of
+    two segments) and long ones, mixed: every row against the oracle, both schedules."""
+    lens = (13000, 300, 700, 1500, 90, 2100, 20000, 640, 999, 14000)
+    w = cs.custom(seq_lens=lens, d_idx=128, topk=512, n_layers=2, hq=8, hkv=2, needles=2, seed=71,
+                  name="segments_across_sequences")
+    dw = device_workload(w)
+    for schedule in (clsa.SCHEDULE_LAYER_BATCHED, clsa.SCHEDULE_PER_LAYER):
+        idx, cnt, out = _run_step(dw, schedule)
+        dev = bf16_dev_to_f64(out)
+        for r in range(w.n_rows):
+            res = oracle_row(w, r)
+            assert cnt[r] == res["count"]
+            assert np.array_equal(idx[r], res["idx"]), f"row {r}: {np.sum(idx[r] != res['idx'])} index mismatches"
+            assert_outputs_close(dev[r], res["out"], f"segments across sequences row {r}")
+        _say(f"segments across sequences, schedule {schedule}: {w.n_rows} rows match")
+
+
 def test_step_decode_k_near_the_median_of_a_chunk():
     """k = 490 against 1024-token chunks of tie-heavy scores ({-1, 0, 1} / 4 indexer entries, about
     485 positive scores per chunk): a chunk's 490th largest score is a small positive value or zero
