@@ -204,10 +204,7 @@ clsa_status clsa_topk(const clsa_dims* dims, const clsa_rows* rows, const int32_
   if (clsa_status s = check_workspace(workspace, workspace_bytes_, topk_workspace(dims, rows)); s != CLSA_OK)
     return s;
   const RowsDev rd = rows_dev(rows, cu_seqlens);
-  char* ws = static_cast<char*>(workspace);
-  uint32_t* tickets = reinterpret_cast<uint32_t*>(ws);
-  return device_status(launch_topk(rd, dims->topk, plan, scores, ld_scores, idx, count,
-                                   ws + ticket_region(plan.tickets), tickets, false, stream),
+  return device_status(launch_topk(rd, dims->topk, plan, scores, ld_scores, idx, count, workspace, false, stream),
                        "clsa_topk");
 }
 
@@ -302,10 +299,9 @@ clsa_status clsa_step(const clsa_dims* dims, const clsa_rows* rows, const clsa_s
   const int64_t row_elems = (int64_t)L * hq * CLSA_HEAD_DIM;
   const float scale = softmax_scale(dims);
   const int chunk = sp.chunk_rows;
-  // tickets: [top-k select, R][attention, R * hkv * qblocks]; the chunk's first kernel clears them
+  // attention tickets, one per (row, KV head, query block); the chunk's first kernel clears them
   uint32_t* tickets = reinterpret_cast<uint32_t*>(ws + sp.ticket_off);
-  uint32_t* topk_tickets = tickets;
-  uint32_t* attn_tickets = tickets + sp.topk.tickets;
+  uint32_t* attn_tickets = tickets;
   if (a->schedule == CLSA_SCHEDULE_PER_LAYER_ROUTING) {
     // the ablation: score, select and attend once per layer, each layer with its own query
     const RowsDev rd = rows_dev(rows, a->cu_seqlens);
@@ -333,7 +329,7 @@ clsa_status clsa_step(const clsa_dims* dims, const clsa_rows* rows, const clsa_s
       if (e) return device_status(e, "clsa_step: index scores of a layer");
       int32_t* idx = a->idx + (int64_t)l * R * k;
       int32_t* count = a->count + (int64_t)l * R;
-      e = launch_topk(rd, k, tp, scores, sp.ld_scores, idx, count, topk_ws, topk_tickets, tp.multi_wg, stream,
+      e = launch_topk(rd, k, tp, scores, sp.ld_scores, idx, count, topk_ws, tp.multi_wg, stream,
                       !fused);
       if (e) return device_status(e, "clsa_step: top-k of a layer");
       e = launch_attn(rd, k, hq, hkv, 1, scale, ap, a->q + (int64_t)l * hq * CLSA_HEAD_DIM, row_elems, nullptr,
@@ -379,7 +375,7 @@ clsa_status clsa_step(const clsa_dims* dims, const clsa_rows* rows, const clsa_s
     int32_t* idx = a->idx + (int64_t)c0 * k;
     int32_t* count = a->count + c0;
     // the layer-batched decode step lets the attention workgroups finish the long-row selection
-    e = launch_topk(rd, k, tp, scores, ld, idx, count, topk_ws, topk_tickets, have_hist, stream, !sp.fused_select);
+    e = launch_topk(rd, k, tp, scores, ld, idx, count, topk_ws, have_hist, stream, !sp.fused_select);
     if (e) return device_status(e, "clsa_step: top-k");
     const clsa_bf16* q = a->q + (int64_t)c0 * row_elems;
     clsa_bf16* out = a->out + (int64_t)c0 * row_elems;

@@ -69,7 +69,6 @@ struct TopkPlan {
   size_t list_off = 0;     // uint2 [R, max_row_len]: the concatenated list of the last workgroup
   size_t rowinfo_off = 0;  // uint32 [R, 2]: first-level bin t1 and the count above it
   size_t bytes = 0;
-  int tickets = 0;         // uint32 words of ticket memory needed (R when multi_wg)
 };
 
 struct AttnPlan {
@@ -91,7 +90,7 @@ struct StepPlan {
   AttnPlan attn;
   int chunk_rows = 0;      // prefill: rows per chunk; decode: R
   int64_t ld_scores = 0;   // workspace scores leading dimension
-  size_t ticket_off = 0;   // [topk tickets | attention tickets]
+  size_t ticket_off = 0;   // attention tickets
   int n_tickets = 0;
   size_t scores_off = 0, scores_bytes = 0;
   size_t topk_off = 0;
@@ -156,12 +155,11 @@ int launch_index_scores_decode(const RowsDev& rows, int d_idx, int seg, const ui
                                int topk, int hpart_chunks, uint32_t* clear, int n_clear, void* stream);
 int launch_index_scores_prefill(const RowsDev& rows, int d_idx, const uint16_t* q_idx, const uint16_t* k_idx,
                                 float* scores, int64_t ld, uint32_t* clear, int n_clear, void* stream);
-// have_hist: the score kernel already wrote the histogram partials and cleared the tickets.
+// have_hist: the score kernel already wrote the histogram partials.
 // finish = false (long rows only): the select stops after writing the span lists and each row's
 // first-level bin; the attention launched with SelectIn finishes the selection.
 int launch_topk(const RowsDev& rows, int k, const TopkPlan& plan, const float* scores, int64_t ld,
-                int32_t* idx, int32_t* count, void* ws, uint32_t* tickets, bool have_hist, void* stream,
-                bool finish = true);
+                int32_t* idx, int32_t* count, void* ws, bool have_hist, void* stream, bool finish = true);
 // Where the attention finds a row's unfinished selection (see launch_topk with finish = false).
 struct SelectIn {
   const void* slot = nullptr;        // uint2 [R, max_row_len] span lists

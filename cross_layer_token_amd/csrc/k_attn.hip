@@ -102,7 +102,7 @@ constexpr float kRescaleLog2 = 8.f;
 constexpr int kCombineBatch = 4;
 
 // SELECT (with FROM_CACHE, TEAMS = 2 and WPT = 4): the workgroup first finishes the row's
-// long-row selection itself from the span lists of the select (see k_topk_select<false>) and
+// long-row selection itself from the span lists of the select (see k_topk_select) and
 // keeps its split's token ids in LDS, instead of reading them from idx.
 template <bool FROM_CACHE, int TEAMS, bool SELECT = false, int WPT = 4>
 __global__ __launch_bounds__(64 * WPT * TEAMS, 64 * WPT * TEAMS == 512 ? 1 : 2) void k_sparse_attn(AttnArgs a) {
@@ -138,7 +138,7 @@ __global__ __launch_bounds__(64 * WPT * TEAMS, 64 * WPT * TEAMS == 512 ? 1 : 2) 
   CandidateLoads<NTH, 2, kMaxSelectSpans> cq;
   uint32_t sel_t1 = 0u, sel_above1 = 0u;
   if constexpr (SELECT) {
-    request_candidates<false>(cq, a.sel_slot + (int64_t)r * a.rw.max_row_len, a.sel_cnt + (int64_t)r * a.sel_spans,
+    request_candidates(cq, a.sel_slot + (int64_t)r * a.rw.max_row_len, a.sel_cnt + (int64_t)r * a.sel_spans,
                               a.sel_spans, a.rw.max_row_len);
     sel_t1 = a.sel_rowinfo[2 * r];
     sel_above1 = a.sel_rowinfo[2 * r + 1];
@@ -188,7 +188,7 @@ __global__ __launch_bounds__(64 * WPT * TEAMS, 64 * WPT * TEAMS == 512 ? 1 : 2) 
       const int nsp = (n + kSelectSpan - 1) / kSelectSpan;
       const uint2* rslot = a.sel_slot + (int64_t)r * a.rw.max_row_len;
       uint2* list_lds = reinterpret_cast<uint2*>(lds);  // the tiles are not in use yet
-      const int L = complete_candidates<false>(cq, rslot, nsp, sl.span_pre, sl.scan, list_lds, nullptr);
+      const int L = complete_candidates(cq, rslot, nsp, sl.span_pre, sl.scan, list_lds, nullptr);
       const bool writer = split == 0 && qb == 0 && g == 0;
       int32_t* orow = a.idx_out + (int64_t)r * a.k;
       auto emit = [&](int pos, int32_t t) {

@@ -8,11 +8,11 @@
 // decisions are integer counts, so the result is unique and independent of thread timing.
 //
 // Short rows (<= kLdsRowCap): one workgroup per row holds the row's keys in LDS.
-// Long rows: a first-level histogram of the top key bits comes in per-chunk partials (written
-// by the score kernel, or by k_topk_hist_partials); each select workgroup sums them, finds the
-// bin holding T, and compacts its span's scores at or above that bin in index order; the last
-// workgroup of the row (one atomic ticket per workgroup, nothing contended) finishes the
-// selection over that short list.  No workgroup ever waits for another.
+// Long rows: a first-level histogram of the top key bits comes in partials (written by the
+// score kernel, or by k_topk_hist_partials); each select workgroup sums them, finds the bin
+// holding T, and compacts its span's scores at or above that bin in index order; a second kernel
+// with one workgroup per row (or the attention workgroups) finishes the selection over that
+// short list.  No workgroup ever waits for another.
 #include "select_common.h"
 
 namespace clsa {
@@ -85,31 +85,28 @@ struct SelectArgs {
   int k;
   int32_t* out;
   int32_t* count;
-  uint16_t* hpart;        // [R, hist_chunks, kTopkBins] per-chunk histograms of key >> (32 - kTopkBinBits)
+  uint16_t* hpart;        // [R, hist_chunks, kTopkBins] per-piece histograms of key >> (32 - kTopkBinBits)
   uint32_t* hinfo;        // [R, hist_chunks] window start | full flag of each partial (write_hist_partial)
   int hist_chunk;         // tokens per partial
   int hist_chunks;
   int hist_flat;          // 1: the decode score kernel's partials, one per (row, segment of the
                           // concatenated sequences); 0: per-row chunks from k_topk_hist_partials
-  uint32_t* ticket;       // [R], zero on entry
   uint32_t* cnt;          // [R, spans]
   int spans;
   uint2* slot;            // [R, max_row_len]
   uint2* list;            // [R, max_row_len]
-  uint32_t* rowinfo;      // [R, 2]: t1 and the count above it, for a selection finished elsewhere
+  uint32_t* rowinfo;      // [R, 2]: t1 and the count above it
 };
 
 constexpr int kSelThreads = 1024;
 constexpr int kHistThreads = 256;
 
-// Histogram partials of the scores (used when no score kernel produced them); clears the tickets.
+// Histogram partials of the scores (used when no score kernel produced them).
 __global__ __launch_bounds__(kHistThreads) void k_topk_hist_partials(SelectArgs a) {
   __shared__ uint32_t hist[kTopkBins];
   __shared__ int scan[2 * kHistThreads / 64];
   __shared__ int res[4];
   const int r = blockIdx.y, c = blockIdx.x;
-  if (r == 0 && c == 0)
-    for (int i = threadIdx.x; i < a.rw.n_rows; i += blockDim.x) a.ticket[i] = 0u;
   const int n = row_len(a.rw, r);
   const int t0 = c * a.hist_chunk;
   if (t0 >= n || (n <= a.k)) return;
@@ -134,15 +131,14 @@ __global__ __launch_bounds__(kHistThreads) void k_topk_hist_partials(SelectArgs 
   write_hist_partial<kHistThreads>(hist, t1 - t0, a.k, hp, a.hinfo + (int64_t)r * a.hist_chunks + c, scan, res);
 }
 
-// Long-row select.  Workgroup (span, row) handles scores [span * kSelectSpan, +kSelectSpan).
+// Long-row select, first kernel.  Workgroup (span, row) handles scores [span * kSelectSpan,
+// +kSelectSpan).
 //  1. Sum the row's histogram partials (exact from the largest window start up, see
 //     write_hist_partial); find the bin t1 holding the m-th largest key.
-//  2. Append (key, index) of every score whose bin is >= t1 to the span's slot, in index order.
-//  3. The last workgroup of the row (ticket) concatenates the span lists (still in index order),
-//     refines the exact m-th largest key T over the remaining key bits, and writes the output:
-//     keys above T, then the lowest-index ties at T up to m, in list (= index) order.
-constexpr int kMaxSpans = kMaxSelectSpans;
-static_assert(kMaxSpans % kSelThreads == 0, "whole spans per select thread");
+//  2. Append (key, index) of every score whose bin is >= t1 to the span's slot, in index order,
+//     and publish the span's count; span 0 publishes t1 and the count above it.
+// The selection is then finished by k_topk_finish, or by the attention workgroups themselves.
+static_assert(kMaxSelectSpans % kSelThreads == 0, "whole spans per select thread");
 static_assert(kSelectSpan == kSelThreads * 8, "each select thread classifies 8 consecutive scores");
 
 // Finds, in the kTopkBins-bin LDS histogram, the bin d (from the top bin down) whose cumulative
@@ -165,16 +161,10 @@ __device__ __forceinline__ void find_bin_from_top(const uint32_t* hist, int need
   __syncthreads();
 }
 
-// FINISH = false: stop after step 2, with the row's t1 and the count above it published for
-// the attention workgroups that finish the selection themselves.
-template <bool FINISH>
 __global__ __launch_bounds__(kSelThreads) void k_topk_select(SelectArgs a) {
   __shared__ uint32_t hist[kTopkBins];
   __shared__ int scan[2 * kSelThreads / 64];
   __shared__ int res[2];
-  __shared__ int flag[1];
-  __shared__ int span_pre[kMaxSpans + 1];
-  __shared__ uint2 list_lds[kListLds];
   const int r = blockIdx.y, sp = blockIdx.x;
   const int n = row_len(a.rw, r);
   const int m = n < a.k ? n : a.k;
@@ -203,8 +193,8 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select(SelectArgs a) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) x[j] = i0 + j < s1 ? srow[i0 + j] : 0.f;
   }
-  // 1. the row's histogram from the chunk partials (exact from the largest window start up); a
-  //    decode row's partials are those of the segments its tokens cu[r] .. cu[r] + n - 1 fall in
+  // 1. the row's histogram from the partials (exact from the largest window start up); a decode
+  //    row's partials are those of the segments its tokens cu[r] .. cu[r] + n - 1 fall in
   const int hoff = a.hist_flat ? a.rw.cu[r] : 0;  // token offsets fit in 32 bits
   const int nch_row = (hoff + n - 1) / a.hist_chunk - hoff / a.hist_chunk + 1;
   const int nch = nch_row < a.hist_chunks ? nch_row : a.hist_chunks;
@@ -214,52 +204,63 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select(SelectArgs a) {
   const uint32_t t1 = (uint32_t)res[0];
   const int above1 = res[1];
   // 2. ordered compaction of the span's scores with bin >= t1 into the span's slot
-  {
-    uint32_t key[8];
-    int c = 0;
+  uint32_t key[8];
+  int c = 0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      key[j] = score_key(x[j]);
-      c += (i0 + j < s1) && (key[j] >> (32 - kTopkBinBits)) >= t1;
-    }
-    int tot;
-    int pos = block_exclusive_scan(c, scan, &tot);
-    uint2* slot = a.slot + (int64_t)r * a.rw.max_row_len + s0;
-    // the row's last workgroup of this kernel reads the lists (device scope); without FINISH only
-    // a later kernel does, and plain stores suffice
+  for (int j = 0; j < 8; ++j) {
+    key[j] = score_key(x[j]);
+    c += (i0 + j < s1) && (key[j] >> (32 - kTopkBinBits)) >= t1;
+  }
+  int tot;
+  int pos = block_exclusive_scan(c, scan, &tot);
+  uint2* slot = a.slot + (int64_t)r * a.rw.max_row_len + s0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if ((i0 + j < s1) && (key[j] >> (32 - kTopkBinBits)) >= t1) {
-        const uint64_t e = ((uint64_t)(uint32_t)(i0 + j) << 32) | key[j];
-        if (FINISH) st_dev(reinterpret_cast<uint64_t*>(slot + pos), e);
-        else *reinterpret_cast<uint64_t*>(slot + pos) = e;
-        ++pos;
-      }
-    }
-    if (threadIdx.x == 0) {
-      if (FINISH) st_dev(&a.cnt[(int64_t)r * a.spans + sp], (uint32_t)tot);
-      else a.cnt[(int64_t)r * a.spans + sp] = (uint32_t)tot;
+  for (int j = 0; j < 8; ++j) {
+    if ((i0 + j < s1) && (key[j] >> (32 - kTopkBinBits)) >= t1) {
+      slot[pos] = make_uint2(key[j], (uint32_t)(i0 + j));
+      ++pos;
     }
   }
-  if (!FINISH) {
-    if (sp == 0 && threadIdx.x == 0) {
+  if (threadIdx.x == 0) {
+    a.cnt[(int64_t)r * a.spans + sp] = (uint32_t)tot;
+    if (sp == 0) {
       a.rowinfo[2 * r] = t1;
       a.rowinfo[2 * r + 1] = (uint32_t)above1;
     }
-    return;
   }
-  // 3. the last workgroup of the row finishes the selection: the span lists concatenated in span
-  //    order (so in token order; in LDS when they fit, else in the workspace), T refined, and the
-  //    selection written in token order
-  const int nsp = (n + kSelectSpan - 1) / kSelectSpan;
-  if (!arrive_last(&a.ticket[r], (uint32_t)nsp, flag)) return;
+}
+
+// Long-row select, second kernel: one workgroup per row concatenates the span lists (in span
+// order, so in token order; in LDS when they fit, else in the workspace), refines the exact m-th
+// largest key T over the remaining key bits, and writes the selection in token order: keys above
+// T, then the lowest-index ties at T up to m.
+__global__ __launch_bounds__(kSelThreads) void k_topk_finish(SelectArgs a) {
+  __shared__ uint32_t hist[512];
+  __shared__ int scan[2 * kSelThreads / 64];
+  __shared__ int res[4];
+  __shared__ int span_pre[kMaxSelectSpans + 1];
+  __shared__ uint2 list_lds[kListLds];
+  const int r = blockIdx.x;
+  const int n = row_len(a.rw, r);
+  const int m = n < a.k ? n : a.k;
+  if (m == n) return;  // every visible token is selected, written by the select
+  // the span lists and counts come from the previous kernel: plain loads, requested at once
+  CandidateLoads<kSelThreads, 1, kMaxSelectSpans> cq;
   const uint2* rslot = a.slot + (int64_t)r * a.rw.max_row_len;
+  const int nsp = (n + kSelectSpan - 1) / kSelectSpan;
+  request_candidates(cq, rslot, a.cnt + (int64_t)r * a.spans, nsp, n);
+  const uint32_t t1 = a.rowinfo[2 * r];
+  const int above1 = (int)a.rowinfo[2 * r + 1];
   uint2* glist = a.list + (int64_t)r * a.rw.max_row_len;
-  const int L = collect_candidates<kSelThreads, 1, kMaxSpans>(rslot, a.cnt + (int64_t)r * a.spans, nsp, n, span_pre,
-                                                               scan, list_lds, glist);
-  const uint2* list = L <= kListLds ? list_lds : glist;
-  refine_and_emit([&](int i) { return list[i]; }, L, m, t1, above1, hist, scan, res,
-                  [&](int pos, int32_t tok) { orow[pos] = tok; });
+  const int L = complete_candidates(cq, rslot, nsp, span_pre, scan, list_lds, glist);
+  int32_t* orow = a.out + (int64_t)r * a.k;
+  auto emit = [&](int pos, int32_t tok) { orow[pos] = tok; };
+  if (L <= kListLds) {
+    static_assert(kListLds % kSelThreads == 0, "the LDS list fits the threads' registers");
+    refine_and_emit_regs<kListLds / kSelThreads>(list_lds, L, m, t1, above1, hist, scan, res, emit);
+  } else {
+    refine_and_emit([&](int i) { return glist[i]; }, L, m, t1, above1, hist, scan, res, emit);
+  }
   for (int i = m + threadIdx.x; i < a.k; i += blockDim.x) orow[i] = -1;
   if (threadIdx.x == 0) a.count[r] = m;
 }
@@ -267,7 +268,7 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select(SelectArgs a) {
 }  // namespace
 
 int launch_topk(const RowsDev& rows, int k, const TopkPlan& plan, const float* scores, int64_t ld, int32_t* idx,
-                int32_t* count, void* ws, uint32_t* tickets, bool have_hist, void* stream, bool finish) {
+                int32_t* count, void* ws, bool have_hist, void* stream, bool finish) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (!plan.multi_wg) {
     hipLaunchKernelGGL(k_topk_rows_lds, dim3(rows.n_rows), dim3(kRowThreads), 0, s, rows, scores, ld, k, idx, count);
@@ -286,7 +287,6 @@ int launch_topk(const RowsDev& rows, int k, const TopkPlan& plan, const float* s
   a.hist_chunk = plan.hist_chunk;
   a.hist_chunks = plan.hist_chunks;
   a.hist_flat = have_hist ? 1 : 0;
-  a.ticket = tickets;
   a.cnt = reinterpret_cast<uint32_t*>(w + plan.cnt_off);
   a.spans = plan.spans;
   a.slot = reinterpret_cast<uint2*>(w + plan.slot_off);
@@ -294,10 +294,8 @@ int launch_topk(const RowsDev& rows, int k, const TopkPlan& plan, const float* s
   a.rowinfo = reinterpret_cast<uint32_t*>(w + plan.rowinfo_off);
   if (!have_hist)
     hipLaunchKernelGGL(k_topk_hist_partials, dim3(plan.hist_chunks, rows.n_rows), dim3(kHistThreads), 0, s, a);
-  if (finish)
-    hipLaunchKernelGGL(k_topk_select<true>, dim3(plan.spans, rows.n_rows), dim3(kSelThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL(k_topk_select<false>, dim3(plan.spans, rows.n_rows), dim3(kSelThreads), 0, s, a);
+  hipLaunchKernelGGL(k_topk_select, dim3(plan.spans, rows.n_rows), dim3(kSelThreads), 0, s, a);
+  if (finish) hipLaunchKernelGGL(k_topk_finish, dim3(rows.n_rows), dim3(kSelThreads), 0, s, a);
   return (int)hipGetLastError();
 }
 

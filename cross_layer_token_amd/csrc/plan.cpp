@@ -103,7 +103,6 @@ TopkPlan plan_topk(const clsa_dims* d, const clsa_rows* r) {
   p.hist_chunk = decode ? idx_seg_for(r->total_tokens) : idx_chunk_for(r->n_rows, r->max_row_len);
   p.hist_chunks = (r->max_row_len + p.hist_chunk - 1) / p.hist_chunk + (decode ? 1 : 0);
   p.spans = (r->max_row_len + kSelectSpan - 1) / kSelectSpan;
-  p.tickets = r->n_rows;
   size_t off = 0;
   p.hpart_off = off;
   off = align_up(off + R * p.hist_chunks * kTopkBins * 2, 256);
@@ -174,7 +173,7 @@ StepPlan plan_step(const clsa_dims* d, const clsa_rows* r, int schedule, bool us
                    s.attn.keys_per_split <= kFusedMaxIds;
   size_t off = 0;
   s.ticket_off = off;
-  s.n_tickets = s.topk.tickets + s.attn.tickets;
+  s.n_tickets = s.attn.tickets;
   off += ticket_region(s.n_tickets);
   if (!user_scores) {
     s.scores_off = off;
@@ -197,8 +196,7 @@ StepPlan plan_step(const clsa_dims* d, const clsa_rows* r, int schedule, bool us
 }
 
 size_t topk_workspace(const clsa_dims* d, const clsa_rows* r) {
-  const TopkPlan t = plan_topk(d, r);
-  return ticket_region(t.tickets) + t.bytes;
+  return plan_topk(d, r).bytes;
 }
 
 size_t attn_workspace(const AttnPlan& a) { return ticket_region(a.tickets) + a.part_bytes; }

@@ -153,8 +153,8 @@ __device__ void sum_hist_partials(const uint32_t* hp, const uint32_t* info, int 
 // complete_candidates then gathers the counts of the row's nsp spans into span_pre[0..nsp]
 // (prefix counts, span_pre[nsp] = L) and returns L.  When L <= kListLds the span lists are
 // concatenated into list_lds, otherwise into list_global when it is given; with neither the lists
-// stay in the spans.  DEV selects device-scope loads, for spans written by other workgroups of the
-// same kernel.  complete_candidates ends with __syncthreads().
+// stay in the spans.  The spans come from an earlier kernel, so plain loads see them.
+// complete_candidates ends with __syncthreads().
 template <int NT, int NSPEC, int kMaxSpansSel>
 struct CandidateLoads {
   static_assert(kMaxSpansSel % NT == 0, "whole spans per thread");
@@ -163,13 +163,9 @@ struct CandidateLoads {
   uint32_t c[SPT];
 };
 
-template <bool DEV>
-__device__ __forceinline__ uint64_t load_entry(const uint2* p) {
-  if constexpr (DEV) return ld_dev(reinterpret_cast<const uint64_t*>(p));
-  else return *reinterpret_cast<const uint64_t*>(p);
-}
+__device__ __forceinline__ uint64_t load_entry(const uint2* p) { return *reinterpret_cast<const uint64_t*>(p); }
 
-template <bool DEV, int NT, int NSPEC, int kMaxSpansSel>
+template <int NT, int NSPEC, int kMaxSpansSel>
 __device__ __forceinline__ void request_candidates(CandidateLoads<NT, NSPEC, kMaxSpansSel>& q, const uint2* slot,
                                                    const uint32_t* cnt, int span_bound, int len_bound) {
   constexpr int kWaves = NT / 64;
@@ -180,17 +176,17 @@ __device__ __forceinline__ void request_candidates(CandidateLoads<NT, NSPEC, kMa
 #pragma unroll
     for (int j = 0; j < kSpecPerLane; ++j) {
       const int e = sp * kSelectSpan + j * 64 + lane;
-      q.spec[u][j] = (sp < span_bound && e < len_bound) ? load_entry<DEV>(slot + e) : 0;
+      q.spec[u][j] = (sp < span_bound && e < len_bound) ? load_entry(slot + e) : 0;
     }
   }
 #pragma unroll
   for (int i = 0; i < q.SPT; ++i) {
     const int sp = threadIdx.x * q.SPT + i;
-    q.c[i] = sp < span_bound ? (DEV ? ld_dev(&cnt[sp]) : cnt[sp]) : 0u;
+    q.c[i] = sp < span_bound ? cnt[sp] : 0u;
   }
 }
 
-template <bool DEV, int NT, int NSPEC, int kMaxSpansSel>
+template <int NT, int NSPEC, int kMaxSpansSel>
 __device__ int complete_candidates(const CandidateLoads<NT, NSPEC, kMaxSpansSel>& q, const uint2* slot, int nsp,
                                    int* span_pre, int* scan, uint2* list_lds, uint2* list_global) {
   constexpr int kWaves = NT / 64;
@@ -238,7 +234,7 @@ __device__ int complete_candidates(const CandidateLoads<NT, NSPEC, kMaxSpansSel>
 #pragma unroll
       for (int j = 0; j < kCopyBatch; ++j) {
         const int e = e0 + j * 64 + lane;
-        v[j] = e < cnt_s ? load_entry<DEV>(src + e) : 0;
+        v[j] = e < cnt_s ? load_entry(src + e) : 0;
       }
 #pragma unroll
       for (int j = 0; j < kCopyBatch; ++j) {
@@ -249,15 +245,6 @@ __device__ int complete_candidates(const CandidateLoads<NT, NSPEC, kMaxSpansSel>
   }
   __syncthreads();
   return L;
-}
-
-// Both halves at once, bounded by the row (spans written by other workgroups of this kernel).
-template <int NT, int NSPEC, int kMaxSpansSel>
-__device__ int collect_candidates(const uint2* slot, const uint32_t* cnt, int nsp, int n, int* span_pre, int* scan,
-                                  uint2* list_lds, uint2* list_global) {
-  CandidateLoads<NT, NSPEC, kMaxSpansSel> q;
-  request_candidates<true>(q, slot, cnt, nsp, n);
-  return complete_candidates<true>(q, slot, nsp, span_pre, scan, list_lds, list_global);
 }
 
 // Refines the m-th largest key T below the first level (bin t1, `above1` keys in higher bins)
