@@ -77,6 +77,7 @@ struct AttnPlan {
   int qblocks = 0;         // blocks of 16 wpt query rows
   int teams = 2;           // teams per workgroup (1 or 2)
   int wpt = 4;             // waves per team (4, or 2 for rows of at most 32 query rows with many blocks)
+  bool pair = false;       // many blocks: team t takes KV head 2p + t of the pair p (whole stages, no splits)
   int splits = 1;          // the selected rows are split over this many workgroups
   int keys_per_split = 0;  // multiple of kAttnTile
   size_t part_bytes = 0;   // fp32 partials [splits, R, hkv, qblocks, kAttnPartFloats] when splits > 1

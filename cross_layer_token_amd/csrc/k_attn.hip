@@ -104,21 +104,28 @@ constexpr int kCombineBatch = 4;
 // SELECT (with FROM_CACHE, TEAMS = 2 and WPT = 4): the workgroup first finishes the row's
 // long-row selection itself from the span lists of the select (see k_topk_select) and
 // keeps its split's token ids in LDS, instead of reading them from idx.
-template <bool FROM_CACHE, int TEAMS, bool SELECT = false, int WPT = 4>
+// PAIR (TEAMS = 2, WPT = 4, no splits): team t takes KV head 2p + t of the workgroup's pair p,
+// with its own tiles, loader and output, over the same selected keys; the teams pass the same
+// barriers, so they stay in lockstep.
+template <bool FROM_CACHE, int TEAMS, bool SELECT = false, int WPT = 4, bool PAIR = false>
 __global__ __launch_bounds__(64 * WPT * TEAMS, 64 * WPT * TEAMS == 512 ? 1 : 2) void k_sparse_attn(AttnArgs a) {
   constexpr int NTH = 64 * WPT * TEAMS;            // threads
   constexpr int QB = 16 * WPT;                     // query rows per block
   constexpr int STAGE = kAttnTiles * kAttnTile;
   constexpr int TILE_ELEMS = kAttnTile * CLSA_HEAD_DIM;
-  constexpr int TPT = kAttnTiles / TEAMS;          // tiles each team computes per stage
-  constexpr int TPP = NTH / 256;                   // tiles the loader covers per group of 4 pieces
+  constexpr int HEADS = PAIR ? 2 : 1;              // KV heads per workgroup
+  constexpr int HEAD_LDS = 2 * kAttnTiles * TILE_ELEMS;  // one head's K and V tiles, elements
+  constexpr int LT = NTH / HEADS;                  // threads loading one head's rows
+  constexpr int TPT = PAIR ? kAttnTiles : kAttnTiles / TEAMS;  // tiles each team computes per stage
+  constexpr int TPP = LT / 256;                    // tiles the loader covers per group of 4 pieces
   constexpr int LPT = 4 * (kAttnTiles / TPP);      // K (and V) pieces each thread loads per stage
   static_assert(NTH == 256 || NTH == 512, "four or eight waves");
   static_assert(!SELECT || WPT == 4, "the fused selection runs on eight-wave workgroups");
   static_assert(TEAMS == 1 || TEAMS == 2, "one or two teams");
-  // tiles: K of tile t at t * TILE_ELEMS, V of tile t at (kAttnTiles + t) * TILE_ELEMS; the same
-  // memory holds the team exchange at the end
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kAttnTiles * TILE_ELEMS];
+  static_assert(!PAIR || (TEAMS == 2 && WPT == 4), "a pair is two teams of four waves");
+  // per head: K of tile t at t * TILE_ELEMS, V of tile t at (kAttnTiles + t) * TILE_ELEMS; the
+  // same memory holds the team exchange at the end
+  __shared__ __attribute__((aligned(16))) uint16_t lds[HEADS * HEAD_LDS];
   __shared__ int flag[1];
   __shared__ SelectLds<SELECT> sl;
   static_assert(!SELECT || (FROM_CACHE && TEAMS == 2), "the fused selection reads the cache with two teams");
@@ -130,7 +137,8 @@ __global__ __launch_bounds__(64 * WPT * TEAMS, 64 * WPT * TEAMS == 512 ? 1 : 2) 
   const int split = bid % a.splits;
   bid /= a.splits;
   const int qb = bid % a.qblocks;
-  const int g = bid / a.qblocks;
+  const int gblk = bid / a.qblocks;                 // KV head, or pair of heads
+  const int g = PAIR ? 2 * gblk + team : gblk;      // this team's KV head
   const int r = blockIdx.y;
   // The fused selection's loads (span counts, the first entries of the span lists, t1 and the count
   // above it) are requested first, bounded by the buffers' extents rather than by the row length,
@@ -189,7 +197,7 @@ __global__ __launch_bounds__(64 * WPT * TEAMS, 64 * WPT * TEAMS == 512 ? 1 : 2) 
       const uint2* rslot = a.sel_slot + (int64_t)r * a.rw.max_row_len;
       uint2* list_lds = reinterpret_cast<uint2*>(lds);  // the tiles are not in use yet
       const int L = complete_candidates(cq, rslot, nsp, sl.span_pre, sl.scan, list_lds, nullptr);
-      const bool writer = split == 0 && qb == 0 && g == 0;
+      const bool writer = split == 0 && qb == 0 && gblk == 0;  // the same for every thread of the workgroup
       int32_t* orow = a.idx_out + (int64_t)r * a.k;
       auto emit = [&](int pos, int32_t t) {
         if (pos >= kbeg && pos < kend) sl.ids[pos - kbeg] = t;
@@ -228,8 +236,9 @@ __global__ __launch_bounds__(64 * WPT * TEAMS, 64 * WPT * TEAMS == 512 ? 1 : 2) 
   };
   // loader mapping: thread -> one 16-byte chunk of head_dim of keys 4 (ld_key4 % 16) + i (i < 4)
   // of the tiles ld_key4 / 16 + TPP * t (t < kAttnTiles / TPP)
-  const int ld_chunk = threadIdx.x & 15;
-  const int ld_key4 = threadIdx.x >> 4;  // 0 .. 16 TPP - 1
+  const int ltid = PAIR ? (int)threadIdx.x % LT : (int)threadIdx.x;  // loader thread of this head
+  const int ld_chunk = ltid & 15;
+  const int ld_key4 = ltid >> 4;  // 0 .. 16 TPP - 1
   auto piece_key = [&](int p) {           // stage-relative key of load piece p (< LPT)
     return ((ld_key4 >> 4) + TPP * (p >> 2)) * kAttnTile + (ld_key4 & 15) * 4 + (p & 3);
   };
@@ -269,7 +278,7 @@ __global__ __launch_bounds__(64 * WPT * TEAMS, 64 * WPT * TEAMS == 512 ? 1 : 2) 
   //   K fragment: row mt*16 + l16, chunk 4kk + grp  -> slot (grp ^ l16) ^ 4kk
   //   V^T fragment (transposed read): row 32kk + 4grp + l16/4 (+16), head_dim 16ht + 4(l16 % 4)
   //     -> slot (2ht + (l16/2 % 2)) ^ (4grp + l16/4) = z ^ 2ht, byte 8 (l16 % 2) inside the chunk
-  char* const lds_bytes = reinterpret_cast<char*>(lds);
+  char* const lds_bytes = reinterpret_cast<char*>(lds) + (PAIR ? team * HEAD_LDS * 2 : 0);  // this head's tiles
   int soff[LPT];
 #pragma unroll
   for (int i = 0; i < LPT; ++i) {
@@ -413,7 +422,7 @@ __global__ __launch_bounds__(64 * WPT * TEAMS, 64 * WPT * TEAMS == 512 ? 1 : 2) 
     if (wave_active) {
 #pragma unroll
       for (int t = 0; t < TPT; ++t) {
-        const int tile = team + TEAMS * t;
+        const int tile = PAIR ? t : team + TEAMS * t;
         const int nvalid = kend - (kt + tile * kAttnTile);  // keys of this tile
         if (nvalid > 0) compute_tile(tile, nvalid < kAttnTile ? nvalid : kAttnTile);
       }
@@ -426,7 +435,7 @@ __global__ __launch_bounds__(64 * WPT * TEAMS, 64 * WPT * TEAMS == 512 ? 1 : 2) 
   // per wave [acc: 8 ht x 4 j x 64 lanes][m: 64][l: 64], fp32.
   float* xch = reinterpret_cast<float*>(lds) + tw * kAttnPartWave;
   static_assert(WPT * kAttnPartWave * 4 <= (int)sizeof(lds), "team exchange fits the tiles");
-  if (TEAMS == 2 && team == 1 && wave_active) {
+  if (TEAMS == 2 && !PAIR && team == 1 && wave_active) {
 #pragma unroll
     for (int ht = 0; ht < 8; ++ht)
 #pragma unroll
@@ -434,8 +443,8 @@ __global__ __launch_bounds__(64 * WPT * TEAMS, 64 * WPT * TEAMS == 512 ? 1 : 2) 
     xch[32 * 64 + lane] = m_run;
     xch[33 * 64 + lane] = l_run;
   }
-  if (TEAMS == 2) __syncthreads();
-  if (TEAMS == 2 && team == 0 && wave_active) {
+  if (TEAMS == 2 && !PAIR) __syncthreads();
+  if (TEAMS == 2 && !PAIR && team == 0 && wave_active) {
     const float m1 = xch[32 * 64 + lane], l1 = xch[33 * 64 + lane];
     const float M = fmaxf(m_run, m1);
     if (M != -INFINITY) {  // both -inf: no keys in this split
@@ -451,7 +460,7 @@ __global__ __launch_bounds__(64 * WPT * TEAMS, 64 * WPT * TEAMS == 512 ? 1 : 2) 
   // acc[ht][j]: head_dim ht*16 + grp*4 + j of this lane's query (team 0 holds the workgroup's result)
   uint16_t* op = a.out + (int64_t)r * a.o_stride + ((int64_t)layer * a.hq + head) * CLSA_HEAD_DIM;
   if (a.splits == 1) {
-    if (team != 0 || !q_valid) return;
+    if ((!PAIR && team != 0) || !q_valid) return;  // paired teams each hold their own head's result
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
 #pragma unroll
     for (int ht = 0; ht < 8; ++ht) store_out4(op + ht * 16 + grp * 4, acc[ht], inv);
@@ -605,9 +614,19 @@ int launch_attn(const RowsDev& rows, int k, int hq, int hkv, int n_layers_call, 
     return (int)hipErrorInvalidValue;
   if (plan.splits > 1 && !tickets_clear)
     hipLaunchKernelGGL(k_clear_u32, dim3((plan.tickets + 255) / 256), dim3(256), 0, s, tickets, plan.tickets);
-  const dim3 grid((unsigned)(plan.splits * plan.qblocks * hkv), (unsigned)rows.n_rows);
+  if (plan.pair && (plan.splits != 1 || plan.teams != 2 || plan.wpt != 4 || hkv % 2 != 0))
+    return (int)hipErrorInvalidValue;
+  const int gblocks = plan.pair ? hkv / 2 : hkv;
+  const dim3 grid((unsigned)(plan.splits * plan.qblocks * gblocks), (unsigned)rows.n_rows);
   const dim3 block((unsigned)(64 * plan.wpt * plan.teams));
-  if (plan.teams == 2 && plan.wpt == 2) {
+  if (plan.pair) {
+    if (fused)
+      hipLaunchKernelGGL((k_sparse_attn<true, 2, true, 4, true>), grid, block, 0, s, a);
+    else if (from_cache)
+      hipLaunchKernelGGL((k_sparse_attn<true, 2, false, 4, true>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((k_sparse_attn<false, 2, false, 4, true>), grid, block, 0, s, a);
+  } else if (plan.teams == 2 && plan.wpt == 2) {
     if (fused) return (int)hipErrorInvalidValue;
     if (from_cache)
       hipLaunchKernelGGL((k_sparse_attn<true, 2, false, 2>), grid, block, 0, s, a);

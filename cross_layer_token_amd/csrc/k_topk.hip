@@ -165,6 +165,7 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select(SelectArgs a) {
   __shared__ uint32_t hist[kTopkBins];
   __shared__ int scan[2 * kSelThreads / 64];
   __shared__ int res[2];
+  __shared__ int any_full;
   const int r = blockIdx.y, sp = blockIdx.x;
   const int n = row_len(a.rw, r);
   const int m = n < a.k ? n : a.k;
@@ -199,7 +200,7 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_select(SelectArgs a) {
   const int nch_row = (hoff + n - 1) / a.hist_chunk - hoff / a.hist_chunk + 1;
   const int nch = nch_row < a.hist_chunks ? nch_row : a.hist_chunks;
   sum_hist_partials<kSelThreads>(reinterpret_cast<const uint32_t*>(a.hpart + (int64_t)r * a.hist_chunks * kTopkBins),
-                                 a.hinfo + (int64_t)r * a.hist_chunks, nch, hist);
+                                 a.hinfo + (int64_t)r * a.hist_chunks, nch, hist, &any_full);
   find_bin_from_top(hist, m, scan, res);
   const uint32_t t1 = (uint32_t)res[0];
   const int above1 = res[1];

@@ -130,6 +130,15 @@ AttnPlan plan_attn(const clsa_dims* d, int n_rows, int n_layers_call, int split_
   const int64_t base = (int64_t)(split_rows > 0 ? split_rows : n_rows) * d->hkv * p.qblocks;
   const int tiles = (d->topk + kAttnTile - 1) / kAttnTile;
   p.teams = base >= kAttnManyBlocks ? 1 : 2;
+  if (p.teams == 1 && p.qrows > 32 && p.qblocks == 1 && d->hkv % 2 == 0) {
+    // many blocks of more than 32 query rows: one eight-wave workgroup per (row, pair of KV heads),
+    // a team per head, in lockstep (two four-wave workgroups per CU drift apart, and the kernel
+    // waits for the one that fell behind); one round of workgroups, no splits
+    p.teams = 2;
+    p.pair = true;
+    p.keys_per_split = tiles * kAttnTile;
+    return p;
+  }
   if (p.teams == 1 && p.qrows <= 32) {
     // one team of four waves would leave half of them (two SIMDs of the CU) without MFMA work:
     // two teams of two waves split each stage's tiles instead

@@ -101,16 +101,21 @@ __device__ void write_hist_partial(const uint32_t* hist, int len, int m, uint32_
 }
 
 // Sums the row's chunk partials into the LDS histogram hist (NT threads; nch chunks, the partial
-// of chunk c at hp + c * kTopkBins / 2).  Window words and info words are requested kSumBatch
-// chunk groups at a time; hist is cleared while the first batch is in flight.  Ends with
-// __syncthreads().
+// of chunk c at hp + c * kTopkBins / 2).  Windows: window words and info words are requested
+// kSumBatch chunk groups at a time, added with LDS atomics, and hist is cleared while the first
+// batch is in flight.  Full partials (pieces shorter than k) are summed in a second pass, only when
+// there are any: thread t owns word t (bins 2t and 2t + 1) of every partial and adds it over all
+// full partials in registers, with kFullBatch chunks' words in flight at a time, then adds the two
+// sums to hist.  Ends with __syncthreads().
 template <int NT>
-__device__ void sum_hist_partials(const uint32_t* hp, const uint32_t* info, int nch, uint32_t* hist) {
+__device__ void sum_hist_partials(const uint32_t* hp, const uint32_t* info, int nch, uint32_t* hist, int* any_full) {
   constexpr int kWords = kHistWin / 2;
   constexpr int kGroup = NT / kWords;  // chunks per pass
   constexpr int kSumBatch = 8;
+  constexpr int kFullBatch = 16;
   const int w = threadIdx.x % kWords, cg = threadIdx.x / kWords;
-  bool cleared = false;
+  if (threadIdx.x == 0) *any_full = 0;
+  bool cleared = false, full_seen = false;
   for (int cb = 0; cb < nch; cb += kGroup * kSumBatch) {
     uint32_t iv[kSumBatch], wv[kSumBatch];
 #pragma unroll
@@ -129,11 +134,7 @@ __device__ void sum_hist_partials(const uint32_t* hp, const uint32_t* info, int 
       const int c = cb + p * kGroup + cg;
       if (c >= nch) continue;
       if (iv[p] & kHistFull) {
-        for (int i = w; i < kTopkBins / 2; i += kWords) {
-          const uint32_t v = i == w ? wv[p] : hp[(int64_t)c * (kTopkBins / 2) + i];
-          if (v & 0xFFFFu) atomicAdd(&hist[2 * i], v & 0xFFFFu);
-          if (v >> 16) atomicAdd(&hist[2 * i + 1], v >> 16);
-        }
+        full_seen = true;
       } else {
         const int b = (int)(iv[p] & (kTopkBins - 1)) + 2 * w;
         if ((wv[p] & 0xFFFFu) && b < kTopkBins) atomicAdd(&hist[b], wv[p] & 0xFFFFu);
@@ -143,6 +144,30 @@ __device__ void sum_hist_partials(const uint32_t* hp, const uint32_t* info, int 
   }
   if (!cleared)
     for (int i = threadIdx.x; i < kTopkBins; i += NT) hist[i] = 0u;
+  if (full_seen) *any_full = 1;
+  __syncthreads();
+  if (*any_full == 0) return;
+  for (int t = threadIdx.x; t < kTopkBins / 2; t += NT) {
+    uint32_t lo = 0u, hi = 0u;
+    for (int c0 = 0; c0 < nch; c0 += kFullBatch) {
+      uint32_t iv[kFullBatch], v[kFullBatch];
+#pragma unroll
+      for (int j = 0; j < kFullBatch; ++j) {
+        const int c = c0 + j;
+        iv[j] = c < nch ? info[c] : 0u;
+        v[j] = c < nch ? hp[(int64_t)c * (kTopkBins / 2) + t] : 0u;  // inside the partial whatever its kind
+      }
+#pragma unroll
+      for (int j = 0; j < kFullBatch; ++j) {
+        if (iv[j] & kHistFull) {
+          lo += v[j] & 0xFFFFu;
+          hi += v[j] >> 16;
+        }
+      }
+    }
+    if (lo) atomicAdd(&hist[2 * t], lo);
+    if (hi) atomicAdd(&hist[2 * t + 1], hi);
+  }
   __syncthreads();
 }
 

@@ -258,6 +258,37 @@ def test_gather_and_attention_on_oracle_selection(cfg):
         assert_outputs_close(bf16_dev_to_f64(out), ref, f"cfg{cfg} {src} per layer")
 
 
+def test_attention_paired_kv_heads():
+    """Many (row, KV head) blocks of 33-64 query rows (256 rows x 2 KV heads, 3 layers x 12 heads
+    per KV head = 36 query rows) run one eight-wave workgroup per (row, pair of KV heads), a team
+    per head.  The oracle's selections read through idx from the cache and from the gathered
+    compact buffers, every row against the oracle."""
+    rng = np.random.default_rng(5)
+    lens = tuple(int(x) for x in rng.integers(150, 900, 256))
+    w = cs.custom(seq_lens=lens, d_idx=64, topk=128, n_layers=3, hq=24, hkv=2, needles=1, seed=73,
+                  name="paired_heads")
+    dw = device_workload(w)
+    res = _oracle_idx(w, range(w.n_rows))
+    R, k, L, hq = w.n_rows, w.topk, w.n_layers, w.hq
+    idx = torch.from_numpy(np.stack([x["idx"] for x in res])).cuda()
+    cnt = torch.from_numpy(np.array([x["count"] for x in res], dtype=np.int32)).cuda()
+    dims, rows = dims_of(dw), rows_of(dw)
+    ksel = torch.empty((R, w.hkv, k, 128), dtype=torch.int16, device="cuda")
+    vsel = torch.empty_like(ksel)
+    clsa.gather_kv(dims, rows, dw.k_cache, dw.v_cache, dw.cu_seqlens, idx, cnt, ksel, vsel)
+    row_el = L * hq * 128
+    ws, nws = workspace(dims, rows, clsa.SCHEDULE_PER_LAYER)
+    ref = np.stack([x["out"] for x in res])
+    for src in ("cache", "compact"):
+        out = torch.zeros((R, L, hq, 128), dtype=torch.int16, device="cuda")
+        ks_, vs_ = (ksel, vsel) if src == "compact" else (None, None)
+        clsa.sparse_attn(dims, rows, dw.q, row_el, L, ks_, vs_, dw.k_cache, dw.v_cache, dw.cu_seqlens, idx, cnt, out,
+                         row_el, ws, nws)
+        torch.cuda.synchronize()
+        st = assert_outputs_close(bf16_dev_to_f64(out), ref, f"paired heads, {src}")
+        _say(f"paired heads from {src}: {R} rows", st)
+
+
 @pytest.mark.parametrize("counts", [[1, 2, 63, 64, 65, 100], [5, 5, 5, 5, 5, 5]])
 def test_attention_ragged_counts_and_splits(counts):
     """Short selections (count < k), single-row selections, tiles with a ragged tail."""
