@@ -72,13 +72,13 @@ def measured_traffic(bytes_alg_launch: float):
 WORKLOAD_TAG = "decode_b16_n128k"
 PROFILE_COMMANDS = {
     "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d rocprof_out/trace -o bench -- "
-             "python3 bench.py --steps 20 --warmup 3 --no-cpu-baseline --no-prefill",
+             "python3 bench.py --steps 20 --warmup 3 --no-cpu-baseline --no-prefill --no-decode-configs",
     "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d rocprof_out/fetch -o bench -- "
-             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-per-layer --no-prefill --no-append --no-distill "
-             "--profile-copy-mib 1024",
+             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-per-layer --no-prefill --no-append "
+             "--no-distill --no-decode-configs --profile-copy-mib 1024",
     "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d rocprof_out/write -o bench -- "
-             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-per-layer --no-prefill --no-append --no-distill "
-             "--profile-copy-mib 1024",
+             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-per-layer --no-prefill --no-append "
+             "--no-distill --no-decode-configs --profile-copy-mib 1024",
 }
 
 
@@ -189,6 +189,51 @@ def infinity_cache_gbps(stream, mib: int = 128) -> dict:
     read = rate(lambda: x.sum(), mib << 20)
     copy = rate(lambda: dst.copy_(half), mib << 20)
     return {"read_gbps": round(read, 1), "copy_gbps": round(copy, 1), "gbps": round(max(read, copy), 1)}
+
+
+def decode_configs_report(configs=(1, 2, 5), steps: int = 50, warmup: int = 10) -> dict:
+    """The layer-batched decode step on the other decode workloads (the single short row, the
+    32K batch, and the ragged 64-sequence batch with tie-heavy indexer entries), reported beside
+    the 128K line: time per step, tokens/s, and the algorithmic HBM rate against the 8 TB/s peak."""
+    import torch
+
+    import clsa_synth as cs
+    import cross_layer_token_amd as clsa
+    from clsa_synth.device import DeviceWorkload
+
+    out_rep = {}
+    stream = torch.cuda.current_stream()
+    for ci in configs:
+        w = cs.config(ci)
+        dw = DeviceWorkload(w)
+        dims = clsa.make_dims(**dw.dims())
+        rows = clsa.make_rows(**dw.rows())
+        R, k = w.n_rows, w.topk
+        out = torch.empty((R, w.n_layers, w.hq, 128), dtype=torch.int16, device="cuda")
+        idx = torch.empty((R, k), dtype=torch.int32, device="cuda")
+        cnt = torch.empty((R,), dtype=torch.int32, device="cuda")
+        nws = clsa.workspace_bytes(dims, rows)
+        ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+
+        def run(n):
+            for _ in range(n):
+                clsa.step(dims, rows, dw.q_idx, dw.k_idx, dw.k_cache, dw.v_cache, dw.cu_seqlens, dw.q, out, idx, cnt,
+                          ws, nws, stream=stream)
+
+        run(warmup)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        run(steps)
+        torch.cuda.synchronize()
+        t = (time.perf_counter() - t0) / steps
+        b = algorithmic_bytes(w)["total"]
+        out_rep[w.name] = {"rows": R, "tokens": w.total_tokens, "max_row_len": w.max_row_len, "topk": k,
+                           "layers": w.n_layers, "ms_per_step": round(t * 1e3, 4), "tokens_per_s": round(R / t, 1),
+                           "bytes_alg_per_step": b, "hbm_gbps_alg": round(b / t / 1e9, 1),
+                           "roofline_frac": round(b / t / 1e9 / HBM_PEAK_GBPS, 4)}
+        del dw, out, idx, cnt, ws
+        torch.cuda.empty_cache()
+    return out_rep
 
 
 def prefill_report(steps: int = 3, chunk: int = 8192) -> dict:
@@ -335,6 +380,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill report")
     ap.add_argument("--no-append", action="store_true", help="skip the new-token projection + append report")
     ap.add_argument("--no-distill", action="store_true", help="skip the distillation target and loss report")
+    ap.add_argument("--no-decode-configs", action="store_true", help="skip the other decode workloads' report")
     ap.add_argument("--profile-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a counter calibration reference)")
     ap.add_argument("--summarize-trace", metavar="DIR", help="write the kernel-trace summary under profiles/ and exit")
@@ -499,6 +545,7 @@ def main():
 
     del dw, out, idx, cnt, ws, scores
     torch.cuda.empty_cache()
+    decode_configs = None if args.no_decode_configs else decode_configs_report()
     prefill = None if args.no_prefill else prefill_report()
     distill = None if args.no_distill else distill_report()
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_budget)
@@ -526,6 +573,7 @@ def main():
         "per_layer_schedule": per_layer,
         "per_layer_routing": routing,
         "new_token_append": append,
+        "decode_configs": decode_configs,
         "prefill": prefill,
         "distill": distill,
         "cpu_baseline": cpu,
