@@ -62,11 +62,11 @@ struct TopkPlan {
   int hist_chunk = 0;      // tokens per histogram partial (the score kernel's segment or chunk)
   int hist_chunks = 0;     // histogram partials per row (a decode row may straddle one more segment)
   int spans = 0;           // select workgroups per row (kSelectSpan scores each)
-  size_t hpart_off = 0;    // uint16 [R, hist_chunks, kTopkBins]: per-chunk partials (full or windowed)
+  size_t hpart_off = 0;    // uint16 [R, hist_chunks, kTopkBins]: per-piece partials (full or windowed)
   size_t hinfo_off = 0;    // uint32 [R, hist_chunks]: window start | full flag of each partial
   size_t cnt_off = 0;      // uint32 [R, spans]
   size_t slot_off = 0;     // uint2 [R, max_row_len]: per-span ordered lists (key, index)
-  size_t list_off = 0;     // uint2 [R, max_row_len]: the concatenated list of the last workgroup
+  size_t list_off = 0;     // uint2 [R, max_row_len]: the concatenated list, when it overflows LDS
   size_t rowinfo_off = 0;  // uint32 [R, 2]: first-level bin t1 and the count above it
   size_t bytes = 0;
 };

@@ -5,8 +5,9 @@
 // gathers those rows (same explainer, CLSA: Sharing the Index Across Layers).
 //
 // One workgroup owns (query row r, KV head g, a block of up to 64 query rows, a split of the
-// selected keys).  The query rows of a KV head are all layers x the heads of its GQA group, so
-// in the layer-batched schedule every K/V tile brought into LDS serves L * Hq / Hkv queries.
+// selected keys), or, with many blocks, (row r, a pair of adjacent KV heads), a team per head.
+// The query rows of a KV head are all layers x the heads of its GQA group, so in the
+// layer-batched schedule every K/V tile brought into LDS serves L * Hq / Hkv queries.
 // The selected keys stream through LDS in stages of two 64-key tiles; the next stage's K/V rows
 // are loaded into registers while the current one is computed.  Per tile: S^T = K Q^T and
 // O^T += V^T P^T on bf16 MFMA 16x16x32 with fp32 accumulate; the online softmax (exp2 domain)

@@ -1,6 +1,7 @@
-// The last steps of the long-row top-k select (TopK(I_t, k) of eq. 2 in the picx.dev summary of
-// "You Only Index Once", Methodology > Architecture Overview), shared by the select's last
-// workgroup of a row and by the attention workgroups that finish the selection themselves.
+// The steps of the long-row top-k select (TopK(I_t, k) of eq. 2 in the picx.dev summary of
+// "You Only Index Once", Methodology > Architecture Overview) that more than one kernel runs:
+// the histogram partials (score kernel, select), and the finish over the candidates (the
+// select's finishing kernel, and the attention workgroups that finish the selection themselves).
 //
 // The candidates of a row are the (key, token) pairs whose first-level bin is at or above the bin
 // t1 holding the m-th largest key.  Span s of the row (kSelectSpan scores) holds cnt[s] of them
