@@ -422,6 +422,33 @@ def test_step_decode_segments_spanning_several_sequences():
         _say(f"segments across sequences, schedule {schedule}: {w.n_rows} rows match")
 
 
+def test_step_decode_segments_holding_hundreds_of_short_sequences():
+    """One score-kernel segment can hold hundreds of short sequences (1 to 40 tokens here, all
+    taken whole at k = 24 or cut to 24) between two long ones that need the multi-workgroup
+    select: the workgroup walks every piece in order.  Sampled rows and every row's count and
+    structure against the oracle, layer-batched schedule."""
+    rng = np.random.default_rng(11)
+    short = tuple(int(x) for x in rng.integers(1, 41, 300))
+    lens = (14000,) + short + (13000,)
+    w = cs.custom(seq_lens=lens, d_idx=64, topk=24, n_layers=2, hq=4, hkv=2, needles=1, seed=79,
+                  name="hundreds_of_short_sequences")
+    dw = device_workload(w)
+    idx, cnt, out = _run_step(dw, clsa.SCHEDULE_LAYER_BATCHED)
+    dev = bf16_dev_to_f64(out)
+    check = [0, 1, 2, 57, 150, 299, 300, w.n_rows - 1]
+    for r in check:
+        res = oracle_row(w, r)
+        assert cnt[r] == res["count"]
+        assert np.array_equal(idx[r], res["idx"]), f"row {r}: {np.sum(idx[r] != res['idx'])} index mismatches"
+        assert_outputs_close(dev[r], res["out"], f"short sequences row {r}")
+    for r in range(w.n_rows):
+        m = min(w.topk, w.row_len(r))
+        assert cnt[r] == m
+        row = idx[r]
+        assert np.all(np.diff(row[:m]) > 0) and row[0] >= 0 and row[m - 1] < w.row_len(r) and np.all(row[m:] == -1)
+    _say(f"hundreds of short sequences: {w.n_rows} rows, {len(check)} against the oracle")
+
+
 def test_step_decode_k_near_the_median_of_a_chunk():
     """k = 490 against 1024-token chunks of tie-heavy scores ({-1, 0, 1} / 4 indexer entries, about
     485 positive scores per chunk): a chunk's 490th largest score is a small positive value or zero
