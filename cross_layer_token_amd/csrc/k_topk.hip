@@ -91,6 +91,7 @@ struct SelectArgs {
   int hist_chunks;
   int hist_flat;          // 1: the decode score kernel's partials, one per (row, segment of the
                           // concatenated sequences); 0: per-row chunks from k_topk_hist_partials
+  int span_flat;          // 1 (decode): blockIdx.x enumerates the (row, span) pairs that exist
   uint32_t* cnt;          // [R, spans]
   int spans;
   uint2* slot;            // [R, max_row_len]
@@ -161,12 +162,45 @@ __device__ __forceinline__ void find_bin_from_top(const uint32_t* hist, int need
   __syncthreads();
 }
 
+// Decode: the (row, span) pair of flat workgroup w, enumerating each row's ceil(n / kSelectSpan)
+// spans row after row (the grid holds an upper bound of them, so that a ragged batch launches no
+// workgroup per span of its longest row for every row); {-1, -1} when w is past the last pair.
+// All threads call it; it ends with __syncthreads().
+__device__ int2 flat_span(const RowsDev& rw, int w, int* scan, int* found) {
+  if (threadIdx.x == 0) {
+    found[0] = -1;
+    found[1] = -1;
+  }
+  int base = 0;
+  for (int r0 = 0; r0 < rw.n_rows; r0 += kSelThreads) {  // uniform across the workgroup
+    const int r = r0 + (int)threadIdx.x;
+    const int n = r < rw.n_rows ? row_len(rw, r) : 0;
+    const int c = (n + kSelectSpan - 1) / kSelectSpan;
+    int total;
+    const int pre = base + block_exclusive_scan(c, scan, &total);
+    if (c > 0 && w >= pre && w < pre + c) {
+      found[0] = r;
+      found[1] = w - pre;
+    }
+    base += total;
+  }
+  __syncthreads();
+  return make_int2(found[0], found[1]);
+}
+
 __global__ __launch_bounds__(kSelThreads) void k_topk_select(SelectArgs a) {
   __shared__ uint32_t hist[kTopkBins];
   __shared__ int scan[2 * kSelThreads / 64];
   __shared__ int res[2];
   __shared__ int any_full;
-  const int r = blockIdx.y, sp = blockIdx.x;
+  __shared__ int found[2];
+  int r = blockIdx.y, sp = blockIdx.x;
+  if (a.span_flat) {
+    const int2 rs = flat_span(a.rw, blockIdx.x, scan, found);
+    if (rs.x < 0) return;
+    r = rs.x;
+    sp = rs.y;
+  }
   const int n = row_len(a.rw, r);
   const int m = n < a.k ? n : a.k;
   const int s0 = sp * kSelectSpan;
@@ -288,6 +322,11 @@ int launch_topk(const RowsDev& rows, int k, const TopkPlan& plan, const float* s
   a.hist_chunk = plan.hist_chunk;
   a.hist_chunks = plan.hist_chunks;
   a.hist_flat = have_hist ? 1 : 0;
+  // decode rows: one workgroup per (row, span) that exists, at most T / kSelectSpan + R of them
+  const bool flat = rows.mode == CLSA_MODE_DECODE;
+  const int64_t flat_wgs = (rows.total_tokens + kSelectSpan - 1) / kSelectSpan + rows.n_rows;
+  const bool use_flat = flat && flat_wgs < (int64_t)plan.spans * rows.n_rows;
+  a.span_flat = use_flat ? 1 : 0;
   a.cnt = reinterpret_cast<uint32_t*>(w + plan.cnt_off);
   a.spans = plan.spans;
   a.slot = reinterpret_cast<uint2*>(w + plan.slot_off);
@@ -295,7 +334,10 @@ int launch_topk(const RowsDev& rows, int k, const TopkPlan& plan, const float* s
   a.rowinfo = reinterpret_cast<uint32_t*>(w + plan.rowinfo_off);
   if (!have_hist)
     hipLaunchKernelGGL(k_topk_hist_partials, dim3(plan.hist_chunks, rows.n_rows), dim3(kHistThreads), 0, s, a);
-  hipLaunchKernelGGL(k_topk_select, dim3(plan.spans, rows.n_rows), dim3(kSelThreads), 0, s, a);
+  if (use_flat)
+    hipLaunchKernelGGL(k_topk_select, dim3((unsigned)flat_wgs), dim3(kSelThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_topk_select, dim3(plan.spans, rows.n_rows), dim3(kSelThreads), 0, s, a);
   if (finish) hipLaunchKernelGGL(k_topk_finish, dim3(rows.n_rows), dim3(kSelThreads), 0, s, a);
   return (int)hipGetLastError();
 }
