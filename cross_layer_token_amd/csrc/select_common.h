@@ -152,18 +152,19 @@ __device__ void sum_hist_partials(const uint32_t* hp, const uint32_t* info, int 
     uint32_t lo = 0u, hi = 0u;
     for (int c0 = 0; c0 < nch; c0 += kFullBatch) {
       uint32_t iv[kFullBatch], v[kFullBatch];
+      // unconditional loads of a clamped chunk (predicated loads would each get their own wait),
+      // masked when added
 #pragma unroll
       for (int j = 0; j < kFullBatch; ++j) {
-        const int c = c0 + j;
-        iv[j] = c < nch ? info[c] : 0u;
-        v[j] = c < nch ? hp[(int64_t)c * (kTopkBins / 2) + t] : 0u;  // inside the partial whatever its kind
+        const int c = c0 + j < nch ? c0 + j : nch - 1;
+        iv[j] = info[c];
+        v[j] = hp[(int64_t)c * (kTopkBins / 2) + t];  // inside the partial whatever its kind
       }
 #pragma unroll
       for (int j = 0; j < kFullBatch; ++j) {
-        if (iv[j] & kHistFull) {
-          lo += v[j] & 0xFFFFu;
-          hi += v[j] >> 16;
-        }
+        const bool take = c0 + j < nch && (iv[j] & kHistFull);
+        lo += take ? (v[j] & 0xFFFFu) : 0u;
+        hi += take ? (v[j] >> 16) : 0u;
       }
     }
     if (lo) atomicAdd(&hist[2 * t], lo);
