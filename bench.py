@@ -112,6 +112,25 @@ def summarize_trace(trace_dir: str) -> str:
     for r in _csv_rows(path):
         lines.append(f"| `{_short_kernel(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
+    # The score kernel's launches by kind: the scores-only loop (the roofline line) launches it back
+    # to back, while the step and the ablations follow each launch with the top-k select.
+    traces = sorted(glob.glob(os.path.join(trace_dir, "*_kernel_trace.csv")))
+    if traces:
+        tr = sorted(_csv_rows(traces[0]), key=lambda r: int(r["Start_Timestamp"]))
+        is_idx = ["k_index_scores_decode" in r["Kernel_Name"] for r in tr]
+        alone, other = [], []
+        for i, r in enumerate(tr):
+            if not is_idx[i]:
+                continue
+            us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            back_to_back = (i > 0 and is_idx[i - 1]) or (i + 1 < len(tr) and is_idx[i + 1])
+            (alone if back_to_back else other).append(us)
+        lines += ["", "`k_index_scores_decode<128>` by kind of launch (from the per-dispatch trace):", "",
+                  "| launches | calls | avg us | min us | max us |", "|---|---:|---:|---:|---:|"]
+        for name, v in (("scores only, back to back (the roofline line)", alone),
+                        ("followed by the top-k select (step, routing ablation, append)", other)):
+            if v:
+                lines.append(f"| {name} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
     return "\n".join(lines) + "\n"
 
 
