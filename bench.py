@@ -134,6 +134,9 @@ def summarize_trace(trace_dir: str) -> str:
     return "\n".join(lines) + "\n"
 
 
+FUSED_ATTN_KERNEL = "k_sparse_attn<true, 2, true, 4, false>"
+
+
 def summarize_counters(fetch_dir: str, write_dir: str, copy_mib: int = 1024) -> tuple:
     """HBM bytes per launch of the score kernel from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
     each scaled by what the same counter reads for a plain device copy of copy_mib MiB."""
@@ -151,9 +154,12 @@ def summarize_counters(fetch_dir: str, write_dir: str, copy_mib: int = 1024) -> 
                     if "k_index_scores_decode" in r["Kernel_Name"] and int(r["Dispatch_Id"]) > last_attn]
         in_step = [float(r["Counter_Value"]) for r in rr
                    if "k_index_scores_decode" in r["Kernel_Name"] and int(r["Dispatch_Id"]) < last_attn]
+        # the step's attention, which also finishes the selection and reads K/V through the index
+        attn = [float(r["Counter_Value"]) for r in rr if FUSED_ATTN_KERNEL in r["Kernel_Name"]]
         out[tag] = {"copy_kib": float(copy["Counter_Value"]), "scale": scale,
                     "kib_per_launch": sum(idx_only) / len(idx_only), "launches": len(idx_only),
-                    "kib_per_launch_in_step": sum(in_step) / len(in_step)}
+                    "kib_per_launch_in_step": sum(in_step) / len(in_step),
+                    "attn_kib_per_launch": sum(attn) / len(attn) if attn else None, "attn_launches": len(attn)}
     traffic = (out["fetch"]["kib_per_launch"] * out["fetch"]["scale"]
                + out["write"]["kib_per_launch"] * out["write"]["scale"]) * 1024.0
     import clsa_synth as cs
@@ -181,6 +187,18 @@ def summarize_counters(fetch_dir: str, write_dir: str, copy_mib: int = 1024) -> 
           f"scores written): {alg:,} B; ratio {traffic / alg:.4f}.", "",
           f"Kernel source hash (first 16 hex of sha256 over {', '.join(INDEX_KERNEL_SOURCES)}): "
           f"`{rec['kernel_source_sha']}`."]
+    if out["fetch"]["attn_kib_per_launch"] is not None and out["write"]["attn_kib_per_launch"] is not None:
+        at = (out["fetch"]["attn_kib_per_launch"] * out["fetch"]["scale"]
+              + out["write"]["attn_kib_per_launch"] * out["write"]["scale"]) * 1024.0
+        at_alg = b["kv_selected"] + b["q_and_out"]
+        rec["attn"] = {"kernel": FUSED_ATTN_KERNEL, "traffic_bytes_per_launch": round(at),
+                       "algorithmic_bytes_per_launch": at_alg, "traffic_over_algorithmic": round(at / at_alg, 4)}
+        md += ["", f"The step's attention, `{FUSED_ATTN_KERNEL}` ({out['fetch']['attn_launches']} launches), from the same runs:", "",
+               "| | FETCH_SIZE KiB | WRITE_SIZE KiB |", "|---|---:|---:|",
+               f"| per launch | {out['fetch']['attn_kib_per_launch']:.2f} | {out['write']['attn_kib_per_launch']:.2f} |", "",
+               f"Scaled traffic per launch: {at:,.0f} B; algorithmic (each selected K and V row read once, the",
+               f"queries read and the outputs written): {at_alg:,} B; ratio {at / at_alg:.4f}. The rest is the",
+               "selection's candidate lists, the index output and the split partials."]
     return rec, "\n".join(md) + "\n"
 
 
