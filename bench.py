@@ -4,7 +4,9 @@
 
 One step = routing scores over the whole shared cache + top-k once + all L layers of sparse
 attention over the selection (clsa_step, layer-batched), on inputs already resident in HBM.
-Prints one JSON line.  ``value`` is decoded tokens/s of the whole step (B tokens per step).
+Prints one JSON line.  ``value`` is decoded tokens/s of the whole step (B tokens per step), from
+the median device time of the steps: HIP events around each step, with a 512 MiB read before
+every step (outside its events) so that the caches hold nothing of the previous step.
 ``roofline`` covers the dominant kernel (the routing-score stream over K_idx), timed live with
 HIP events on the launch stream; ``cpu_baseline`` times the fp64 oracle on the host.
 """
@@ -33,6 +35,11 @@ INDEX_KERNEL_SOURCES = ["cross_layer_token_amd/csrc/k_index.hip", "cross_layer_t
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_index_scores_decode_b16_n128k.json")
 
 
+def log(*a):
+    """A progress line on stderr (the JSON line alone goes to stdout)."""
+    print("bench:", *a, file=sys.stderr, flush=True)
+
+
 def algorithmic_bytes(w) -> dict:
     """Bytes the method must move per decode step: the K_idx scan once, each selected K and V row
     once, the queries and outputs of every layer, and the index output."""
@@ -47,6 +54,84 @@ def algorithmic_bytes(w) -> dict:
     qo = 2 * 2 * w.batch * w.n_layers * w.hq * w.head_dim
     return {"k_idx": kidx, "q_idx": q_idx, "kv_selected": kv, "q_and_out": qo, "indices": idx,
             "total": kidx + q_idx + kv + qo + idx}
+
+
+FLUSH_MIB = 512
+
+
+class Flush:
+    """Evicts the caches between timed calls: a read of FLUSH_MIB MiB (twice the 256 MB Infinity
+    Cache) on the timing stream, enqueued before a call and outside its events.  A read evicts as
+    well as a write does, and leaves no dirty lines whose write-back the next call would pay for."""
+
+    def __init__(self, stream, mib: int = FLUSH_MIB):
+        import torch
+        self.stream = stream
+        self.mib = mib
+        self.buf = torch.ones(mib << 18, dtype=torch.float32, device="cuda")
+        self.out = torch.empty((), dtype=torch.float32, device="cuda")
+
+    def __call__(self):
+        import torch
+        with torch.cuda.stream(self.stream):
+            torch.sum(self.buf, dim=0, out=self.out)
+
+
+def event_times(stream, fn, n: int, flush=None) -> tuple:
+    """Device time of each of n calls of fn() on `stream`, from a pair of HIP events around each
+    call (flush(), when given, is enqueued before each call, outside its events), and the host wall
+    time of the whole loop between two device synchronisations.  Returns (seconds[n], wall)."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in ev:
+        if flush is not None:
+            flush()
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return np.array([a.elapsed_time(b) / 1e3 for a, b in ev]), wall
+
+
+def distribution(ts) -> dict:
+    """Median, 10th and 90th percentile and mean of per-call times, in ms."""
+    t = np.asarray(ts) * 1e3
+    return {"median_ms": round(float(np.median(t)), 4), "p10_ms": round(float(np.percentile(t, 10)), 4),
+            "p90_ms": round(float(np.percentile(t, 90)), 4), "mean_ms": round(float(t.mean()), 4), "n": int(t.size)}
+
+
+def cache_flush_check(stream, flush) -> dict:
+    """Evidence that the flush evicts: the read rate of a 128 MiB buffer read twice in a row (the
+    second read can be served by the Infinity Cache) against the same read right after a flush."""
+    import torch
+    x = torch.ones(128 << 18, dtype=torch.float32, device="cuda")
+    out = torch.empty((), dtype=torch.float32, device="cuda")
+
+    def read():
+        with torch.cuda.stream(stream):
+            torch.sum(x, dim=0, out=out)
+
+    hot, _ = event_times(stream, read, 20, flush=read)
+    cold, _ = event_times(stream, read, 20, flush=flush)
+    nbytes = 128 << 20
+    return {"read_mib": 128, "hot_gbps": round(nbytes / float(np.median(hot)) / 1e9, 1),
+            "after_flush_gbps": round(nbytes / float(np.median(cold)) / 1e9, 1)}
+
+
+def host_cpu() -> dict:
+    """The host's logical CPU count and CPU model name."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "cpu_model": model}
 
 
 def index_kernel_sha() -> str:
@@ -70,9 +155,8 @@ def measured_traffic(bytes_alg_launch: float):
 
 # ---- rocprofv3 summaries (text under profiles/, made from rocprofv3's own CSV output) ----------
 WORKLOAD_TAG = "decode_b16_n128k"
+_DECODE_ONLY = "--no-cpu-baseline --no-prefill --no-decode-configs --no-distill"
 PROFILE_COMMANDS = {
-    "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d rocprof_out/trace -o bench -- "
-             "python3 bench.py --steps 20 --warmup 3 --no-cpu-baseline --no-prefill --no-decode-configs",
     "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d rocprof_out/fetch -o bench -- "
              "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-per-layer --no-prefill --no-append "
              "--no-distill --no-decode-configs --profile-copy-mib 1024",
@@ -80,6 +164,17 @@ PROFILE_COMMANDS = {
              "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-per-layer --no-prefill --no-append "
              "--no-distill --no-decode-configs --profile-copy-mib 1024",
 }
+
+
+def trace_command(config: int) -> str:
+    """The rocprofv3 kernel-trace command whose summary profiles/kernel_trace_<workload>.md holds."""
+    if config == 4:
+        return ("rocprofv3 --kernel-trace --stats --output-format csv -d rocprof_out/trace_prefill_n8k -o bench -- "
+                "python3 bench.py --prefill-only --prefill-steps 3")
+    import clsa_synth as cs
+    tag = cs.config(config).name
+    return (f"rocprofv3 --kernel-trace --stats --output-format csv -d rocprof_out/trace_{tag} -o bench -- "
+            f"python3 bench.py --config {config} --steps 20 --warmup 3 {_DECODE_ONLY}")
 
 
 def _csv_rows(path):
@@ -95,43 +190,56 @@ def _short_kernel(name: str) -> str:
     return n.strip()
 
 
-def summarize_trace(trace_dir: str) -> str:
-    """Markdown table of rocprofv3's kernel statistics (``*_kernel_stats.csv``)."""
+_TRACE_CONTENT = {
+    "decode": ["The run holds warmup and timed steps of the layer-batched step (score kernel with histogram,",
+               "top-k select, sparse attention), each preceded by the cache flush (a torch reduction over",
+               "512 MiB), the same steps back to back, the score kernel alone (the roofline line), the",
+               "per-layer schedule (gather + one attention per layer), the per-layer routing ablation",
+               "(scores, top-k and one attention per layer), the new-token indexer projections and cache",
+               "append ahead of the step, the Infinity Cache probes (torch reduce and copy) and the",
+               "synthetic-input fill."],
+    "prefill": ["The run holds the causal prefill step (8192 rows in one chunk: the causal indexer GEMM, the",
+                "per-row top-k, the sparse attention of every row over its own selection), the indexer GEMM",
+                "alone, the distillation target and loss passes, and the synthetic-input fill."],
+}
+
+
+def summarize_trace(trace_dir: str, config: int = 3) -> tuple:
+    """Markdown table of rocprofv3's kernel statistics (``*_kernel_stats.csv``); returns
+    (workload tag, markdown)."""
     import glob
+
+    import clsa_synth as cs
+    tag = cs.config(config).name
     path = sorted(glob.glob(os.path.join(trace_dir, "*_kernel_stats.csv")))[0]
-    lines = [f"# Kernel trace: decode step, {WORKLOAD_TAG}", "",
-             "Made by (on one MI355X):", "", f"    {PROFILE_COMMANDS['trace']}",
-             f"    python bench.py --summarize-trace {trace_dir}", "",
-             "The run holds warmup + timed steps of the layer-batched step (score kernel with histogram,",
-             "top-k select, sparse attention), the score kernel alone (the roofline line), the",
-             "per-layer schedule (gather + one attention per layer), the per-layer routing ablation",
-             "(scores, top-k and one attention per layer), the new-token indexer projections and cache",
-             "append ahead of the step, the Infinity Cache probes (torch reduce and copy) and the",
-             "synthetic-input fill.", "",
+    kind = "prefill" if config == 4 else "decode"
+    lines = [f"# Kernel trace: {kind} step, {tag}", "",
+             "Made by (on one MI355X):", "", f"    {trace_command(config)}",
+             f"    python bench.py --summarize-trace {trace_dir} --config {config}", "",
+             *_TRACE_CONTENT[kind], "",
              "| kernel | calls | avg us | min us | max us | share % |", "|---|---:|---:|---:|---:|---:|"]
     for r in _csv_rows(path):
         lines.append(f"| `{_short_kernel(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
-    # The score kernel's launches by kind: the scores-only loop (the roofline line) launches it back
-    # to back, while the step and the ablations follow each launch with the top-k select.
+    # The decode score kernel's launches by kind: in the step (and the ablations) each launch is
+    # followed by the top-k select; the scores-only launches (the roofline line) are not.
     traces = sorted(glob.glob(os.path.join(trace_dir, "*_kernel_trace.csv")))
-    if traces:
+    if traces and kind == "decode":
         tr = sorted(_csv_rows(traces[0]), key=lambda r: int(r["Start_Timestamp"]))
-        is_idx = ["k_index_scores_decode" in r["Kernel_Name"] for r in tr]
         alone, other = [], []
         for i, r in enumerate(tr):
-            if not is_idx[i]:
+            if "k_index_scores_decode" not in r["Kernel_Name"]:
                 continue
             us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
-            back_to_back = (i > 0 and is_idx[i - 1]) or (i + 1 < len(tr) and is_idx[i + 1])
-            (alone if back_to_back else other).append(us)
-        lines += ["", "`k_index_scores_decode<128>` by kind of launch (from the per-dispatch trace):", "",
+            in_step = i + 1 < len(tr) and "k_topk" in tr[i + 1]["Kernel_Name"]
+            (other if in_step else alone).append(us)
+        lines += ["", "`k_index_scores_decode` by kind of launch (from the per-dispatch trace):", "",
                   "| launches | calls | avg us | min us | max us |", "|---|---:|---:|---:|---:|"]
-        for name, v in (("scores only, back to back (the roofline line)", alone),
+        for name, v in (("scores only (the roofline line)", alone),
                         ("followed by the top-k select (step, routing ablation, append)", other)):
             if v:
                 lines.append(f"| {name} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
-    return "\n".join(lines) + "\n"
+    return tag, "\n".join(lines) + "\n"
 
 
 FUSED_ATTN_KERNEL = "k_sparse_attn<true, 2, true, 4, false>"
@@ -165,9 +273,18 @@ def summarize_counters(fetch_dir: str, write_dir: str, copy_mib: int = 1024) -> 
     import clsa_synth as cs
     w = cs.config(3)
     b = algorithmic_bytes(w)
-    alg = b["k_idx"] + b["q_idx"] + 4 * w.total_tokens
+    # the roofline's algorithmic bytes are the reads (K_idx + q_idx); the fp32 score write is an
+    # intermediate, counted here on the write side
+    alg_read = b["k_idx"] + b["q_idx"]
+    score_write = 4 * w.total_tokens
+    alg = alg_read + score_write
+    fetch_b = out["fetch"]["kib_per_launch"] * out["fetch"]["scale"] * 1024.0
+    write_b = out["write"]["kib_per_launch"] * out["write"]["scale"] * 1024.0
     rec = {"kernel": "k_index_scores_decode<128>", "workload": WORKLOAD_TAG, "kernel_source_sha": index_kernel_sha(),
            "kernel_sources": INDEX_KERNEL_SOURCES, "traffic_bytes_per_launch": round(traffic),
+           "algorithmic_read_bytes_per_launch": alg_read, "score_write_bytes_per_launch": score_write,
+           "fetch_over_algorithmic_read": round(fetch_b / alg_read, 4),
+           "write_over_score_write": round(write_b / score_write, 4),
            "algorithmic_bytes_per_launch": alg, "traffic_over_algorithmic": round(traffic / alg, 4),
            "fetch": out["fetch"], "write": out["write"], "copy_mib": copy_mib,
            "commands": [PROFILE_COMMANDS["fetch"], PROFILE_COMMANDS["write"],
@@ -184,7 +301,10 @@ def summarize_counters(fetch_dir: str, write_dir: str, copy_mib: int = 1024) -> 
           f"| in the step (with the top-k histogram) | {out['fetch']['kib_per_launch_in_step']:.2f} | "
           f"{out['write']['kib_per_launch_in_step']:.2f} |", "",
           f"Scaled traffic per scores-only launch: {traffic:,.0f} B; algorithmic (K_idx + q_idx read, fp32",
-          f"scores written): {alg:,} B; ratio {traffic / alg:.4f}.", "",
+          f"scores written): {alg:,} B; ratio {traffic / alg:.4f}.",
+          f"Reads: {fetch_b:,.0f} B against {alg_read:,} B of K_idx + q_idx (ratio {fetch_b / alg_read:.4f}; the",
+          "roofline line counts these bytes). Writes: "
+          f"{write_b:,.0f} B against {score_write:,} B of fp32 scores (ratio {write_b / score_write:.4f}).", "",
           f"Kernel source hash (first 16 hex of sha256 over {', '.join(INDEX_KERNEL_SOURCES)}): "
           f"`{rec['kernel_source_sha']}`."]
     if out["fetch"]["attn_kib_per_launch"] is not None and out["write"]["attn_kib_per_launch"] is not None:
@@ -228,10 +348,12 @@ def infinity_cache_gbps(stream, mib: int = 128) -> dict:
     return {"read_gbps": round(read, 1), "copy_gbps": round(copy, 1), "gbps": round(max(read, copy), 1)}
 
 
-def decode_configs_report(configs=(1, 2, 5), steps: int = 50, warmup: int = 10) -> dict:
+def decode_configs_report(configs=(1, 2, 5), steps: int = 50, warmup: int = 10, flush=None) -> dict:
     """The layer-batched decode step on the other decode workloads (the single short row, the
     32K batch, and the ragged 64-sequence batch with tie-heavy indexer entries), reported beside
-    the 128K line: time per step, tokens/s, and the algorithmic HBM rate against the 8 TB/s peak."""
+    the 128K line: device time per step from HIP events around each step, with the caches flushed
+    before every step (median, p10, p90) and back to back with no flush ("hot"), the host wall time
+    per step of the hot loop, tokens/s and the algorithmic HBM rate against the 8 TB/s peak."""
     import torch
 
     import clsa_synth as cs
@@ -252,22 +374,24 @@ def decode_configs_report(configs=(1, 2, 5), steps: int = 50, warmup: int = 10) 
         nws = clsa.workspace_bytes(dims, rows)
         ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
 
-        def run(n):
-            for _ in range(n):
-                clsa.step(dims, rows, dw.q_idx, dw.k_idx, dw.k_cache, dw.v_cache, dw.cu_seqlens, dw.q, out, idx, cnt,
-                          ws, nws, stream=stream)
+        def one():
+            clsa.step(dims, rows, dw.q_idx, dw.k_idx, dw.k_cache, dw.v_cache, dw.cu_seqlens, dw.q, out, idx, cnt,
+                      ws, nws, stream=stream)
 
-        run(warmup)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        run(steps)
-        torch.cuda.synchronize()
-        t = (time.perf_counter() - t0) / steps
+        for _ in range(warmup):
+            one()
+        cold, _ = event_times(stream, one, steps, flush=flush)
+        hot, hot_wall = event_times(stream, one, steps)
+        t = float(np.median(cold))
         b = algorithmic_bytes(w)["total"]
+        log(f"{w.name}: {t * 1e6:.1f} us flushed, {float(np.median(hot)) * 1e6:.1f} us hot")
         out_rep[w.name] = {"rows": R, "tokens": w.total_tokens, "max_row_len": w.max_row_len, "topk": k,
                            "layers": w.n_layers, "ms_per_step": round(t * 1e3, 4), "tokens_per_s": round(R / t, 1),
                            "bytes_alg_per_step": b, "hbm_gbps_alg": round(b / t / 1e9, 1),
-                           "roofline_frac": round(b / t / 1e9 / HBM_PEAK_GBPS, 4)}
+                           "roofline_frac": round(b / t / 1e9 / HBM_PEAK_GBPS, 4),
+                           "flushed": distribution(cold), "hot": distribution(hot),
+                           "hot_wall_ms_per_step": round(hot_wall / steps * 1e3, 4),
+                           "hot_roofline_frac": round(b / float(np.median(hot)) / 1e9 / HBM_PEAK_GBPS, 4)}
         del dw, out, idx, cnt, ws
         torch.cuda.empty_cache()
     return out_rep
@@ -307,6 +431,7 @@ def prefill_report(steps: int = 3, chunk: int = 8192) -> dict:
     run(steps)
     torch.cuda.synchronize()
     t_step = (time.perf_counter() - t0) / steps
+    log(f"prefill step: {t_step * 1e3:.3f} ms")
     sel = sum(min(k, t + 1) for t in range(R))                  # selected (row, token) pairs
     attn_flop = 4.0 * sel * L * w.hq * w.head_dim                # QK^T and PV, 2 flop per MAC
     gather_bytes = float(sel) * w.hkv * w.head_dim * 2 * 2       # K and V rows each row reads
@@ -368,6 +493,7 @@ def distill_report(reps: int = 3) -> dict:
     ev1.record(stream)
     torch.cuda.synchronize()
     t = ev0.elapsed_time(ev1) / reps / 1e3
+    log(f"distillation: {t * 1e3:.3f} ms")
     pairs = R * (R + 1) // 2                          # causal (position, key) pairs
     flop = 2 * pairs * L * hq * w.head_dim * 2         # two passes of q.k, 2 flop per MAC
     exps = 2 * pairs * L * hq                          # one exp2 per score and pass
@@ -385,19 +511,21 @@ def cpu_baseline(w, budget_s: float) -> dict:
     threads; each row stays single-threaded)."""
     from oracle import cpp as C
 
+    # at most 16 threads: the host share that one GPU's box grants, whatever os.cpu_count() shows
     threads = max(1, min(16, os.cpu_count() or 1))
     one_rows, one_t = 0, 0.0
     while one_t < budget_s / 2 and one_rows < 4 * w.n_rows:
         _, t = C.oracle_rows_timed(w, [one_rows % w.n_rows], threads=1)
         one_t += t
         one_rows += 1
+    log(f"oracle on one thread: {one_rows} rows in {one_t:.1f} s")
     all_rows, all_t = 0, 0.0
     while all_t < budget_s / 2:
         _, t = C.oracle_rows_timed(w, list(range(w.n_rows)), threads=threads)
         all_t += t
         all_rows += w.n_rows
     return {"value": round(all_rows / all_t, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "one_core_tokens_per_s": round(one_rows / one_t, 3),
+            **host_cpu(), "one_core_tokens_per_s": round(one_rows / one_t, 3),
             "sample": f"{w.name}: {all_rows} decode rows on {threads} threads ({all_t:.1f} s) and {one_rows} rows on "
                       f"one thread ({one_t:.1f} s); each row evaluated from scratch by the fp64 C++ oracle (inputs "
                       f"regenerated, scores over the full {w.max_row_len}-token context, top-k by full sort, "
@@ -420,15 +548,20 @@ def main():
     ap.add_argument("--no-decode-configs", action="store_true", help="skip the other decode workloads' report")
     ap.add_argument("--profile-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a counter calibration reference)")
-    ap.add_argument("--summarize-trace", metavar="DIR", help="write the kernel-trace summary under profiles/ and exit")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="write the kernel-trace summary of --config's workload under profiles/ and exit")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="run only the prefill report (and the distillation report unless --no-distill)")
+    ap.add_argument("--prefill-steps", type=int, default=3)
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the score kernel's HBM traffic summary under profiles/ and exit")
     args = ap.parse_args()
     if args.summarize_trace or args.summarize_counters:
         os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
         if args.summarize_trace:
-            p = os.path.join(ROOT, "profiles", f"kernel_trace_{WORKLOAD_TAG}.md")
-            open(p, "w").write(summarize_trace(args.summarize_trace))
+            tag, md = summarize_trace(args.summarize_trace, args.config)
+            p = os.path.join(ROOT, "profiles", f"kernel_trace_{tag}.md")
+            open(p, "w").write(md)
             print("wrote", p)
         if args.summarize_counters:
             rec, md = summarize_counters(*args.summarize_counters)
@@ -448,6 +581,12 @@ def main():
     from clsa_synth.device import DeviceWorkload
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.prefill_only:
+        rep = {"prefill": prefill_report(steps=args.prefill_steps)}
+        if not args.no_distill:
+            rep["distill"] = distill_report()
+        print(json.dumps(rep), flush=True)
+        return
     w = cs.config(args.config, args.seed)
     if w.mode != "decode":
         print("bench.py times the decode step; the prefill workload is covered by the tests", file=sys.stderr)
@@ -477,16 +616,29 @@ def main():
         wall = time.perf_counter() - t0
         return ev0.elapsed_time(ev1) / 1e3, wall
 
+    flush = Flush(stream)
+
     # ---- the step (layer-batched schedule) ------------------------------------------------------
+    # Timed protocol: HIP events around every step, the caches flushed before each step outside
+    # its events (so neither K_idx nor the selected K/V rows of the previous step are cache-resident
+    # when a step starts); value and ms_per_step are the median over the steps.  The same steps back
+    # to back with no flush are reported beside it.
     nws = clsa.workspace_bytes(dims, rows, clsa.SCHEDULE_LAYER_BATCHED)
     ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
     run_steps(args.warmup, clsa.SCHEDULE_LAYER_BATCHED, ws, nws)
-    t_gpu, t_wall = timed(lambda n: run_steps(n, clsa.SCHEDULE_LAYER_BATCHED, ws, nws), args.steps)
-    t_step = t_wall / args.steps
+    step_times, step_wall = event_times(stream, lambda: run_steps(1, clsa.SCHEDULE_LAYER_BATCHED, ws, nws),
+                                        args.steps, flush=flush)
+    t_step = float(np.median(step_times))
+    t_gpu_hot, t_wall_hot = timed(lambda n: run_steps(n, clsa.SCHEDULE_LAYER_BATCHED, ws, nws), args.steps)
+    hot_times, _ = event_times(stream, lambda: run_steps(1, clsa.SCHEDULE_LAYER_BATCHED, ws, nws), args.steps)
     balg = algorithmic_bytes(w)
     hbm_gbps = balg["total"] / t_step / 1e9
+    log(f"{w.name} step: median {t_step * 1e6:.1f} us flushed, {float(np.median(hot_times)) * 1e6:.1f} us hot")
 
     # ---- the dominant kernel alone: routing scores streamed from K_idx --------------------------
+    # Its algorithmic bytes are the K_idx scan and the queries; the fp32 score write is an
+    # intermediate of the method and is reported separately.  Each launch is timed by its own
+    # events, with the flush before it.
     ld = ((w.max_row_len + 63) // 64) * 64
     scores = torch.empty((R, ld), dtype=torch.float32, device="cuda")
 
@@ -495,14 +647,19 @@ def main():
             clsa.index_scores(dims, rows, dw.q_idx, dw.k_idx, dw.cu_seqlens, scores, ld, stream=stream)
 
     run_scores(args.warmup)
-    t_idx, _ = timed(run_scores, args.steps)
-    t_idx /= args.steps
-    idx_bytes = balg["k_idx"] + balg["q_idx"] + 4 * w.total_tokens   # K_idx + q_idx read, scores written
+    idx_times, _ = event_times(stream, lambda: run_scores(1), args.steps, flush=flush)
+    t_idx = float(np.mean(idx_times))
+    idx_bytes = balg["k_idx"] + balg["q_idx"]          # K_idx + q_idx read
     achieved = idx_bytes / t_idx / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(idx_bytes),
                 "kernel": "k_index_scores_decode<128>", "bytes_per_launch": idx_bytes,
-                "us_per_launch": round(t_idx * 1e6, 2)}
+                "score_write_bytes_per_launch": 4 * w.total_tokens, "us_per_launch": round(t_idx * 1e6, 2),
+                "launch_timing_us": {k2.replace("_ms", ""): (round(v * 1e3, 2) if k2.endswith("_ms") else v)
+                                     for k2, v in distribution(idx_times).items()},
+                "with_score_write_frac": round((idx_bytes + 4 * w.total_tokens) / t_idx / 1e9 / HBM_PEAK_GBPS, 4)}
+    flush_check = cache_flush_check(stream, flush)
+    log(f"score kernel alone: {t_idx * 1e6:.2f} us per launch; flush check {flush_check}")
 
     # ---- dependent-layer schedule (one attention pass per layer), reported beside -----------------
     per_layer = None
@@ -510,14 +667,17 @@ def main():
         nws2 = clsa.workspace_bytes(dims, rows, clsa.SCHEDULE_PER_LAYER)
         ws2 = torch.empty(nws2, dtype=torch.uint8, device="cuda")
         run_steps(args.warmup, clsa.SCHEDULE_PER_LAYER, ws2, nws2)
-        t2, w2 = timed(lambda n: run_steps(n, clsa.SCHEDULE_PER_LAYER, ws2, nws2), args.steps)
-        t_pl = w2 / args.steps
+        pl_times, _ = event_times(stream, lambda: run_steps(1, clsa.SCHEDULE_PER_LAYER, ws2, nws2), args.steps,
+                                  flush=flush)
+        t_pl = float(np.median(pl_times))
         # its roofline: the step's algorithmic bytes from HBM, plus the compact K_S/V_S read once
         # per layer from the Infinity Cache, at the rate a cache-resident device copy reaches here
         ic = infinity_cache_gbps(stream)
         sel_bytes = 2 * R * w.hkv * w.topk * w.head_dim * 2
         bound = balg["total"] / (HBM_PEAK_GBPS * 1e9) + w.n_layers * sel_bytes / (ic["gbps"] * 1e9)
-        per_layer = {"ms_per_step": round(t_pl * 1e3, 4), "tokens_per_s": round(R * args.steps / w2, 1),
+        log(f"per-layer schedule: {t_pl * 1e6:.1f} us")
+        per_layer = {"ms_per_step": round(t_pl * 1e3, 4), "tokens_per_s": round(R / t_pl, 1),
+                     "timing": distribution(pl_times),
                      "hbm_gbps_alg": round(balg["total"] / t_pl / 1e9, 1),
                      "roofline": {"infinity_cache": ic, "compact_bytes_per_layer": sel_bytes,
                                   "bound_ms": round(bound * 1e3, 4), "frac": round(bound / t_pl, 4)}}
@@ -539,8 +699,9 @@ def main():
 
         n3 = max(1, args.steps // 5)
         run_routing(max(1, args.warmup // 5))
-        _, w3 = timed(run_routing, n3)
-        t3 = w3 / n3
+        r_times, _ = event_times(stream, lambda: run_routing(1), n3, flush=flush)
+        t3 = float(np.median(r_times))
+        log(f"per-layer routing: {t3 * 1e6:.1f} us")
         routing = {"ms_per_step": round(t3 * 1e3, 4), "tokens_per_s": round(R / t3, 1), "steps": n3,
                    "vs_shared_routing": round(t3 / t_step, 2)}
         del ws3, idx3, cnt3
@@ -562,11 +723,12 @@ def main():
         # weights (query and key projections), hidden states, q_idx and appended rows
         p_bytes = (2 * w.d_idx * d_model + R * d_model + 2 * R * w.d_idx + 2 * R * w.hkv * w.head_dim) * 2
         run_append_steps(args.warmup)
-        _, w4 = timed(run_append_steps, args.steps)
-        t4 = w4 / args.steps
+        a_times, _ = event_times(stream, lambda: run_append_steps(1), args.steps, flush=flush)
+        t4 = float(np.median(a_times))
         # the projection's cost is what it adds to the (device-bound) step; timing the kernel alone
         # from back-to-back host calls would measure the host's call rate instead
         added = t4 - t_step
+        log(f"append + step: {t4 * 1e6:.1f} us")
         append = {"d_model": d_model, "ms_per_step": round(t4 * 1e3, 4), "tokens_per_s": round(R / t4, 1),
                   "added_us_per_step": round(added * 1e6, 2), "project_bytes": p_bytes, "vs_step": round(t4 / t_step, 4)}
         del pin, q_new
@@ -582,13 +744,13 @@ def main():
 
     del dw, out, idx, cnt, ws, scores
     torch.cuda.empty_cache()
-    decode_configs = None if args.no_decode_configs else decode_configs_report()
+    decode_configs = None if args.no_decode_configs else decode_configs_report(flush=flush)
     prefill = None if args.no_prefill else prefill_report()
     distill = None if args.no_distill else distill_report()
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_budget)
     line = {
         "metric": METRIC,
-        "value": round(R * args.steps / t_wall, 1),
+        "value": round(R / t_step, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -605,7 +767,14 @@ def main():
         "hbm_gbps": round(hbm_gbps, 1),
         "step_roofline_frac": round(hbm_gbps / HBM_PEAK_GBPS, 4),
         "bytes_alg_per_step": balg["total"],
-        "gpu_event_ms_per_step": round(t_gpu / args.steps * 1e3, 4),
+        "step_timing": {"protocol": f"HIP events around each step; a {FLUSH_MIB} MiB read before every step, outside "
+                                    "its events; median over the steps",
+                        "flushed": distribution(step_times), "flushed_wall_s": round(step_wall, 3),
+                        "hot": distribution(hot_times),
+                        "hot_back_to_back_ms_per_step": round(t_gpu_hot / args.steps * 1e3, 4),
+                        "hot_wall_ms_per_step": round(t_wall_hot / args.steps * 1e3, 4),
+                        "hot_roofline_frac": round(balg["total"] / (t_gpu_hot / args.steps) / 1e9 / HBM_PEAK_GBPS, 4),
+                        "cache_flush_check": flush_check},
         "roofline": roofline,
         "per_layer_schedule": per_layer,
         "per_layer_routing": routing,

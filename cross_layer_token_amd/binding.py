@@ -47,14 +47,14 @@ class CLSAError(RuntimeError):
         self.status = status
 
 
-def _load():
+def _load(path: str = LIB_PATH):
     # Bind to the HIP runtime torch already carries: libclsa.so needs libamdhip64.so.7 by soname,
     # so loading torch first makes the dynamic linker reuse that runtime instead of pulling a
     # second one (two runtimes in one process cannot share the device or its memory).
     import torch  # noqa: F401
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m cross_layer_token_amd.build`")
-    lib = ctypes.CDLL(LIB_PATH)
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python -m cross_layer_token_amd.build`")
+    lib = ctypes.CDLL(path)
     P = c_void_p
     sig = {
         "clsa_status_string": (c_char_p, [c_int32]),
@@ -183,3 +183,4 @@ def step(dims, rows, q_idx, k_idx, k_cache, v_cache, cu_seqlens, q, out, idx, co
                  prefill_chunk_rows)
     _check(LIB.clsa_step(ctypes.byref(dims), ctypes.byref(rows), ctypes.byref(a), _ptr(workspace), workspace_bytes_,
                          _stream(stream)))
+

@@ -259,9 +259,12 @@ clsa_status clsa_sparse_attn(const clsa_dims* dims, const clsa_rows* rows, const
                        "clsa_sparse_attn");
 }
 
-clsa_status clsa_step(const clsa_dims* dims, const clsa_rows* rows, const clsa_step_args* a, void* workspace,
-                      size_t workspace_bytes_, clsa_stream stream) {
-  g_last_error.clear();
+}  // extern "C"
+
+namespace {
+
+// Every check of clsa_step's arguments except the workspace.
+clsa_status check_step_args(const clsa_dims* dims, const clsa_rows* rows, const clsa_step_args* a) {
   CLSA_TRY(check_common(dims, rows));
   if (a == nullptr) return set_error(CLSA_ERR_INVALID_ARGUMENT, "args is NULL");
   if (a->schedule != CLSA_SCHEDULE_LAYER_BATCHED && a->schedule != CLSA_SCHEDULE_PER_LAYER &&
@@ -290,6 +293,18 @@ clsa_status clsa_step(const clsa_dims* dims, const clsa_rows* rows, const clsa_s
     if (a->scores != nullptr || a->k_sel != nullptr)
       return set_error(CLSA_ERR_INVALID_ARGUMENT, "per-layer routing takes no scores, k_sel or v_sel");
   }
+  return CLSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+clsa_status clsa_step(const clsa_dims* dims, const clsa_rows* rows, const clsa_step_args* a, void* workspace,
+                      size_t workspace_bytes_, clsa_stream stream) {
+  g_last_error.clear();
+  if (clsa_status s = check_step_args(dims, rows, a); s != CLSA_OK) return s;
+  const bool prefill = rows->mode == CLSA_MODE_PREFILL;
   const StepPlan sp = plan_step(dims, rows, a->schedule, a->scores != nullptr, a->k_sel != nullptr,
                                 a->prefill_chunk_rows);
   if (clsa_status s = check_workspace(workspace, workspace_bytes_, sp.total); s != CLSA_OK) return s;

@@ -122,6 +122,22 @@ size_t topk_workspace(const clsa_dims* d, const clsa_rows* r);
 size_t attn_workspace(const AttnPlan& a);
 
 
+// Host and device: the selection positions [*kbeg, *kend) that split `split` of a (row, KV head)
+// block reads, when each split takes kps positions and the row holds `count` selected tokens of at
+// most k.  count is clamped into [0, k] first, so an out-of-range count from a caller cannot send a
+// read of idx (or of a compact K_S/V_S row) past the row's k entries: kend <= k always.
+#if defined(__HIPCC__)
+#define CLSA_HOST_DEVICE __host__ __device__
+#else
+#define CLSA_HOST_DEVICE
+#endif
+CLSA_HOST_DEVICE inline void split_key_range(int count, int k, int split, int kps, int* kbeg, int* kend) {
+  const int cnt = count < 0 ? 0 : (count > k ? k : count);
+  const int b = split * kps;
+  *kbeg = b;
+  *kend = b + kps < cnt ? b + kps : cnt;
+}
+
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline size_t ticket_region(int words) { return words ? align_up((size_t)words * 4, 256) : 0; }
 inline float softmax_scale(const clsa_dims* d) {

@@ -152,10 +152,11 @@ __global__ __launch_bounds__(64 * WPT * TEAMS, 64 * WPT * TEAMS == 512 ? 1 : 2) 
     sel_t1 = a.sel_rowinfo[2 * r];
     sel_above1 = a.sel_rowinfo[2 * r + 1];
   }
+  // the row's selected tokens: the fused selection's count, or the caller's (clamped into [0, k]
+  // by split_key_range, so no position read lies past the row's k entries of idx or K_S/V_S)
   const int cnt = SELECT ? min(a.k, row_len(a.rw, r)) : a.count[r];
-  const int kbeg = split * a.kps;
-  const int kend_raw = kbeg + a.kps;
-  const int kend = kend_raw < cnt ? kend_raw : cnt;
+  int kbeg, kend;
+  split_key_range(cnt, a.k, split, a.kps, &kbeg, &kend);
 
   // this lane's query column: query row qr -> (layer, head) of the GQA group of KV head g
   const int qr = qb * QB + tw * 16 + l16;

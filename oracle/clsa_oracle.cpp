@@ -11,7 +11,8 @@
 //    S_t = TopK(I_t, k) computed once per step; eq. 3, every cross-decoder layer l attends with its
 //    own query Q_t^(l) to the selected rows K_{S_t}, V_{S_t} of the one shared cache.
 //  * [FORUM] zhichai.net explainer "... (CLSA) Explained", Background: attention is
-//    softmax(Q K^T / sqrt(d_k)) V.
+//    softmax(Q K^T / sqrt(d_k)) V; Ablations: the variant without the shared index recomputes the
+//    routing in every layer (clsa_oracle_row_layer_routing).
 // Readings where the pages leave a step open: plain dot-product scores (no scale, no activation);
 // a decode row sees its whole sequence, prefill row t sees tokens 0..t; |S_t| = min(k, visible);
 // ties at the k-th score go to the lower index; S_t ascending; one S_t for every layer and head;
@@ -27,7 +28,7 @@
 //  * fp32 -> bf16 round to nearest even on the bit pattern
 //  * needles: K_idx of a planted token is bf16(2 * q_idx of its row); positions drawn by rejection,
 //    attempt a of row b uses mix(key_needle + (b << 32) + a), position = (x >> 32) * n >> 32
-//  * tensor ids: q_idx 1, K_idx 2, Q 3, K 4, V 5, needles 6.
+//  * tensor ids: q_idx 1, K_idx 2, Q 3, K 4, V 5, needles 6, per-layer indexer queries 8.
 #include <algorithm>
 #include <chrono>
 #include <cmath>
@@ -173,66 +174,120 @@ void clsa_oracle_attention(const double* q, const double* k_sel, const double* v
 }
 
 // ---- one query row of the step, inputs regenerated from the workload definition -------------
-// idx [topk] (ascending, -1 padded), count, out [L, Hq, hd]; scores [visible tokens] optional.
-// Returns 0, or 1 on a bad argument.
-int clsa_oracle_row(const clsa_oracle_workload* w, int32_t row, int32_t* idx, int32_t* count, double* out,
-                    double* scores_out) {
-  if (w == nullptr || w->batch < 1 || w->head_dim < 1 || w->hkv < 1 || w->hq % w->hkv != 0) return 1;
+namespace {
+
+constexpr uint64_t kTidQIdxLayer = 8;
+
+// What a query row sees: its sequence, the cache row of its first token, its n visible tokens
+// and their indexer keys (n x d_idx, needles included).  Returns false on a bad argument.
+struct RowInputs {
+  int32_t seq = 0;
+  int64_t base = 0, n = 0;
+  std::vector<double> k_idx;
+};
+
+bool row_inputs(const clsa_oracle_workload* w, int32_t row, RowInputs* in) {
+  if (w == nullptr || w->batch < 1 || w->head_dim < 1 || w->hkv < 1 || w->hq % w->hkv != 0) return false;
   std::vector<int64_t> cu((size_t)w->batch + 1, 0);
   for (int32_t b = 0; b < w->batch; ++b) cu[(size_t)b + 1] = cu[(size_t)b] + w->seq_lens[b];
   const bool decode = w->mode == 0;
   const int32_t n_rows = decode ? w->batch : (int32_t)w->seq_lens[0];
-  if (row < 0 || row >= n_rows) return 1;
-  const int32_t seq = decode ? row : 0;
-  const int64_t n = decode ? w->seq_lens[row] : (int64_t)row + 1;
-  const int64_t base = cu[(size_t)seq];
-  const int32_t d = w->d_idx, hd = w->head_dim, L = w->n_layers, hq = w->hq, hkv = w->hkv;
+  if (row < 0 || row >= n_rows) return false;
+  in->seq = decode ? row : 0;
+  in->n = decode ? w->seq_lens[row] : (int64_t)row + 1;
+  in->base = cu[(size_t)in->seq];
+  const int32_t d = w->d_idx;
   const uint64_t kq = tensor_key(w->seed, kTidQIdx), kk = tensor_key(w->seed, kTidKIdx);
-  auto q_idx_bits = [&](int64_t r, int32_t c) {
-    return uniform_bits(kq, (uint64_t)(r * d + c), w->idx_lo, w->idx_hi, w->idx_den);
-  };
   // needles planted in this row's sequence: global token -> the q_idx row it copies
   std::unordered_map<int64_t, int64_t> needle;
   if (w->needles > 0) {
     std::vector<int64_t> pos((size_t)w->needles);
     if (decode) {
-      if (clsa_oracle_gen_needles(w->seed, seq, w->seq_lens[seq], w->needles, pos.data())) return 1;
-      for (int64_t p : pos) needle[base + p] = seq;
+      if (clsa_oracle_gen_needles(w->seed, in->seq, w->seq_lens[in->seq], w->needles, pos.data())) return false;
+      for (int64_t p : pos) needle[in->base + p] = in->seq;
     } else {
-      if (clsa_oracle_gen_needles(w->seed, 0, w->seq_lens[0], w->needles, pos.data())) return 1;
+      if (clsa_oracle_gen_needles(w->seed, 0, w->seq_lens[0], w->needles, pos.data())) return false;
       for (int64_t p : pos) needle[p] = w->seq_lens[0] - 1;
     }
   }
-  // scores over the visible tokens
-  std::vector<double> qv((size_t)d), krow((size_t)n * d), sc((size_t)n);
-  for (int32_t c = 0; c < d; ++c) qv[(size_t)c] = bf16_value(q_idx_bits(row, c));
-  for (int64_t j = 0; j < n; ++j) {
-    const int64_t t = base + j;
+  in->k_idx.assign((size_t)(in->n * d), 0.0);
+  for (int64_t j = 0; j < in->n; ++j) {
+    const int64_t t = in->base + j;
     const auto it = needle.find(t);
     for (int32_t c = 0; c < d; ++c) {
       uint16_t bits;
-      if (it != needle.end()) bits = bf16_rne(2.0f * (float)bf16_value(q_idx_bits(it->second, c)));
-      else bits = uniform_bits(kk, (uint64_t)(t * d + c), w->idx_lo, w->idx_hi, w->idx_den);
-      krow[(size_t)(j * d + c)] = bf16_value(bits);
+      if (it != needle.end())
+        bits = bf16_rne(2.0f * (float)bf16_value(uniform_bits(kq, (uint64_t)(it->second * d + c), w->idx_lo,
+                                                               w->idx_hi, w->idx_den)));
+      else
+        bits = uniform_bits(kk, (uint64_t)(t * d + c), w->idx_lo, w->idx_hi, w->idx_den);
+      in->k_idx[(size_t)(j * d + c)] = bf16_value(bits);
     }
   }
-  clsa_oracle_scores(qv.data(), krow.data(), n, d, sc.data());
-  if (scores_out != nullptr) std::copy(sc.begin(), sc.end(), scores_out);
-  clsa_oracle_topk(sc.data(), n, w->topk, idx, count);
-  // attention over the selected rows of the shared cache, every layer and head
-  const int64_t m = *count;
+  return true;
+}
+
+// Attention of layers layer0 .. layer0 + lc - 1 of `row` over the m selected local tokens sel[],
+// read from the one shared cache; out [lc, Hq, hd].
+void attend_row(const clsa_oracle_workload* w, int32_t row, const RowInputs& in, int32_t layer0, int32_t lc,
+                const int32_t* sel, int64_t m, double* out) {
+  const int32_t hd = w->head_dim, L = w->n_layers, hq = w->hq, hkv = w->hkv;
   const uint64_t kqa = tensor_key(w->seed, kTidQ), kka = tensor_key(w->seed, kTidK), kva = tensor_key(w->seed, kTidV);
-  std::vector<double> q((size_t)L * hq * hd), ks((size_t)m * hkv * hd), vs((size_t)m * hkv * hd);
-  for (int64_t e = 0; e < (int64_t)L * hq * hd; ++e)
-    q[(size_t)e] = bf16_value(normal_bits(kqa, (uint64_t)((int64_t)row * L * hq * hd + e)));
+  std::vector<double> q((size_t)lc * hq * hd), ks((size_t)m * hkv * hd), vs((size_t)m * hkv * hd);
+  const int64_t qrow = (int64_t)row * L * hq * hd + (int64_t)layer0 * hq * hd;
+  for (int64_t e = 0; e < (int64_t)lc * hq * hd; ++e) q[(size_t)e] = bf16_value(normal_bits(kqa, (uint64_t)(qrow + e)));
   for (int64_t i = 0; i < m; ++i) {
-    const int64_t t = base + idx[i];
+    const int64_t t = in.base + sel[i];
     for (int64_t e = 0; e < (int64_t)hkv * hd; ++e) {
       ks[(size_t)(i * hkv * hd + e)] = bf16_value(normal_bits(kka, (uint64_t)(t * hkv * hd + e)));
       vs[(size_t)(i * hkv * hd + e)] = bf16_value(normal_bits(kva, (uint64_t)(t * hkv * hd + e)));
     }
   }
-  clsa_oracle_attention(q.data(), ks.data(), vs.data(), m, L, hq, hkv, hd, 0.0, out);
+  clsa_oracle_attention(q.data(), ks.data(), vs.data(), m, lc, hq, hkv, hd, 0.0, out);
+}
+
+}  // namespace
+
+// idx [topk] (ascending, -1 padded), count, out [L, Hq, hd]; scores [visible tokens] optional.
+// Returns 0, or 1 on a bad argument.
+int clsa_oracle_row(const clsa_oracle_workload* w, int32_t row, int32_t* idx, int32_t* count, double* out,
+                    double* scores_out) {
+  RowInputs in;
+  if (!row_inputs(w, row, &in)) return 1;
+  const int32_t d = w->d_idx;
+  const uint64_t kq = tensor_key(w->seed, kTidQIdx);
+  std::vector<double> qv((size_t)d), sc((size_t)in.n);
+  for (int32_t c = 0; c < d; ++c)
+    qv[(size_t)c] = bf16_value(uniform_bits(kq, (uint64_t)((int64_t)row * d + c), w->idx_lo, w->idx_hi, w->idx_den));
+  clsa_oracle_scores(qv.data(), in.k_idx.data(), in.n, d, sc.data());
+  if (scores_out != nullptr) std::copy(sc.begin(), sc.end(), scores_out);
+  clsa_oracle_topk(sc.data(), in.n, w->topk, idx, count);
+  // one selection for every layer and head
+  attend_row(w, row, in, 0, w->n_layers, idx, *count, out);
+  return 0;
+}
+
+// The ablation without the shared index (zhichai.net explainer, Ablations: per-layer recompute;
+// picx.dev summary, Complexity Comparison: eta L N instead of eta N): layer l scores the row's
+// visible tokens with its OWN indexer query (tensor id 8, element (row, l, c) of [R, L, d_idx]),
+// selects its own set and attends with its own query over that set.
+// idx [L, topk], count [L], out [L, Hq, hd].  Returns 0, or 1 on a bad argument.
+int clsa_oracle_row_layer_routing(const clsa_oracle_workload* w, int32_t row, int32_t* idx, int32_t* count,
+                                  double* out) {
+  RowInputs in;
+  if (!row_inputs(w, row, &in)) return 1;
+  const int32_t d = w->d_idx, L = w->n_layers;
+  const uint64_t kql = tensor_key(w->seed, kTidQIdxLayer);
+  std::vector<double> qv((size_t)d), sc((size_t)in.n);
+  for (int32_t l = 0; l < L; ++l) {
+    for (int32_t c = 0; c < d; ++c)
+      qv[(size_t)c] = bf16_value(uniform_bits(kql, (uint64_t)(((int64_t)row * L + l) * d + c), w->idx_lo, w->idx_hi,
+                                              w->idx_den));
+    clsa_oracle_scores(qv.data(), in.k_idx.data(), in.n, d, sc.data());
+    int32_t* li = idx + (int64_t)l * w->topk;
+    clsa_oracle_topk(sc.data(), in.n, w->topk, li, count + l);
+    attend_row(w, row, in, l, 1, li, count[l], out + (int64_t)l * w->hq * w->head_dim);
+  }
   return 0;
 }
 
@@ -253,6 +308,26 @@ int clsa_oracle_rows(const clsa_oracle_workload* w, const int32_t* rows, int32_t
     });
   for (auto& th : pool) th.join();
   *seconds = std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
+  for (int f : fail)
+    if (f) return 1;
+  return 0;
+}
+
+// clsa_oracle_row_layer_routing over rows[0..n) on `threads` host threads.  idx [n, L, topk],
+// count [n, L], out [n, L*Hq*hd].  Returns 0, or 1 if any row failed.
+int clsa_oracle_rows_layer_routing(const clsa_oracle_workload* w, const int32_t* rows, int32_t n, int32_t threads,
+                                   int32_t* idx, int32_t* count, double* out) {
+  if (threads < 1) threads = 1;
+  const int64_t L = w->n_layers, per = L * w->hq * w->head_dim;
+  std::vector<int> fail((size_t)threads, 0);
+  std::vector<std::thread> pool;
+  for (int32_t t = 0; t < threads; ++t)
+    pool.emplace_back([&, t]() {
+      for (int32_t i = t; i < n; i += threads)
+        fail[(size_t)t] |= clsa_oracle_row_layer_routing(w, rows[i], idx + (int64_t)i * L * w->topk, count + i * L,
+                                                         out + i * per);
+    });
+  for (auto& th : pool) th.join();
   for (int f : fail)
     if (f) return 1;
   return 0;

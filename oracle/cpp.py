@@ -24,11 +24,11 @@ class Workload(ctypes.Structure):
                 ("seed", c_uint64)]
 
 
-def _load():
-    if not os.path.exists(_LIB_PATH):
+def _load(path: str = _LIB_PATH):
+    if not os.path.exists(path):
         from . import build
         build.build()
-    lib = ctypes.CDLL(_LIB_PATH)
+    lib = ctypes.CDLL(path)
     dp, ip = POINTER(c_double), POINTER(c_int32)
     lib.clsa_oracle_gen_uniform.restype = c_uint16
     lib.clsa_oracle_gen_uniform.argtypes = [c_uint64, c_uint64, c_uint64, c_int, c_int, c_int]
@@ -43,6 +43,10 @@ def _load():
     lib.clsa_oracle_row.argtypes = [POINTER(Workload), c_int32, ip, ip, dp, dp]
     lib.clsa_oracle_rows.restype = c_int
     lib.clsa_oracle_rows.argtypes = [POINTER(Workload), ip, c_int32, c_int32, ip, ip, dp, POINTER(c_double)]
+    lib.clsa_oracle_row_layer_routing.restype = c_int
+    lib.clsa_oracle_row_layer_routing.argtypes = [POINTER(Workload), c_int32, ip, ip, dp]
+    lib.clsa_oracle_rows_layer_routing.restype = c_int
+    lib.clsa_oracle_rows_layer_routing.argtypes = [POINTER(Workload), ip, c_int32, c_int32, ip, ip, dp]
     return lib
 
 
@@ -124,6 +128,38 @@ def oracle_rows_timed(w, rows, threads: int) -> tuple:
     rc = LIB.clsa_oracle_rows(ctypes.byref(s), _i(rows), n, threads, _i(idx), _i(cnt), _d(out), ctypes.byref(secs))
     assert rc == 0, "clsa_oracle_rows failed"
     return {"idx": idx, "count": cnt, "out": out}, secs.value
+
+
+def oracle_rows(w, rows, threads: int = 8) -> dict:
+    """Several rows over `threads` host threads: idx [n, k], count [n], out [n, L, Hq, hd]."""
+    return oracle_rows_timed(w, rows, threads)[0]
+
+
+def oracle_rows_layer_routing(w, rows, threads: int = 8) -> dict:
+    """The per-layer routing ablation (every layer scores with its own indexer query, selects its
+    own set and attends over it) for several rows over `threads` host threads:
+    idx [n, L, k], count [n, L], out [n, L, Hq, hd]."""
+    s, lens = workload_struct(w)
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int32))
+    n, L = len(rows), w.n_layers
+    idx = np.empty((n, L, w.topk), dtype=np.int32)
+    cnt = np.zeros((n, L), dtype=np.int32)
+    out = np.empty((n, L, w.hq, w.head_dim), dtype=np.float64)
+    rc = LIB.clsa_oracle_rows_layer_routing(ctypes.byref(s), _i(rows), n, threads, _i(idx), _i(cnt), _d(out))
+    assert rc == 0, "clsa_oracle_rows_layer_routing failed"
+    return {"idx": idx, "count": cnt, "out": out}
+
+
+def oracle_row_layer_routing(w, r: int) -> dict:
+    """One row of the per-layer routing ablation: idx [L, k], count [L], out [L, Hq, hd]."""
+    s, lens = workload_struct(w)
+    L = w.n_layers
+    idx = np.empty((L, w.topk), dtype=np.int32)
+    cnt = np.zeros(L, dtype=np.int32)
+    out = np.empty((L, w.hq, w.head_dim), dtype=np.float64)
+    rc = LIB.clsa_oracle_row_layer_routing(ctypes.byref(s), r, _i(idx), _i(cnt), _d(out))
+    assert rc == 0, "clsa_oracle_row_layer_routing rejected its arguments"
+    return {"idx": idx, "count": cnt, "out": out}
 
 
 def gen_uniform(seed: int, tid: int, i: int, lo: int, hi: int, den: int) -> int:

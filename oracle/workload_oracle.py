@@ -119,14 +119,15 @@ def oracle_row_projected(w: Workload, r: int, d_model: int) -> dict:
 # ---------------------------------------------------------------------------------------------
 # The distillation target and loss of eq. 4-5 on a prefill workload
 # ---------------------------------------------------------------------------------------------
-def oracle_distill_row(w: Workload, r: int) -> dict:
+def oracle_distill_row(w: Workload, r: int, scale: float | None = None) -> dict:
     """fp64 eq. 4-5 for query row r of a prefill workload (row r sees tokens 0..r): A-bar_r from
     the row's per-layer queries and the shared K cache, I_r from its indexer query and K_idx, and
-    KL(A-bar_r || softmax(I_r)).  dict(abar, scores, kl)."""
+    KL(A-bar_r || softmax(I_r)).  scale: the attention scale of the layers' distributions (None =
+    1/sqrt(head_dim); 1.0 = the unscaled form eq. 4 prints).  dict(abar, scores, kl)."""
     assert w.mode == "prefill"
     n = w.row_len(r)
     tokens = np.arange(n, dtype=np.int64)
     k = gen.bf16_bits_to_f64(w.kv_bits(tokens, "k"))
-    abar = distill_target(w.q_f64([r])[0], k)
+    abar = distill_target(w.q_f64([r])[0], k, scale)
     scores = index_scores(w.q_idx_f64([r])[0], w.k_idx_f64(tokens))
     return {"abar": abar, "scores": scores, "kl": distill_kl(abar, scores)}

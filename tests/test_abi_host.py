@@ -202,3 +202,17 @@ def test_workspace_sizes_cover_every_call():
     assert per_layer >= 2 * 16 * 8 * 2048 * 128 * 2 + 16 * 131072 * (8 + 4)
     with pytest.raises(B.CLSAError):
         B.workspace_bytes(B.make_dims(16, 128, 2048, 16, 32, 8, head_dim=64), rows)
+
+
+def test_attention_split_ranges_stay_inside_the_row(tmp_path):
+    """The attention's per-split selection range (split_key_range, shared by host and device code)
+    clamps any count a caller passes into [0, k]: compiled with g++ and swept over counts below 0,
+    at 0, above k and far above k, every position read stays below k and the splits cover exactly
+    the clamped count."""
+    import subprocess
+    here = os.path.dirname(os.path.abspath(__file__))
+    exe = str(tmp_path / "split_bounds")
+    subprocess.run(["g++", "-std=c++17", "-O1", "-Wall", "-o", exe, os.path.join(here, "host", "split_bounds.cpp")],
+                   check=True)
+    r = subprocess.run([exe], stdout=subprocess.PIPE, text=True)
+    assert r.returncode == 0 and r.stdout.startswith("ok"), r.stdout

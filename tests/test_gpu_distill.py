@@ -46,10 +46,10 @@ def _check(dev_kl, ref, what):
     return err, bound
 
 
-def _run(dw, rows_kw=None, q=None, q_idx=None):
+def _run(dw, rows_kw=None, q=None, q_idx=None, sm_scale=0.0):
     """Prefill rows of dw: routing scores by clsa_index_scores, then clsa_distill_kl."""
     w = dw.w
-    dims = dims_of(dw)
+    dims = dims_of(dw, sm_scale=sm_scale)
     rows = clsa.make_rows(**dw.rows(**(rows_kw or {})))
     n, r0 = rows.n_rows, (rows_kw or {}).get("row0", 0)
     ld = ((rows.max_row_len + 63) // 64) * 64
@@ -81,6 +81,22 @@ def test_distill_small_prefill_every_row(hq, hkv, L):
     assert kl[0] == 0.0 or abs(kl[0]) < 1e-6
     assert abs(loss - kl.mean()) <= 1e-6 * max(1.0, abs(kl.mean()))
     _say(f"hq={hq} hkv={hkv} L={L}: worst error / bound {worst:.3f}, loss {loss:.6f}")
+
+
+def test_distill_unscaled_form_every_row():
+    """sm_scale = 1: the layers' distributions of the raw products q . k, the unscaled form eq. 4
+    prints, every row of a 600-position workload against the oracle with scale 1."""
+    w = cs.custom(mode="prefill", seq_lens=(600,), d_idx=64, topk=32, n_layers=2, hq=8, hkv=2, seed=9,
+                  name="distill_8_2_2")
+    dw = device_workload(w)
+    kl, loss = _run(dw, rows_kw=dict(row0=0, n_rows=600), sm_scale=1.0)
+    worst = 0.0
+    for r in range(600):
+        ref = oracle_distill_row(w, r, scale=1.0)
+        err, bound = _check(kl[r], ref, f"unscaled row {r}")
+        worst = max(worst, err / bound)
+    assert abs(loss - kl.mean()) <= 1e-6 * max(1.0, abs(kl.mean()))
+    _say(f"unscaled: worst error / bound {worst:.3f}, loss {loss:.6f}")
 
 
 def test_distill_chunk_of_a_later_sequence():

@@ -324,6 +324,26 @@ def test_attention_ragged_counts_and_splits(counts):
 
 
 # ----------------------------------------------------------------------------- whole step
+_CPP_CACHE: dict = {}
+
+
+def _oracle_threads() -> int:
+    import os
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _cpp_rows(w, rows, routing=False):
+    """The C++ fp64 oracle (its own input generator) on the given rows over the host's threads,
+    each row single-threaded; cached per workload, rows and kind, so both schedules compare
+    against one evaluation."""
+    from oracle import cpp as C
+    key = (w.name, w.seed, tuple(int(r) for r in rows), routing)
+    if key not in _CPP_CACHE:
+        f = C.oracle_rows_layer_routing if routing else C.oracle_rows
+        _CPP_CACHE[key] = f(w, list(rows), threads=_oracle_threads())
+    return _CPP_CACHE[key]
+
+
 def _run_step(dw, schedule, rows_kw=None, chunk=0, want_scores=False):
     w = dw.w
     dims = dims_of(dw)
@@ -343,10 +363,22 @@ def _run_step(dw, schedule, rows_kw=None, chunk=0, want_scores=False):
 @pytest.mark.parametrize("cfg,check", [(1, None), (2, None), (3, [0, 7, 15]), (5, [0, 5, 31, 63])])
 @pytest.mark.parametrize("schedule", [clsa.SCHEDULE_LAYER_BATCHED, clsa.SCHEDULE_PER_LAYER])
 def test_step_decode_vs_oracle(cfg, check, schedule):
+    """Every row of the workload against the threaded C++ oracle (selections bitwise, outputs
+    within the tolerance), and the listed rows (all rows of the two small workloads) against the
+    numpy oracle as well, with its needle check."""
     w = cs.config(cfg)
     dw = device_workload(w)
     idx, cnt, out = _run_step(dw, schedule)
     dev = bf16_dev_to_f64(out)
+    ref_all = _cpp_rows(w, range(w.n_rows))
+    worst = np.zeros(3)
+    for r in range(w.n_rows):
+        assert cnt[r] == ref_all["count"][r], f"cfg{cfg} row {r}: count"
+        assert np.array_equal(idx[r], ref_all["idx"][r]), \
+            f"cfg{cfg} row {r}: {np.sum(idx[r] != ref_all['idx'][r])} index mismatches (C++ oracle)"
+        worst = np.maximum(worst, assert_outputs_close(dev[r], ref_all["out"][r], f"cfg{cfg} row {r} (C++ oracle)"))
+    _say(f"cfg{cfg} sched {schedule}: all {w.n_rows} rows vs the C++ oracle, worst max {worst[0]:.2e} "
+         f"mean {worst[1]:.2e} rel {worst[2]:.2e}")
     rows = range(w.n_rows) if check is None else check
     for r in rows:
         res = oracle_row(w, r)
@@ -506,10 +538,11 @@ def test_step_decode_at_the_largest_k():
         assert_outputs_close(bf16_dev_to_f64(out)[0], res["out"], f"largest k, schedule {schedule}")
 
 
-@pytest.mark.parametrize("cfg,check", [(1, None), (2, [0, 7]), (3, [4])])
+@pytest.mark.parametrize("cfg,check", [(1, None), (2, [0, 7]), (3, [4]), (5, [1])])
 def test_step_per_layer_routing_vs_oracle(cfg, check):
     """The ablation without the shared index: every layer scores the cache with its own indexer
-    query, selects its own set and attends over it (same kernels, once per layer)."""
+    query, selects its own set and attends over it (same kernels, once per layer).  Every row and
+    layer against the threaded C++ oracle, the listed rows against the numpy oracle too."""
     from oracle.workload_oracle import oracle_row_layer_routing
     w = cs.config(cfg)
     dw = device_workload(w)
@@ -526,6 +559,13 @@ def test_step_per_layer_routing_vs_oracle(cfg, check):
               schedule=clsa.SCHEDULE_PER_LAYER_ROUTING)
     torch.cuda.synchronize()
     idx_h, cnt_h, dev = idx.cpu().numpy(), cnt.cpu().numpy(), bf16_dev_to_f64(out)
+    ref_all = _cpp_rows(w, range(R), routing=True)
+    for r in range(R):
+        for l in range(L):
+            assert cnt_h[l, r] == ref_all["count"][r, l], f"cfg{cfg} row {r} layer {l}: count"
+            assert np.array_equal(idx_h[l, r], ref_all["idx"][r, l]), f"cfg{cfg} row {r} layer {l} (C++ oracle)"
+        assert_outputs_close(dev[r], ref_all["out"][r], f"routing cfg{cfg} row {r} (C++ oracle)")
+    _say(f"per-layer routing cfg{cfg}: all {R} rows x {L} layers vs the C++ oracle")
     for r in (range(R) if check is None else check):
         ref = oracle_row_layer_routing(w, r)
         for l in range(L):
@@ -536,14 +576,29 @@ def test_step_per_layer_routing_vs_oracle(cfg, check):
     assert not np.array_equal(idx_h[0, 0], idx_h[1, 0])
 
 
-@pytest.mark.parametrize("schedule", [clsa.SCHEDULE_LAYER_BATCHED, clsa.SCHEDULE_PER_LAYER])
-def test_step_prefill_vs_oracle(schedule):
+def _prefill_sample(n, k):
+    """Every 8th row, every row around k (where rows stop taking all their tokens) and the last 64."""
+    return sorted(set(range(0, n, 8)) | set(range(k - 8, k + 9)) | set(range(n - 64, n)))
+
+
+@pytest.mark.parametrize("schedule,chunk", [(clsa.SCHEDULE_LAYER_BATCHED, 8192), (clsa.SCHEDULE_LAYER_BATCHED, 1024),
+                                            (clsa.SCHEDULE_PER_LAYER, 1024)])
+def test_step_prefill_vs_oracle(schedule, chunk):
+    """The 8192-row causal prefill, in one chunk of 8192 rows (the benchmark's) and in chunks of
+    1024: every count, every 8th row, the rows around k and the last 64 rows against the threaded
+    C++ oracle, and a few rows against the numpy oracle as well."""
     w = cs.config(4)
     dw = device_workload(w)
-    idx, cnt, out = _run_step(dw, schedule, chunk=1024)
+    idx, cnt, out = _run_step(dw, schedule, chunk=chunk)
     n = w.n_rows
     assert np.array_equal(cnt, np.minimum(np.arange(1, n + 1), w.topk))
     dev = bf16_dev_to_f64(out)
+    sample = _prefill_sample(n, w.topk)
+    ref_all = _cpp_rows(w, sample)
+    for i, t in enumerate(sample):
+        assert np.array_equal(idx[t], ref_all["idx"][i]), f"row {t}: {np.sum(idx[t] != ref_all['idx'][i])} mismatches"
+        assert_outputs_close(dev[t], ref_all["out"][i], f"prefill row {t} (C++ oracle)")
+    _say(f"prefill chunk {chunk} schedule {schedule}: {len(sample)} rows vs the C++ oracle")
     for t in [0, 1, 2, 100, 1023, 1024, 2046, 2047, 2048, 4095, 5000, 8191]:
         res = oracle_row(w, t)
         assert np.array_equal(idx[t], res["idx"]), f"row {t}"

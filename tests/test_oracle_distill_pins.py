@@ -37,6 +37,33 @@ def test_target_two_keys_closed_form_fixes_the_scale():
     assert np.allclose(O.distill_target(q, k), [0.75, 0.25], rtol=0, atol=1e-15)
 
 
+def test_target_unscaled_form_of_the_page():
+    """eq. 4 prints softmax(Q K^T) with no scale; the oracle's scale argument gives that form
+    (scale = 1): the library softmax of the raw products, and the two-key closed form with the
+    raw logit ln 3."""
+    q, k = _rand(6, L=1, hq=1, hkv=1, n=13, hd=32)
+    assert np.allclose(O.distill_target(q, k, scale=1.0), softmax(k[:, 0, :] @ q[0, 0]), rtol=0, atol=1e-15)
+    qq = np.zeros((1, 1, 128))
+    qq[0, 0, 0] = 1.0
+    kk = np.zeros((2, 1, 128))
+    kk[0, 0, 0] = math.log(3.0)
+    assert np.allclose(O.distill_target(qq, kk, scale=1.0), [0.75, 0.25], rtol=0, atol=1e-15)
+    # the default (1/sqrt(head_dim)) differs from it
+    assert not np.allclose(O.distill_target(qq, kk), [0.75, 0.25], rtol=0, atol=1e-3)
+
+
+def test_workload_row_with_the_unscaled_form():
+    """oracle_distill_row(scale=1) is the target of the raw products q . k over the row's keys."""
+    w = cs.custom(mode="prefill", seq_lens=(200,), d_idx=64, topk=32, n_layers=2, hq=4, hkv=2, seed=13)
+    from clsa_synth import gen
+    r = 150
+    d = oracle_distill_row(w, r, scale=1.0)
+    k = gen.bf16_bits_to_f64(w.kv_bits(np.arange(r + 1), "k"))
+    q = w.q_f64([r])[0]
+    per = [softmax(k[:, h // 2, :] @ q[l, h]) for l in range(2) for h in range(4)]
+    assert np.allclose(d["abar"], np.mean(per, axis=0), rtol=0, atol=1e-15)
+
+
 def test_target_is_a_distribution_and_averages_layers_and_heads():
     q, k = _rand(1, L=3, hq=6, hkv=3, n=11)
     a = O.distill_target(q, k)
