@@ -21,7 +21,8 @@ HEAD_DIM = 128
 
 FUNCTIONS = ["clsa_status_string", "clsa_last_error_message", "clsa_abi_version", "clsa_workspace_bytes",
              "clsa_index_scores", "clsa_topk", "clsa_gather_kv", "clsa_sparse_attn", "clsa_step",
-             "clsa_index_project", "clsa_distill_workspace_bytes", "clsa_distill_kl"]
+             "clsa_index_project", "clsa_distill_workspace_bytes", "clsa_distill_kl", "clsa_step_no_alloc"]
+NO_ALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class Dims(ctypes.Structure):
@@ -67,6 +68,7 @@ def _load(path: str = LIB_PATH):
         "clsa_sparse_attn": (c_int32, [POINTER(Dims), POINTER(Rows), P, c_int64, c_int32, P, P, P, P, P, P, P, P,
                                        c_int64, P, c_size_t, P]),
         "clsa_step": (c_int32, [POINTER(Dims), POINTER(Rows), POINTER(StepArgs), P, c_size_t, P]),
+        "clsa_step_no_alloc": (c_int32, [POINTER(Dims), POINTER(Rows), POINTER(StepArgs), P]),
         "clsa_index_project": (c_int32, [POINTER(Dims), POINTER(Rows), c_int32, P, P, P, P, P, P, P, P, P, P, P]),
         "clsa_distill_workspace_bytes": (c_size_t, [POINTER(Dims), POINTER(Rows)]),
         "clsa_distill_kl": (c_int32, [POINTER(Dims), POINTER(Rows), P, c_int64, P, P, P, c_int64, P, P, P, c_size_t, P]),
@@ -184,3 +186,12 @@ def step(dims, rows, q_idx, k_idx, k_cache, v_cache, cu_seqlens, q, out, idx, co
     _check(LIB.clsa_step(ctypes.byref(dims), ctypes.byref(rows), ctypes.byref(a), _ptr(workspace), workspace_bytes_,
                          _stream(stream)))
 
+
+def step_no_alloc(dims, rows, q_idx, k_idx, k_cache, v_cache, cu_seqlens, q, out, idx, count, scores=None,
+                  ld_scores=0, k_sel=None, v_sel=None, schedule=SCHEDULE_LAYER_BATCHED, prefill_chunk_rows=0,
+                  stream=None):
+    """clsa_step_no_alloc: clsa_step on the library's static per-GPU scratch (no workspace)."""
+    a = StepArgs(_ptr(q_idx), _ptr(k_idx), _ptr(k_cache), _ptr(v_cache), _ptr(cu_seqlens), _ptr(q), _ptr(out),
+                 _ptr(idx), _ptr(count), _ptr(scores), ld_scores, _ptr(k_sel), _ptr(v_sel), schedule,
+                 prefill_chunk_rows)
+    _check(LIB.clsa_step_no_alloc(ctypes.byref(dims), ctypes.byref(rows), ctypes.byref(a), _stream(stream)))

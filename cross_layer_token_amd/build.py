@@ -25,7 +25,8 @@ ARCH = "gfx950"
 HIPFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-mcode-object-version=5", "-Wall",
             "-Wno-unused-function",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-LIB_SOURCES = ["plan.cpp", "api.cpp", "k_index.hip", "k_topk.hip", "k_attn.hip", "k_project.hip", "k_distill.hip"]
+LIB_SOURCES = ["plan.cpp", "api.cpp", "k_index.hip", "k_topk.hip", "k_attn.hip", "k_project.hip", "k_distill.hip",
+               "no_alloc.hip"]
 
 
 def hipcc() -> str:

@@ -428,4 +428,21 @@ clsa_status clsa_step(const clsa_dims* dims, const clsa_rows* rows, const clsa_s
   return CLSA_OK;
 }
 
+clsa_status clsa_step_no_alloc(const clsa_dims* dims, const clsa_rows* rows, const clsa_step_args* args,
+                               clsa_stream stream) {
+  g_last_error.clear();
+  if (clsa_status s = check_step_args(dims, rows, args); s != CLSA_OK) return s;
+  const StepPlan sp = plan_step(dims, rows, args->schedule, args->scores != nullptr, args->k_sel != nullptr,
+                                args->prefill_chunk_rows);
+  if (sp.total > kNoAllocScratchBytes)
+    return set_error(CLSA_ERR_UNSUPPORTED, "clsa_step_no_alloc: this call needs " + std::to_string(sp.total) +
+                                               " bytes of scratch; the static scratch holds " +
+                                               std::to_string(kNoAllocScratchBytes) +
+                                               " (use clsa_step with a workspace, smaller prefill chunks, or "
+                                               "caller-owned scores / k_sel / v_sel)");
+  void* ws = nullptr;
+  if (int e = no_alloc_scratch(&ws, g_err); e != 0) return set_error(CLSA_ERR_DEVICE, "clsa_step_no_alloc: " + g_err);
+  return clsa_step(dims, rows, args, ws, kNoAllocScratchBytes, stream);
+}
+
 }  // extern "C"

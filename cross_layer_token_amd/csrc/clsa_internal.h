@@ -202,4 +202,9 @@ int launch_distill(const RowsDev& rows, int64_t total_tokens, int L, int hq, int
                    void* ws, const DistillPlan& plan, void* stream);
 const char* device_error_string(int err);
 
+// Static device scratch of clsa_step_no_alloc (no_alloc.hip): its size, and the address of the
+// current device's copy (looked up once per device; 0 = success, else a HIP error with `err` set).
+constexpr size_t kNoAllocScratchBytes = CLSA_NO_ALLOC_SCRATCH_BYTES;
+int no_alloc_scratch(void** ptr, std::string& err);
+
 }  // namespace clsa

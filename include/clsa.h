@@ -19,7 +19,8 @@
  *    nothing and touches no memory.
  *  - Ownership: the caller allocates every device buffer (inputs, outputs, workspace) and
  *    keeps it alive until the stream has passed the call.  The library allocates no device
- *    memory and keeps no pointer after returning.
+ *    memory and keeps no pointer after returning.  (clsa_step_no_alloc, at the end, is the one
+ *    exception: its workspace is a static array of the library's own device code.)
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null stream).
  *  - Device pointers must be 16-byte aligned; the workspace 256-byte aligned.  bf16 values are
  *    passed as uint16 bit patterns.
@@ -269,6 +270,24 @@ typedef struct clsa_step_args {
  */
 clsa_status clsa_step(const clsa_dims* dims, const clsa_rows* rows, const clsa_step_args* args,
                       void* workspace, size_t workspace_bytes, clsa_stream stream);
+
+/*
+ * clsa_step for callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  Same arguments (minus the workspace), results and
+ * errors as clsa_step; the caller still passes every input and output buffer.  The workspace is a
+ * static device array of CLSA_NO_ALLOC_SCRATCH_BYTES owned by the library: each GPU holds its own
+ * copy from the first call on that GPU until the process ends.  The call allocates nothing and calls
+ * nothing that allocates.
+ *  - Limit: a call whose step needs more scratch than that (at most clsa_workspace_bytes(dims, rows,
+ *    args->schedule, args->prefill_chunk_rows) bytes) launches nothing and returns
+ *    CLSA_ERR_UNSUPPORTED; smaller prefill chunks, or caller-owned scores / k_sel / v_sel, need less.
+ *  - Concurrency: every call on one GPU shares that GPU's scratch, which keeps the last call's
+ *    contents (each call clears what must start at zero).  Calls that overlap in time on one GPU
+ *    (on other streams or from other threads) race on it and must not be made.
+ */
+#define CLSA_NO_ALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+clsa_status clsa_step_no_alloc(const clsa_dims* dims, const clsa_rows* rows, const clsa_step_args* args,
+                               clsa_stream stream);
 
 #ifdef __cplusplus
 }

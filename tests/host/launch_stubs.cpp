@@ -40,5 +40,10 @@ int launch_distill(const RowsDev&, int64_t, int, int, int, float, const uint16_t
   return kNoDevice;
 }
 const char* device_error_string(int) { return "no device (host-only sanitizer build)"; }
+int no_alloc_scratch(void** ptr, std::string& err) {
+  *ptr = nullptr;
+  err = "no device (host-only sanitizer build)";
+  return kNoDevice;
+}
 
 }  // namespace clsa

@@ -216,3 +216,20 @@ def test_attention_split_ranges_stay_inside_the_row(tmp_path):
                    check=True)
     r = subprocess.run([exe], stdout=subprocess.PIPE, text=True)
     assert r.returncode == 0 and r.stdout.startswith("ok"), r.stdout
+
+
+def test_step_no_alloc_rejects_a_step_beyond_its_scratch():
+    """clsa_step_no_alloc refuses, on the host and before any HIP call, a step whose workspace
+    exceeds its static scratch: 64 rows of 131072 tokens (their scores and candidate lists alone
+    pass 64 MiB)."""
+    R, n = 64, 131072
+    dims = _dims(batch=R, topk=2048)
+    rows = B.make_rows(B.MODE_DECODE, R, n, R * n)
+    with pytest.raises(B.CLSAError) as e:
+        B.step_no_alloc(dims, rows, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0)
+    assert e.value.status == B.ERR_UNSUPPORTED and "static scratch" in str(e.value)
+    assert B.NO_ALLOC_SCRATCH_BYTES == 64 << 20
+    # a NULL argument is reported before the size
+    with pytest.raises(B.CLSAError) as e:
+        B.step_no_alloc(dims, rows, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0)
+    assert e.value.status == B.ERR_INVALID_ARGUMENT
