@@ -166,6 +166,78 @@ PROFILE_COMMANDS = {
 }
 
 
+PREFILL_COUNTER_RUN = "python3 bench.py --prefill-only --prefill-steps 1 --no-distill --profile-copy-mib 1024"
+PREFILL_COUNTER_COMMANDS = {
+    "mfma": "rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 LdsUtil LdsBankConflict --output-format csv "
+            f"-d rocprof_out/prefill_mfma -o bench -- {PREFILL_COUNTER_RUN}",
+    "fetch": f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d rocprof_out/prefill_fetch -o bench -- {PREFILL_COUNTER_RUN}",
+    "write": f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d rocprof_out/prefill_write -o bench -- {PREFILL_COUNTER_RUN}",
+}
+PREFILL_KERNELS = (("k_index_scores_prefill<128>", "k_index_scores_prefill"),
+                   ("k_sparse_attn<true, 2, false, 2, false> (prefill attention)", "k_sparse_attn<true, 2, false, 2, false>"),
+                   ("k_topk_rows_lds", "k_topk_rows_lds"))
+
+
+def summarize_prefill_counters(mfma_dir: str, fetch_dir: str, write_dir: str, copy_mib: int = 1024) -> str:
+    """MFMA and LDS utilisation and HBM traffic per launch of the prefill kernels (the causal
+    indexer GEMM, the prefill attention, the per-row top-k) on the 8192-row prefill workload, from
+    three rocprofv3 counter passes; FETCH_SIZE / WRITE_SIZE are scaled by what the same counters read
+    for a plain device copy of copy_mib MiB."""
+    import glob
+
+    import clsa_synth as cs
+
+    def rows(d):
+        return _csv_rows(sorted(glob.glob(os.path.join(d, "*_counter_collection.csv")))[0])
+
+    def per_kernel(rr, cname, pat):
+        v = [float(r["Counter_Value"]) for r in rr if r["Counter_Name"] == cname and pat in r["Kernel_Name"]]
+        return (sum(v) / len(v), len(v)) if v else (None, 0)
+
+    m, f, wr = rows(mfma_dir), rows(fetch_dir), rows(write_dir)
+    scale = {}
+    for tag, rr, cname in (("fetch", f, "FETCH_SIZE"), ("write", wr, "WRITE_SIZE")):
+        copy = max((r for r in rr if r["Counter_Name"] == cname and "copyBuffer" in r["Kernel_Name"]),
+                   key=lambda r: int(r["Grid_Size"]))
+        scale[tag] = (copy_mib * 1024.0) / float(copy["Counter_Value"])
+    w = cs.config(4)
+    n, L = w.n_rows, w.n_layers
+    sel = sum(min(w.topk, t + 1) for t in range(n))
+    alg_flop = {"k_index_scores_prefill": 2.0 * w.d_idx * n * (n + 1) / 2,
+                "k_sparse_attn<true, 2, false, 2, false>": 4.0 * sel * L * w.hq * w.head_dim}
+    alg_bytes = {"k_index_scores_prefill": 2 * 2 * n * w.d_idx + 4 * n * (n + 1) // 2}
+    md = ["# MFMA, LDS and HBM counters of the prefill kernels, prefill_n8k", "",
+          "Made by (on one MI355X; each counter pass runs separately):", "",
+          *[f"    {c}" for c in PREFILL_COUNTER_COMMANDS.values()],
+          f"    python bench.py --summarize-prefill-counters {mfma_dir} {fetch_dir} {write_dir}", "",
+          "The run holds one causal prefill step of the 8192-row workload in one chunk of 8192 rows, then the",
+          "indexer GEMM alone ten times. `MfmaUtil` is rocprofv3's derived percentage of the SIMDs' MFMA-busy",
+          "cycles over the kernel's active cycles; `MfmaFlopsBF16` counts the bf16 MFMA work done (512 per",
+          "MOPS); `LdsUtil` is the share of cycles the CUs' LDS is active; `LdsBankConflict` is conflicts per",
+          f"access. FETCH_SIZE and WRITE_SIZE are scaled by a plain {copy_mib} MiB device copy in the same runs",
+          f"(factors {scale['fetch']:.4f} and {scale['write']:.4f}).", "",
+          "| kernel | launches | MfmaUtil % | MFMA TFLOP per launch | algorithmic TFLOP | LdsUtil % | LDS conflicts / access | HBM read MB | HBM write MB |",
+          "|---|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    for label, pat in PREFILL_KERNELS:
+        mu, cnt = per_kernel(m, "MfmaUtil", pat)
+        fl, _ = per_kernel(m, "MfmaFlopsBF16", pat)
+        lu, _ = per_kernel(m, "LdsUtil", pat)
+        lb, _ = per_kernel(m, "LdsBankConflict", pat)
+        fe, _ = per_kernel(f, "FETCH_SIZE", pat)
+        wb, _ = per_kernel(wr, "WRITE_SIZE", pat)
+
+        def fmt(x, k=2):
+            return "-" if x is None else f"{x:.{k}f}"
+        af = alg_flop.get(pat)
+        md.append(f"| `{label}` | {cnt} | {fmt(mu)} | {fmt(None if fl is None else fl / 1e12, 4)} | "
+                  f"{fmt(None if af is None else af / 1e12, 4)} | {fmt(lu)} | {fmt(lb, 4)} | "
+                  f"{fmt(None if fe is None else fe * scale['fetch'] * 1024 / 1e6, 1)} | "
+                  f"{fmt(None if wb is None else wb * scale['write'] * 1024 / 1e6, 1)} |")
+    md += ["", f"Algorithmic bytes of the indexer GEMM: Q_idx and K_idx read once ({4 * n * w.d_idx / 1e6:.1f} MB) and the",
+           f"causal fp32 scores written ({4 * n * (n + 1) // 2 / 1e6:.1f} MB), {alg_bytes['k_index_scores_prefill'] / 1e6:.1f} MB per launch."]
+    return "\n".join(md) + "\n"
+
+
 def trace_command(config: int) -> str:
     """The rocprofv3 kernel-trace command whose summary profiles/kernel_trace_<workload>.md holds."""
     if config == 4:
@@ -341,14 +413,22 @@ def infinity_cache_gbps(stream, mib: int = 128) -> dict:
                 fn()
             ev1.record(stream)
         torch.cuda.synchronize()
-        return nbytes / (ev0.elapsed_time(ev1) / 50 / 1e3) / 1e9
+        return nbytes / ((ev0.elapsed_time(ev1) / 1e3) / 50) / 1e9
 
     read = rate(lambda: x.sum(), mib << 20)
     copy = rate(lambda: dst.copy_(half), mib << 20)
     return {"read_gbps": round(read, 1), "copy_gbps": round(copy, 1), "gbps": round(max(read, copy), 1)}
 
 
-def decode_configs_report(configs=(1, 2, 5), steps: int = 50, warmup: int = 10, flush=None) -> dict:
+def per_layer_bound(w, balg_total: float, ic_gbps: float) -> tuple:
+    """The dependent-layer schedule's roofline: the step's algorithmic bytes from HBM at the peak,
+    plus the compact K_S/V_S re-read once per layer at the rate measured for cache-resident data.
+    Returns (bound seconds, compact bytes per layer)."""
+    sel = sum(2 * w.hkv * min(w.topk, n) * w.head_dim * 2 for n in w.seq_lens)
+    return balg_total / (HBM_PEAK_GBPS * 1e9) + w.n_layers * sel / (ic_gbps * 1e9), sel
+
+
+def decode_configs_report(configs=(1, 2, 5), steps: int = 50, warmup: int = 10, flush=None, ic_gbps=None) -> dict:
     """The layer-batched decode step on the other decode workloads (the single short row, the
     32K batch, and the ragged 64-sequence batch with tie-heavy indexer entries), reported beside
     the 128K line: device time per step from HIP events around each step, with the caches flushed
@@ -384,6 +464,24 @@ def decode_configs_report(configs=(1, 2, 5), steps: int = 50, warmup: int = 10, 
         hot, hot_wall = event_times(stream, one, steps)
         t = float(np.median(cold))
         b = algorithmic_bytes(w)["total"]
+        per_layer = None
+        if ic_gbps:
+            nws2 = clsa.workspace_bytes(dims, rows, clsa.SCHEDULE_PER_LAYER)
+            ws2 = torch.empty(nws2, dtype=torch.uint8, device="cuda")
+
+            def one_pl():
+                clsa.step(dims, rows, dw.q_idx, dw.k_idx, dw.k_cache, dw.v_cache, dw.cu_seqlens, dw.q, out, idx,
+                          cnt, ws2, nws2, schedule=clsa.SCHEDULE_PER_LAYER, stream=stream)
+
+            for _ in range(3):
+                one_pl()
+            pl, _ = event_times(stream, one_pl, max(10, steps // 5), flush=flush)
+            t_pl = float(np.median(pl))
+            bound, sel = per_layer_bound(w, b, ic_gbps)
+            per_layer = {"ms_per_step": round(t_pl * 1e3, 4), "compact_bytes_per_layer": sel,
+                         "bound_ms": round(bound * 1e3, 4), "frac": round(bound / t_pl, 4)}
+            log(f"{w.name} per-layer schedule: {t_pl * 1e6:.1f} us (bound {bound * 1e6:.1f} us)")
+            del ws2
         log(f"{w.name}: {t * 1e6:.1f} us flushed, {float(np.median(hot)) * 1e6:.1f} us hot")
         out_rep[w.name] = {"rows": R, "tokens": w.total_tokens, "max_row_len": w.max_row_len, "topk": k,
                            "layers": w.n_layers, "ms_per_step": round(t * 1e3, 4), "tokens_per_s": round(R / t, 1),
@@ -391,7 +489,8 @@ def decode_configs_report(configs=(1, 2, 5), steps: int = 50, warmup: int = 10, 
                            "roofline_frac": round(b / t / 1e9 / HBM_PEAK_GBPS, 4),
                            "flushed": distribution(cold), "hot": distribution(hot),
                            "hot_wall_ms_per_step": round(hot_wall / steps * 1e3, 4),
-                           "hot_roofline_frac": round(b / float(np.median(hot)) / 1e9 / HBM_PEAK_GBPS, 4)}
+                           "hot_roofline_frac": round(b / float(np.median(hot)) / 1e9 / HBM_PEAK_GBPS, 4),
+                           "per_layer_schedule": per_layer}
         del dw, out, idx, cnt, ws
         torch.cuda.empty_cache()
     return out_rep
@@ -445,7 +544,7 @@ def prefill_report(steps: int = 3, chunk: int = 8192) -> dict:
         clsa.index_scores(dims, rows, dw.q_idx, dw.k_idx, dw.cu_seqlens, scores, ld, stream=stream)
     ev1.record(stream)
     torch.cuda.synchronize()
-    t_idx = ev0.elapsed_time(ev1) / 10 / 1e3
+    t_idx = (ev0.elapsed_time(ev1) / 1e3) / 10
     idx_flop = 2.0 * w.d_idx * (R * (R + 1) // 2)
     return {"workload": w.name, "rows": R, "topk": k, "layers": L, "chunk_rows": chunk, "steps": steps,
             "ms_per_step": round(t_step * 1e3, 3), "tokens_per_s": round(R / t_step, 1),
@@ -492,7 +591,7 @@ def distill_report(reps: int = 3) -> dict:
     run(reps)
     ev1.record(stream)
     torch.cuda.synchronize()
-    t = ev0.elapsed_time(ev1) / reps / 1e3
+    t = (ev0.elapsed_time(ev1) / 1e3) / reps
     log(f"distillation: {t * 1e3:.3f} ms")
     pairs = R * (R + 1) // 2                          # causal (position, key) pairs
     flop = 2 * pairs * L * hq * w.head_dim * 2         # two passes of q.k, 2 flop per MAC
@@ -550,12 +649,19 @@ def main():
                     help="also run one plain device copy of this many MiB (a counter calibration reference)")
     ap.add_argument("--summarize-trace", metavar="DIR",
                     help="write the kernel-trace summary of --config's workload under profiles/ and exit")
+    ap.add_argument("--summarize-prefill-counters", nargs=3, metavar=("MFMA_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="write the prefill kernels' counter summary under profiles/ and exit")
     ap.add_argument("--prefill-only", action="store_true",
                     help="run only the prefill report (and the distillation report unless --no-distill)")
     ap.add_argument("--prefill-steps", type=int, default=3)
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the score kernel's HBM traffic summary under profiles/ and exit")
     args = ap.parse_args()
+    if args.summarize_prefill_counters:
+        p = os.path.join(ROOT, "profiles", "counters_prefill_kernels_prefill_n8k.md")
+        open(p, "w").write(summarize_prefill_counters(*args.summarize_prefill_counters))
+        print("wrote", p)
+        return
     if args.summarize_trace or args.summarize_counters:
         os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
         if args.summarize_trace:
@@ -585,6 +691,11 @@ def main():
         rep = {"prefill": prefill_report(steps=args.prefill_steps)}
         if not args.no_distill:
             rep["distill"] = distill_report()
+        if args.profile_copy_mib > 0:
+            src = torch.ones(args.profile_copy_mib << 20, dtype=torch.uint8, device="cuda")
+            dst = torch.empty_like(src)
+            dst.copy_(src)
+            torch.cuda.synchronize()
         print(json.dumps(rep), flush=True)
         return
     w = cs.config(args.config, args.seed)
@@ -614,7 +725,7 @@ def main():
         ev1.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        return ev0.elapsed_time(ev1) / 1e3, wall
+        return (ev0.elapsed_time(ev1) / 1e3), wall
 
     flush = Flush(stream)
 
@@ -637,8 +748,12 @@ def main():
 
     # ---- the dominant kernel alone: routing scores streamed from K_idx --------------------------
     # Its algorithmic bytes are the K_idx scan and the queries; the fp32 score write is an
-    # intermediate of the method and is reported separately.  Each launch is timed by its own
-    # events, with the flush before it.
+    # intermediate of the method and is reported separately.  The launch time is the mean over
+    # launches back to back between one pair of events: K_idx (512 MiB, streamed with non-temporal
+    # loads) is larger than the Infinity Cache, so no launch finds the previous one's bytes cached,
+    # and a kernel recorded alone between two events starts about 5.5 us after its start event
+    # (the event's completion handshake; see the kernel trace), which would be counted as kernel
+    # time.  Per-launch events with the flush before each launch are reported beside it.
     ld = ((w.max_row_len + 63) // 64) * 64
     scores = torch.empty((R, ld), dtype=torch.float32, device="cuda")
 
@@ -647,16 +762,18 @@ def main():
             clsa.index_scores(dims, rows, dw.q_idx, dw.k_idx, dw.cu_seqlens, scores, ld, stream=stream)
 
     run_scores(args.warmup)
+    t_idx_all, _ = timed(run_scores, args.steps)
+    t_idx = t_idx_all / args.steps
     idx_times, _ = event_times(stream, lambda: run_scores(1), args.steps, flush=flush)
-    t_idx = float(np.mean(idx_times))
     idx_bytes = balg["k_idx"] + balg["q_idx"]          # K_idx + q_idx read
     achieved = idx_bytes / t_idx / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(idx_bytes),
                 "kernel": "k_index_scores_decode<128>", "bytes_per_launch": idx_bytes,
                 "score_write_bytes_per_launch": 4 * w.total_tokens, "us_per_launch": round(t_idx * 1e6, 2),
-                "launch_timing_us": {k2.replace("_ms", ""): (round(v * 1e3, 2) if k2.endswith("_ms") else v)
-                                     for k2, v in distribution(idx_times).items()},
+                "launches": args.steps,
+                "flushed_per_launch_events_us": {k2.replace("_ms", ""): (round(v * 1e3, 2) if k2.endswith("_ms") else v)
+                                                 for k2, v in distribution(idx_times).items()},
                 "with_score_write_frac": round((idx_bytes + 4 * w.total_tokens) / t_idx / 1e9 / HBM_PEAK_GBPS, 4)}
     flush_check = cache_flush_check(stream, flush)
     log(f"score kernel alone: {t_idx * 1e6:.2f} us per launch; flush check {flush_check}")
@@ -673,8 +790,7 @@ def main():
         # its roofline: the step's algorithmic bytes from HBM, plus the compact K_S/V_S read once
         # per layer from the Infinity Cache, at the rate a cache-resident device copy reaches here
         ic = infinity_cache_gbps(stream)
-        sel_bytes = 2 * R * w.hkv * w.topk * w.head_dim * 2
-        bound = balg["total"] / (HBM_PEAK_GBPS * 1e9) + w.n_layers * sel_bytes / (ic["gbps"] * 1e9)
+        bound, sel_bytes = per_layer_bound(w, balg["total"], ic["gbps"])
         log(f"per-layer schedule: {t_pl * 1e6:.1f} us")
         per_layer = {"ms_per_step": round(t_pl * 1e3, 4), "tokens_per_s": round(R / t_pl, 1),
                      "timing": distribution(pl_times),
@@ -744,7 +860,8 @@ def main():
 
     del dw, out, idx, cnt, ws, scores
     torch.cuda.empty_cache()
-    decode_configs = None if args.no_decode_configs else decode_configs_report(flush=flush)
+    decode_configs = None if args.no_decode_configs else decode_configs_report(
+        flush=flush, ic_gbps=per_layer["roofline"]["infinity_cache"]["gbps"] if per_layer else None)
     prefill = None if args.no_prefill else prefill_report()
     distill = None if args.no_distill else distill_report()
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_budget)
@@ -768,7 +885,8 @@ def main():
         "step_roofline_frac": round(hbm_gbps / HBM_PEAK_GBPS, 4),
         "bytes_alg_per_step": balg["total"],
         "step_timing": {"protocol": f"HIP events around each step; a {FLUSH_MIB} MiB read before every step, outside "
-                                    "its events; median over the steps",
+                                    "its events; median over the steps (the step's first kernel starts about 5.5 us "
+                                    "after its start event, which this figure counts)",
                         "flushed": distribution(step_times), "flushed_wall_s": round(step_wall, 3),
                         "hot": distribution(hot_times),
                         "hot_back_to_back_ms_per_step": round(t_gpu_hot / args.steps * 1e3, 4),

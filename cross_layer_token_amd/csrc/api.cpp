@@ -407,21 +407,40 @@ clsa_status clsa_step(const clsa_dims* dims, const clsa_rows* rows, const clsa_s
                       out, row_elems, ws + sp.part_off, attn_tickets, true, stream, sp.fused_select ? &sel : nullptr,
                       idx, count);
       if (e) return device_status(e, "clsa_step: attention");
-    } else {
+    } else if (prefill) {
+      // prefill rows gather their own selections inside the attention (no compact buffer)
       const AttnPlan ap = plan_attn(dims, cr.n_rows, 1, rows->n_rows);
-      clsa_bf16* ksel = nullptr;
-      clsa_bf16* vsel = nullptr;
-      if (!prefill) {
-        ksel = a->k_sel ? a->k_sel : reinterpret_cast<clsa_bf16*>(ws + sp.ksel_off);
-        vsel = a->v_sel ? a->v_sel : reinterpret_cast<clsa_bf16*>(ws + sp.vsel_off);
-        e = launch_gather(rd, k, hkv, a->k_cache, a->v_cache, idx, count, ksel, vsel, stream);
-        if (e) return device_status(e, "clsa_step: gather");
-      }
       for (int l = 0; l < L; ++l) {
-        e = launch_attn(rd, k, hq, hkv, 1, scale, ap, q + (int64_t)l * hq * CLSA_HEAD_DIM, row_elems, ksel, vsel,
+        e = launch_attn(rd, k, hq, hkv, 1, scale, ap, q + (int64_t)l * hq * CLSA_HEAD_DIM, row_elems, nullptr, nullptr,
                         a->k_cache, a->v_cache, idx, count, out + (int64_t)l * hq * CLSA_HEAD_DIM, row_elems,
                         ws + sp.part_off, attn_tickets, true, stream);
         if (e) return device_status(e, "clsa_step: attention layer");
+      }
+    } else {
+      // decode: gather K_S/V_S of a chunk of rows into the compact buffers, then the L passes over
+      // them while they are cache-resident; decode row r is sequence r, so a chunk's rows are the
+      // sequences s0.. and read cu_seqlens from s0
+      const int sc = sp.sel_chunk_rows;
+      const size_t sel_row = (size_t)hkv * k * CLSA_HEAD_DIM;
+      for (int s0 = 0; s0 < cr.n_rows; s0 += sc) {
+        RowsDev rs = rd;
+        rs.n_rows = cr.n_rows - s0 < sc ? cr.n_rows - s0 : sc;
+        rs.cu = rd.cu + s0;
+        const AttnPlan ap = plan_attn(dims, rs.n_rows, 1, rs.n_rows);
+        clsa_bf16* ksel = a->k_sel ? a->k_sel + s0 * sel_row : reinterpret_cast<clsa_bf16*>(ws + sp.ksel_off);
+        clsa_bf16* vsel = a->v_sel ? a->v_sel + s0 * sel_row : reinterpret_cast<clsa_bf16*>(ws + sp.vsel_off);
+        const int32_t* cidx = idx + (int64_t)s0 * k;
+        const int32_t* ccnt = count + s0;
+        e = launch_gather(rs, k, hkv, a->k_cache, a->v_cache, cidx, ccnt, ksel, vsel, stream);
+        if (e) return device_status(e, "clsa_step: gather");
+        const clsa_bf16* cq = q + (int64_t)s0 * row_elems;
+        clsa_bf16* cout = out + (int64_t)s0 * row_elems;
+        for (int l = 0; l < L; ++l) {
+          e = launch_attn(rs, k, hq, hkv, 1, scale, ap, cq + (int64_t)l * hq * CLSA_HEAD_DIM, row_elems, ksel, vsel,
+                          a->k_cache, a->v_cache, cidx, ccnt, cout + (int64_t)l * hq * CLSA_HEAD_DIM, row_elems,
+                          ws + sp.part_off, attn_tickets, true, stream);
+          if (e) return device_status(e, "clsa_step: attention layer");
+        }
       }
     }
   }

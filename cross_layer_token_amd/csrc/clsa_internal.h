@@ -55,6 +55,10 @@ constexpr int kAttnManyBlocks = 512;
 constexpr int kAttnPartFloats = 4 * 34 * 64;
 // Default rows per prefill chunk of clsa_step.
 constexpr int kPrefillChunkRows = 1024;
+// The per-layer decode schedule gathers K_S/V_S of this many bytes at most at a time (a chunk of
+// rows), so that the compact buffers the L attention passes re-read stay in the 256 MB Infinity
+// Cache.
+constexpr size_t kPerLayerResidentBytes = (size_t)192 << 20;
 
 // ---- host-side plan (pure functions, no HIP) ------------------------------------------------
 struct TopkPlan {
@@ -90,6 +94,7 @@ struct StepPlan {
   TopkPlan topk;
   AttnPlan attn;
   int chunk_rows = 0;      // prefill: rows per chunk; decode: R
+  int sel_chunk_rows = 0;  // per-layer decode: rows whose compact K_S/V_S are gathered at once
   int64_t ld_scores = 0;   // workspace scores leading dimension
   size_t ticket_off = 0;   // attention tickets
   int n_tickets = 0;
@@ -136,6 +141,40 @@ CLSA_HOST_DEVICE inline void split_key_range(int count, int k, int split, int kp
   const int b = split * kps;
   *kbeg = b;
   *kend = b + kps < cnt ? b + kps : cnt;
+}
+
+// Prefill routing scores: the causal tiles of kPfTile rows x kPfTile token columns.  Row block rb
+// (rows kPfTile rb .. of the call) has column blocks 0 .. (pos0 + its last row) / kPfTile: c0 + rb of
+// them for every block but the last (c0 = ceil(pos0 / kPfTile) + 1), so tile t lies in the row block
+// whose prefix P(rb) = rb c0 + rb (rb - 1) / 2 is the largest at or below t.
+constexpr int kPfTile = 128;
+struct PrefillGrid {
+  int c0;        // column blocks of row block 0
+  int last_rb;   // last row block
+  int64_t tiles; // tiles holding a visible entry
+};
+CLSA_HOST_DEVICE inline int64_t pf_prefix(int64_t rb, int c0) { return rb * c0 + rb * (rb - 1) / 2; }
+inline PrefillGrid prefill_grid(int pos0, int n_rows) {
+  PrefillGrid g;
+  g.c0 = (pos0 + kPfTile - 1) / kPfTile + 1;
+  g.last_rb = (n_rows - 1) / kPfTile;
+  g.tiles = pf_prefix(g.last_rb, g.c0) + (int64_t)(pos0 + n_rows - 1) / kPfTile + 1;
+  return g;
+}
+// Row block and column block of tile t < g.tiles.
+CLSA_HOST_DEVICE inline void prefill_tile(const PrefillGrid& g, int64_t t, int* rb_out, int* cb_out) {
+  int64_t rb;
+  if (t >= pf_prefix(g.last_rb, g.c0)) {
+    rb = g.last_rb;
+  } else {
+    // P(rb) <= t  <=>  rb <= (sqrt((2 c0 - 1)^2 + 8 t) - (2 c0 - 1)) / 2; then fix the rounding
+    const double b = 2.0 * g.c0 - 1.0;
+    rb = (int64_t)((__builtin_sqrt(b * b + 8.0 * (double)t) - b) * 0.5);
+    while (rb > 0 && pf_prefix(rb, g.c0) > t) --rb;
+    while (rb < g.last_rb && pf_prefix(rb + 1, g.c0) <= t) ++rb;
+  }
+  *rb_out = (int)rb;
+  *cb_out = (int)(t - pf_prefix(rb, g.c0));
 }
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }

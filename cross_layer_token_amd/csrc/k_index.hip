@@ -11,7 +11,7 @@
 // saves the select a pass over the scores.
 //
 // Prefill: the causal product Q_idx K_idx^T on the matrix cores (bf16 MFMA 16x16x32, fp32
-// accumulate), skipping tiles above the diagonal.
+// accumulate) over the causal tiles only, each K_idx tile staged once in LDS.
 #include "select_common.h"
 
 namespace clsa {
@@ -172,51 +172,103 @@ __global__ __launch_bounds__(kIdxThreads) void k_index_scores_decode(const uint1
   }
 }
 
-// Prefill: rows i (query positions pos0 + i of sequence `seq`), columns j (tokens of the same
-// sequence); only j <= pos0 + i is computed and written.  64 x 64 tile per workgroup, each wave
-// 16 rows x 64 columns.
+// Prefill: the causal product Q_idx K_idx^T.  Rows i are the query positions pos0 + i of sequence
+// `seq`, columns j the tokens of that sequence; only j <= pos0 + i is written.  The grid enumerates
+// only the 128 x 128 tiles (128 rows of the call x 128 token columns) that hold a visible entry:
+// row block rb (rows 128 rb ..) has column blocks 0 .. (pos0 + its last row) / 128, that is c0 + rb
+// of them for every block but the last (c0 = ceil(pos0 / 128) + 1), so tile t lies in the row
+// block whose prefix P(rb) = rb c0 + rb (rb - 1) / 2 is the largest at or below t.
+// The workgroup stages its 128 K_idx rows once in LDS (16-byte chunks XOR-swizzled by the row, so
+// the fragment reads of 16 rows x 4 chunks hit 64 distinct banks) and each of its four waves takes
+// a quarter of the query rows.  The product runs transposed, S^T = K Q^T, on bf16 MFMA 16x16x32: a lane's four
+// accumulators are then four consecutive columns of one row, stored as one 16-byte write, and a
+// store instruction covers 64 contiguous bytes of 16 rows.
+constexpr int kPfThreads = 256;
+
 template <int D>
-__global__ __launch_bounds__(256) void k_index_scores_prefill(const uint16_t* __restrict__ q_idx,
-                                                               const uint16_t* __restrict__ k_idx,
-                                                               const int32_t* __restrict__ cu, int seq, int pos0,
-                                                               int n_rows, float* __restrict__ scores, int64_t ld,
-                                                               uint32_t* __restrict__ clear, int n_clear) {
-  constexpr int KS = D / 32;
+__global__ __launch_bounds__(kPfThreads) void k_index_scores_prefill(const uint16_t* __restrict__ q_idx,
+                                                                      const uint16_t* __restrict__ k_idx,
+                                                                      const int32_t* __restrict__ cu, int seq, int pos0,
+                                                                      int n_rows, float* __restrict__ scores, int64_t ld,
+                                                                      PrefillGrid grid, uint32_t* __restrict__ clear,
+                                                                      int n_clear) {
+  constexpr int KS = D / 32;                       // MFMA k-steps
+  constexpr int CH = D / 8;                        // 16-byte chunks per K_idx row
+  constexpr int WROWS = kPfTile / (kPfThreads / 64);  // query rows per wave
+  constexpr int RPW = WROWS / 16;                  // 16-row MFMA blocks per wave
+  static_assert(RPW >= 1 && kPfTile * CH % kPfThreads == 0, "tile shape");
+  __shared__ __attribute__((aligned(16))) uint16_t kt[kPfTile * D];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
-  if (clear != nullptr && blockIdx.x == 0 && blockIdx.y == 0)
-    for (int i = threadIdx.x; i < n_clear; i += blockDim.x) clear[i] = 0u;
-  const int last_row = (r0 + 63 < n_rows - 1) ? r0 + 63 : n_rows - 1;
-  if (c0 > pos0 + last_row) return;  // tile entirely above the causal diagonal
-  const int64_t base = cu[seq];
-  const int wr0 = r0 + wave * 16;
-  if (wr0 >= n_rows) return;
   const int l16 = lane & 15, grp = lane >> 4;
-  bf16x8_t a[KS];
-  {
-    const int row = wr0 + l16;
+  if (clear != nullptr && blockIdx.x == 0)
+    for (int i = threadIdx.x; i < n_clear; i += blockDim.x) clear[i] = 0u;
+  const int64_t base = cu[seq];
+  const int ncols = pos0 + n_rows;  // tokens any row of this call sees
+  // Workgroup ids are dealt to the 8 XCDs in turn, so workgroup b takes tile (b % 8) per_xcd + b / 8:
+  // each XCD then works through one contiguous band of row blocks, and its L2 holds that band's
+  // queries and the keys they see instead of every tile's inputs.
+  const int64_t per_xcd = (grid.tiles + 7) / 8;
+  for (int64_t b = blockIdx.x; b < 8 * per_xcd; b += gridDim.x) {
+    const int64_t t = (b % 8) * per_xcd + b / 8;
+    if (t >= grid.tiles) continue;  // the padding of the last band (uniform in the workgroup)
+    int rb, cb;
+    prefill_tile(grid, t, &rb, &cb);
+    const int r0 = rb * kPfTile;  // first row of the tile
+    const int k0 = cb * kPfTile;  // first token column
+    __syncthreads();  // the previous tile's fragment reads are done
+    // stage the tile's K_idx rows (columns past the call's last token read that token, unused)
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (row < n_rows) v = *reinterpret_cast<const uint4*>(q_idx + (int64_t)row * D + ks * 32 + grp * 8);
-      a[ks] = bitcast<bf16x8_t>(v);
+    for (int i = 0; i < kPfTile * CH / kPfThreads; ++i) {
+      const int e = i * kPfThreads + threadIdx.x;
+      const int key = e / CH, ch = e % CH;
+      const int col = k0 + key < ncols ? k0 + key : ncols - 1;
+      const uint4 v = load16(k_idx + (base + col) * D + ch * 8);
+      *reinterpret_cast<uint4*>(kt + key * D + ((ch ^ (key & (CH - 1))) * 8)) = v;
     }
-  }
-  const int ncols = pos0 + n_rows;  // tokens any row of this call may see
+    // this wave's query fragments: rows r0 + WROWS wave + 16 rblk + l16, d = 32 ks + 8 grp ..
+    bf16x8_t qf[RPW][KS];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int col = c0 + nt * 16 + l16;
-    floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int rblk = 0; rblk < RPW; ++rblk) {
+      const int row = r0 + wave * WROWS + rblk * 16 + l16;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (col < ncols) v = *reinterpret_cast<const uint4*>(k_idx + (base + col) * D + ks * 32 + grp * 8);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], bitcast<bf16x8_t>(v), acc, 0, 0, 0);
+      for (int ks = 0; ks < KS; ++ks) {
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (row < n_rows) v = load16(q_idx + (int64_t)row * D + ks * 32 + grp * 8);
+        qf[rblk][ks] = bitcast<bf16x8_t>(v);
+      }
     }
+    __syncthreads();
+    const int wrow0 = r0 + wave * WROWS;
+    if (wrow0 >= n_rows || k0 > pos0 + wrow0 + WROWS - 1) continue;  // no visible entry for this wave
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = wr0 + grp * 4 + j;
-      if (row < n_rows && col <= pos0 + row) scores[(int64_t)row * ld + col] = acc[j];
+    for (int kb = 0; kb < kPfTile / 16; ++kb) {
+      const int key = kb * 16 + l16;
+      floatx4_t acc[RPW];
+#pragma unroll
+      for (int rblk = 0; rblk < RPW; ++rblk) acc[rblk] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint4 a = *reinterpret_cast<const uint4*>(kt + key * D + (((ks * 4 + grp) ^ (key & (CH - 1))) * 8));
+#pragma unroll
+        for (int rblk = 0; rblk < RPW; ++rblk)
+          acc[rblk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8_t>(a), qf[rblk][ks], acc[rblk], 0, 0, 0);
+      }
+      // acc[rblk][j]: row wrow0 + 16 rblk + l16, column k0 + 16 kb + 4 grp + j
+      const int col = k0 + kb * 16 + grp * 4;
+#pragma unroll
+      for (int rblk = 0; rblk < RPW; ++rblk) {
+        const int row = wrow0 + rblk * 16 + l16;
+        if (row >= n_rows) continue;
+        const int lim = pos0 + row;  // last visible column of the row
+        float* p = scores + (int64_t)row * ld + col;
+        if (col + 3 <= lim) {
+          *reinterpret_cast<floatx4_t*>(p) = acc[rblk];
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (col + j <= lim) p[j] = acc[rblk][j];
+        }
+      }
     }
   }
 }
@@ -242,15 +294,18 @@ int launch_index_scores_decode(const RowsDev& rows, int d_idx, int seg, const ui
 
 int launch_index_scores_prefill(const RowsDev& rows, int d_idx, const uint16_t* q_idx, const uint16_t* k_idx,
                                 float* scores, int64_t ld, uint32_t* clear, int n_clear, void* stream) {
-  const int ncols = rows.pos0 + rows.n_rows;
-  dim3 grid((ncols + 63) / 64, (rows.n_rows + 63) / 64);
+  const PrefillGrid g = prefill_grid(rows.pos0, rows.n_rows);
+  // one workgroup per tile, up to a cap beyond which workgroups loop over tiles
+  const int64_t cap = (int64_t)1 << 20;
+  const int64_t padded = (g.tiles + 7) / 8 * 8;  // whole rounds over the 8 XCDs
+  const dim3 grid((unsigned)(padded < cap ? padded : cap));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (d_idx == 128)
-    hipLaunchKernelGGL(k_index_scores_prefill<128>, grid, dim3(256), 0, s, q_idx, k_idx, rows.cu, rows.seq,
-                       rows.pos0, rows.n_rows, scores, ld, clear, n_clear);
+    hipLaunchKernelGGL(k_index_scores_prefill<128>, grid, dim3(kPfThreads), 0, s, q_idx, k_idx, rows.cu, rows.seq,
+                       rows.pos0, rows.n_rows, scores, ld, g, clear, n_clear);
   else
-    hipLaunchKernelGGL(k_index_scores_prefill<64>, grid, dim3(256), 0, s, q_idx, k_idx, rows.cu, rows.seq,
-                       rows.pos0, rows.n_rows, scores, ld, clear, n_clear);
+    hipLaunchKernelGGL(k_index_scores_prefill<64>, grid, dim3(kPfThreads), 0, s, q_idx, k_idx, rows.cu, rows.seq,
+                       rows.pos0, rows.n_rows, scores, ld, g, clear, n_clear);
   return (int)hipGetLastError();
 }
 

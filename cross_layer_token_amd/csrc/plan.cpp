@@ -177,6 +177,23 @@ StepPlan plan_step(const clsa_dims* d, const clsa_rows* r, int schedule, bool us
   // every chunk (the shorter tail included) splits like the whole call, so results do not
   // depend on the chunk size; buffers are sized for the largest chunk
   s.attn = plan_attn(d, s.chunk_rows, lc, r->n_rows);
+  const bool compact = schedule == CLSA_SCHEDULE_PER_LAYER && !prefill;
+  if (compact) {
+    // the gather and the L attention passes run over chunks of rows whose K_S/V_S fit
+    // kPerLayerResidentBytes; each chunk splits for its own size (a function of the sizes alone),
+    // so the partials and tickets cover both the full chunk and the shorter tail
+    const size_t row_sel = (size_t)2 * d->hkv * d->topk * CLSA_HEAD_DIM * 2;  // K and V of one row
+    int64_t rows_fit = (int64_t)(kPerLayerResidentBytes / row_sel);
+    if (rows_fit < 1) rows_fit = 1;
+    s.sel_chunk_rows = rows_fit < r->n_rows ? (int)rows_fit : r->n_rows;
+    const int tail = r->n_rows % s.sel_chunk_rows;
+    s.attn = plan_attn(d, s.sel_chunk_rows, 1, s.sel_chunk_rows);
+    if (tail > 0) {
+      const AttnPlan t = plan_attn(d, tail, 1, tail);
+      if (t.part_bytes > s.attn.part_bytes) s.attn.part_bytes = t.part_bytes;
+      if (t.tickets > s.attn.tickets) s.attn.tickets = t.tickets;
+    }
+  }
   s.ld_scores = (int64_t)align_up((size_t)r->max_row_len, 64);
   s.fused_select = !prefill && schedule == CLSA_SCHEDULE_LAYER_BATCHED && s.topk.multi_wg && s.attn.teams == 2 && s.attn.wpt == 4 &&
                    s.attn.keys_per_split <= kFusedMaxIds;
@@ -193,8 +210,8 @@ StepPlan plan_step(const clsa_dims* d, const clsa_rows* r, int schedule, bool us
   off += s.topk.bytes;
   s.part_off = off;
   off += s.attn.part_bytes;
-  if (schedule == CLSA_SCHEDULE_PER_LAYER && !prefill && !user_sel) {
-    s.sel_bytes = align_up((size_t)r->n_rows * d->hkv * d->topk * CLSA_HEAD_DIM * 2, 256);
+  if (compact && !user_sel) {
+    s.sel_bytes = align_up((size_t)s.sel_chunk_rows * d->hkv * d->topk * CLSA_HEAD_DIM * 2, 256);
     s.ksel_off = off;
     off += s.sel_bytes;
     s.vsel_off = off;

@@ -233,3 +233,30 @@ def test_step_no_alloc_rejects_a_step_beyond_its_scratch():
     with pytest.raises(B.CLSAError) as e:
         B.step_no_alloc(dims, rows, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0)
     assert e.value.status == B.ERR_INVALID_ARGUMENT
+
+
+def test_prefill_score_tiles_cover_the_causal_triangle_once(tmp_path):
+    """The prefill score kernel's grid enumerates only the causal 128 x 128 tiles: compiled with g++
+    (with the address and undefined-behaviour sanitizers) and swept over call offsets and row
+    counts, every tile index maps to a distinct causal tile and every causal tile is reached."""
+    import subprocess
+    here = os.path.dirname(os.path.abspath(__file__))
+    exe = str(tmp_path / "prefill_tiles")
+    subprocess.run(["g++", "-std=c++17", "-O1", "-Wall", "-fsanitize=address,undefined", "-o", exe,
+                    os.path.join(here, "host", "prefill_tiles.cpp")], check=True)
+    r = subprocess.run([exe], stdout=subprocess.PIPE, text=True, env={**os.environ, "LD_PRELOAD": ""})
+    assert r.returncode == 0 and r.stdout.startswith("ok"), r.stdout
+
+
+def test_per_layer_workspace_gathers_in_cache_sized_chunks():
+    """The per-layer decode schedule gathers the compact K_S/V_S of a chunk of rows at a time (at most
+    192 MiB, inside the 256 MB Infinity Cache): for 64 rows of 131072 tokens with k = 2048 and 8 KV
+    heads (8 MiB of K_S/V_S per row) its workspace holds 24 rows of compact buffers, not 64."""
+    R, n = 64, 131072
+    dims = _dims(batch=R, topk=2048, hq=32, hkv=8, n_layers=12)
+    rows = B.make_rows(B.MODE_DECODE, R, n, R * n)
+    batched = B.workspace_bytes(dims, rows, B.SCHEDULE_LAYER_BATCHED)
+    per_layer = B.workspace_bytes(dims, rows, B.SCHEDULE_PER_LAYER)
+    per_row = 2 * 8 * 2048 * 128 * 2
+    # the compact buffers of 24 rows, plus the per-layer passes' own split partials
+    assert 24 * per_row <= per_layer - batched <= 24 * per_row + (16 << 20)

@@ -71,30 +71,44 @@ def test_index_scores_decode_bitwise(cfg, check_rows):
     _say(f"cfg{cfg} scores bitwise OK")
 
 
+def _prefill_scores_check(w, dw, pos0, m, ld):
+    """clsa_index_scores on prefill rows pos0 .. pos0 + m - 1 of sequence 0: every row bitwise
+    against the oracle's scores of its visible tokens, and nothing written above the diagonal."""
+    sc = torch.full((m, ld), float("nan"), dtype=torch.float32, device="cuda")
+    clsa.index_scores(dims_of(dw), rows_of(dw, row0=pos0, n_rows=m), dw.q_idx[pos0:], dw.k_idx, dw.cu_seqlens, sc, ld)
+    torch.cuda.synchronize()
+    cols = torch.arange(ld, device="cuda")[None, :]
+    lim = pos0 + torch.arange(m, device="cuda")[:, None]
+    assert torch.isnan(sc.masked_fill(cols <= lim, float("nan"))).all(), "wrote above the causal diagonal"
+    assert not torch.isnan(sc.masked_fill(cols > lim, 0.0)).any(), "left a visible entry unwritten"
+    host = sc.cpu().numpy()
+    kf = w.k_idx_f64(np.arange(pos0 + m))
+    qf = w.q_idx_f64(np.arange(pos0, pos0 + m))
+    for i in range(m):
+        t = pos0 + i
+        ref = O.index_scores(qf[i], kf[: t + 1])
+        got = host[i, : t + 1].astype(np.float64)
+        assert np.array_equal(got, ref), f"row {t}: {np.sum(got != ref)} mismatches"
+
+
 def test_index_scores_prefill_bitwise():
+    """The causal indexer GEMM on the 8192-row prefill workload in one call: every row bitwise
+    against the oracle, nothing written above the diagonal; then calls that start mid-sequence at
+    offsets that are not multiples of the 128-row tile."""
     w = cs.config(4)
     dw = device_workload(w, with_kv=False, with_q=False)
-    n = w.n_rows
-    scores = torch.full((n, n), float("nan"), dtype=torch.float32, device="cuda")
-    clsa.index_scores(dims_of(dw), rows_of(dw), dw.q_idx, dw.k_idx, dw.cu_seqlens, scores, n)
-    torch.cuda.synchronize()
-    kf = w.k_idx_f64(np.arange(n))
-    for t in [0, 1, 15, 63, 64, 1000, 2047, 2048, 4095, 6000, 8191]:
-        ref = O.index_scores(w.q_idx_f64([t])[0], kf[: t + 1])
-        got = scores[t, : t + 1].cpu().numpy().astype(np.float64)
-        assert np.array_equal(got, ref), f"row {t}"
-        if t + 1 < n:
-            assert torch.isnan(scores[t, t + 1:]).all(), "wrote above the causal diagonal"
-    # a chunk of rows starting mid-sequence
-    pos0, m = 3000, 200
-    sc2 = torch.full((m, pos0 + m), float("nan"), dtype=torch.float32, device="cuda")
-    clsa.index_scores(dims_of(dw), rows_of(dw, row0=pos0, n_rows=m), dw.q_idx[pos0:], dw.k_idx, dw.cu_seqlens, sc2,
-                      pos0 + m)
-    torch.cuda.synchronize()
-    for i in [0, 77, 199]:
-        t = pos0 + i
-        ref = O.index_scores(w.q_idx_f64([t])[0], kf[: t + 1])
-        assert np.array_equal(sc2[i, : t + 1].cpu().numpy().astype(np.float64), ref)
+    _prefill_scores_check(w, dw, 0, w.n_rows, w.n_rows)
+    _say("prefill scores: all 8192 rows bitwise")
+    for pos0, m, ld in ((3000, 200, 3200), (50, 700, 752), (8000, 192, 8192), (127, 1, 128)):
+        _prefill_scores_check(w, dw, pos0, m, ld)
+
+
+def test_index_scores_prefill_d64_bitwise():
+    w = cs.custom(mode="prefill", seq_lens=(1500,), d_idx=64, topk=64, n_layers=1, hq=4, hkv=1, needles=3, seed=57,
+                  name="prefill_scores_d64")
+    dw = device_workload(w, with_kv=False, with_q=False)
+    _prefill_scores_check(w, dw, 0, 1500, 1536)
+    _prefill_scores_check(w, dw, 333, 1000, 1336)
 
 
 # ----------------------------------------------------------------------------- a2 top-k
@@ -522,6 +536,37 @@ def test_step_decode_chunk_holding_the_largest_keys(lens, planted):
             assert set(w.needle_positions_of_row(r)) <= set(idx[r].tolist())
             assert_outputs_close(dev[r], res["out"], f"packed needles row {r}")
         _say(f"packed needles {lens}, schedule {schedule}: {w.n_rows} rows match")
+
+
+def test_step_per_layer_chunks_with_caller_buffers():
+    """The per-layer schedule gathers K_S/V_S a chunk of rows at a time (at most 192 MiB): at k = 65536
+    with 8 KV heads a row's K_S/V_S alone is 256 MiB, so every row is its own chunk.  The caller's
+    compact buffers and the workspace's give the same result bit for bit, and every row matches the
+    C++ oracle."""
+    w = cs.custom(seq_lens=(70000, 66000, 90000), d_idx=64, topk=65536, n_layers=2, hq=8, hkv=8, needles=2, seed=97,
+                  name="per_layer_chunks")
+    dw = device_workload(w)
+    dims, rows = dims_of(dw), rows_of(dw)
+    R, L, k = w.n_rows, w.n_layers, w.topk
+    idx_a, cnt_a, out_a = _run_step(dw, clsa.SCHEDULE_PER_LAYER)
+    ws, nws = workspace(dims, rows, clsa.SCHEDULE_PER_LAYER)
+    ksel = torch.empty((R, w.hkv, k, 128), dtype=torch.int16, device="cuda")
+    vsel = torch.empty_like(ksel)
+    out = torch.zeros((R, L, w.hq, 128), dtype=torch.int16, device="cuda")
+    idx = torch.full((R, k), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.full((R,), -7, dtype=torch.int32, device="cuda")
+    clsa.step(dims, rows, dw.q_idx, dw.k_idx, dw.k_cache, dw.v_cache, dw.cu_seqlens, dw.q, out, idx, cnt, ws, nws,
+              k_sel=ksel, v_sel=vsel, schedule=clsa.SCHEDULE_PER_LAYER)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), idx_a) and torch.equal(out, out_a)
+    ref = _cpp_rows(w, range(R))
+    dev = bf16_dev_to_f64(out)
+    for r in range(R):
+        assert cnt_a[r] == ref["count"][r] and np.array_equal(idx_a[r], ref["idx"][r]), f"row {r}"
+        assert_outputs_close(dev[r], ref["out"][r], f"per-layer chunk row {r}")
+    # the caller's compact buffers hold each row's gathered K_S/V_S
+    toks = w.cu_seqlens[2] + ref["idx"][2][: ref["count"][2]][:100]
+    assert np.array_equal(ksel[2, :, :100].permute(1, 0, 2).cpu().numpy().view(np.uint16), w.kv_bits(toks, "k"))
 
 
 def test_step_decode_at_the_largest_k():
