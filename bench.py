@@ -174,7 +174,7 @@ PREFILL_COUNTER_COMMANDS = {
     "write": f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d rocprof_out/prefill_write -o bench -- {PREFILL_COUNTER_RUN}",
 }
 PREFILL_KERNELS = (("k_index_scores_prefill<128>", "k_index_scores_prefill"),
-                   ("k_sparse_attn<true, 2, false, 2, false> (prefill attention)", "k_sparse_attn<true, 2, false, 2, false>"),
+                   ("k_prefill_attn (prefill attention)", "k_prefill_attn"),
                    ("k_topk_rows_lds", "k_topk_rows_lds"))
 
 
@@ -204,7 +204,7 @@ def summarize_prefill_counters(mfma_dir: str, fetch_dir: str, write_dir: str, co
     n, L = w.n_rows, w.n_layers
     sel = sum(min(w.topk, t + 1) for t in range(n))
     alg_flop = {"k_index_scores_prefill": 2.0 * w.d_idx * n * (n + 1) / 2,
-                "k_sparse_attn<true, 2, false, 2, false>": 4.0 * sel * L * w.hq * w.head_dim}
+                "k_prefill_attn": 4.0 * sel * L * w.hq * w.head_dim}
     alg_bytes = {"k_index_scores_prefill": 2 * 2 * n * w.d_idx + 4 * n * (n + 1) // 2}
     md = ["# MFMA, LDS and HBM counters of the prefill kernels, prefill_n8k", "",
           "Made by (on one MI355X; each counter pass runs separately):", "",

@@ -536,6 +536,255 @@ __global__ __launch_bounds__(64 * WPT * TEAMS, 64 * WPT * TEAMS == 512 ? 1 : 2) 
   }
 }
 
+// ---------------------------------------------------------------------------- prefill rows
+// Prefill attention: every query row (position) has its own selection, so its K/V rows are
+// gathered for it alone and never reused by another row.  One workgroup = (row r, KV head g, block
+// of up to 32 query rows, i.e. (layer, head) pairs of g's GQA group).  Its four waves take
+// interleaved 32-key tiles of the row's selection, and each wave computes all 32 query columns of
+// its tile: two 16-column MFMA blocks share every K and V fragment, which halves the LDS reads per
+// MFMA against one 16-column block per wave.  A wave loads its tile's K and V rows (16 lanes per
+// 256-byte row, so every quarter-wave reads whole rows) into LDS buffers of its own, so the waves
+// never wait for each other inside the loop; the next tile's rows are in flight while a tile is
+// computed.  The four waves' (m, l, acc) are merged in LDS at the end, in wave order.
+constexpr int kPfaKeys = 32;     // keys per tile
+constexpr int kPfaWaves = 4;
+constexpr int kPfaCols = 32;     // query columns per workgroup (and per wave)
+constexpr int kPfaPart = 68;     // floats per lane of a wave's merge record: acc 2 x 8 x 4, m 2, l 2
+constexpr int kPfaTileBytes = kPfaKeys * CLSA_HEAD_DIM * 2;  // one tile of K (or V)
+constexpr int kPfaWaveBytes = 2 * kPfaTileBytes;             // a wave's K and V tiles
+constexpr int kPfaLds = (kPfaWaves - 1) * kPfaPart * 64 * 4 > kPfaWaves * kPfaWaveBytes
+                            ? (kPfaWaves - 1) * kPfaPart * 64 * 4
+                            : kPfaWaves * kPfaWaveBytes;
+
+__global__ __launch_bounds__(64 * kPfaWaves, 2) void k_prefill_attn(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[kPfaLds];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, grp = lane >> 4;
+  const int qb = blockIdx.x % a.qblocks;
+  const int g = blockIdx.x / a.qblocks;
+  const int r = blockIdx.y;
+  int kbeg, cnt;  // the row's selection positions 0 .. cnt - 1 (count clamped into [0, k])
+  split_key_range(a.count[r], a.k, 0, a.k, &kbeg, &cnt);
+  const int ntiles = (cnt + kPfaKeys - 1) / kPfaKeys;
+
+  // query columns 16 cb + l16 of the block -> (layer, head)
+  bf16x8_t qf[2][4];
+  int layer[2], head[2];
+  bool qvalid[2];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const int qr = qb * kPfaCols + cb * 16 + l16;
+    qvalid[cb] = qr < a.qrows;
+    layer[cb] = qvalid[cb] ? qr / a.group : 0;
+    head[cb] = g * a.group + (qvalid[cb] ? qr % a.group : 0);
+    const uint16_t* qp = a.q + (int64_t)r * a.q_stride + ((int64_t)layer[cb] * a.hq + head[cb]) * CLSA_HEAD_DIM;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (qvalid[cb]) v = load16(qp + kk * 32 + grp * 8);
+      qf[cb][kk] = bitcast<bf16x8_t>(v);
+    }
+  }
+
+  const int seq = row_seq(a.rw, r);
+  const int64_t tok_base = (int64_t)a.rw.cu[seq];
+  const int tok_last = max(row_len(a.rw, r) - 1, 0);
+  const int32_t* irow = a.idx + (int64_t)r * a.k;
+  const int row_elems = a.hkv * CLSA_HEAD_DIM;
+  // this lane's 16-byte chunk of every row it loads
+  const uint16_t* kbase = a.ksrc + (tok_base * a.hkv + g) * CLSA_HEAD_DIM + l16 * 8;
+  const uint16_t* vbase = a.vsrc + (tok_base * a.hkv + g) * CLSA_HEAD_DIM + l16 * 8;
+  // the lane loads chunk l16 of tile keys grp + 4 i (i < 8); positions past the count are clamped
+  // onto the last selected one (a valid row, masked below)
+  int nid[8];  // token ids of the tile whose rows are requested next
+  auto fetch_ids = [&](int tile) {
+    const int p0 = tile * kPfaKeys + grp;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int pos = p0 + 4 * i;
+      const int id = irow[pos < cnt ? pos : cnt - 1];
+      nid[i] = id < 0 ? 0 : (id > tok_last ? tok_last : id);
+    }
+  };
+  uint4 kr[8], vr[8];
+  auto load_tile = [&]() {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t off = (int64_t)nid[i] * row_elems;
+      kr[i] = load16(kbase + off);
+      vr[i] = load16(vbase + off);
+    }
+  };
+
+  // this wave's tiles: key row kr, 16-byte chunk c at slot c ^ (kr & 15) (see the tile layout above)
+  char* const kbuf = lds + wave * kPfaWaveBytes;
+  char* const vbuf = kbuf + kPfaTileBytes;
+  int soff[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int key = grp + 4 * i;
+    soff[i] = key * 256 + ((l16 ^ (key & 15)) << 4);
+  }
+  // K fragment (mt, kk): key 16 mt + l16, chunk 4 kk + grp; mt adds 16 rows = 4096 bytes
+  int koff[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) koff[kk] = l16 * 256 + ((((kk * 4) + grp) ^ l16) << 4);
+  int voff[8];
+  {
+    const int y = 4 * grp + (l16 >> 2);
+    const int z = ((l16 >> 1) & 1) ^ y;
+#pragma unroll
+    for (int ht = 0; ht < 8; ++ht) voff[ht] = y * 256 + ((z ^ (2 * ht)) << 4) + 8 * (l16 & 1);
+  }
+
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  floatx4_t acc[2][8];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[cb][i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  const float scale = a.scale_log2;
+
+  int t = wave;
+  if (t < ntiles) {
+    fetch_ids(t);
+    load_tile();
+    if (t + kPfaWaves < ntiles) fetch_ids(t + kPfaWaves);
+  }
+  for (; t < ntiles; t += kPfaWaves) {
+    // this tile's rows into the wave's buffers (the previous tile's reads have completed: their
+    // values fed its MFMAs), then the next tile's loads and the ids of the one after
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      *reinterpret_cast<uint4*>(kbuf + soff[i]) = kr[i];
+      *reinterpret_cast<uint4*>(vbuf + soff[i]) = vr[i];
+    }
+    if (t + kPfaWaves < ntiles) {
+      load_tile();
+      if (t + 2 * kPfaWaves < ntiles) fetch_ids(t + 2 * kPfaWaves);
+    }
+    // S^T = K Q^T: s[mt][cb][j] = q . k of key 16 mt + 4 grp + j, query column 16 cb + l16
+    floatx4_t s[2][2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      floatx4_t c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const bf16x8_t kfrag = bitcast<bf16x8_t>(*reinterpret_cast<const uint4*>(kbuf + koff[kk] + mt * 4096));
+        c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfrag, qf[0][kk], c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfrag, qf[1][kk], c1, 0, 0, 0);
+      }
+      s[mt][0] = c0;
+      s[mt][1] = c1;
+    }
+    const int nvalid = cnt - t * kPfaKeys;
+    if (nvalid < kPfaKeys) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (mt * 16 + grp * 4 + j >= nvalid) {
+            s[mt][0][j] = -INFINITY;
+            s[mt][1][j] = -INFINITY;
+          }
+    }
+    // online softmax (exp2 domain) per query column, with the lazy rescale of the decode kernel;
+    // P^T operand slots 0..3 <- keys 4 grp + j, slots 4..7 <- keys 16 + 4 grp + j
+    bf16x8_t pb[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+        mx = fmaxf(fmaxf(mx, fmaxf(s[mt][cb][0], s[mt][cb][1])), fmaxf(s[mt][cb][2], s[mt][cb][3]));
+      if (__any(mx * scale > m_run[cb] + kRescaleLog2)) {
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float m_new = fmaxf(m_run[cb], mx * scale);
+        const float corr = __builtin_amdgcn_exp2f(m_run[cb] - m_new);
+        m_run[cb] = m_new;
+        l_run[cb] *= corr;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[cb][i] *= corr;
+      }
+      uint32_t w[4];
+      float psum = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        float p[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          p[j] = __builtin_amdgcn_exp2f(fmaf(s[mt][cb][j], scale, -m_run[cb]));
+          psum += p[j];
+        }
+        w[2 * mt] = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)p[0], (__bf16)p[1]});
+        w[2 * mt + 1] = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)p[2], (__bf16)p[3]});
+      }
+      l_run[cb] += psum;
+      pb[cb] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
+    }
+    // O^T += V^T P^T, one V^T fragment per 16 head dims shared by both column blocks
+#pragma unroll
+    for (int ht = 0; ht < 8; ++ht) {
+      const uint2 v0 = lds_read_tr(reinterpret_cast<const uint16_t*>(vbuf + voff[ht]));
+      const uint2 v1 = lds_read_tr(reinterpret_cast<const uint16_t*>(vbuf + voff[ht] + 4096));
+      const bf16x8_t va = bitcast<bf16x8_t>(make_uint4(v0.x, v0.y, v1.x, v1.y));
+      acc[0][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[0], acc[0][ht], 0, 0, 0);
+      acc[1][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[1], acc[1][ht], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    l_run[cb] += __shfl_xor(l_run[cb], 16, 64);
+    l_run[cb] += __shfl_xor(l_run[cb], 32, 64);
+  }
+  // merge waves 1..3 into wave 0 through LDS (the tile buffers are free once every wave is past
+  // its loop)
+  __syncthreads();
+  float* rec = reinterpret_cast<float*>(lds);
+  if (wave > 0) {
+    float* pw = rec + (wave - 1) * kPfaPart * 64;
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+#pragma unroll
+      for (int ht = 0; ht < 8; ++ht)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pw[((cb * 8 + ht) * 4 + j) * 64 + lane] = acc[cb][ht][j];
+      pw[(64 + cb) * 64 + lane] = m_run[cb];
+      pw[(66 + cb) * 64 + lane] = l_run[cb];
+    }
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int w2 = 1; w2 < kPfaWaves; ++w2) {
+    const float* pw = rec + (w2 - 1) * kPfaPart * 64;
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const float m1 = pw[(64 + cb) * 64 + lane], l1 = pw[(66 + cb) * 64 + lane];
+      const float M = fmaxf(m_run[cb], m1);
+      if (M == -INFINITY) continue;  // neither has keys
+      const float c0 = __builtin_amdgcn_exp2f(m_run[cb] - M), c1 = __builtin_amdgcn_exp2f(m1 - M);
+      l_run[cb] = l_run[cb] * c0 + l1 * c1;
+#pragma unroll
+      for (int ht = 0; ht < 8; ++ht)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[cb][ht][j] = acc[cb][ht][j] * c0 + pw[((cb * 8 + ht) * 4 + j) * 64 + lane] * c1;
+      m_run[cb] = M;
+    }
+  }
+  // acc[cb][ht][j]: head dim 16 ht + 4 grp + j of query column 16 cb + l16
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    if (!qvalid[cb]) continue;
+    uint16_t* op = a.out + (int64_t)r * a.o_stride + ((int64_t)layer[cb] * a.hq + head[cb]) * CLSA_HEAD_DIM;
+    const float inv = l_run[cb] > 0.f ? 1.f / l_run[cb] : 0.f;
+#pragma unroll
+    for (int ht = 0; ht < 8; ++ht) store_out4(op + ht * 16 + grp * 4, acc[cb][ht], inv);
+  }
+}
+
 __global__ void k_clear_u32(uint32_t* __restrict__ p, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0u;
@@ -611,6 +860,13 @@ int launch_attn(const RowsDev& rows, int k, int hq, int hkv, int n_layers_call, 
   a.idx_out = idx_out;
   a.count_out = count_out;
   const bool fused = sel != nullptr;
+  if (rows.mode == CLSA_MODE_PREFILL && from_cache && !fused) {
+    // prefill rows: each gathers its own selection; no key splits, no partials
+    a.qblocks = (plan.qrows + kPfaCols - 1) / kPfaCols;
+    const dim3 grid((unsigned)(a.qblocks * hkv), (unsigned)rows.n_rows);
+    hipLaunchKernelGGL(k_prefill_attn, grid, dim3(64 * kPfaWaves), 0, s, a);
+    return (int)hipGetLastError();
+  }
   if (fused && (plan.teams != 2 || plan.wpt != 4 || ksel != nullptr || plan.keys_per_split > kFusedMaxIds || idx_out == nullptr ||
                 count_out == nullptr))
     return (int)hipErrorInvalidValue;
