@@ -294,23 +294,45 @@ def summarize_trace(trace_dir: str, config: int = 3) -> tuple:
         lines.append(f"| `{_short_kernel(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
     # The decode score kernel's launches by kind: in the step (and the ablations) each launch is
-    # followed by the top-k select; the scores-only launches (the roofline line) are not.
+    # followed by the top-k select; the scores-only launches run back to back (the roofline line)
+    # or each after the cache flush.
     traces = sorted(glob.glob(os.path.join(trace_dir, "*_kernel_trace.csv")))
     if traces and kind == "decode":
         tr = sorted(_csv_rows(traces[0]), key=lambda r: int(r["Start_Timestamp"]))
-        alone, other = [], []
+        b2b, flushed, other = [], [], []
         for i, r in enumerate(tr):
             if "k_index_scores_decode" not in r["Kernel_Name"]:
                 continue
             us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
-            in_step = i + 1 < len(tr) and "k_topk" in tr[i + 1]["Kernel_Name"]
-            (other if in_step else alone).append(us)
+            if i + 1 < len(tr) and "k_topk" in tr[i + 1]["Kernel_Name"]:
+                other.append(us)
+            elif i > 0 and "reduce_kernel" in tr[i - 1]["Kernel_Name"]:
+                flushed.append(us)
+            else:
+                b2b.append(us)
         lines += ["", "`k_index_scores_decode` by kind of launch (from the per-dispatch trace):", "",
                   "| launches | calls | avg us | min us | max us |", "|---|---:|---:|---:|---:|"]
-        for name, v in (("scores only (the roofline line)", alone),
+        for name, v in (("scores only, back to back (the roofline line)", b2b),
+                        ("scores only, each right after the cache flush", flushed),
                         ("followed by the top-k select (step, routing ablation, append)", other)):
             if v:
                 lines.append(f"| {name} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
+        # the layer-batched step's kernels, from the first kernel's start to the last one's end, per
+        # kind of step; the bench runs those steps before its first scores-only launch
+        first_alone = next((i for i, r in enumerate(tr) if "k_index_scores_decode" in r["Kernel_Name"] and not (
+            i + 1 < len(tr) and "k_topk" in tr[i + 1]["Kernel_Name"])), len(tr))
+        steps = {"after the cache flush": [], "back to back": []}
+        for i in range(min(first_alone, len(tr)) - 2):
+            if ("k_index_scores_decode" in tr[i]["Kernel_Name"] and "k_topk_select" in tr[i + 1]["Kernel_Name"]
+                    and "k_sparse_attn" in tr[i + 2]["Kernel_Name"]):
+                span = (int(tr[i + 2]["End_Timestamp"]) - int(tr[i]["Start_Timestamp"])) / 1e3
+                fl = i > 0 and "reduce_kernel" in tr[i - 1]["Kernel_Name"]
+                steps["after the cache flush" if fl else "back to back"].append(span)
+        lines += ["", "The layer-batched step's three kernels, first start to last end:", "",
+                  "| steps | calls | median us | min us | max us |", "|---|---:|---:|---:|---:|"]
+        for name, v in steps.items():
+            if v:
+                lines.append(f"| {name} | {len(v)} | {float(np.median(v)):.2f} | {min(v):.2f} | {max(v):.2f} |")
     return tag, "\n".join(lines) + "\n"
 
 
