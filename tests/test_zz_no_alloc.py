@@ -86,3 +86,36 @@ def test_no_alloc_prefill_chunks():
     ref, got = _both(w, chunk=1024)
     _same(ref, got, "prefill")
 
+
+
+def test_no_alloc_step_under_graph_capture():
+    """The use the entry point exists for: clsa_step_no_alloc captured into a HIP graph (through
+    torch.cuda.graph) and replayed three times, with eager work and synchronisations between the
+    replays; every replay equals the eager clsa_step bit for bit.  The step clears its tickets with
+    its own kernels, so the graph records no memset."""
+    w = cs.custom(seq_lens=(30000, 20000, 26000), d_idx=128, topk=1024, n_layers=3, hq=8, hkv=2, needles=2, seed=95,
+                  name="no_alloc_graph")
+    ref, got = _both(w)
+    _same(ref, got, "eager")
+    dw = device_workload(w)
+    dims, rows = dims_of(dw), rows_of(dw)
+    out, idx, cnt = _buffers(w, rows.n_rows)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # warm up on the capture stream (the scratch address is looked up here)
+        clsa.step_no_alloc(dims, rows, dw.q_idx, dw.k_idx, dw.k_cache, dw.v_cache, dw.cu_seqlens, dw.q, out, idx, cnt)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        clsa.step_no_alloc(dims, rows, dw.q_idx, dw.k_idx, dw.k_cache, dw.v_cache, dw.cu_seqlens, dw.q, out, idx, cnt)
+    for rep in range(3):
+        out.fill_(7)
+        idx.fill_(-7)
+        cnt.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _same(ref, (out, idx, cnt), f"graph replay {rep}")
+        _ = (dw.q.float() * 0).sum().item()  # eager work between the replays
+    _say("no-alloc step: three graph replays identical to the eager step")
