@@ -550,14 +550,25 @@ constexpr int kPfaKeys = 32;     // keys per tile
 constexpr int kPfaWaves = 4;
 constexpr int kPfaCols = 32;     // query columns per workgroup (and per wave)
 constexpr int kPfaPart = 68;     // floats per lane of a wave's merge record: acc 2 x 8 x 4, m 2, l 2
+constexpr int kPfaIds = 2048;    // selection positions whose token ids sit in LDS at a time
 constexpr int kPfaTileBytes = kPfaKeys * CLSA_HEAD_DIM * 2;  // one tile of K (or V)
 constexpr int kPfaWaveBytes = 2 * kPfaTileBytes;             // a wave's K and V tiles
 constexpr int kPfaLds = (kPfaWaves - 1) * kPfaPart * 64 * 4 > kPfaWaves * kPfaWaveBytes
                             ? (kPfaWaves - 1) * kPfaPart * 64 * 4
                             : kPfaWaves * kPfaWaveBytes;
+// Buffer resource word 3 for plain (unformatted) dword loads on gfx9-family chips.
+constexpr int kBufferWord3 = 0x00020000;
 
+// Token ids of the row's selection are staged in LDS, kPfaIds positions at a time, already
+// clamped into the row's tokens (and positions past the count set to token 0, a valid row that the
+// softmax masks), so the loop reads 8 ids with two LDS reads and forms each row address with one
+// 24-bit multiply-add.  BUF: the rows are read with buffer loads, whose 32-bit byte offset from
+// the (sequence, KV head) base covers every visible row (checked at launch); otherwise with 64-bit
+// global addresses.
+template <bool BUF>
 __global__ __launch_bounds__(64 * kPfaWaves, 2) void k_prefill_attn(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[kPfaLds];
+  __shared__ __attribute__((aligned(16))) int ids[kPfaIds];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, grp = lane >> 4;
   const int qb = blockIdx.x % a.qblocks;
@@ -565,7 +576,6 @@ __global__ __launch_bounds__(64 * kPfaWaves, 2) void k_prefill_attn(AttnArgs a) 
   const int r = blockIdx.y;
   int kbeg, cnt;  // the row's selection positions 0 .. cnt - 1 (count clamped into [0, k])
   split_key_range(a.count[r], a.k, 0, a.k, &kbeg, &cnt);
-  const int ntiles = (cnt + kPfaKeys - 1) / kPfaKeys;
 
   // query columns 16 cb + l16 of the block -> (layer, head)
   bf16x8_t qf[2][4];
@@ -591,28 +601,35 @@ __global__ __launch_bounds__(64 * kPfaWaves, 2) void k_prefill_attn(AttnArgs a) 
   const int tok_last = max(row_len(a.rw, r) - 1, 0);
   const int32_t* irow = a.idx + (int64_t)r * a.k;
   const int row_elems = a.hkv * CLSA_HEAD_DIM;
-  // this lane's 16-byte chunk of every row it loads
-  const uint16_t* kbase = a.ksrc + (tok_base * a.hkv + g) * CLSA_HEAD_DIM + l16 * 8;
-  const uint16_t* vbase = a.vsrc + (tok_base * a.hkv + g) * CLSA_HEAD_DIM + l16 * 8;
-  // the lane loads chunk l16 of tile keys grp + 4 i (i < 8); positions past the count are clamped
-  // onto the last selected one (a valid row, masked below)
-  int nid[8];  // token ids of the tile whose rows are requested next
-  auto fetch_ids = [&](int tile) {
-    const int p0 = tile * kPfaKeys + grp;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int pos = p0 + 4 * i;
-      const int id = irow[pos < cnt ? pos : cnt - 1];
-      nid[i] = id < 0 ? 0 : (id > tok_last ? tok_last : id);
-    }
-  };
+  const uint32_t row_bytes = (uint32_t)row_elems * 2u;
+  // the (sequence, KV head) base; the lane reads 16-byte chunk l16 of every row it loads
+  const int64_t base_el = (tok_base * a.hkv + g) * CLSA_HEAD_DIM;
+  const uint16_t* kbase = a.ksrc + base_el;
+  const uint16_t* vbase = a.vsrc + base_el;
+  const uint32_t lane_off = (uint32_t)l16 * 16u;
+  __amdgpu_buffer_rsrc_t rk, rv;
+  if constexpr (BUF) {
+    const int nrec = (int)((uint32_t)tok_last * row_bytes + 256u);  // bytes up to the last visible row
+    rk = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, nrec, kBufferWord3);
+    rv = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, nrec, kBufferWord3);
+  }
+  // the lane loads chunk l16 of tile keys 8 grp + i (i < 8)
   uint4 kr[8], vr[8];
-  auto load_tile = [&]() {
+  auto load_tile = [&](int tile) {
+    const int4 i0 = *reinterpret_cast<const int4*>(&ids[tile * kPfaKeys + grp * 8]);
+    const int4 i1 = *reinterpret_cast<const int4*>(&ids[tile * kPfaKeys + grp * 8 + 4]);
+    const int id[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int64_t off = (int64_t)nid[i] * row_elems;
-      kr[i] = load16(kbase + off);
-      vr[i] = load16(vbase + off);
+      if constexpr (BUF) {
+        const uint32_t off = __umul24((uint32_t)id[i], row_bytes) + lane_off;
+        kr[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
+        vr[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
+      } else {
+        const int64_t off = (int64_t)id[i] * row_elems + l16 * 8;
+        kr[i] = load16(kbase + off);
+        vr[i] = load16(vbase + off);
+      }
     }
   };
 
@@ -622,7 +639,7 @@ __global__ __launch_bounds__(64 * kPfaWaves, 2) void k_prefill_attn(AttnArgs a) 
   int soff[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int key = grp + 4 * i;
+    const int key = grp * 8 + i;
     soff[i] = key * 256 + ((l16 ^ (key & 15)) << 4);
   }
   // K fragment (mt, kk): key 16 mt + l16, chunk 4 kk + grp; mt adds 16 rows = 4096 bytes
@@ -645,92 +662,97 @@ __global__ __launch_bounds__(64 * kPfaWaves, 2) void k_prefill_attn(AttnArgs a) 
     for (int i = 0; i < 8; ++i) acc[cb][i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   const float scale = a.scale_log2;
 
-  int t = wave;
-  if (t < ntiles) {
-    fetch_ids(t);
-    load_tile();
-    if (t + kPfaWaves < ntiles) fetch_ids(t + kPfaWaves);
-  }
-  for (; t < ntiles; t += kPfaWaves) {
-    // this tile's rows into the wave's buffers (the previous tile's reads have completed: their
-    // values fed its MFMAs), then the next tile's loads and the ids of the one after
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      *reinterpret_cast<uint4*>(kbuf + soff[i]) = kr[i];
-      *reinterpret_cast<uint4*>(vbuf + soff[i]) = vr[i];
+  for (int c0 = 0; c0 < cnt; c0 += kPfaIds) {
+    const int clen = min(kPfaIds, cnt - c0);
+    const int ctiles = (clen + kPfaKeys - 1) / kPfaKeys;
+    if (c0 > 0) __syncthreads();  // every wave is done with the previous ids
+    for (int i = threadIdx.x; i < ctiles * kPfaKeys; i += blockDim.x) {
+      const int id = i < clen ? irow[c0 + i] : 0;
+      ids[i] = id < 0 ? 0 : (id > tok_last ? tok_last : id);
     }
-    if (t + kPfaWaves < ntiles) {
-      load_tile();
-      if (t + 2 * kPfaWaves < ntiles) fetch_ids(t + 2 * kPfaWaves);
-    }
-    // S^T = K Q^T: s[mt][cb][j] = q . k of key 16 mt + 4 grp + j, query column 16 cb + l16
-    floatx4_t s[2][2];
+    __syncthreads();
+    int t = wave;
+    if (t < ctiles) load_tile(t);
+    for (; t < ctiles; t += kPfaWaves) {
+      // this tile's rows into the wave's buffers (the previous tile's reads have completed: their
+      // values fed its MFMAs), then the next tile's loads
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      floatx4_t c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8_t kfrag = bitcast<bf16x8_t>(*reinterpret_cast<const uint4*>(kbuf + koff[kk] + mt * 4096));
-        c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfrag, qf[0][kk], c0, 0, 0, 0);
-        c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfrag, qf[1][kk], c1, 0, 0, 0);
+      for (int i = 0; i < 8; ++i) {
+        *reinterpret_cast<uint4*>(kbuf + soff[i]) = kr[i];
+        *reinterpret_cast<uint4*>(vbuf + soff[i]) = vr[i];
       }
-      s[mt][0] = c0;
-      s[mt][1] = c1;
-    }
-    const int nvalid = cnt - t * kPfaKeys;
-    if (nvalid < kPfaKeys) {
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (mt * 16 + grp * 4 + j >= nvalid) {
-            s[mt][0][j] = -INFINITY;
-            s[mt][1][j] = -INFINITY;
-          }
-    }
-    // online softmax (exp2 domain) per query column, with the lazy rescale of the decode kernel;
-    // P^T operand slots 0..3 <- keys 4 grp + j, slots 4..7 <- keys 16 + 4 grp + j
-    bf16x8_t pb[2];
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-        mx = fmaxf(fmaxf(mx, fmaxf(s[mt][cb][0], s[mt][cb][1])), fmaxf(s[mt][cb][2], s[mt][cb][3]));
-      if (__any(mx * scale > m_run[cb] + kRescaleLog2)) {
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = fmaxf(m_run[cb], mx * scale);
-        const float corr = __builtin_amdgcn_exp2f(m_run[cb] - m_new);
-        m_run[cb] = m_new;
-        l_run[cb] *= corr;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[cb][i] *= corr;
-      }
-      uint32_t w[4];
-      float psum = 0.f;
+      if (t + kPfaWaves < ctiles) load_tile(t + kPfaWaves);
+      // S^T = K Q^T: s[mt][cb][j] = q . k of key 16 mt + 4 grp + j, query column 16 cb + l16
+      floatx4_t s[2][2];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
-        float p[4];
+        floatx4_t c0v = {0.f, 0.f, 0.f, 0.f}, c1v = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          p[j] = __builtin_amdgcn_exp2f(fmaf(s[mt][cb][j], scale, -m_run[cb]));
-          psum += p[j];
+        for (int kk = 0; kk < 4; ++kk) {
+          const bf16x8_t kfrag = bitcast<bf16x8_t>(*reinterpret_cast<const uint4*>(kbuf + koff[kk] + mt * 4096));
+          c0v = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfrag, qf[0][kk], c0v, 0, 0, 0);
+          c1v = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfrag, qf[1][kk], c1v, 0, 0, 0);
         }
-        w[2 * mt] = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)p[0], (__bf16)p[1]});
-        w[2 * mt + 1] = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)p[2], (__bf16)p[3]});
+        s[mt][0] = c0v;
+        s[mt][1] = c1v;
       }
-      l_run[cb] += psum;
-      pb[cb] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
-    }
-    // O^T += V^T P^T, one V^T fragment per 16 head dims shared by both column blocks
+      const int nvalid = clen - t * kPfaKeys;
+      if (nvalid < kPfaKeys) {
 #pragma unroll
-    for (int ht = 0; ht < 8; ++ht) {
-      const uint2 v0 = lds_read_tr(reinterpret_cast<const uint16_t*>(vbuf + voff[ht]));
-      const uint2 v1 = lds_read_tr(reinterpret_cast<const uint16_t*>(vbuf + voff[ht] + 4096));
-      const bf16x8_t va = bitcast<bf16x8_t>(make_uint4(v0.x, v0.y, v1.x, v1.y));
-      acc[0][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[0], acc[0][ht], 0, 0, 0);
-      acc[1][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[1], acc[1][ht], 0, 0, 0);
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (mt * 16 + grp * 4 + j >= nvalid) {
+              s[mt][0][j] = -INFINITY;
+              s[mt][1][j] = -INFINITY;
+            }
+      }
+      // online softmax (exp2 domain) per query column, with the lazy rescale of the decode kernel;
+      // P^T operand slots 0..3 <- keys 4 grp + j, slots 4..7 <- keys 16 + 4 grp + j.  The tile
+      // maximum uses the NaN-propagating maximum (three operands per instruction; the scores are
+      // finite or -inf).
+      bf16x8_t pb[2];
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        float mx = __builtin_elementwise_maximum(s[0][cb][0], s[0][cb][1]);
+        mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(s[0][cb][2], s[0][cb][3]));
+        mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(s[1][cb][0], s[1][cb][1]));
+        mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(s[1][cb][2], s[1][cb][3]));
+        if (__any(mx * scale > m_run[cb] + kRescaleLog2)) {
+          mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 16, 64));
+          mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 32, 64));
+          const float m_new = fmaxf(m_run[cb], mx * scale);
+          const float corr = __builtin_amdgcn_exp2f(m_run[cb] - m_new);
+          m_run[cb] = m_new;
+          l_run[cb] *= corr;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[cb][i] *= corr;
+        }
+        uint32_t w[4];
+        float psum = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          float p[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            p[j] = __builtin_amdgcn_exp2f(fmaf(s[mt][cb][j], scale, -m_run[cb]));
+            psum += p[j];
+          }
+          w[2 * mt] = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)p[0], (__bf16)p[1]});
+          w[2 * mt + 1] = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)p[2], (__bf16)p[3]});
+        }
+        l_run[cb] += psum;
+        pb[cb] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
+      }
+      // O^T += V^T P^T, one V^T fragment per 16 head dims shared by both column blocks
+#pragma unroll
+      for (int ht = 0; ht < 8; ++ht) {
+        const uint2 v0 = lds_read_tr(reinterpret_cast<const uint16_t*>(vbuf + voff[ht]));
+        const uint2 v1 = lds_read_tr(reinterpret_cast<const uint16_t*>(vbuf + voff[ht] + 4096));
+        const bf16x8_t va = bitcast<bf16x8_t>(make_uint4(v0.x, v0.y, v1.x, v1.y));
+        acc[0][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[0], acc[0][ht], 0, 0, 0);
+        acc[1][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[1], acc[1][ht], 0, 0, 0);
+      }
     }
   }
 #pragma unroll
@@ -864,7 +886,12 @@ int launch_attn(const RowsDev& rows, int k, int hq, int hkv, int n_layers_call, 
     // prefill rows: each gathers its own selection; no key splits, no partials
     a.qblocks = (plan.qrows + kPfaCols - 1) / kPfaCols;
     const dim3 grid((unsigned)(a.qblocks * hkv), (unsigned)rows.n_rows);
-    hipLaunchKernelGGL(k_prefill_attn, grid, dim3(64 * kPfaWaves), 0, s, a);
+    // buffer loads when a 32-bit byte offset reaches every visible row (device row lengths are
+    // clamped to max_row_len)
+    if ((int64_t)rows.max_row_len * hkv * CLSA_HEAD_DIM * 2 <= (int64_t)INT32_MAX)
+      hipLaunchKernelGGL(k_prefill_attn<true>, grid, dim3(64 * kPfaWaves), 0, s, a);
+    else
+      hipLaunchKernelGGL(k_prefill_attn<false>, grid, dim3(64 * kPfaWaves), 0, s, a);
     return (int)hipGetLastError();
   }
   if (fused && (plan.teams != 2 || plan.wpt != 4 || ksel != nullptr || plan.keys_per_split > kFusedMaxIds || idx_out == nullptr ||

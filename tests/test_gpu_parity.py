@@ -680,6 +680,28 @@ def test_step_prefill_chunking_invariance():
     assert np.array_equal(a[0][5000:6000], c[0]) and torch.equal(a[2][5000:6000], c[2])
 
 
+def test_step_prefill_rows_past_32bit_offsets():
+    """The last rows of a prefill over a 2^20 + 2^18-token sequence with 8 KV heads: the rows a
+    query row may select span more than 2^31 bytes of the cache from the sequence's base, so the
+    prefill attention forms 64-bit row addresses instead of 32-bit buffer offsets.  Every row
+    against the C++ oracle."""
+    n = (1 << 20) + (1 << 18)
+    w = cs.custom(mode="prefill", seq_lens=(n,), d_idx=64, topk=512, n_layers=1, hq=8, hkv=8, needles=2, seed=71,
+                  name="prefill_past_32bit")
+    assert n * w.hkv * 128 * 2 > 2**31 - 1
+    dw = device_workload(w)
+    rows = list(range(n - 6, n))
+    idx, cnt, out = _run_step(dw, clsa.SCHEDULE_LAYER_BATCHED, rows_kw=dict(row0=rows[0], n_rows=len(rows)), chunk=8)
+    ref = _cpp_rows(w, rows)
+    dev = bf16_dev_to_f64(out)
+    for i, t in enumerate(rows):
+        assert cnt[i] == ref["count"][i] == w.topk
+        assert np.array_equal(idx[i], ref["idx"][i]), f"row {t}"
+        assert_outputs_close(dev[i], ref["out"][i], f"prefill row {t}")
+    # the selections reach past the first 2^31 bytes of the head's rows
+    assert max(int(idx[i].max()) for i in range(len(rows))) * w.hkv * 256 > 2**31
+
+
 def test_step_is_deterministic():
     w = cs.config(2)
     dw = device_workload(w)
