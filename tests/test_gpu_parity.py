@@ -680,6 +680,23 @@ def test_step_prefill_chunking_invariance():
     assert np.array_equal(a[0][5000:6000], c[0]) and torch.equal(a[2][5000:6000], c[2])
 
 
+def test_step_prefill_selection_past_one_id_stage():
+    """Prefill rows that select more tokens than the attention stages in LDS at a time (2048 ids):
+    k = 5000 over a 6000-token sequence, so rows from 2048 on run the staged loop two or three
+    times.  Rows around every stage boundary and the last rows against the C++ oracle."""
+    w = cs.custom(mode="prefill", seq_lens=(6000,), d_idx=64, topk=5000, n_layers=2, hq=8, hkv=2, needles=3, seed=77,
+                  name="prefill_k5000")
+    dw = device_workload(w)
+    idx, cnt, out = _run_step(dw, clsa.SCHEDULE_LAYER_BATCHED, chunk=1024)
+    assert np.array_equal(cnt, np.minimum(np.arange(1, w.n_rows + 1), w.topk))
+    rows = [0, 31, 2046, 2047, 2048, 2049, 2080, 4095, 4096, 4097, 4999, 5000, 5001, 5998, 5999]
+    ref = _cpp_rows(w, rows)
+    dev = bf16_dev_to_f64(out)
+    for i, t in enumerate(rows):
+        assert np.array_equal(idx[t], ref["idx"][i]), f"row {t}"
+        assert_outputs_close(dev[t], ref["out"][i], f"prefill row {t}")
+
+
 def test_step_prefill_rows_past_32bit_offsets():
     """The last rows of a prefill over a 2^20 + 2^18-token sequence with 8 KV heads: the rows a
     query row may select span more than 2^31 bytes of the cache from the sequence's base, so the
