@@ -30,10 +30,12 @@ __device__ void write_all(int32_t* out, int32_t* count, int r, int n, int k) {
 __global__ __launch_bounds__(kRowThreads) void k_topk_rows_lds(RowsDev rw, const float* __restrict__ scores,
                                                                  int64_t ld, int k, int32_t* __restrict__ out,
                                                                  int32_t* __restrict__ count) {
-  __shared__ uint32_t keys[kLdsRowCap];
-  __shared__ uint32_t hist[256];
+  // the row's keys: dynamic LDS sized for the launch's longest row (at most kLdsRowCap keys), so
+  // that shorter rows leave room for more workgroups per CU
+  extern __shared__ uint32_t keys[];
+  __shared__ uint32_t hist[kTopkBins];  // the first level's bins; its first 256 serve the 8-bit passes
   __shared__ int scan[2 * kRowThreads / 64];
-  __shared__ int res[2];
+  __shared__ int res[4];
   const int r = blockIdx.x;
   const int n = row_len(rw, r);
   const int m = n < k ? n : k;
@@ -42,11 +44,28 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_rows_lds(RowsDev rw, const
     return;
   }
   const float* srow = scores + (int64_t)r * ld;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) keys[i] = score_key(srow[i]);
-  uint32_t prefix = 0, pmask = 0;
-  int need = m;
+  for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) hist[i] = 0u;
+  __syncthreads();
+  // First level: the top kTopkBinBits key bits (sign, exponent, two mantissa bits).  A row's scores
+  // spread over many of those bins, where the top 8 bits alone put nearly all of them in a few and
+  // the LDS atomics of a wave then queue on the same addresses.
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const uint32_t key = score_key(srow[i]);
+    keys[i] = key;
+    atomicAdd(&hist[key >> (32 - kTopkBinBits)], 1u);
+  }
+  __syncthreads();
+  find_two_bins_from_top_block<kRowThreads>(hist, m, m, scan, res);
+  uint32_t prefix = (uint32_t)res[0] << (32 - kTopkBinBits), pmask = ~0u << (32 - kTopkBinBits);
+  int need = m - res[1];
   auto key_at = [&](int i) { return keys[i]; };
-  for (int shift = 24; shift >= 0; shift -= 8) radix_pass8(hist, n, key_at, prefix, pmask, shift, need, res);
+  // then 8-bit passes below it, the last aligned to bit 0 (its window overlaps bits the prefix
+  // already fixes, which then match)
+  for (int shift = 32 - kTopkBinBits - 8;; shift -= 8) {
+    if (shift < 0) shift = 0;
+    radix_pass8(hist, n, key_at, prefix, pmask, shift, need, res);
+    if (shift == 0) break;
+  }
   const uint32_t T = prefix;  // the m-th largest key; `need` ties at T are taken
   // ordered compaction: thread t owns the contiguous element range [t*E, t*E + E)
   const int E = (n + blockDim.x - 1) / blockDim.x;
@@ -306,7 +325,9 @@ int launch_topk(const RowsDev& rows, int k, const TopkPlan& plan, const float* s
                 int32_t* count, void* ws, bool have_hist, void* stream, bool finish) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (!plan.multi_wg) {
-    hipLaunchKernelGGL(k_topk_rows_lds, dim3(rows.n_rows), dim3(kRowThreads), 0, s, rows, scores, ld, k, idx, count);
+    const size_t key_bytes = (size_t)(rows.max_row_len < kLdsRowCap ? rows.max_row_len : kLdsRowCap) * sizeof(uint32_t);
+    hipLaunchKernelGGL(k_topk_rows_lds, dim3(rows.n_rows), dim3(kRowThreads), key_bytes, s, rows, scores, ld, k, idx,
+                       count);
     return (int)hipGetLastError();
   }
   char* w = static_cast<char*>(ws);
