@@ -27,15 +27,47 @@ __device__ void write_all(int32_t* out, int32_t* count, int r, int n, int k) {
 }
 
 // ---------------------------------------------------------------------------- short rows
+// The bin (from the top bin down) whose cumulative count first reaches `need` among kTopkBins
+// 16-bit counts packed two per word (bin b in half b & 1 of word b >> 1): res[0] = the bin,
+// res[1] = the count of the bins above it.  NT threads each own kTopkBins / NT consecutive bins;
+// all must call it; it ends with __syncthreads().
+static_assert(kLdsRowCap < 65536, "a short row's bin counts fit 16 bits");
+
+template <int NT>
+__device__ void find_packed_bin_from_top(const uint32_t* hpk, int need, int* scan, int* res) {
+  constexpr int B = kTopkBins / NT;
+  static_assert(kTopkBins % NT == 0, "whole bins per thread");
+  const int hi = kTopkBins - 1 - B * (int)threadIdx.x;
+  int h[B], loc = 0;
+#pragma unroll
+  for (int j = 0; j < B; ++j) {
+    const int b = hi - j;
+    h[j] = (int)((hpk[b >> 1] >> ((b & 1) * 16)) & 0xFFFFu);
+    loc += h[j];
+  }
+  int total;
+  int run = block_exclusive_scan(loc, scan, &total);
+#pragma unroll
+  for (int j = 0; j < B; ++j) {
+    if (run < need && run + h[j] >= need) {
+      res[0] = hi - j;
+      res[1] = run;
+    }
+    run += h[j];
+  }
+  __syncthreads();
+}
+
 __global__ __launch_bounds__(kRowThreads) void k_topk_rows_lds(RowsDev rw, const float* __restrict__ scores,
                                                                  int64_t ld, int k, int32_t* __restrict__ out,
                                                                  int32_t* __restrict__ count) {
   // the row's keys: dynamic LDS sized for the launch's longest row (at most kLdsRowCap keys), so
   // that shorter rows leave room for more workgroups per CU
   extern __shared__ uint32_t keys[];
-  __shared__ uint32_t hist[kTopkBins];  // the first level's bins; its first 256 serve the 8-bit passes
+  __shared__ uint32_t hpk[kTopkBins / 2];  // the first level's counts, 16 bits each (a row holds < 2^16 keys)
+  __shared__ uint32_t hist[256];           // the 8-bit passes
   __shared__ int scan[2 * kRowThreads / 64];
-  __shared__ int res[4];
+  __shared__ int res[2];
   const int r = blockIdx.x;
   const int n = row_len(rw, r);
   const int m = n < k ? n : k;
@@ -44,18 +76,18 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_rows_lds(RowsDev rw, const
     return;
   }
   const float* srow = scores + (int64_t)r * ld;
-  for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x) hist[i] = 0u;
+  for (int i = threadIdx.x; i < kTopkBins / 2; i += blockDim.x) hpk[i] = 0u;
   __syncthreads();
-  // First level: the top kTopkBinBits key bits (sign, exponent, two mantissa bits).  A row's scores
-  // spread over many of those bins, where the top 8 bits alone put nearly all of them in a few and
-  // the LDS atomics of a wave then queue on the same addresses.
+  // First level: the top kTopkBinBits key bits (sign, exponent, two mantissa bits), the same bins
+  // as the long-row select, counted in 16-bit halves of LDS words.
   for (int i = threadIdx.x; i < n; i += blockDim.x) {
     const uint32_t key = score_key(srow[i]);
+    const uint32_t bin = key >> (32 - kTopkBinBits);
     keys[i] = key;
-    atomicAdd(&hist[key >> (32 - kTopkBinBits)], 1u);
+    atomicAdd(&hpk[bin >> 1], 1u << ((bin & 1u) * 16u));
   }
   __syncthreads();
-  find_two_bins_from_top_block<kRowThreads>(hist, m, m, scan, res);
+  find_packed_bin_from_top<kRowThreads>(hpk, m, scan, res);
   uint32_t prefix = (uint32_t)res[0] << (32 - kTopkBinBits), pmask = ~0u << (32 - kTopkBinBits);
   int need = m - res[1];
   auto key_at = [&](int i) { return keys[i]; };
