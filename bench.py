@@ -442,6 +442,35 @@ def infinity_cache_gbps(stream, mib: int = 128) -> dict:
     return {"read_gbps": round(read, 1), "copy_gbps": round(copy, 1), "gbps": round(max(read, copy), 1)}
 
 
+def hbm_stream_gbps(stream, read_mib: int = 2048, copy_mib: int = 1024) -> dict:
+    """What plain streaming kernels reach from HBM on this machine, as a secondary yardstick for the
+    step's algorithmic rate: a read-only reduction over read_mib MiB and a device copy of copy_mib
+    MiB (read and write bytes counted), both larger than the 256 MB Infinity Cache."""
+    import torch
+    src = torch.ones(read_mib << 18, dtype=torch.float32, device="cuda")
+    a = torch.ones(copy_mib << 18, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+
+    def rate(fn, nbytes, reps=10):
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                fn()
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record(stream)
+            for _ in range(reps):
+                fn()
+            ev1.record(stream)
+        torch.cuda.synchronize()
+        return nbytes / ((ev0.elapsed_time(ev1) / 1e3) / reps) / 1e9
+
+    read = rate(lambda: src.sum(), read_mib << 20)
+    copy = rate(lambda: b.copy_(a), 2 * (copy_mib << 20))
+    del src, a, b
+    torch.cuda.empty_cache()
+    return {"read_mib": read_mib, "read_gbps": round(read, 1), "copy_mib": copy_mib, "copy_gbps": round(copy, 1),
+            "gbps": round(max(read, copy), 1)}
+
+
 def per_layer_bound(w, balg_total: float, ic_gbps: float) -> tuple:
     """The dependent-layer schedule's roofline: the step's algorithmic bytes from HBM at the peak,
     plus the compact K_S/V_S re-read once per layer at the rate measured for cache-resident data.
@@ -882,6 +911,8 @@ def main():
 
     del dw, out, idx, cnt, ws, scores
     torch.cuda.empty_cache()
+    stream_bw = hbm_stream_gbps(stream)
+    log(f"HBM stream rates measured here: {stream_bw}")
     decode_configs = None if args.no_decode_configs else decode_configs_report(
         flush=flush, ic_gbps=per_layer["roofline"]["infinity_cache"]["gbps"] if per_layer else None)
     prefill = None if args.no_prefill else prefill_report()
@@ -905,6 +936,8 @@ def main():
                    "schedule": "layer_batched", "seed": w.seed},
         "hbm_gbps": round(hbm_gbps, 1),
         "step_roofline_frac": round(hbm_gbps / HBM_PEAK_GBPS, 4),
+        "hbm_stream": stream_bw,
+        "step_frac_of_measured_stream": round(hbm_gbps / stream_bw["gbps"], 4),
         "bytes_alg_per_step": balg["total"],
         "step_timing": {"protocol": f"HIP events around each step; a {FLUSH_MIB} MiB read before every step, outside "
                                     "its events; median over the steps (the step's first kernel starts about 5.5 us "
