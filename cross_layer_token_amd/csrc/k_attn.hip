@@ -622,6 +622,8 @@ __global__ __launch_bounds__(64 * kPfaWaves, 2) void k_prefill_attn(AttnArgs a) 
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       if constexpr (BUF) {
+        // exact in 24 bits: the launch keeps max_row_len * row_bytes below 2^31, so the id is
+        // below 2^23 and the product below 2^31
         const uint32_t off = __umul24((uint32_t)id[i], row_bytes) + lane_off;
         kr[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
         vr[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
