@@ -622,8 +622,8 @@ __global__ __launch_bounds__(64 * kPfaWaves, 2) void k_prefill_attn(AttnArgs a) 
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       if constexpr (BUF) {
-        // exact in 24 bits: the launch keeps max_row_len * row_bytes below 2^31, so the id is
-        // below 2^23 and the product below 2^31
+        // exact in 24 bits: the launch keeps row_bytes below 2^24 and max_row_len * row_bytes
+        // below 2^31, so the id is below 2^23 and the product below 2^31
         const uint32_t off = __umul24((uint32_t)id[i], row_bytes) + lane_off;
         kr[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
         vr[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
@@ -889,8 +889,9 @@ int launch_attn(const RowsDev& rows, int k, int hq, int hkv, int n_layers_call, 
     a.qblocks = (plan.qrows + kPfaCols - 1) / kPfaCols;
     const dim3 grid((unsigned)(a.qblocks * hkv), (unsigned)rows.n_rows);
     // buffer loads when a 32-bit byte offset reaches every visible row (device row lengths are
-    // clamped to max_row_len)
-    if ((int64_t)rows.max_row_len * hkv * CLSA_HEAD_DIM * 2 <= (int64_t)INT32_MAX)
+    // clamped to max_row_len) and the row stride fits the 24-bit multiply that forms it
+    const int64_t row_bytes = (int64_t)hkv * CLSA_HEAD_DIM * 2;
+    if ((int64_t)rows.max_row_len * row_bytes <= (int64_t)INT32_MAX && row_bytes < ((int64_t)1 << 24))
       hipLaunchKernelGGL(k_prefill_attn<true>, grid, dim3(64 * kPfaWaves), 0, s, a);
     else
       hipLaunchKernelGGL(k_prefill_attn<false>, grid, dim3(64 * kPfaWaves), 0, s, a);
