@@ -569,6 +569,22 @@ def test_step_per_layer_chunks_with_caller_buffers():
     assert np.array_equal(ksel[2, :, :100].permute(1, 0, 2).cpu().numpy().view(np.uint16), w.kv_bits(toks, "k"))
 
 
+def test_step_decode_several_query_blocks_per_kv_head():
+    """128 query rows per KV head (8 layers x a GQA group of 16): two 64-row query blocks per
+    (row, KV head), each with its own split partials and ticket, and one selection finished by the
+    first block's first split.  Both schedules, every row against the C++ oracle."""
+    w = cs.custom(seq_lens=(20000, 15000, 30000), d_idx=64, topk=512, n_layers=8, hq=32, hkv=2, needles=2, seed=79,
+                  name="decode_qblocks")
+    dw = device_workload(w)
+    ref = _cpp_rows(w, range(w.n_rows))
+    for schedule in (clsa.SCHEDULE_LAYER_BATCHED, clsa.SCHEDULE_PER_LAYER):
+        idx, cnt, out = _run_step(dw, schedule)
+        dev = bf16_dev_to_f64(out)
+        for r in range(w.n_rows):
+            assert cnt[r] == ref["count"][r] and np.array_equal(idx[r], ref["idx"][r]), f"schedule {schedule} row {r}"
+            assert_outputs_close(dev[r], ref["out"][r], f"query blocks, schedule {schedule}, row {r}")
+
+
 def test_step_decode_at_the_largest_k():
     """k = CLSA_MAX_TOPK = 65536 of a 100000-token row (one KV head, so one attention block split
     16 ways over 4096 keys each): selection and attention against the oracle, both schedules."""
