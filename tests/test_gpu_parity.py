@@ -585,6 +585,23 @@ def test_step_decode_several_query_blocks_per_kv_head():
             assert_outputs_close(dev[r], ref["out"][r], f"query blocks, schedule {schedule}, row {r}")
 
 
+def test_step_decode_many_blocks_in_one_team():
+    """1024 (row, KV head, query block) blocks of 64 query rows (128 rows x 4 KV heads x two
+    blocks of a 128-row GQA group): four-wave workgroups, two per CU, one team each and no key
+    split, since blocks with two query blocks per head do not pair KV heads.  Both schedules,
+    every row against the C++ oracle."""
+    w = cs.custom(seq_lens=tuple(700 + 13 * i for i in range(128)), d_idx=64, topk=256, n_layers=8, hq=64, hkv=4,
+                  seed=83, name="decode_one_team")
+    dw = device_workload(w)
+    ref = _cpp_rows(w, range(w.n_rows))
+    for schedule in (clsa.SCHEDULE_LAYER_BATCHED, clsa.SCHEDULE_PER_LAYER):
+        idx, cnt, out = _run_step(dw, schedule)
+        dev = bf16_dev_to_f64(out)
+        for r in range(w.n_rows):
+            assert cnt[r] == ref["count"][r] and np.array_equal(idx[r], ref["idx"][r]), f"schedule {schedule} row {r}"
+            assert_outputs_close(dev[r], ref["out"][r], f"one team, schedule {schedule}, row {r}")
+
+
 def test_step_decode_at_the_largest_k():
     """k = CLSA_MAX_TOPK = 65536 of a 100000-token row (one KV head, so one attention block split
     16 ways over 4096 keys each): selection and attention against the oracle, both schedules."""
