@@ -185,8 +185,43 @@ inline float softmax_scale(const clsa_dims* d) {
 
 // Distillation target and loss (eq. 4-5): keys per KL partial, and the workspace layout.
 constexpr int kDistillKeyBlock = 256;
+// The KL pass's causal tiles of kDistillRowBlock positions x kDistillKeyBlock keys, row-block-major.
+// Full row block r (positions pos0 + 32 r .. pos0 + 32 r + 31) sees key blocks
+// 0 .. floor((pos0 + 32 r + 31) / 256) = floor((a + r) / 8), with a = floor((pos0 + 31) / 32); the
+// last row block, possibly partial, sees key blocks 0 .. floor((pos0 + n_rows - 1) / 256).
+constexpr int kDistillRowBlock = 32;
+static_assert(kDistillKeyBlock == 8 * kDistillRowBlock, "eight row blocks per key block");
+CLSA_HOST_DEVICE inline int64_t kl_floor8_sum(int64_t x) {  // sum over y < x of floor(y / 8)
+  const int64_t q = x >> 3, r = x & 7;
+  return 4 * q * (q - 1) + r * q;
+}
+// tiles of the full row blocks below r
+CLSA_HOST_DEVICE inline int64_t kl_prefix(int64_t a, int64_t r) { return r + kl_floor8_sum(a + r) - kl_floor8_sum(a); }
+CLSA_HOST_DEVICE inline int64_t kl_tile_count(int pos0, int n_rows) {
+  const int64_t a = (pos0 + 31) / 32;
+  const int64_t last_rb = (n_rows - 1) / kDistillRowBlock;
+  return kl_prefix(a, last_rb) + ((int64_t)pos0 + n_rows - 1) / kDistillKeyBlock + 1;
+}
+// Row block and key block of tile t < kl_tile_count(pos0, n_rows): a binary search over the prefix.
+CLSA_HOST_DEVICE inline void kl_tile(int pos0, int n_rows, int64_t t, int* rb_out, int* kb_out) {
+  const int64_t a = (pos0 + 31) / 32;
+  const int last_rb = (n_rows - 1) / kDistillRowBlock;
+  const int64_t last0 = kl_prefix(a, last_rb);
+  int rb = last_rb;
+  if (t < last0) {
+    int lo = 0, hi = last_rb;  // prefix(lo) <= t < prefix(hi)
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (kl_prefix(a, mid) <= t) lo = mid; else hi = mid;
+    }
+    rb = lo;
+  }
+  *rb_out = rb;
+  *kb_out = (int)(t - kl_prefix(a, rb));
+}
 struct DistillPlan {
   int n_kb = 0;           // key blocks of kDistillKeyBlock per row
+  int64_t kl_tiles = 0;   // workgroups of the KL pass: kl_tile_count(pos0, n_rows)
   size_t lse2_off = 0;    // fp32 [R, L * hq]
   size_t lse_i_off = 0;   // fp32 [R]
   size_t part_off = 0;    // fp32 [R, n_kb]

@@ -20,8 +20,9 @@
 //     fixed order into one partial per (position, 256-key block).
 // k_row_lse gives the log-sum-exp of each row of I, k_distill_rowsum sums the partials of every
 // position and k_distill_loss the rows, each in a fixed order, so the results do not depend on
-// timing.  The exp2 of every score in both passes, not the matrix cores, bounds the time: a
-// wave issues one v_exp_f32 per score, against 1/16 of a 16x16x32 MFMA.
+// timing.  The vector ALU, not the matrix cores, bounds both passes: per 64 scores a wave spends
+// 24 SIMD cycles on the exp2 (quarter rate), its fma and the add, against 16 cycles of MFMA for
+// the q.k products.
 #include "device_common.h"
 
 namespace clsa {
@@ -39,7 +40,7 @@ constexpr int kStatTilesPerStep = 2;                    // 64-key tiles per LDS 
 constexpr int kKlWaves = 4;
 constexpr int kKlThreads = 64 * kKlWaves;
 constexpr int kKlBlocksPerCU = 3;
-constexpr int kKlRows = 32;                              // positions per KL workgroup
+constexpr int kKlRows = kDistillRowBlock;                // positions per KL workgroup
 constexpr int kKlTq = kKlRows / 16;                      // 16-position MFMA blocks
 constexpr int kKlKeysPerWave = 64;
 constexpr int kKlKeys = kKlWaves * kKlKeysPerWave;       // keys per KL workgroup
@@ -69,6 +70,7 @@ struct DistillArgs {
   float* part;            // [n_rows, n_kb]
   float* kl;              // [n_rows]
   float* loss;            // [1] or null
+  int64_t kl_tiles;       // workgroups of the KL pass, one per causal tile
 };
 
 // Byte offset, in a tile of 64 rows x 128 bf16, of the 16-byte chunk `chunk` of row `row`: chunk
@@ -105,7 +107,9 @@ __global__ __launch_bounds__(kDstThreads) void k_distill_stats(DistillArgs a) {
   char* const lds_bytes = reinterpret_cast<char*>(lds);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, grp = lane >> 4;
-  const int r0 = blockIdx.x * kStatRows;
+  // row blocks last first: a block's work grows with its positions, so within each KV head the
+  // longest blocks are dispatched first and the grid ends on short ones
+  const int r0 = (int)(gridDim.x - 1 - blockIdx.x) * kStatRows;
   const int g = blockIdx.y % a.hkv, chunk = blockIdx.y / a.hkv;
   const int last_row = (r0 + kStatRows < a.n_rows ? r0 + kStatRows : a.n_rows) - 1;
   const int t_lo = a.pos0 + r0, t_hi = a.pos0 + last_row;  // keys 0 .. t_hi are read
@@ -257,11 +261,20 @@ __global__ __launch_bounds__(kKlThreads, kKlBlocksPerCU) void k_distill_kl(Disti
   char* const q_bytes = reinterpret_cast<char*>(qlds);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, grp = lane >> 4;
-  const int kb = blockIdx.x, r0 = blockIdx.y * kKlRows;
+  // one workgroup per causal tile (kl_tile in clsa_internal.h), and no others: a 2-D grid over
+  // every (key block, row block) pair holds about as many tiles past the diagonal as before it,
+  // and those workgroups, though they exit at once, still wait for a free slot to be dispatched
+  // (on the 8192-position workload fewer than half the slots were busy, and the pass took 3.8 ms
+  // instead of 2.4)
+  const int64_t tile = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+  if (tile >= a.kl_tiles) return;  // the last grid row of a call with more than 2^23 tiles
+  int kb, rb;
+  kl_tile(a.pos0, a.n_rows, tile, &rb, &kb);
+  const int r0 = rb * kKlRows;
   const int last_row = (r0 + kKlRows < a.n_rows ? r0 + kKlRows : a.n_rows) - 1;
   const int t_hi = a.pos0 + last_row;
   const int k0 = kb * kKlKeys;
-  if (k0 > t_hi) return;  // the whole key block lies past every position of the tile
+  if (k0 > t_hi) return;  // not a tile of the list (never true for tiles below kl_tile_count)
   const int wk0 = k0 + wave * kKlKeysPerWave;
   const bool wave_active = wk0 <= t_hi;
   const int P = a.L * a.hq;
@@ -479,8 +492,11 @@ int launch_distill(const RowsDev& rows, int64_t total_tokens, int L, int hq, int
   hipLaunchKernelGGL(k_row_lse, dim3((unsigned)rows.n_rows), dim3(256), 0, s, a);
   hipLaunchKernelGGL(k_distill_stats, dim3((unsigned)((rows.n_rows + kStatRows - 1) / kStatRows), (unsigned)(hkv * chunks)),
                      dim3(kDstThreads), 0, s, a);
-  hipLaunchKernelGGL(k_distill_kl, dim3((unsigned)plan.n_kb, (unsigned)((rows.n_rows + kKlRows - 1) / kKlRows)),
-                     dim3(kKlThreads), 0, s, a);
+  a.kl_tiles = plan.kl_tiles;
+  // at most 2^23 workgroups per grid row (2^31 threads), further rows for larger calls
+  const unsigned kl_x = (unsigned)(plan.kl_tiles < (1 << 23) ? plan.kl_tiles : (1 << 23));
+  const unsigned kl_y = (unsigned)((plan.kl_tiles + kl_x - 1) / kl_x);
+  hipLaunchKernelGGL(k_distill_kl, dim3(kl_x, kl_y), dim3(kKlThreads), 0, s, a);
   hipLaunchKernelGGL(k_distill_rowsum, dim3((unsigned)((rows.n_rows + kRowSumThreads / 64 - 1) / (kRowSumThreads / 64))),
                      dim3(kRowSumThreads), 0, s, a);
   if (loss != nullptr) hipLaunchKernelGGL(k_distill_loss, dim3(1), dim3(kLossThreads), 0, s, a);

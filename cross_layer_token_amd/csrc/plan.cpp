@@ -231,6 +231,7 @@ DistillPlan plan_distill(const clsa_dims* d, const clsa_rows* r) {
   DistillPlan p;
   const size_t R = (size_t)r->n_rows;
   p.n_kb = (r->max_row_len + kDistillKeyBlock - 1) / kDistillKeyBlock;
+  p.kl_tiles = kl_tile_count(r->pos0, r->n_rows);
   size_t off = 0;
   p.lse2_off = off;
   off = align_up(off + R * d->n_layers * d->hq * 4, 256);

@@ -248,6 +248,21 @@ def test_prefill_score_tiles_cover_the_causal_triangle_once(tmp_path):
     assert r.returncode == 0 and r.stdout.startswith("ok"), r.stdout
 
 
+def test_distill_kl_tiles_cover_the_causal_triangle_once(tmp_path):
+    """The distillation KL pass launches one workgroup per causal 32-position x 256-key tile: compiled
+    with g++ (with the address and undefined-behaviour sanitizers) and swept over call offsets and
+    row counts, every tile index maps to a distinct tile holding a visible (position, key) pair, and
+    every such tile is reached; the 2^24-position call, whose tiles fill more than one grid row, maps
+    its ends correctly."""
+    import subprocess
+    here = os.path.dirname(os.path.abspath(__file__))
+    exe = str(tmp_path / "distill_tiles")
+    subprocess.run(["g++", "-std=c++17", "-O1", "-Wall", "-fsanitize=address,undefined", "-o", exe,
+                    os.path.join(here, "host", "distill_tiles.cpp")], check=True)
+    r = subprocess.run([exe], stdout=subprocess.PIPE, text=True, env={**os.environ, "LD_PRELOAD": ""})
+    assert r.returncode == 0 and r.stdout.startswith("ok"), r.stdout
+
+
 def test_per_layer_workspace_gathers_in_cache_sized_chunks():
     """The per-layer decode schedule gathers the compact K_S/V_S of a chunk of rows at a time (at most
     192 MiB, inside the 256 MB Infinity Cache): for 64 rows of 131072 tokens with k = 2048 and 8 KV
