@@ -200,15 +200,23 @@ __global__ __launch_bounds__(kDstThreads) void k_distill_stats(DistillArgs a) {
 #pragma unroll
             for (int qb = 0; qb < kStatPairsPerWave; ++qb) s[qb][mt][j] = -INFINITY;
     }
+    // The maxima use the NaN-propagating maximum: three operands per instruction and no
+    // canonicalisation of the MFMA results, which the IEEE maxNum of fmaxf needs on each input
+    // (the scores are finite or -inf, so both give the same value).
+    auto max3 = [](float x, float y, float z) {
+      return __builtin_elementwise_maximum(__builtin_elementwise_maximum(x, y), z);
+    };
 #pragma unroll
     for (int qb = 0; qb < kStatPairsPerWave; ++qb) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) mx = fmaxf(fmaxf(mx, fmaxf(s[qb][mt][0], s[qb][mt][1])), fmaxf(s[qb][mt][2], s[qb][mt][3]));
+      const floatx4_t* v = s[qb];  // 16 scores: a tree of eight three-operand maxima
+      float mx = max3(max3(v[0][0], v[0][1], v[0][2]), max3(v[0][3], v[1][0], v[1][1]),
+                      max3(v[1][2], v[1][3], v[2][0]));
+      mx = max3(mx, max3(v[2][1], v[2][2], v[2][3]), max3(v[3][0], v[3][1], v[3][2]));
+      mx = __builtin_elementwise_maximum(mx, v[3][3]);
       if (__any(mx * c > m_run[qb] + kRescaleLog2)) {
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = fmaxf(m_run[qb], mx * c);
+        mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 16, 64));
+        mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 32, 64));
+        const float m_new = __builtin_elementwise_maximum(m_run[qb], mx * c);
         l_run[qb] *= __builtin_amdgcn_exp2f(m_run[qb] - m_new);
         m_run[qb] = m_new;
       }
