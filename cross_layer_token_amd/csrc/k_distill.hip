@@ -20,9 +20,8 @@
 //     fixed order into one partial per (position, 256-key block).
 // k_row_lse gives the log-sum-exp of each row of I, k_distill_rowsum sums the partials of every
 // position and k_distill_loss the rows, each in a fixed order, so the results do not depend on
-// timing.  The vector ALU, not the matrix cores, bounds both passes: per 64 scores a wave spends
-// 24 SIMD cycles on the exp2 (quarter rate), its fma and the add, against 16 cycles of MFMA for
-// the q.k products.
+// timing.  The vector ALU, not the matrix cores, bounds both passes: every score costs one exp2,
+// one fma and one add, against 1/16 of a 16x16x32 MFMA for the q.k products.
 #include "device_common.h"
 
 namespace clsa {
