@@ -34,6 +34,8 @@ constexpr int kStatRows = 16;                          // positions per stats wo
 constexpr int kStatPairsPerWave = 4;
 constexpr int kStatPairs = kDstWaves * kStatPairsPerWave;
 constexpr int kStatTilesPerStep = 2;                    // 64-key tiles per LDS step
+constexpr int kStatPieces = 64 * 16 / kDstThreads;      // 16-byte pieces of a 64-key tile per thread
+static_assert(kStatPieces * kDstThreads == 64 * 16, "whole tile pieces per thread");
 // KL pass: four-wave workgroups of 32 positions x 256 keys, three per CU (each wave keeps its 64
 // keys of the current KV head in registers and accumulates 64 keys x 32 positions of A)
 constexpr int kKlWaves = 4;
@@ -133,22 +135,22 @@ __global__ __launch_bounds__(kDstThreads) void k_distill_stats(DistillArgs a) {
       qf[qb][kk] = bitcast<bf16x8_t>(v);
     }
   }
-  // loader: 64 keys x 16 chunks per tile, two pieces per thread; keys past t_hi re-read t_hi
+  // loader: 64 keys x 16 chunks per tile, kStatPieces pieces per thread; keys past t_hi re-read t_hi
   const int64_t kbase = (seq_base * a.hkv + g) * CLSA_HEAD_DIM;
-  int lkey[2], lchunk[2], soff[2];
+  int lkey[kStatPieces], lchunk[kStatPieces], soff[kStatPieces];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < kStatPieces; ++i) {
     const int piece = threadIdx.x + i * kDstThreads;
     lkey[i] = piece >> 4;
     lchunk[i] = piece & 15;
     soff[i] = tile_off(lkey[i], lchunk[i]);
   }
-  uint4 rk[kStatTilesPerStep][2];
+  uint4 rk[kStatTilesPerStep][kStatPieces];
   auto load_step = [&](int st) {
 #pragma unroll
     for (int u = 0; u < kStatTilesPerStep; ++u)
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < kStatPieces; ++i) {
         int key = (st * kStatTilesPerStep + u) * kTileKeys + lkey[i];
         key = key < key_cap ? key : key_cap;
         rk[u][i] = load16(a.k + kbase + (int64_t)key * a.hkv * CLSA_HEAD_DIM + lchunk[i] * 8);
@@ -237,7 +239,7 @@ __global__ __launch_bounds__(kDstThreads) void k_distill_stats(DistillArgs a) {
 #pragma unroll
     for (int u = 0; u < kStatTilesPerStep; ++u)
 #pragma unroll
-      for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(sb + u * kTileBytes + soff[i]) = rk[u][i];
+      for (int i = 0; i < kStatPieces; ++i) *reinterpret_cast<uint4*>(sb + u * kTileBytes + soff[i]) = rk[u][i];
     __syncthreads();  // one barrier per step: buffer st & 1 was last read two steps ago
     if (st + 1 < steps) load_step(st + 1);
     if (!wave_active) continue;
