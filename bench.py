@@ -606,7 +606,7 @@ def prefill_report(steps: int = 3, chunk: int = 8192) -> dict:
             "index_gemm_mfma_frac": round(idx_flop / t_idx / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
 
 
-def distill_report(reps: int = 3) -> dict:
+def distill_report(reps: int = 7) -> dict:
     """The multi-layer distillation target and loss (eq. 4-5) over all 8192 positions of the
     prefill workload (L = 8, Hq = 32, Hkv = 8), from the routing scores.  Two passes over every
     causal (position, key) pair for each of the L * Hq (layer, head) pairs: bf16 MFMA work against
@@ -636,18 +636,23 @@ def distill_report(reps: int = 3) -> dict:
             clsa.distill_kl(dims, rows, dw.q, L * hq * 128, dw.k_cache, dw.cu_seqlens, scores, ld, kl, loss, ws, nws,
                             stream=stream)
 
-    run(1)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    run(reps)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    t = (ev0.elapsed_time(ev1) / 1e3) / reps
-    log(f"distillation: {t * 1e3:.3f} ms")
+    run(2)
+    times = []
+    for _ in range(reps):  # each call timed on its own, the median reported
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        run(1)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        times.append(ev0.elapsed_time(ev1) / 1e3)
+    times.sort()
+    t = times[len(times) // 2]
+    log(f"distillation: {t * 1e3:.3f} ms (min {times[0] * 1e3:.3f}, max {times[-1] * 1e3:.3f})")
     pairs = R * (R + 1) // 2                          # causal (position, key) pairs
     flop = 2 * pairs * L * hq * w.head_dim * 2         # two passes of q.k, 2 flop per MAC
     exps = 2 * pairs * L * hq                          # one exp2 per score and pass
     return {"workload": w.name, "rows": R, "layers": L, "heads": hq, "reps": reps, "ms": round(t * 1e3, 3),
+            "ms_min": round(times[0] * 1e3, 3), "ms_max": round(times[-1] * 1e3, 3),
             "mfma_tflops": round(flop / t / 1e12, 1), "mfma_frac": round(flop / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
             "exp_per_s": float(f"{exps / t:.4g}"), "exp_frac": round(exps / t / EXP2_PEAK_PER_S, 4),
             "loss": round(float(loss.cpu()[0]), 6)}
