@@ -770,3 +770,90 @@ def test_step_k_at_least_n_is_dense_attention():
         assert cnt[b] == n and np.array_equal(idx[b, :n], np.arange(n))
         kf, vf = w.kv_f64(cu[b] + np.arange(n))
         assert_outputs_close(dev[b], O.sparse_attention(w.q_f64([b])[0], kf, vf), f"dense row {b}")
+
+
+# ---- seeded random shapes ---------------------------------------------------------------------
+# Shapes drawn once from a fixed seed, so the cases are the same on every run.  k and the
+# (query head, KV head) counts cycle through their lists (every value appears); batch sizes,
+# sequence lengths from 1 token to tens of thousands (some exactly k - 1, k or k + 1), 1 to 6
+# layers, both indexer widths and the needles are drawn; every third decode shape has tie-heavy
+# indexer values and every fifth one sequence of 100K-140K tokens.  They reach the plan's choices (one or two
+# teams, paired KV heads, 1 to 16 splits, the fused or separate selection, the LDS or span-list
+# top-k) in combinations the named cases above do not.
+_HEADS = [(4, 4), (8, 2), (16, 4), (32, 8), (12, 3), (6, 1), (8, 8), (2, 1)]
+_KS = [1, 7, 100, 512, 1500, 2048, 3000]
+
+
+def _decode_draws(n=20, seed=2024):
+    rng = np.random.default_rng(seed)
+    draws = []
+    for i in range(n):
+        k = _KS[i % len(_KS)]
+        b = int(rng.integers(1, 17))
+        lens = [max(1, int(np.exp(rng.uniform(0.0, np.log(30000))))) for _ in range(b)]
+        for j in range(b):
+            if rng.random() < 0.2:
+                lens[j] = max(1, k + int(rng.integers(-1, 2)))
+        if i % 5 == 4:  # one long sequence: the multi-workgroup select over many spans
+            lens[0] = int(rng.integers(100000, 140001))
+        hq, hkv = _HEADS[i % len(_HEADS)]
+        ties = i % 3 == 0
+        draws.append(dict(seq_lens=tuple(lens), topk=k, n_layers=int(rng.integers(1, 7)), hq=hq, hkv=hkv,
+                          d_idx=int(rng.choice([64, 128])), needles=int(rng.choice([0, 2])) if min(lens) >= 2 else 0,
+                          idx_lo=-1 if ties else -8, idx_hi=1 if ties else 8, idx_den=4 if ties else 8,
+                          seed=1000 + i, name=f"random_decode_{i}"))
+    return draws
+
+
+def _prefill_draws(n=10, seed=4096):
+    rng = np.random.default_rng(seed)
+    draws = []
+    for i in range(n):
+        length = int(rng.integers(50, 1201))
+        row0 = 0 if rng.random() < 0.5 else int(rng.integers(0, length))
+        n_rows = length - row0 if rng.random() < 0.5 else int(rng.integers(1, length - row0 + 1))
+        chunk = 0 if rng.random() < 0.3 else int(rng.integers(1, n_rows + 1))
+        hq, hkv = _HEADS[(3 * i + 1) % len(_HEADS)]
+        draws.append(dict(w=dict(mode="prefill", seq_lens=(length,), topk=[1, 50, 256, 1000, 3000][i % 5],
+                                 n_layers=int(rng.integers(1, 5)), hq=hq, hkv=hkv, d_idx=int(rng.choice([64, 128])),
+                                 needles=int(rng.choice([0, 2])), seed=2000 + i, name=f"random_prefill_{i}"),
+                          row0=row0, n_rows=n_rows, chunk=chunk))
+    return draws
+
+
+@pytest.mark.parametrize("draw", _decode_draws(), ids=lambda d: d["name"])
+def test_step_decode_random_shapes(draw):
+    """A seeded random decode shape: every row against the C++ oracle, both schedules."""
+    w = cs.custom(**draw)
+    dw = device_workload(w)
+    ref = _cpp_rows(w, range(w.n_rows))
+    for schedule in (clsa.SCHEDULE_LAYER_BATCHED, clsa.SCHEDULE_PER_LAYER):
+        idx, cnt, out = _run_step(dw, schedule)
+        dev = bf16_dev_to_f64(out)
+        for r in range(w.n_rows):
+            assert cnt[r] == ref["count"][r] == min(w.topk, w.row_len(r)), (schedule, r)
+            assert np.array_equal(idx[r], ref["idx"][r]), f"schedule {schedule} row {r}: index mismatch"
+            assert_outputs_close(dev[r], ref["out"][r], f"{w.name} schedule {schedule} row {r}")
+    _say(f"{w.name}: B={w.batch} k={w.topk} L={w.n_layers} hq/hkv={w.hq}/{w.hkv} d_idx={w.d_idx} match")
+
+
+@pytest.mark.parametrize("draw", _prefill_draws(), ids=lambda d: d["w"]["name"])
+def test_step_prefill_random_shapes(draw):
+    """A seeded random prefill call (start position, row count and chunk drawn too): every row of
+    the call, or about 150 of them for long calls, against the C++ oracle, both schedules."""
+    w = cs.custom(**draw["w"])
+    dw = device_workload(w)
+    row0, n_rows, chunk = draw["row0"], draw["n_rows"], draw["chunk"]
+    pos = list(range(row0, row0 + n_rows))
+    if len(pos) > 150:
+        pos = sorted(set(pos[::len(pos) // 100]) | set(pos[-20:]) | {p for p in pos if abs(p - w.topk) <= 2})
+    ref = _cpp_rows(w, pos)
+    for schedule in (clsa.SCHEDULE_LAYER_BATCHED, clsa.SCHEDULE_PER_LAYER):
+        idx, cnt, out = _run_step(dw, schedule, rows_kw=dict(row0=row0, n_rows=n_rows), chunk=chunk)
+        assert np.array_equal(cnt, np.minimum(np.arange(row0 + 1, row0 + n_rows + 1), w.topk))
+        dev = bf16_dev_to_f64(out)
+        for i, t in enumerate(pos):
+            assert np.array_equal(idx[t - row0], ref["idx"][i]), f"schedule {schedule} position {t}: index mismatch"
+            assert_outputs_close(dev[t - row0], ref["out"][i], f"{w.name} schedule {schedule} position {t}")
+    _say(f"{w.name}: rows {row0}..{row0 + n_rows - 1} chunk {chunk} k={w.topk} L={w.n_layers} "
+         f"hq/hkv={w.hq}/{w.hkv}: {len(pos)} positions match")
