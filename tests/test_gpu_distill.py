@@ -161,3 +161,46 @@ def test_distill_prefill_8k_sampled_rows():
         _say(f"8k row {r}: dev {kl[r]:.6f} ref {ref['kl']:.6f} err {err:.2e} bound {bound:.2e}")
     assert abs(loss - kl.mean()) <= 1e-5 * max(1.0, abs(kl.mean()))
     _say(f"8k: worst error / bound {worst:.3f}, loss {loss:.5f}")
+
+
+def _distill_draws(n=6, seed=5150):
+    """Prefill calls drawn from a fixed seed: sequence length, start position and row count, 1 to
+    6 layers, one to six query heads per KV head (up to 36 (layer, head) pairs per KV head, past
+    one stats workgroup's 32), both indexer widths and three attention scales."""
+    heads = [(8, 2), (6, 1), (32, 8), (12, 3), (4, 4), (2, 1)]
+    scales = [0.0, 1.0, 0.05]
+    rng = np.random.default_rng(seed)
+    draws = []
+    for i in range(n):
+        length = int(rng.integers(40, 901))
+        row0 = 0 if i % 2 == 0 else int(rng.integers(1, length))
+        n_rows = int(rng.integers(1, length - row0 + 1))
+        hq, hkv = heads[i % len(heads)]
+        n_layers = 6 if hq // hkv == 6 else int(rng.integers(1, 7))
+        draws.append(dict(w=dict(mode="prefill", seq_lens=(length,), d_idx=int(rng.choice([64, 128])), topk=16,
+                                 n_layers=n_layers, hq=hq, hkv=hkv, seed=3000 + i,
+                                 name=f"distill_random_{i}"),
+                          row0=row0, n_rows=n_rows, scale=scales[i % len(scales)]))
+    return draws
+
+
+@pytest.mark.parametrize("draw", _distill_draws(), ids=lambda d: d["w"]["name"])
+def test_distill_random_shapes(draw):
+    """A seeded random prefill call: up to about 60 of its rows (the first, the last, the rows
+    around the 32-position and 256-key block edges and an even spread) against the oracle, and the
+    loss against the mean of the call's KL values."""
+    w = cs.custom(**draw["w"])
+    dw = device_workload(w)
+    row0, n_rows, scale = draw["row0"], draw["n_rows"], draw["scale"]
+    kl, loss = _run(dw, rows_kw=dict(row0=row0, n_rows=n_rows), sm_scale=scale)
+    pos = set(range(row0, row0 + n_rows, max(1, n_rows // 40))) | {row0, row0 + n_rows - 1}
+    pos |= {t for t in range(row0, row0 + n_rows) if t % 32 in (0, 31) and t % 256 < 64}
+    pos = sorted(pos)[:60] + [row0 + n_rows - 1]
+    worst = 0.0
+    for t in sorted(set(pos)):
+        ref = oracle_distill_row(w, t, scale=None if scale == 0.0 else scale)
+        err, bound = _check(kl[t - row0], ref, f"{w.name} position {t}")
+        worst = max(worst, err / bound)
+    assert abs(loss - kl.mean()) <= 1e-6 * max(1.0, abs(kl.mean()))
+    _say(f"{w.name}: positions {row0}..{row0 + n_rows - 1} L={w.n_layers} hq/hkv={w.hq}/{w.hkv} "
+         f"scale={scale}: worst error / bound {worst:.3f}")
