@@ -176,6 +176,58 @@ PREFILL_COUNTER_COMMANDS = {
 PREFILL_KERNELS = (("k_index_scores_prefill<128>", "k_index_scores_prefill"),
                    ("k_prefill_attn (prefill attention)", "k_prefill_attn"),
                    ("k_topk_rows_lds", "k_topk_rows_lds"))
+# one pass of eight SQ counters and the GPU's active cycles over the prefill step and the
+# distillation passes (their issue and residency picture)
+SQ_COUNTERS = ("SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_VALU "
+               "SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_LDS SQ_INSTS_VALU_TRANS_F32 GRBM_GUI_ACTIVE")
+SQ_COUNTER_COMMAND = (f"rocprofv3 --pmc {SQ_COUNTERS} --output-format csv -d rocprof_out/prefill_sq -o bench -- "
+                      "python3 bench.py --prefill-only --prefill-steps 1")
+SQ_KERNELS = (("k_prefill_attn<true>", "k_prefill_attn"), ("k_index_scores_prefill<128>", "k_index_scores_prefill"),
+              ("k_topk_rows_lds", "k_topk_rows_lds"), ("k_row_lse", "k_row_lse"),
+              ("k_distill_stats", "k_distill_stats"), ("k_distill_kl", "k_distill_kl"))
+MI355X_XCDS, MI355X_SIMDS = 8, 1024
+
+
+def summarize_sq_counters(sq_dir: str) -> str:
+    """Issue and residency counters of the prefill and distillation kernels, per launch, from one
+    rocprofv3 pass: resident waves per SIMD, the vector-ALU and MFMA busy shares of the SIMDs'
+    cycles (rocprofv3's VALUBusy and MfmaUtil), the share of resident wave-cycles spent waiting,
+    and the transcendental instructions issued (one v_exp_f32 per score in the distillation)."""
+    import glob
+
+    rr = _csv_rows(sorted(glob.glob(os.path.join(sq_dir, "*_counter_collection.csv")))[0])
+    by = {}
+    for r in rr:
+        d = by.setdefault((r["Kernel_Name"], r["Dispatch_Id"]), {"_us": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    md = ["# Issue and residency counters of the prefill and distillation kernels, prefill_n8k", "",
+          "Made by (on one MI355X):", "", f"    {SQ_COUNTER_COMMAND}",
+          f"    python bench.py --summarize-sq-counters {sq_dir}", "",
+          "The run holds one causal prefill step of the 8192-row workload (8192 rows in one chunk) and the",
+          "distillation target and loss passes over the same positions. Per launch, averaged over the",
+          f"launches: the GPU's active cycles per XCD (GRBM_GUI_ACTIVE over {MI355X_XCDS} XCDs); resident",
+          f"waves per SIMD (SQ_WAVE_CYCLES, in quad-cycles, over {MI355X_SIMDS} SIMDs and the active cycles);",
+          "vector-ALU busy (SQ_ACTIVE_INST_VALU per CU over the active cycles: rocprofv3's VALUBusy); MFMA",
+          "busy (SQ_VALU_MFMA_BUSY_CYCLES per SIMD over the active cycles: rocprofv3's MfmaUtil); the share",
+          "of resident wave-cycles waiting on a dependency or a barrier (SQ_WAIT_ANY) and for issue",
+          "(SQ_WAIT_INST_ANY); and the float32 transcendental instructions issued per launch.", "",
+          "| kernel | launches | us (counter run) | active Mcycles per XCD | waves per SIMD | VALU busy % | MFMA busy % | waiting % | waiting for issue % | exp/log instructions (M) |",
+          "|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    for label, pat in SQ_KERNELS:
+        ds = [d for (name, _), d in by.items() if pat in name and "GRBM_GUI_ACTIVE" in d]
+        if not ds:
+            continue
+
+        def avg(key):
+            return sum(d.get(key, 0.0) for d in ds) / len(ds)
+        act = avg("GRBM_GUI_ACTIVE") / MI355X_XCDS
+        wc = avg("SQ_WAVE_CYCLES")
+        md.append(f"| `{label}` | {len(ds)} | {avg('_us'):.1f} | {act / 1e6:.3f} | "
+                  f"{4 * wc / MI355X_SIMDS / act:.2f} | {400 * avg('SQ_ACTIVE_INST_VALU') / MI355X_SIMDS / act:.1f} | "
+                  f"{100 * avg('SQ_VALU_MFMA_BUSY_CYCLES') / MI355X_SIMDS / act:.1f} | "
+                  f"{100 * avg('SQ_WAIT_ANY') / wc:.1f} | {100 * avg('SQ_WAIT_INST_ANY') / wc:.1f} | "
+                  f"{avg('SQ_INSTS_VALU_TRANS_F32') / 1e6:.1f} |")
+    return "\n".join(md) + "\n"
 
 
 def summarize_prefill_counters(mfma_dir: str, fetch_dir: str, write_dir: str, copy_mib: int = 1024) -> str:
@@ -710,9 +762,16 @@ def main():
     ap.add_argument("--prefill-only", action="store_true",
                     help="run only the prefill report (and the distillation report unless --no-distill)")
     ap.add_argument("--prefill-steps", type=int, default=3)
+    ap.add_argument("--summarize-sq-counters", metavar="DIR",
+                    help="write the prefill and distillation kernels' issue and residency summary under profiles/ and exit")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the score kernel's HBM traffic summary under profiles/ and exit")
     args = ap.parse_args()
+    if args.summarize_sq_counters:
+        p = os.path.join(ROOT, "profiles", "counters_issue_prefill_distill_prefill_n8k.md")
+        open(p, "w").write(summarize_sq_counters(args.summarize_sq_counters))
+        print("wrote", p)
+        return
     if args.summarize_prefill_counters:
         p = os.path.join(ROOT, "profiles", "counters_prefill_kernels_prefill_n8k.md")
         open(p, "w").write(summarize_prefill_counters(*args.summarize_prefill_counters))
