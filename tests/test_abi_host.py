@@ -275,3 +275,50 @@ def test_per_layer_workspace_gathers_in_cache_sized_chunks():
     per_row = 2 * 8 * 2048 * 128 * 2
     # the compact buffers of 24 rows, plus the per-layer passes' own split partials
     assert 24 * per_row <= per_layer - batched <= 24 * per_row + (16 << 20)
+
+
+# ---- workspace sizing over arbitrary arguments -------------------------------------------------
+# The sizing calls validate and plan on the host only, so any argument values may be tried here;
+# under tests/test_sanitizers.py this runs against the address- and undefined-behaviour-sanitized
+# build, where a signed overflow or an out-of-bounds read in the planning aborts the run.
+def _sizing_args():
+    from hypothesis import strategies as st
+    i32 = st.one_of(st.integers(-3, 3), st.sampled_from([31, 32, 33, 63, 64, 127, 128, 255, 256, 257, 2047, 2048,
+                                                          2049, 8192, 12288, 12289, 65535, 65536, 65537, 2**20,
+                                                          2**24 - 1, 2**24, 2**24 + 1, 2**30, 2**31 - 1, -(2**31)]),
+                    st.integers(-(2**31), 2**31 - 1))
+    return dict(batch=st.one_of(st.integers(1, 9), i32), d_idx=st.sampled_from([-1, 0, 32, 64, 96, 128, 256]),
+                topk=i32, n_layers=st.one_of(st.integers(-1, 20), i32), hq=st.one_of(st.integers(-1, 64), i32),
+                hkv=st.one_of(st.integers(-1, 16), i32), head_dim=st.sampled_from([64, 128, 128, 128]),
+                sm_scale=st.sampled_from([0.0, -1.0, 0.088, 1.0, float("nan"), float("inf")]),
+                mode=st.sampled_from([0, 1, 1, 0, 2, -1]), n_rows=i32, seq=st.one_of(st.integers(-1, 9), i32),
+                pos0=i32, max_row_len=i32, total_tokens=st.one_of(i32, st.integers(-(2**63), 2**63 - 1)),
+                cu=st.one_of(st.none(), st.lists(st.integers(-5, 2**24 + 5), min_size=1, max_size=10)),
+                schedule=st.sampled_from([0, 1, 2, 3, -1]), chunk=st.one_of(st.integers(-2, 3), i32))
+
+
+def test_workspace_sizing_never_fails_uncleanly():
+    """Any clsa_dims / clsa_rows contents, schedule and chunk: the sizing calls return 0 with an
+    error message or a positive size that is a multiple of 256, and never crash or overflow."""
+    pytest.importorskip("hypothesis")
+    from hypothesis import HealthCheck, given, settings
+
+    @settings(max_examples=600, deadline=None, derandomize=True, database=None,
+              suppress_health_check=list(HealthCheck))
+    @given(**_sizing_args())
+    def check(batch, d_idx, topk, n_layers, hq, hkv, head_dim, sm_scale, mode, n_rows, seq, pos0, max_row_len,
+              total_tokens, cu, schedule, chunk):
+        dims = B.Dims(batch, d_idx, topk, n_layers, hq, hkv, head_dim, sm_scale)
+        # a host cu_seqlens must hold batch + 1 entries; a shorter list is only passed for a
+        # batch it fits (reading past a caller's array is the caller's contract, not tested here)
+        host = cu if cu is not None and 1 <= batch <= len(cu) - 1 else None
+        rows = B.make_rows(mode, n_rows, max_row_len, total_tokens, seq=seq, pos0=pos0,
+                           cu_seqlens_host=host[:batch + 1] if host is not None else None)
+        for n in (B.LIB.clsa_workspace_bytes(ctypes.byref(dims), ctypes.byref(rows), schedule, chunk),
+                  B.LIB.clsa_distill_workspace_bytes(ctypes.byref(dims), ctypes.byref(rows))):
+            if n == 0:
+                assert B.last_error(), "a zero size must leave an error message"
+            else:
+                assert n % 256 == 0, n
+
+    check()
