@@ -334,13 +334,19 @@ __global__ __launch_bounds__(64 * WPT * TEAMS, 64 * WPT * TEAMS == 512 ? 1 : 2) 
         for (int j = 0; j < 4; ++j)
           if (mt * 16 + grp * 4 + j >= nvalid) s[mt][j] = -INFINITY;
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) mx = fmaxf(fmaxf(mx, fmaxf(s[mt][0], s[mt][1])), fmaxf(s[mt][2], s[mt][3]));
+    // the NaN-propagating maximum: three operands per instruction and no canonicalisation of the
+    // MFMA results, which fmaxf's IEEE maxNum needs on each input (the scores are finite or -inf,
+    // so both give the same value)
+    auto max3 = [](float x, float y, float z) {
+      return __builtin_elementwise_maximum(__builtin_elementwise_maximum(x, y), z);
+    };
+    float mx = max3(max3(s[0][0], s[0][1], s[0][2]), max3(s[0][3], s[1][0], s[1][1]), max3(s[1][2], s[1][3], s[2][0]));
+    mx = max3(mx, max3(s[2][1], s[2][2], s[2][3]), max3(s[3][0], s[3][1], s[3][2]));
+    mx = __builtin_elementwise_maximum(mx, s[3][3]);
     if (__any(mx * scale > m_run + kRescaleLog2)) {
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx * scale);
+      mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 16, 64));
+      mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = __builtin_elementwise_maximum(m_run, mx * scale);
       const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
       l_run *= corr;
