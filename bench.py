@@ -599,7 +599,7 @@ def decode_configs_report(configs=(1, 2, 5), steps: int = 50, warmup: int = 10, 
     return out_rep
 
 
-def prefill_report(steps: int = 3, chunk: int = 8192) -> dict:
+def prefill_report(steps: int = 8, chunk: int = 8192) -> dict:
     """The causal chunked-prefill step (8192 rows, k=2048, L=8), reported beside the decode line.
     Its attention FLOPs run against the bf16 MFMA peak. Each row gathers its own selection of K/V
     rows (about 60 GB per step, served from the Infinity Cache and L2), so the gather rate is
@@ -627,13 +627,15 @@ def prefill_report(steps: int = 3, chunk: int = 8192) -> dict:
             clsa.step(dims, rows, dw.q_idx, dw.k_idx, dw.k_cache, dw.v_cache, dw.cu_seqlens, dw.q, out, idx, cnt,
                       ws, nws, prefill_chunk_rows=chunk, stream=stream)
 
-    run(1)
+    run(3)  # warm-up, as for the decode steps
+    step_times, _ = event_times(stream, lambda: run(1), steps)
+    t_step = float(np.median(step_times))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     run(steps)
     torch.cuda.synchronize()
-    t_step = (time.perf_counter() - t0) / steps
-    log(f"prefill step: {t_step * 1e3:.3f} ms")
+    t_wall = (time.perf_counter() - t0) / steps
+    log(f"prefill step: median {t_step * 1e3:.3f} ms (events per step), {t_wall * 1e3:.3f} ms back to back (wall)")
     sel = sum(min(k, t + 1) for t in range(R))                  # selected (row, token) pairs
     attn_flop = 4.0 * sel * L * w.hq * w.head_dim                # QK^T and PV, 2 flop per MAC
     gather_bytes = float(sel) * w.hkv * w.head_dim * 2 * 2       # K and V rows each row reads
@@ -650,7 +652,8 @@ def prefill_report(steps: int = 3, chunk: int = 8192) -> dict:
     t_idx = (ev0.elapsed_time(ev1) / 1e3) / 10
     idx_flop = 2.0 * w.d_idx * (R * (R + 1) // 2)
     return {"workload": w.name, "rows": R, "topk": k, "layers": L, "chunk_rows": chunk, "steps": steps,
-            "ms_per_step": round(t_step * 1e3, 3), "tokens_per_s": round(R / t_step, 1),
+            "ms_per_step": round(t_step * 1e3, 3), "timing": distribution(step_times),
+            "wall_ms_per_step_back_to_back": round(t_wall * 1e3, 3), "tokens_per_s": round(R / t_step, 1),
             "attn_tflops_alg": round(attn_flop / t_step / 1e12, 1),
             "attn_mfma_frac_of_step": round(attn_flop / t_step / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
             "gather_bytes": gather_bytes, "gather_tbps": round(gather_bytes / t_step / 1e12, 2),
@@ -761,7 +764,7 @@ def main():
                     help="write the prefill kernels' counter summary under profiles/ and exit")
     ap.add_argument("--prefill-only", action="store_true",
                     help="run only the prefill report (and the distillation report unless --no-distill)")
-    ap.add_argument("--prefill-steps", type=int, default=3)
+    ap.add_argument("--prefill-steps", type=int, default=8)
     ap.add_argument("--summarize-sq-counters", metavar="DIR",
                     help="write the prefill and distillation kernels' issue and residency summary under profiles/ and exit")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
