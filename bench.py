@@ -203,7 +203,7 @@ def summarize_sq_counters(sq_dir: str) -> str:
     md = ["# Issue and residency counters of the prefill and distillation kernels, prefill_n8k", "",
           "Made by (on one MI355X):", "", f"    {SQ_COUNTER_COMMAND}",
           f"    python bench.py --summarize-sq-counters {sq_dir}", "",
-          "The run holds one causal prefill step of the 8192-row workload (8192 rows in one chunk) and the",
+          "The run holds warm-up and timed causal prefill steps of the 8192-row workload (8192 rows in one chunk) and the",
           "distillation target and loss passes over the same positions. Per launch, averaged over the",
           f"launches: the GPU's active cycles per XCD (GRBM_GUI_ACTIVE over {MI355X_XCDS} XCDs); resident",
           f"waves per SIMD (SQ_WAVE_CYCLES, in quad-cycles, over {MI355X_SIMDS} SIMDs and the active cycles);",
@@ -262,7 +262,7 @@ def summarize_prefill_counters(mfma_dir: str, fetch_dir: str, write_dir: str, co
           "Made by (on one MI355X; each counter pass runs separately):", "",
           *[f"    {c}" for c in PREFILL_COUNTER_COMMANDS.values()],
           f"    python bench.py --summarize-prefill-counters {mfma_dir} {fetch_dir} {write_dir}", "",
-          "The run holds one causal prefill step of the 8192-row workload in one chunk of 8192 rows, then the",
+          "The run holds warm-up and timed causal prefill steps of the 8192-row workload in one chunk of 8192 rows, then the",
           "indexer GEMM alone ten times. `MfmaUtil` is rocprofv3's derived percentage of the SIMDs' MFMA-busy",
           "cycles over the kernel's active cycles; `MfmaFlopsBF16` counts the bf16 MFMA work done (512 per",
           "MOPS); `LdsUtil` is the share of cycles the CUs' LDS is active; `LdsBankConflict` is conflicts per",
@@ -322,7 +322,7 @@ _TRACE_CONTENT = {
                "(scores, top-k and one attention per layer), the new-token indexer projections and cache",
                "append ahead of the step, the Infinity Cache probes (torch reduce and copy) and the",
                "synthetic-input fill."],
-    "prefill": ["The run holds the causal prefill step (8192 rows in one chunk: the causal indexer GEMM, the",
+    "prefill": ["The run holds warm-up and timed causal prefill steps (8192 rows in one chunk: the causal indexer GEMM, the",
                 "per-row top-k, the sparse attention of every row over its own selection), the indexer GEMM",
                 "alone, the distillation target and loss passes, and the synthetic-input fill."],
 }
