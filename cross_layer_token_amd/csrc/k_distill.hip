@@ -28,14 +28,16 @@ namespace clsa {
 
 namespace {
 
+constexpr int kTileKeys = 64;
+constexpr int kTileBytes = kTileKeys * CLSA_HEAD_DIM * 2;  // 16 KB: 64 rows of 256 bytes
 constexpr int kDstWaves = 8;
 constexpr int kDstThreads = 64 * kDstWaves;
 constexpr int kStatRows = 16;                          // positions per stats workgroup
 constexpr int kStatPairsPerWave = 4;
 constexpr int kStatPairs = kDstWaves * kStatPairsPerWave;
 constexpr int kStatTilesPerStep = 2;                    // 64-key tiles per LDS step
-constexpr int kStatPieces = 64 * 16 / kDstThreads;      // 16-byte pieces of a 64-key tile per thread
-static_assert(kStatPieces * kDstThreads == 64 * 16, "whole tile pieces per thread");
+constexpr int kStatPieces = kTileKeys * 16 / kDstThreads;  // 16-byte pieces of a key tile per thread
+static_assert(kStatPieces * kDstThreads == kTileKeys * 16, "whole tile pieces per thread");
 // KL pass: four-wave workgroups of 32 positions x 256 keys, three per CU (each wave keeps its 64
 // keys of the current KV head in registers and accumulates 64 keys x 32 positions of A)
 constexpr int kKlWaves = 4;
@@ -50,8 +52,6 @@ constexpr int kKlQBytes = kKlRows * CLSA_HEAD_DIM * 2;   // one (layer, head) qu
 constexpr int kKlPairsPerStep = 2;                       // (layer, head) query blocks per LDS step
 static_assert(kKlPieces * kKlThreads == kKlRows * 16, "whole query pieces per thread");
 static_assert(kKlKeys == kDistillKeyBlock, "key block of the KL partials");
-constexpr int kTileKeys = 64;
-constexpr int kTileBytes = kTileKeys * CLSA_HEAD_DIM * 2;  // 16 KB: 64 rows of 256 bytes
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kRescaleLog2 = 8.f;
 
